@@ -1,0 +1,183 @@
+/*
+ * csa_mi355x.h — C ABI of the CSA / HCA hybrid-attention hot path for AMD
+ * Instinct MI355X (CDNA4, gfx950).
+ *
+ * The method (DeepSeek-V4 summaries: hyper.ai "Method", CSA and HCA
+ * paragraphs; aiboss88 "Technical Principles", CSA / HCA / FP4 bullets):
+ *   CSA  compresses every m tokens of the (single, MQA-shared) KV head into one
+ *        entry, scores entries with a lightning indexer, keeps the top-k and
+ *        attends over them plus a sliding window of raw tokens and a per-head
+ *        attention sink.
+ *   HCA  compresses every m' >> m tokens (no overlap) and attends densely over
+ *        all completed entries (plus the sink and an optional window).
+ * The pages give no equations; the forms implemented are:
+ *   compress : a_i = k_i.g + b_(i mod m);  p = softmax over the block;
+ *              Kc_j = sum p_i k_i, Vc_j = sum p_i v_i, KIc_j = sum p_i kI_i
+ *   indexer  : I[t,j] = sum_h w[t,h] * max(0, qI[t,h].KIc_j),  j < floor((t+1)/m)
+ *   top-k    : the k largest I[t,.], equal scores to the lower index,
+ *              emitted ascending by index and padded with -1
+ *   attention: one softmax over {selected entries} U {window tokens} U {sink}:
+ *              o = sum e^(l-M) v / (e^(s_h-M) + sum e^(l-M)),  l = scale*q.key,
+ *              lse = M + ln(denominator)
+ *
+ * Conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the
+ *     library keeps no reference after the call returns and allocates no
+ *     memory.  Scratch space is passed in as `workspace` (size from the
+ *     matching *_workspace query; NULL allowed when that size is 0).
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is only
+ *     enqueued; nothing synchronises.
+ *   - Arguments are validated on the host first.  On any error the call
+ *     returns a non-zero status, launches nothing, writes nothing, and
+ *     csa_last_error() describes the problem.
+ *   - Tensors are dense and row-major in the shapes given; the batch stride
+ *     of a cache is Nc_cap rows.  Every pointer must be 16-byte aligned.
+ *   - Inputs must be finite; behaviour on NaN/Inf inputs is unspecified.
+ *   - Index/position inputs that fall outside the stated bounds are clamped
+ *     or skipped by the kernels (they never read or write out of bounds),
+ *     but the result is then unspecified.
+ */
+#ifndef CSA_MI355X_H
+#define CSA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA_ABI_VERSION 1
+
+typedef enum {
+  CSA_OK = 0,
+  CSA_INVALID_ARGUMENT = 1,    /* null/misaligned pointer, bad size, inconsistent shapes */
+  CSA_UNSUPPORTED = 2,         /* valid but not built: head dim, dtype, head count ...  */
+  CSA_WORKSPACE_TOO_SMALL = 3,
+  CSA_DEVICE_ERROR = 4         /* a HIP call or kernel launch failed                    */
+} csa_status_t;
+
+typedef enum {
+  CSA_F32 = 0,
+  CSA_BF16 = 1,
+  CSA_FP8_E4M3 = 2,            /* OCP E4M3 "fn" codes, one fp32 scale per row          */
+  CSA_FP4_E2M1 = 3             /* OCP E2M1 codes, 2 per byte (even element in the low
+                                  nibble), one E8M0 scale per 32 elements              */
+} csa_dtype_t;
+
+/* Returns CSA_ABI_VERSION of the built library. */
+int csa_abi_version(void);
+
+/* Text of the last error on the calling thread ("" if none).  Valid until the
+ * next call into the library on the same thread. */
+const char *csa_last_error(void);
+
+/*
+ * csa_compress — block compression (CSA with m, HCA with m').
+ * hyper.ai "Method", CSA paragraph (m tokens -> one entry with learnable
+ * compression weights and positional biases) and HCA paragraph (m' tokens,
+ * non-overlapping).
+ *
+ *   k, v      [B, T, d]   raw keys / values of the one KV head (dt)
+ *   ki        [B, T, dI]  raw indexer keys (dt), or NULL (then kic is NULL)
+ *   gate      [d]  fp32   gate vector g;  a_i = k_i . g + pos_bias[i mod m]
+ *   pos_bias  [m]  fp32   or NULL (= 0)
+ *   kc, vc    [B, Nc_cap, d], kic [B, Nc_cap, dI]  outputs (dt); rows
+ *             0 .. T/m - 1 are written (a trailing partial block is not).
+ *   dt ∈ {CSA_F32, CSA_BF16}; d ∈ {64, 128}; dI ∈ {32, 64}; 1 <= m <= 4096;
+ *   T/m <= Nc_cap.  Accumulation in fp32, bf16 outputs rounded to nearest even.
+ */
+csa_status_t csa_compress(const void *k, const void *v, const void *ki,
+                          const float *gate, const float *pos_bias,
+                          int B, int T, int d, int dI, int m, int Nc_cap, csa_dtype_t dt,
+                          void *kc, void *vc, void *kic, void *stream);
+
+/*
+ * csa_indexer_topk — lightning-indexer scores and top-k selection.
+ * hyper.ai "Method", CSA paragraph (a lightning indexer selects the top-k
+ * compressed entries); aiboss88 "Technical Principles", CSA bullet (index
+ * scores, top-k sparse selection) and FP4 bullet (FP4 indexer QK path, FP8
+ * for dynamic range).
+ *
+ *   qi        [B, Tq, HI, dI]  indexer queries: F32/BF16 values, FP8 codes, or
+ *             FP4 packed codes [B, Tq, HI, dI/2]
+ *   qi_scale  NULL for F32/BF16; fp32 [B, Tq, HI] for FP8;
+ *             uint8 E8M0 [B, Tq, HI, dI/32] for FP4
+ *   w         [B, Tq, HI] fp32 per-token head weights (must be >= 0)
+ *   kic       [B, Nc_cap, dI] compressed indexer keys (same encoding as qi;
+ *             FP4: [B, Nc_cap, dI/2])
+ *   kic_scale NULL / fp32 [B, Nc_cap] / uint8 E8M0 [B, Nc_cap, dI/32]
+ *   pos0      [B] int32 device: query i of sequence b sits at absolute
+ *             position pos0[b] + i and sees entries j < floor((pos+1)/m)
+ *   max_pos   host upper bound of pos0[b] + Tq - 1 over b (validation: the
+ *             last query may see at most Nc_cap entries)
+ *   idx_out   [B, Tq, topk] int32: selected entries ascending, -1 padded when
+ *             fewer than topk are eligible
+ *   score_out [B, Tq, topk] fp32 scores aligned with idx_out (-inf where
+ *             idx_out is -1), or NULL
+ *   qk_dt ∈ {F32, BF16, FP8_E4M3, FP4_E2M1}; dI ∈ {32, 64}; HI ∈ {1, 2, 4};
+ *   1 <= topk <= 4096.  Scores accumulate in fp32; ReLU yields +0.
+ */
+size_t csa_indexer_topk_workspace(int B, int Tq, int Nc_cap, int HI, int dI, int topk,
+                                  csa_dtype_t qk_dt);
+csa_status_t csa_indexer_topk(const void *qi, const void *qi_scale, const float *w,
+                              const void *kic, const void *kic_scale,
+                              const int32_t *pos0, int max_pos,
+                              int B, int Tq, int Nc_cap, int HI, int dI, int m, int topk,
+                              csa_dtype_t qk_dt, int32_t *idx_out, float *score_out,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * csa_sparse_attend — CSA core attention (MQA: H query heads, one KV head).
+ * hyper.ai "Method", CSA paragraph (core attention over the selected entries,
+ * MQA with shared keys and values) and HCA paragraph (sliding-window branch);
+ * aiboss88 "Technical Principles", CSA bullet (sliding window + attention sink).
+ *
+ *   q, out    [B, Tq, H, d] (dt)
+ *   kc, vc    [B, Nc_cap, d] compressed entries (dt)
+ *   idx       [B, Tq, topk] int32 selected entries (-1 = unused slot)
+ *   kw, vw    [B, R, d] raw tokens; row r holds absolute position
+ *             raw_pos0[b] + r (prefill passes the whole sequence with
+ *             raw_pos0 = 0, decode the last `window` tokens); NULL when
+ *             window == 0
+ *   raw_pos0  [B] int32 device (NULL when window == 0)
+ *   pos0      [B] int32 device: query positions as for csa_indexer_topk
+ *   window    W >= 0: the query at t also attends raw positions
+ *             max(0, t-W+1) .. t (its own token included)
+ *   sink      [H] fp32 sink logits, or NULL for no sink
+ *   lse_out   [B, Tq, H] fp32 natural-log denominators (incl. sink), or NULL
+ *   dt ∈ {F32, BF16}; d ∈ {64, 128}; 1 <= H <= 128; topk <= 4096.
+ */
+size_t csa_sparse_attend_workspace(int B, int Tq, int H, int d, int topk, int window);
+csa_status_t csa_sparse_attend(const void *q, const void *kc, const void *vc,
+                               const int32_t *idx, int topk,
+                               const void *kw, const void *vw, const int32_t *raw_pos0, int R,
+                               const int32_t *pos0, int max_pos, int window,
+                               const float *sink, float softmax_scale,
+                               int B, int Tq, int H, int d, int Nc_cap, csa_dtype_t dt,
+                               void *out, float *lse_out,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * hca_attend — HCA dense attention over every completed m'-block.
+ * hyper.ai "Method", HCA paragraph (dense attention over heavily compressed
+ * entries, no sparse selection, plus a sliding-window branch).
+ *
+ *   q, out    [B, Tq, H, d]; kc, vc [B, Nc_cap, d] (dt)
+ *   the query at t sees entries j < min(floor((t+1)/m_prime), Nc_cap) and,
+ *   when window > 0, raw positions max(0,t-W+1)..t from kw/vw as above.
+ *   Other arguments as for csa_sparse_attend.
+ */
+size_t hca_attend_workspace(int B, int Tq, int H, int d, int Nc_cap, int m_prime, int window);
+csa_status_t hca_attend(const void *q, const void *kc, const void *vc, int m_prime, int Nc_cap,
+                        const void *kw, const void *vw, const int32_t *raw_pos0, int R,
+                        int window, const int32_t *pos0, int max_pos,
+                        const float *sink, float softmax_scale,
+                        int B, int Tq, int H, int d, csa_dtype_t dt,
+                        void *out, float *lse_out,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA_MI355X_H */

@@ -1,0 +1,63 @@
+"""ctypes loader for libcsa_mi355x.so (built in-tree by ``build.py``).
+
+Loading fails loudly when the library is missing: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libcsa_mi355x.so")
+
+# status codes (csa_status_t)
+OK, INVALID_ARGUMENT, UNSUPPORTED, WORKSPACE_TOO_SMALL, DEVICE_ERROR = range(5)
+# csa_dtype_t
+F32, BF16, FP8_E4M3, FP4_E2M1 = range(4)
+
+_P = C.c_void_p
+_I = C.c_int
+_SZ = C.c_size_t
+
+EXPORTS = {
+    "csa_abi_version": (_I, []),
+    "csa_last_error": (C.c_char_p, []),
+    "csa_compress": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P]),
+    "csa_indexer_topk_workspace": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
+    "csa_indexer_topk": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I,
+                              _P, _P, _P, _SZ, _P]),
+    "csa_sparse_attend_workspace": (_SZ, [_I, _I, _I, _I, _I, _I]),
+    "csa_sparse_attend": (_I, [_P, _P, _P, _P, _I, _P, _P, _P, _I, _P, _I, _I, _P, C.c_float,
+                               _I, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
+    "hca_attend_workspace": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
+    "hca_attend": (_I, [_P, _P, _P, _I, _I, _P, _P, _P, _I, _I, _P, _I, _P, C.c_float,
+                        _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
+}
+
+_lib = None
+
+
+class CsaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"status {status}: {msg}")
+        self.status = status
+
+
+def load() -> C.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with `python -m sparse_attention_17_amd.build`")
+        lib = C.CDLL(LIB_PATH)
+        for name, (res, args) in EXPORTS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def check(status: int) -> None:
+    if status != OK:
+        raise CsaError(status, load().csa_last_error().decode())

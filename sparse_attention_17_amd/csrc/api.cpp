@@ -1,0 +1,240 @@
+// C ABI of the CSA/HCA hot path: host-side validation, workspace sizing,
+// thread-local error text, and dispatch to the gfx950 kernels.  Every entry
+// point checks its arguments before touching the device; on any error it
+// returns a status and launches nothing.
+#include "../../include/csa_mi355x.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+csa_status_t fail(csa_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+csa_status_t ok() {
+  g_err.clear();
+  return CSA_OK;
+}
+
+csa_status_t device_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(CSA_DEVICE_ERROR, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+#define REQUIRE(cond, st, ...)                 \
+  do {                                         \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+
+#define REQUIRE_PTR(p, name)                                                        \
+  do {                                                                              \
+    REQUIRE((p) != nullptr, CSA_INVALID_ARGUMENT, "%s must not be NULL", name);     \
+    REQUIRE(aligned((p), 16), CSA_INVALID_ARGUMENT, "%s must be 16-byte aligned", name); \
+  } while (0)
+
+#define REQUIRE_PTR4(p, name)                                                       \
+  do {                                                                              \
+    REQUIRE((p) != nullptr, CSA_INVALID_ARGUMENT, "%s must not be NULL", name);     \
+    REQUIRE(aligned((p), 4), CSA_INVALID_ARGUMENT, "%s must be 4-byte aligned", name); \
+  } while (0)
+
+bool head_dim_ok(int d) { return d == 64 || d == 128; }
+bool idx_dim_ok(int dI) { return dI == 32 || dI == 64; }
+bool attn_dtype_ok(csa_dtype_t dt) { return dt == CSA_F32 || dt == CSA_BF16; }
+
+// positions are int32: keep every derived count inside int range
+constexpr long long kMaxElems = (long long)1 << 40;
+
+}  // namespace
+
+extern "C" {
+
+int csa_abi_version(void) { return CSA_ABI_VERSION; }
+
+const char* csa_last_error(void) { return g_err.c_str(); }
+
+csa_status_t csa_compress(const void* k, const void* v, const void* ki, const float* gate,
+                          const float* pos_bias, int B, int T, int d, int dI, int m, int Nc_cap,
+                          csa_dtype_t dt, void* kc, void* vc, void* kic, void* stream) {
+  REQUIRE(B >= 0 && T >= 0, CSA_INVALID_ARGUMENT, "B and T must be >= 0 (got %d, %d)", B, T);
+  REQUIRE(m >= 1 && m <= 4096, CSA_INVALID_ARGUMENT, "m must be in [1, 4096] (got %d)", m);
+  REQUIRE(Nc_cap >= 0 && T / m <= Nc_cap, CSA_INVALID_ARGUMENT,
+          "Nc_cap (%d) must hold T/m = %d entries", Nc_cap, T / m);
+  REQUIRE(attn_dtype_ok(dt), CSA_UNSUPPORTED, "csa_compress: dtype must be CSA_F32 or CSA_BF16");
+  REQUIRE(head_dim_ok(d), CSA_UNSUPPORTED, "head dim d=%d not built (64, 128)", d);
+  REQUIRE((ki == nullptr) == (kic == nullptr), CSA_INVALID_ARGUMENT,
+          "ki and kic must both be given or both be NULL");
+  if (ki) REQUIRE(idx_dim_ok(dI), CSA_UNSUPPORTED, "indexer dim dI=%d not built (32, 64)", dI);
+  REQUIRE((long long)B * T * d < kMaxElems, CSA_INVALID_ARGUMENT, "tensor too large");
+  if (B == 0 || T / m == 0) return ok();
+  REQUIRE_PTR(k, "k");
+  REQUIRE_PTR(v, "v");
+  REQUIRE_PTR(kc, "kc");
+  REQUIRE_PTR(vc, "vc");
+  REQUIRE_PTR4(gate, "gate");
+  if (ki) {
+    REQUIRE_PTR(ki, "ki");
+    REQUIRE_PTR(kic, "kic");
+  }
+  if (pos_bias) REQUIRE(aligned(pos_bias, 4), CSA_INVALID_ARGUMENT, "pos_bias must be 4-byte aligned");
+  csa::CompressArgs a{k, v, ki, gate, pos_bias, B, T, d, dI, m, Nc_cap, dt == CSA_F32, kc, vc, kic};
+  return device_status(csa::launch_compress(a, (hipStream_t)stream), "csa_compress launch");
+}
+
+size_t csa_indexer_topk_workspace(int B, int Tq, int Nc_cap, int HI, int dI, int topk,
+                                  csa_dtype_t qk_dt) {
+  if (B <= 0 || Tq <= 0 || Nc_cap <= 0) return 0;
+  return csa::indexer_workspace(B, Tq, Nc_cap, HI, dI, topk, (int)qk_dt);
+}
+
+csa_status_t csa_indexer_topk(const void* qi, const void* qi_scale, const float* w,
+                              const void* kic, const void* kic_scale, const int32_t* pos0,
+                              int max_pos, int B, int Tq, int Nc_cap, int HI, int dI, int m,
+                              int topk, csa_dtype_t qk_dt, int32_t* idx_out, float* score_out,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  REQUIRE(B >= 0 && Tq >= 0, CSA_INVALID_ARGUMENT, "B and Tq must be >= 0");
+  REQUIRE(Nc_cap >= 1, CSA_INVALID_ARGUMENT, "Nc_cap must be >= 1");
+  REQUIRE(m >= 1, CSA_INVALID_ARGUMENT, "m must be >= 1");
+  REQUIRE(topk >= 1 && topk <= 4096, CSA_INVALID_ARGUMENT, "topk must be in [1, 4096] (got %d)", topk);
+  REQUIRE(qk_dt == CSA_F32 || qk_dt == CSA_BF16 || qk_dt == CSA_FP8_E4M3 || qk_dt == CSA_FP4_E2M1,
+          CSA_INVALID_ARGUMENT, "unknown qk dtype %d", (int)qk_dt);
+  REQUIRE(HI == 1 || HI == 2 || HI == 4, CSA_UNSUPPORTED, "indexer heads HI=%d not built (1, 2, 4)", HI);
+  REQUIRE(idx_dim_ok(dI), CSA_UNSUPPORTED, "indexer dim dI=%d not built (32, 64)", dI);
+  REQUIRE(max_pos >= Tq - 1 && max_pos < INT_MAX / 2, CSA_INVALID_ARGUMENT,
+          "max_pos (%d) must be >= Tq-1 and < 2^30", max_pos);
+  REQUIRE((max_pos + 1) / m <= Nc_cap, CSA_INVALID_ARGUMENT,
+          "the last query sees %d entries but Nc_cap is %d", (max_pos + 1) / m, Nc_cap);
+  REQUIRE((long long)B * Tq * topk < kMaxElems && (long long)B * Nc_cap * dI < kMaxElems,
+          CSA_INVALID_ARGUMENT, "tensor too large");
+  if (B == 0 || Tq == 0) return ok();
+  REQUIRE_PTR(qi, "qi");
+  REQUIRE_PTR(kic, "kic");
+  REQUIRE_PTR4(w, "w");
+  REQUIRE_PTR4(pos0, "pos0");
+  REQUIRE_PTR4(idx_out, "idx_out");
+  if (score_out) REQUIRE(aligned(score_out, 4), CSA_INVALID_ARGUMENT, "score_out must be 4-byte aligned");
+  if (qk_dt == CSA_FP8_E4M3) {
+    REQUIRE_PTR4(qi_scale, "qi_scale");
+    REQUIRE_PTR4(kic_scale, "kic_scale");
+  } else if (qk_dt == CSA_FP4_E2M1) {
+    REQUIRE(qi_scale && kic_scale, CSA_INVALID_ARGUMENT, "FP4 needs qi_scale and kic_scale");
+  }
+  const size_t need = csa_indexer_topk_workspace(B, Tq, Nc_cap, HI, dI, topk, qk_dt);
+  REQUIRE(workspace_bytes >= need, CSA_WORKSPACE_TOO_SMALL,
+          "workspace holds %zu bytes, %zu needed", workspace_bytes, need);
+  if (need) REQUIRE_PTR(workspace, "workspace");
+  csa::IndexerArgs a{qi, qi_scale, w, kic, kic_scale, pos0, max_pos, B, Tq, Nc_cap, HI, dI, m,
+                     topk, (csa::QkType)qk_dt, idx_out, score_out, workspace};
+  return device_status(csa::launch_indexer_topk(a, (hipStream_t)stream), "csa_indexer_topk launch");
+}
+
+size_t csa_sparse_attend_workspace(int B, int Tq, int H, int d, int topk, int window) {
+  if (B <= 0 || Tq <= 0 || H <= 0) return 0;
+  return csa::attend_workspace(true, B, Tq, H, d, topk, window, 1, 1, INT_MAX / 2);
+}
+
+size_t hca_attend_workspace(int B, int Tq, int H, int d, int Nc_cap, int m_prime, int window) {
+  if (B <= 0 || Tq <= 0 || H <= 0 || m_prime <= 0) return 0;
+  return csa::attend_workspace(false, B, Tq, H, d, 0, window, Nc_cap, m_prime, INT_MAX / 2);
+}
+
+static csa_status_t check_attend_common(const void* q, const void* kc, const void* vc,
+                                        const void* kw, const void* vw, const int32_t* raw_pos0,
+                                        int R, int window, const int32_t* pos0, int max_pos,
+                                        const float* sink, int B, int Tq, int H, int d,
+                                        int Nc_cap, csa_dtype_t dt, void* out, float* lse_out) {
+  REQUIRE(B >= 0 && Tq >= 0, CSA_INVALID_ARGUMENT, "B and Tq must be >= 0");
+  REQUIRE(H >= 1 && H <= 128, CSA_UNSUPPORTED, "query heads H=%d not supported (1..128)", H);
+  REQUIRE(head_dim_ok(d), CSA_UNSUPPORTED, "head dim d=%d not built (64, 128)", d);
+  REQUIRE(attn_dtype_ok(dt), CSA_UNSUPPORTED, "attention dtype must be CSA_F32 or CSA_BF16");
+  REQUIRE(Nc_cap >= 1, CSA_INVALID_ARGUMENT, "Nc_cap must be >= 1");
+  REQUIRE(window >= 0, CSA_INVALID_ARGUMENT, "window must be >= 0");
+  REQUIRE(max_pos >= Tq - 1 && max_pos < INT_MAX / 2, CSA_INVALID_ARGUMENT,
+          "max_pos (%d) must be >= Tq-1 and < 2^30", max_pos);
+  REQUIRE((long long)B * Tq * H * d < kMaxElems && (long long)B * Nc_cap * d < kMaxElems,
+          CSA_INVALID_ARGUMENT, "tensor too large");
+  if (B == 0 || Tq == 0) return ok();
+  REQUIRE_PTR(q, "q");
+  REQUIRE_PTR(kc, "kc");
+  REQUIRE_PTR(vc, "vc");
+  REQUIRE_PTR(out, "out");
+  REQUIRE_PTR4(pos0, "pos0");
+  if (window > 0) {
+    REQUIRE(R >= 1, CSA_INVALID_ARGUMENT, "window > 0 needs a raw buffer with R >= 1 rows");
+    REQUIRE_PTR(kw, "kw");
+    REQUIRE_PTR(vw, "vw");
+    REQUIRE_PTR4(raw_pos0, "raw_pos0");
+  }
+  if (sink) REQUIRE(aligned(sink, 4), CSA_INVALID_ARGUMENT, "sink must be 4-byte aligned");
+  if (lse_out) REQUIRE(aligned(lse_out, 4), CSA_INVALID_ARGUMENT, "lse_out must be 4-byte aligned");
+  return ok();
+}
+
+csa_status_t csa_sparse_attend(const void* q, const void* kc, const void* vc, const int32_t* idx,
+                               int topk, const void* kw, const void* vw, const int32_t* raw_pos0,
+                               int R, const int32_t* pos0, int max_pos, int window,
+                               const float* sink, float softmax_scale, int B, int Tq, int H, int d,
+                               int Nc_cap, csa_dtype_t dt, void* out, float* lse_out,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  REQUIRE(topk >= 1 && topk <= 4096, CSA_INVALID_ARGUMENT, "topk must be in [1, 4096] (got %d)", topk);
+  csa_status_t st = check_attend_common(q, kc, vc, kw, vw, raw_pos0, R, window, pos0, max_pos,
+                                        sink, B, Tq, H, d, Nc_cap, dt, out, lse_out);
+  if (st != CSA_OK || B == 0 || Tq == 0) return st;
+  REQUIRE_PTR4(idx, "idx");
+  const size_t need = csa::attend_workspace(true, B, Tq, H, d, topk, window, Nc_cap, 1, max_pos);
+  REQUIRE(workspace_bytes >= need, CSA_WORKSPACE_TOO_SMALL,
+          "workspace holds %zu bytes, %zu needed", workspace_bytes, need);
+  if (need) REQUIRE_PTR(workspace, "workspace");
+  csa::AttendArgs a{};
+  a.sparse = true; a.q = q; a.kc = kc; a.vc = vc; a.idx = idx; a.topk = topk; a.m_prime = 1;
+  a.kw = window > 0 ? kw : nullptr; a.vw = window > 0 ? vw : nullptr;
+  a.raw_pos0 = window > 0 ? raw_pos0 : nullptr; a.R = window > 0 ? R : 0; a.window = window;
+  a.pos0 = pos0; a.max_pos = max_pos; a.sink = sink; a.scale = softmax_scale;
+  a.B = B; a.Tq = Tq; a.H = H; a.d = d; a.Nc_cap = Nc_cap; a.f32 = dt == CSA_F32;
+  a.out = out; a.lse = lse_out; a.ws = workspace;
+  return device_status(csa::launch_attend(a, (hipStream_t)stream), "csa_sparse_attend launch");
+}
+
+csa_status_t hca_attend(const void* q, const void* kc, const void* vc, int m_prime, int Nc_cap,
+                        const void* kw, const void* vw, const int32_t* raw_pos0, int R,
+                        int window, const int32_t* pos0, int max_pos, const float* sink,
+                        float softmax_scale, int B, int Tq, int H, int d, csa_dtype_t dt,
+                        void* out, float* lse_out, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  REQUIRE(m_prime >= 1, CSA_INVALID_ARGUMENT, "m_prime must be >= 1");
+  csa_status_t st = check_attend_common(q, kc, vc, kw, vw, raw_pos0, R, window, pos0, max_pos,
+                                        sink, B, Tq, H, d, Nc_cap, dt, out, lse_out);
+  if (st != CSA_OK || B == 0 || Tq == 0) return st;
+  const size_t need = csa::attend_workspace(false, B, Tq, H, d, 0, window, Nc_cap, m_prime, max_pos);
+  REQUIRE(workspace_bytes >= need, CSA_WORKSPACE_TOO_SMALL,
+          "workspace holds %zu bytes, %zu needed", workspace_bytes, need);
+  if (need) REQUIRE_PTR(workspace, "workspace");
+  csa::AttendArgs a{};
+  a.sparse = false; a.q = q; a.kc = kc; a.vc = vc; a.idx = nullptr; a.topk = 0; a.m_prime = m_prime;
+  a.kw = window > 0 ? kw : nullptr; a.vw = window > 0 ? vw : nullptr;
+  a.raw_pos0 = window > 0 ? raw_pos0 : nullptr; a.R = window > 0 ? R : 0; a.window = window;
+  a.pos0 = pos0; a.max_pos = max_pos; a.sink = sink; a.scale = softmax_scale;
+  a.B = B; a.Tq = Tq; a.H = H; a.d = d; a.Nc_cap = Nc_cap; a.f32 = dt == CSA_F32;
+  a.out = out; a.lse = lse_out; a.ws = workspace;
+  return device_status(csa::launch_attend(a, (hipStream_t)stream), "hca_attend launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,420 @@
+// Core attention for CSA (selected compressed entries + sliding window + sink)
+// and HCA (every completed m'-block + optional window + sink).
+// Method: DeepSeek-V4 summary (hyper.ai), "Method": CSA core attention is MQA
+// over the top-k compressed entries with shared keys and values; HCA attends
+// densely over its heavily compressed entries; both add a sliding-window
+// branch.  aiboss88 "Technical Principles", CSA bullet: sliding window plus an
+// attention sink.  Form implemented (one softmax over all three parts):
+//   o = sum_j e^(l_j - M) v_j / (e^(s_h - M) + sum_j e^(l_j - M)),
+//   l_j = scale * q.k_j,  lse = M + ln(denominator).
+//
+// Mapping (MI355X, wave64, MFMA 32x32x16 bf16 / 32x32x2 fp32):
+//   * a workgroup owns a tile of query rows = (token, head) pairs: all H
+//     heads of one token for CSA (each token has its own key set), several
+//     tokens x H heads for HCA (all share the block prefix);
+//   * keys are staged KT=64 at a time in LDS: K row-major, V transposed;
+//   * each wave computes S^T = K Q^T for its 32 query rows, so every lane owns
+//     one query column: the online-softmax statistics stay in-lane (one
+//     cross-half shuffle), the probabilities already sit in the B-operand
+//     layout of O^T = V^T P^T, and the O^T accumulator rescale is per lane;
+//   * decode (one query token) splits the key list over workgroups and a
+//     combine kernel merges the partial (o, max, sum) in fixed split order,
+//     so results do not depend on the batch size.
+#include "common.hpp"
+#include "launch.hpp"
+
+#include <climits>
+
+namespace csa {
+
+static constexpr int KT = 64;
+static constexpr float LOG2E = 1.4426950408889634f;
+static constexpr float LN2 = 0.6931471805599453f;
+
+struct AttnGeom {
+  int TT;          // tokens per tile
+  int nsplit;      // key splits
+  int kps;         // keys per split (multiple of KT)
+  float scale_log2;
+};
+
+__host__ __device__ __forceinline__ int hca_ne(int pos, int mp, int cap) {
+  return max(0, min((pos + 1) / mp, cap));
+}
+
+template <typename T>
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <typename T, int D, int NW, bool SPARSE>
+__global__ __launch_bounds__(NW * 64) void attend_kernel(AttendArgs a, AttnGeom gm) {
+  constexpr int NT = NW * 64;
+  constexpr int VEC = 16 / sizeof(T);          // elements per 16-byte chunk
+  constexpr int KPAD = VEC;                    // Ks row padding (16 bytes)
+  constexpr int VPAD = 4;                      // Vt row padding (elements)
+  constexpr int KS = D + KPAD;                 // Ks row stride (elements)
+  constexpr int VS = KT + VPAD;                // Vt row stride (elements)
+  constexpr int DSTEP = D / 16;                // k-steps of S^T
+  constexpr int DVT = D / 32;                  // 32-wide dv tiles of O^T
+
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  T* Ks = reinterpret_cast<T*>(smem_raw);
+  T* Vt = Ks + KT * KS;
+  int* sel = reinterpret_cast<int*>(Vt + D * VS);
+  __shared__ uint32_t scan_sm[NW];
+  __shared__ int s_nsel;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, col = lane & 31;
+  const int b = blockIdx.z, split = blockIdx.y;
+  const int t0 = blockIdx.x * gm.TT;
+  const int tl = min(t0 + gm.TT, a.Tq) - 1;
+  const int p0 = a.pos0[b];
+  const int pos_first = p0 + t0, pos_last = p0 + tl;
+  const int rp0 = a.raw_pos0 ? a.raw_pos0[b] : 0;
+
+  // ---- the tile's key list: [compressed part][window part] ----
+  int ncomp;
+  if constexpr (SPARSE) {
+    // compact the valid selected entries of this (single) token into LDS
+    const int32_t* ir = a.idx + ((size_t)b * a.Tq + t0) * a.topk;
+    uint32_t base = 0;
+    for (int c0 = 0; c0 < a.topk; c0 += NT) {
+      const int i = c0 + tid;
+      const int e = i < a.topk ? ir[i] : -1;
+      const uint32_t ok = (e >= 0 && e < a.Nc_cap) ? 1u : 0u;
+      uint32_t tot;
+      const uint32_t pos = block_excl_scan<NT>(ok, scan_sm, &tot);
+      if (ok) sel[base + pos] = e;
+      base += tot;
+    }
+    if (tid == 0) s_nsel = (int)base;
+    __syncthreads();
+    ncomp = s_nsel;
+  } else {
+    ncomp = hca_ne(pos_last, a.m_prime, a.Nc_cap);
+  }
+  const int wlo = a.window > 0 ? max(0, pos_first - a.window + 1) : 0;
+  const int nwin = a.window > 0 ? pos_last - wlo + 1 : 0;
+  const int nkeys = ncomp + nwin;
+  const int kbeg = split * gm.kps;
+  const int kend = min(nkeys, kbeg + gm.kps);
+
+  // ---- this lane's query row ----
+  const int qr = wave * 32 + col;
+  const int tt = qr / a.H, hq = qr % a.H;
+  const int tq = t0 + tt;
+  const bool qvalid = (tt < gm.TT) && (tq < a.Tq);
+  const int qpos = p0 + tq;
+  const int q_ne = SPARSE ? ncomp : hca_ne(qpos, a.m_prime, a.Nc_cap);
+  const int q_wlo = max(0, qpos - a.window + 1);
+  Frag<T> qf[DSTEP];
+  {
+    const T* qrow = reinterpret_cast<const T*>(a.q) + (((size_t)b * a.Tq + tq) * a.H + hq) * D;
+#pragma unroll
+    for (int s = 0; s < DSTEP; ++s) {
+      if (qvalid) frag_load(qf[s], qrow + 16 * s + 8 * half);
+      else frag_zero(qf[s]);
+    }
+  }
+
+  f32x16 o[DVT];
+#pragma unroll
+  for (int i = 0; i < DVT; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[i][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const T* kcb = reinterpret_cast<const T*>(a.kc) + (size_t)b * a.Nc_cap * D;
+  const T* vcb = reinterpret_cast<const T*>(a.vc) + (size_t)b * a.Nc_cap * D;
+  const T* kwb = a.kw ? reinterpret_cast<const T*>(a.kw) + (size_t)b * a.R * D : nullptr;
+  const T* vwb = a.vw ? reinterpret_cast<const T*>(a.vw) + (size_t)b * a.R * D : nullptr;
+
+  // source row of key slot s (nullptr = absent)
+  auto key_src = [&](int s, const T*& kp, const T*& vp) {
+    kp = vp = nullptr;
+    if (s < kbeg || s >= kend) return;
+    if (s < ncomp) {
+      const int e = SPARSE ? sel[s] : s;
+      kp = kcb + (size_t)e * D;
+      vp = vcb + (size_t)e * D;
+    } else {
+      const int r = wlo + (s - ncomp) - rp0;
+      if (r >= 0 && r < a.R && kwb) {
+        kp = kwb + (size_t)r * D;
+        vp = vwb + (size_t)r * D;
+      }
+    }
+  };
+
+  for (int s0 = kbeg; s0 < kend; s0 += KT) {
+    // ---- stage K (row-major) and V (transposed) ----
+    constexpr int KCH = D / VEC;                         // 16-byte chunks per row
+    for (int c = tid; c < KT * KCH; c += NT) {
+      const int kk = c / KCH, ch = c % KCH;
+      const T *kp, *vp;
+      key_src(s0 + kk, kp, vp);
+      u32x4 val = {0, 0, 0, 0};
+      if (kp) val = *reinterpret_cast<const u32x4*>(kp + ch * VEC);
+      *reinterpret_cast<u32x4*>(Ks + kk * KS + ch * VEC) = val;
+    }
+    for (int c = tid; c < (KT / 4) * KCH; c += NT) {
+      const int kg = c / KCH, ch = c % KCH;
+      T rows[4][VEC];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const T *kp, *vp;
+        key_src(s0 + kg * 4 + u, kp, vp);
+        u32x4 val = {0, 0, 0, 0};
+        if (vp) val = *reinterpret_cast<const u32x4*>(vp + ch * VEC);
+        *reinterpret_cast<u32x4*>(rows[u]) = val;
+      }
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        T four[4] = {rows[0][e], rows[1][e], rows[2][e], rows[3][e]};
+        T* dst = Vt + (ch * VEC + e) * VS + kg * 4;
+        if constexpr (sizeof(T) == 2) *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<uint2*>(four);
+        else *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<u32x4*>(four);
+      }
+    }
+    __syncthreads();
+
+    // ---- S^T = K Q^T for two 32-key sub-tiles ----
+    f32x16 st[2];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st[sub][r] = 0.f;
+#pragma unroll
+      for (int s = 0; s < DSTEP; ++s) {
+        Frag<T> kf;
+        frag_load(kf, Ks + (sub * 32 + col) * KS + 16 * s + 8 * half);
+        mma32(st[sub], kf, qf[s]);
+      }
+    }
+    // ---- mask, online softmax ----
+    float mt = -INFINITY;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int s = s0 + sub * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        bool ok = qvalid && s < kend;
+        if (ok && s >= ncomp) {
+          const int p = wlo + (s - ncomp);
+          ok = (p - rp0 >= 0) && (p - rp0 < a.R) && (kwb != nullptr);   // row present
+          if (!SPARSE) ok = ok && p >= q_wlo && p <= qpos;
+        } else if (ok && !SPARSE) {
+          ok = s < q_ne;
+        }
+        const float x = ok ? st[sub][r] * gm.scale_log2 : -INFINITY;
+        st[sub][r] = x;
+        mt = fmaxf(mt, x);
+      }
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float m_new = fmaxf(m_run, mt);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fexp2<T>(m_run - m_use);
+    float psum = 0.f;
+    Frag<T> pf[2][2];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      float pv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        pv[r] = fexp2<T>(st[sub][r] - m_use);
+        psum += pv[r];
+      }
+      frag_from_f32(pf[sub][0], pv);
+      frag_from_f32(pf[sub][1], pv + 8);
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int i = 0; i < DVT; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+
+    // ---- O^T += V^T P^T ----
+#pragma unroll
+    for (int i = 0; i < DVT; ++i) {
+      const T* vrow = Vt + (i * 32 + col) * VS;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int kb = sub * 32 + 16 * ks + 4 * half;
+          Frag<T> vf;
+          if constexpr (sizeof(T) == 2) {
+            const uint2 lo = *reinterpret_cast<const uint2*>(vrow + kb);
+            const uint2 hi = *reinterpret_cast<const uint2*>(vrow + kb + 8);
+            vf.v = u32x4{lo.x, lo.y, hi.x, hi.y};
+          } else {
+            const f32x4 lo = *reinterpret_cast<const f32x4*>(vrow + kb);
+            const f32x4 hi = *reinterpret_cast<const f32x4*>(vrow + kb + 8);
+            float* fv = reinterpret_cast<float*>(&vf);
+            fv[0] = lo[0]; fv[1] = lo[1]; fv[2] = lo[2]; fv[3] = lo[3];
+            fv[4] = hi[0]; fv[5] = hi[1]; fv[6] = hi[2]; fv[7] = hi[3];
+          }
+          mma32(o[i], vf, pf[sub][ks]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue ----
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if (!qvalid) return;
+  const size_t grow = ((size_t)b * a.Tq + tq) * a.H + hq;
+  if (gm.nsplit > 1) {
+    const size_t rows_total = (size_t)a.B * a.Tq * a.H;
+    float* po = reinterpret_cast<float*>(a.ws) + ((size_t)split * rows_total + grow) * D;
+    float* pm = reinterpret_cast<float*>(a.ws) + (size_t)gm.nsplit * rows_total * D;
+    float* pl = pm + (size_t)gm.nsplit * rows_total;
+#pragma unroll
+    for (int i = 0; i < DVT; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<f32x4*>(po + i * 32 + 8 * g + 4 * half) =
+            f32x4{o[i][4 * g], o[i][4 * g + 1], o[i][4 * g + 2], o[i][4 * g + 3]};
+    if (half == 0) {
+      pm[(size_t)split * rows_total + grow] = m_run;
+      pl[(size_t)split * rows_total + grow] = l_tot;
+    }
+    return;
+  }
+  const float s2 = a.sink ? a.sink[hq] * LOG2E : -INFINITY;
+  const float M = fmaxf(m_run, s2);
+  float fac = 0.f, lse = -INFINITY;
+  if (M != -INFINITY) {
+    const float cm = fexp2<T>(m_run - M);             // m_run = -inf -> 0
+    const float Z = l_tot * cm + fexp2<T>(s2 - M);
+    fac = cm / Z;
+    lse = (M + __log2f(Z)) * LN2;
+  }
+  T* orow = reinterpret_cast<T*>(a.out) + grow * D;
+#pragma unroll
+  for (int i = 0; i < DVT; ++i)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      T v4[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v4[u] = from_f32<T>(o[i][4 * g + u] * fac);
+      T* dst = orow + i * 32 + 8 * g + 4 * half;
+      if constexpr (sizeof(T) == 2) *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<uint2*>(v4);
+      else *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<u32x4*>(v4);
+    }
+  if (a.lse && half == 0) a.lse[grow] = lse;
+}
+
+// Merge split partials in fixed split order (one wave per query row).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void combine_kernel(AttendArgs a, int nsplit) {
+  const int lane = threadIdx.x & 63;
+  const size_t rows_total = (size_t)a.B * a.Tq * a.H;
+  const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows_total) return;
+  const float* po = reinterpret_cast<const float*>(a.ws);
+  const float* pm = po + (size_t)nsplit * rows_total * D;
+  const float* pl = pm + (size_t)nsplit * rows_total;
+  const int h = (int)(row % a.H);
+  const float s2 = a.sink ? a.sink[h] * LOG2E : -INFINITY;
+  float M = s2;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pm[s * rows_total + row]);
+  constexpr int PER = D / 64;
+  float acc[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) acc[u] = 0.f;
+  float Z = 0.f, lse = -INFINITY;
+  if (M != -INFINITY) {
+    Z = __builtin_amdgcn_exp2f(s2 - M);
+    for (int s = 0; s < nsplit; ++s) {
+      const float ms = pm[s * rows_total + row];
+      const float c = __builtin_amdgcn_exp2f(ms - M);
+      Z += pl[s * rows_total + row] * c;
+#pragma unroll
+      for (int u = 0; u < PER; ++u) acc[u] += po[(s * rows_total + row) * D + lane * PER + u] * c;
+    }
+    lse = (M + __log2f(Z)) * LN2;
+  }
+  const float inv = (M != -INFINITY) ? 1.f / Z : 0.f;
+  T* orow = reinterpret_cast<T*>(a.out) + row * D;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) orow[lane * PER + u] = from_f32<T>(acc[u] * inv);
+  if (a.lse && lane == 0) a.lse[row] = lse;
+}
+
+// ---------------------------------- host -----------------------------------
+static int keys_per_split(bool sparse, int Tq) {
+  if (Tq != 1) return INT_MAX / 2;
+  return sparse ? 128 : 512;
+}
+
+static int tokens_per_tile(bool sparse, int H, int Tq) {
+  if (sparse) return 1;
+  return std::max(1, std::min(128 / H, Tq));
+}
+
+static int nkeys_upper(bool sparse, int topk, int window, int Nc_cap, int m_prime, int max_pos) {
+  const int w = window > 0 ? std::min(window, max_pos + 1) : 0;
+  if (sparse) return topk + w;
+  return hca_ne(max_pos, m_prime, Nc_cap) + w;
+}
+
+size_t attend_workspace(bool sparse, int B, int Tq, int H, int d, int topk, int window,
+                        int Nc_cap, int m_prime, int max_pos) {
+  const int kps = keys_per_split(sparse, Tq);
+  const long nk = nkeys_upper(sparse, topk, window, Nc_cap, m_prime, max_pos);
+  const long ns = std::max(1L, (nk + kps - 1) / kps);
+  if (ns <= 1) return 0;
+  return (size_t)ns * B * Tq * H * (d + 2) * sizeof(float);
+}
+
+template <typename T, int D, int NW, bool SPARSE>
+static hipError_t launch4(const AttendArgs& a, const AttnGeom& gm, hipStream_t st) {
+  constexpr int KS = D + 16 / sizeof(T);
+  constexpr int VS = KT + 4;
+  const size_t lds = (size_t)(KT * KS + D * VS) * sizeof(T) + (SPARSE ? (size_t)a.topk * 4 : 0);
+  auto kfn = attend_kernel<T, D, NW, SPARSE>;
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  dim3 grid((a.Tq + gm.TT - 1) / gm.TT, gm.nsplit, a.B);
+  hipLaunchKernelGGL(kfn, grid, dim3(NW * 64), lds, st, a, gm);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || gm.nsplit <= 1) return e;
+  const size_t rows = (size_t)a.B * a.Tq * a.H;
+  hipLaunchKernelGGL((combine_kernel<T, D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st,
+                     a, gm.nsplit);
+  return hipGetLastError();
+}
+
+template <typename T, int D, bool SPARSE>
+static hipError_t launch3(const AttendArgs& a, const AttnGeom& gm, hipStream_t st) {
+  const int rows = gm.TT * a.H;
+  if (rows <= 32) return launch4<T, D, 1, SPARSE>(a, gm, st);
+  if (rows <= 64) return launch4<T, D, 2, SPARSE>(a, gm, st);
+  return launch4<T, D, 4, SPARSE>(a, gm, st);
+}
+
+template <typename T, int D>
+static hipError_t launch2(const AttendArgs& a, const AttnGeom& gm, hipStream_t st) {
+  return a.sparse ? launch3<T, D, true>(a, gm, st) : launch3<T, D, false>(a, gm, st);
+}
+
+hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
+  if (a.B == 0 || a.Tq == 0) return hipSuccess;
+  AttnGeom gm;
+  gm.TT = tokens_per_tile(a.sparse, a.H, a.Tq);
+  const int kps = keys_per_split(a.sparse, a.Tq);
+  const long nk = nkeys_upper(a.sparse, a.topk, a.window, a.Nc_cap, a.m_prime, a.max_pos);
+  gm.nsplit = (int)std::max(1L, (nk + kps - 1) / kps);
+  gm.kps = gm.nsplit > 1 ? kps : INT_MAX / 2;
+  gm.scale_log2 = a.scale * LOG2E;
+  if (a.f32) return a.d == 64 ? launch2<float, 64>(a, gm, st) : launch2<float, 128>(a, gm, st);
+  return a.d == 64 ? launch2<bf16, 64>(a, gm, st) : launch2<bf16, 128>(a, gm, st);
+}
+
+}  // namespace csa

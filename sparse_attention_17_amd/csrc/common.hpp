@@ -1,0 +1,129 @@
+// Device helpers shared by the gfx950 kernels: element types, bf16 rounding,
+// MFMA fragment wrappers, wave/block reductions and scans.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+struct bf16 { uint16_t x; };   // storage type: raw bfloat16 bits
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16 v) { return __uint_as_float((uint32_t)v.x << 16); }
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// fp32 -> bf16, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+template <typename T> __device__ __forceinline__ T from_f32(float f);
+template <> __device__ __forceinline__ float from_f32<float>(float f) { return f; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float f) { bf16 r; r.x = (uint16_t)f32_to_bf16_bits(f); return r; }
+
+// ---------------------------------------------------------------------------
+// MFMA fragments.  A "k-chunk fragment" is the 8 consecutive k-values one lane
+// contributes to one bf16 MFMA (16x16x32 or 32x32x16).  For fp32 data the
+// same 8 k-values are fed to 8 fp32 MFMAs (16x16x4 / 32x32x2) in which the
+// lane's single k-slot stands for k = 8*(lane group) + s at step s, so both
+// element types share one fragment layout and one reduction order per lane.
+// ---------------------------------------------------------------------------
+template <typename T> struct Frag;
+template <> struct Frag<bf16> { u32x4 v; };          // 8 packed bf16
+template <> struct Frag<float> { float v[8]; };
+
+__device__ __forceinline__ void frag_load(Frag<bf16>& f, const void* p) {
+  f.v = *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void frag_load(Frag<float>& f, const void* p) {
+  const f32x4* q = reinterpret_cast<const f32x4*>(p);
+  f32x4 a = q[0], b = q[1];
+  f.v[0] = a[0]; f.v[1] = a[1]; f.v[2] = a[2]; f.v[3] = a[3];
+  f.v[4] = b[0]; f.v[5] = b[1]; f.v[6] = b[2]; f.v[7] = b[3];
+}
+__device__ __forceinline__ void frag_zero(Frag<bf16>& f) { f.v = u32x4{0, 0, 0, 0}; }
+__device__ __forceinline__ void frag_zero(Frag<float>& f) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f.v[i] = 0.f;
+}
+// Build a fragment from 8 fp32 values (bf16: round to nearest even).
+__device__ __forceinline__ void frag_from_f32(Frag<bf16>& f, const float* x) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    f.v[i] = f32_to_bf16_bits(x[2 * i]) | (f32_to_bf16_bits(x[2 * i + 1]) << 16);
+}
+__device__ __forceinline__ void frag_from_f32(Frag<float>& f, const float* x) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f.v[i] = x[i];
+}
+
+// C(32x32) += A(32 x 16) * B(16 x 32)
+__device__ __forceinline__ void mma32(f32x16& c, const Frag<bf16>& a, const Frag<bf16>& b) {
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a.v),
+                                              __builtin_bit_cast(bf16x8, b.v), c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma32(f32x16& c, const Frag<float>& a, const Frag<float>& b) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.v[s], b.v[s], c, 0, 0, 0);
+}
+// C(16x16) += A(16 x 32) * B(32 x 16)
+__device__ __forceinline__ void mma16(f32x4& c, const Frag<bf16>& a, const Frag<bf16>& b) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a.v),
+                                              __builtin_bit_cast(bf16x8, b.v), c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma16(f32x4& c, const Frag<float>& a, const Frag<float>& b) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[s], b.v[s], c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Reductions / scans.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+// Exclusive prefix sum over a block of NT threads; `smem` holds NT/64 words.
+// Returns the exclusive prefix; *total receives the block sum.
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* smem, uint32_t* total) {
+  constexpr int NWV = NT / 64;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  uint32_t inc = wave_incl_scan(v);
+  if (lane == 63) smem[wv] = inc;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NWV; ++i) {
+    uint32_t s = smem[i];
+    if (i < wv) base += s;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + inc - v;
+}
+
+}  // namespace csa

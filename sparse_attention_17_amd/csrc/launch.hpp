@@ -1,0 +1,59 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernels.
+// Arguments arrive here already validated.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa {
+
+struct CompressArgs {
+  const void *k, *v, *ki;
+  const float *gate, *pos_bias;
+  int B, T, d, dI, m, Nc_cap;
+  bool f32;
+  void *kc, *vc, *kic;
+};
+hipError_t launch_compress(const CompressArgs& a, hipStream_t st);
+
+enum QkType { QK_F32 = 0, QK_BF16 = 1, QK_FP8 = 2, QK_FP4 = 3 };
+
+struct IndexerArgs {
+  const void *qi, *qi_scale;
+  const float* w;
+  const void *kic, *kic_scale;
+  const int32_t* pos0;
+  int max_pos;
+  int B, Tq, Nc_cap, HI, dI, m, topk;
+  QkType qk;
+  int32_t* idx_out;
+  float* score_out;
+  void* ws;
+};
+size_t indexer_workspace(int B, int Tq, int Nc_cap, int HI, int dI, int topk, int qk);
+hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t st);
+
+struct AttendArgs {
+  bool sparse;                     // CSA (idx list) or HCA (dense over completed blocks)
+  const void *q, *kc, *vc;
+  const int32_t* idx;
+  int topk;
+  int m_prime;                     // HCA block size
+  const void *kw, *vw;
+  const int32_t* raw_pos0;
+  int R, window;
+  const int32_t* pos0;
+  int max_pos;
+  const float* sink;
+  float scale;
+  int B, Tq, H, d, Nc_cap;
+  bool f32;
+  void* out;
+  float* lse;
+  void* ws;
+};
+size_t attend_workspace(bool sparse, int B, int Tq, int H, int d, int topk, int window,
+                        int Nc_cap, int m_prime, int max_pos);
+hipError_t launch_attend(const AttendArgs& a, hipStream_t st);
+
+}  // namespace csa

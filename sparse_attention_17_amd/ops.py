@@ -1,0 +1,136 @@
+"""Torch-facing wrappers over the C ABI (argument marshalling only).
+
+Every step of the computation runs in the HIP kernels of libcsa_mi355x.so;
+PyTorch only provides device memory (outputs and workspace are allocated
+with torch.empty on the inputs' device) and the current HIP stream.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib as L
+
+_ATTN_DT = {torch.float32: L.F32, torch.bfloat16: L.BF16}
+
+
+def _p(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dev_check(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("all tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all tensors must be on one device")
+    return dev
+
+
+def _stream(dev) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _attn_dt(t):
+    try:
+        return _ATTN_DT[t.dtype]
+    except KeyError:
+        raise ValueError(f"unsupported dtype {t.dtype}; use float32 or bfloat16") from None
+
+
+def _ws(nbytes: int, dev):
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=dev)
+
+
+def compress(k, v, ki, gate, m, pos_bias=None, Nc_cap=None):
+    """Softmax-gated block pooling.  k, v [B,T,d]; ki [B,T,dI] or None;
+    gate [d] fp32; pos_bias [m] fp32 or None.  Returns kc, vc [B,Nc_cap,d],
+    kic [B,Nc_cap,dI] (None without ki); rows >= T//m are left unwritten."""
+    dev = _dev_check(k, v, ki, gate, pos_bias)
+    B, T, d = k.shape
+    dI = ki.shape[-1] if ki is not None else 0
+    cap = T // m if Nc_cap is None else Nc_cap
+    kc = torch.empty(B, cap, d, dtype=k.dtype, device=dev)
+    vc = torch.empty_like(kc)
+    kic = torch.empty(B, cap, dI, dtype=k.dtype, device=dev) if ki is not None else None
+    L.check(L.load().csa_compress(_p(k), _p(v), _p(ki), _p(gate), _p(pos_bias), B, T, d, dI, m,
+                                  cap, _attn_dt(k), _p(kc), _p(vc), _p(kic), _stream(dev)))
+    return kc, vc, kic
+
+
+def _qk_code(qi, qk_dtype):
+    if qk_dtype is None:
+        if qi.dtype == torch.float32:
+            return L.F32
+        if qi.dtype == torch.bfloat16:
+            return L.BF16
+        raise ValueError("uint8 indexer inputs need qk_dtype='fp8' or 'fp4'")
+    return {"f32": L.F32, "bf16": L.BF16, "fp8": L.FP8_E4M3, "fp4": L.FP4_E2M1}[qk_dtype]
+
+
+def indexer_topk(qi, w, kic, pos0, m, topk, max_pos, qi_scale=None, kic_scale=None,
+                 qk_dtype=None, return_scores=False):
+    """Lightning-indexer scores + lowest-index top-k.  qi [B,Tq,HI,dI] (FP4:
+    [..,dI/2] packed), w [B,Tq,HI] fp32, kic [B,Nc_cap,dI] (FP4 [..,dI/2]),
+    pos0 [B] int32 (positions of the first query).  Returns idx [B,Tq,topk]
+    int32 (and scores [B,Tq,topk] fp32 if asked)."""
+    dev = _dev_check(qi, w, kic, pos0, qi_scale, kic_scale)
+    code = _qk_code(qi, qk_dtype)
+    B, Tq, HI = w.shape
+    dI = qi.shape[-1] * (2 if code == L.FP4_E2M1 else 1)
+    Nc_cap = kic.shape[1]
+    lib = L.load()
+    nws = lib.csa_indexer_topk_workspace(B, Tq, Nc_cap, HI, dI, topk, code)
+    ws = _ws(nws, dev)
+    idx = torch.empty(B, Tq, topk, dtype=torch.int32, device=dev)
+    sc = torch.empty(B, Tq, topk, dtype=torch.float32, device=dev) if return_scores else None
+    L.check(lib.csa_indexer_topk(_p(qi), _p(qi_scale), _p(w), _p(kic), _p(kic_scale), _p(pos0),
+                                 int(max_pos), B, Tq, Nc_cap, HI, dI, m, topk, code, _p(idx),
+                                 _p(sc), _p(ws), nws, _stream(dev)))
+    return (idx, sc) if return_scores else idx
+
+
+def sparse_attend(q, kc, vc, idx, pos0, max_pos, window, kw=None, vw=None, raw_pos0=None,
+                  sink=None, scale=None, return_lse=False):
+    """CSA core attention.  q [B,Tq,H,d]; kc, vc [B,Nc_cap,d]; idx [B,Tq,k];
+    kw, vw [B,R,d] raw tokens with row r at position raw_pos0[b]+r."""
+    dev = _dev_check(q, kc, vc, idx, pos0, kw, vw, raw_pos0, sink)
+    B, Tq, H, d = q.shape
+    topk = idx.shape[-1]
+    R = kw.shape[1] if kw is not None else 0
+    scale = d ** -0.5 if scale is None else scale
+    lib = L.load()
+    nws = lib.csa_sparse_attend_workspace(B, Tq, H, d, topk, window)
+    ws = _ws(nws, dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(B, Tq, H, dtype=torch.float32, device=dev) if return_lse else None
+    L.check(lib.csa_sparse_attend(_p(q), _p(kc), _p(vc), _p(idx), topk, _p(kw), _p(vw),
+                                  _p(raw_pos0), R, _p(pos0), int(max_pos), window, _p(sink),
+                                  float(scale), B, Tq, H, d, kc.shape[1], _attn_dt(q), _p(out),
+                                  _p(lse), _p(ws), nws, _stream(dev)))
+    return (out, lse) if return_lse else out
+
+
+def hca_attend(q, kc, vc, m_prime, pos0, max_pos, sink=None, scale=None, window=0, kw=None,
+               vw=None, raw_pos0=None, return_lse=False):
+    """HCA dense attention over completed m'-blocks (+ optional window)."""
+    dev = _dev_check(q, kc, vc, pos0, kw, vw, raw_pos0, sink)
+    B, Tq, H, d = q.shape
+    Nc_cap = kc.shape[1]
+    R = kw.shape[1] if kw is not None else 0
+    scale = d ** -0.5 if scale is None else scale
+    lib = L.load()
+    nws = lib.hca_attend_workspace(B, Tq, H, d, Nc_cap, m_prime, window)
+    ws = _ws(nws, dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(B, Tq, H, dtype=torch.float32, device=dev) if return_lse else None
+    L.check(lib.hca_attend(_p(q), _p(kc), _p(vc), m_prime, Nc_cap, _p(kw), _p(vw), _p(raw_pos0),
+                           R, window, _p(pos0), int(max_pos), _p(sink), float(scale), B, Tq, H, d,
+                           _attn_dt(q), _p(out), _p(lse), _p(ws), nws, _stream(dev)))
+    return (out, lse) if return_lse else out

@@ -8,3 +8,16 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+import pytest  # noqa: E402
+
+
+@pytest.fixture(scope="session")
+def lib():
+    """The built HIP library (built here if it is missing)."""
+    from sparse_attention_17_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from sparse_attention_17_amd import build
+        build.build()
+    return _lib.load()

@@ -1,0 +1,137 @@
+"""Host-side checks of the C ABI that need no GPU: every declared symbol is
+exported, and invalid arguments are rejected with the right status before any
+device work (the pointers used here are never dereferenced)."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+from sparse_attention_17_amd import _lib as L
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "csa_mi355x.h")
+FAKE = 0x100000          # aligned, never dereferenced: validation fails first
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa_\w+|hca_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_four_ops():
+    names = declared_functions()
+    for n in ("csa_compress", "csa_indexer_topk", "csa_sparse_attend", "hca_attend"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    for n in names:
+        assert n in exported, n
+        assert hasattr(lib, n)
+    assert set(names) == set(L.EXPORTS)
+
+
+def test_version(lib):
+    assert lib.csa_abi_version() == 1
+
+
+def _compress(lib, **kw):
+    a = dict(k=FAKE, v=FAKE, ki=None, gate=FAKE, pos_bias=None, B=1, T=64, d=128, dI=64, m=4,
+             Nc_cap=16, dt=L.BF16, kc=FAKE, vc=FAKE, kic=None, stream=None)
+    a.update(kw)
+    return lib.csa_compress(*a.values())
+
+
+def test_compress_validation(lib):
+    assert _compress(lib, d=96) == L.UNSUPPORTED
+    assert b"head dim" in lib.csa_last_error()
+    assert _compress(lib, m=0) == L.INVALID_ARGUMENT
+    assert _compress(lib, Nc_cap=15) == L.INVALID_ARGUMENT
+    assert _compress(lib, k=None) == L.INVALID_ARGUMENT
+    assert _compress(lib, k=FAKE + 4) == L.INVALID_ARGUMENT          # misaligned
+    assert _compress(lib, ki=FAKE) == L.INVALID_ARGUMENT             # ki without kic
+    assert _compress(lib, ki=FAKE, kic=FAKE, dI=48) == L.UNSUPPORTED
+    assert _compress(lib, dt=L.FP8_E4M3) == L.UNSUPPORTED
+    # nothing to do: succeeds without touching the device
+    assert _compress(lib, B=0) == L.OK
+    assert _compress(lib, T=3) == L.OK
+    assert lib.csa_last_error() == b""
+
+
+def _indexer(lib, **kw):
+    a = dict(qi=FAKE, qi_scale=None, w=FAKE, kic=FAKE, kic_scale=None, pos0=FAKE, max_pos=1023,
+             B=1, Tq=1, Nc_cap=256, HI=4, dI=64, m=4, topk=32, qk=L.BF16, idx=FAKE, score=None,
+             ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return lib.csa_indexer_topk(*a.values())
+
+
+def test_indexer_validation(lib):
+    assert _indexer(lib, topk=0) == L.INVALID_ARGUMENT
+    assert _indexer(lib, topk=4097) == L.INVALID_ARGUMENT
+    assert _indexer(lib, HI=3) == L.UNSUPPORTED
+    assert _indexer(lib, dI=48) == L.UNSUPPORTED
+    assert _indexer(lib, max_pos=1027) == L.INVALID_ARGUMENT          # sees 257 > Nc_cap entries
+    assert _indexer(lib, qk=L.FP8_E4M3) == L.INVALID_ARGUMENT         # scales missing
+    assert _indexer(lib, qk=7) == L.INVALID_ARGUMENT
+    assert _indexer(lib, qi=None) == L.INVALID_ARGUMENT
+    need = lib.csa_indexer_topk_workspace(1, 1, 256, 4, 64, 32, L.BF16)
+    assert need > 0
+    assert _indexer(lib, ws=FAKE, ws_bytes=need - 1) == L.WORKSPACE_TOO_SMALL
+    assert _indexer(lib, Tq=0) == L.OK
+
+
+def _sparse(lib, **kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, idx=FAKE, topk=64, kw=FAKE, vw=FAKE, raw_pos0=FAKE, R=128,
+             pos0=FAKE, max_pos=4095, window=128, sink=None, scale=C.c_float(0.1), B=2, Tq=1,
+             H=64, d=128, Nc_cap=1024, dt=L.BF16, out=FAKE, lse=None, ws=None, ws_bytes=0,
+             stream=None)
+    a.update(kw)
+    return lib.csa_sparse_attend(*a.values())
+
+
+def test_sparse_attend_validation(lib):
+    assert _sparse(lib, H=129) == L.UNSUPPORTED
+    assert _sparse(lib, d=32) == L.UNSUPPORTED
+    assert _sparse(lib, topk=0) == L.INVALID_ARGUMENT
+    assert _sparse(lib, window=-1) == L.INVALID_ARGUMENT
+    assert _sparse(lib, kw=None) == L.INVALID_ARGUMENT
+    assert _sparse(lib, R=0) == L.INVALID_ARGUMENT
+    assert _sparse(lib, dt=L.FP4_E2M1) == L.UNSUPPORTED
+    assert _sparse(lib, max_pos=-5) == L.INVALID_ARGUMENT
+    need = lib.csa_sparse_attend_workspace(2, 1, 64, 128, 64, 128)
+    assert need > 0                                          # one decode token: split-KV partials
+    assert _sparse(lib, ws=FAKE, ws_bytes=need - 1) == L.WORKSPACE_TOO_SMALL
+    assert lib.csa_sparse_attend_workspace(1, 4096, 64, 128, 512, 128) == 0   # prefill: no split
+
+
+def _hca(lib, **kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, m_prime=128, Nc_cap=8192, kw=None, vw=None, raw_pos0=None,
+             R=0, window=0, pos0=FAKE, max_pos=(1 << 20) - 1, sink=None, scale=C.c_float(0.1),
+             B=16, Tq=1, H=64, d=128, dt=L.BF16, out=FAKE, lse=None, ws=None, ws_bytes=0,
+             stream=None)
+    a.update(kw)
+    return lib.hca_attend(*a.values())
+
+
+def test_hca_validation(lib):
+    assert _hca(lib, m_prime=0) == L.INVALID_ARGUMENT
+    assert _hca(lib, window=16) == L.INVALID_ARGUMENT          # window without a raw buffer
+    assert _hca(lib, H=0) == L.UNSUPPORTED
+    need = lib.hca_attend_workspace(16, 1, 64, 128, 8192, 128, 0)
+    assert need == 16 * 16 * 64 * 130 * 4                      # 16 splits of 512 entries
+    assert _hca(lib, ws=FAKE, ws_bytes=need - 1) == L.WORKSPACE_TOO_SMALL
+    assert _hca(lib, B=0) == L.OK
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(L, "_lib", None)
+    monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(ImportError):
+        L.load()

@@ -1,0 +1,135 @@
+"""GPU parity of csa_indexer_topk: index sets against the fp64 oracle's
+scores under the near-tie band rule, for fp32/bf16 prefill (chained on the
+GPU's own compressed keys) and bf16 / FP8 / FP4 decode."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import check_topk_row, dev, f64
+from oracle import formats
+from sparse_attention_17_amd import ops
+from synth import configs, inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _dequant(x, name, qk):
+    if qk == "fp8":
+        return formats.dequant_fp8_rows(x[name].numpy(), x[name + "_scale"].numpy())
+    if qk == "fp4":
+        return formats.dequant_fp4_blocks(x[name].numpy(), x[name + "_scale"].numpy())
+    return f64(x[name])
+
+
+def _check_rows(idx, qi64, w64, kic64, positions, m, k, sample=None):
+    rows = range(len(positions)) if sample is None else sample
+    exact = 0
+    n = 0
+    for t in rows:
+        pos = int(positions[t])
+        ne = min((pos + 1) // m, kic64.shape[0])
+        sc = oracle.csa.indexer_scores(qi64[t:t + 1], w64[t:t + 1], kic64[:ne])[0]
+        exact += check_topk_row(idx[t], sc, ne, k)
+        n += 1
+    return exact, n
+
+
+def _prefill(w, return_scores=False):
+    x = inputs.make_inputs(w)
+    g = {k: v.to(dev()) for k, v in x.items()}
+    _, _, kic = ops.compress(g["k"], g["v"], g["ki"], g["g"], w.m)
+    pos0 = torch.zeros(w.B, dtype=torch.int32, device=dev())
+    res = ops.indexer_topk(g["qi"], g["w"], kic, pos0, w.m, w.topk, max_pos=w.ctx - 1,
+                           return_scores=return_scores)
+    torch.cuda.synchronize()
+    return x, kic, res
+
+
+def test_tiny_f32_prefill_all_rows():
+    w = configs.TINY
+    x, kic, (idx, sc) = _prefill(w, return_scores=True)
+    idx = idx.cpu().numpy()
+    exact, n = _check_rows(idx[0], f64(x["qi"][0]), f64(x["w"][0]), f64(kic[0]),
+                           np.arange(w.ctx), w.m, w.topk)
+    assert exact == n          # fp32 ties this far apart: the sets must match exactly
+    # returned scores line up with the returned indices
+    s = sc.cpu().numpy()[0]
+    ref = oracle.csa.indexer_scores(f64(x["qi"][0]), f64(x["w"][0]), f64(kic[0]))
+    for t in (200, 700, 1023):
+        ne = (t + 1) // w.m
+        sel = idx[0, t][idx[0, t] >= 0]
+        np.testing.assert_allclose(s[t, :sel.size], ref[t, sel], rtol=1e-5, atol=1e-7)
+        assert np.all(np.isneginf(s[t, sel.size:]))
+        assert ne >= sel.size
+
+
+@pytest.mark.parametrize("HI,dI,k", [(4, 64, 512), (2, 32, 100), (1, 64, 64)])
+def test_bf16_prefill_slice(HI, dI, k):
+    w = configs.CSA_PREFILL_32K.with_(ctx=4096, Tq=4096, HI=HI, dI=dI, topk=k)
+    x, kic, idx = _prefill(w)
+    idx = idx.cpu().numpy()
+    sample = list(range(0, 16)) + list(range(2040, 2056)) + list(range(4080, 4096)) + \
+        list(np.random.default_rng(0).integers(0, 4096, 64))
+    exact, n = _check_rows(idx[0], f64(x["qi"][0]), f64(x["w"][0]), f64(kic[0]),
+                           np.arange(w.ctx), w.m, w.topk, sample)
+    assert exact >= n - 2
+
+
+def _decode(w):
+    x = inputs.make_inputs(w)
+    g = {k: v.to(dev()) for k, v in x.items()}
+    pos0 = torch.full((w.B,), w.ctx - 1, dtype=torch.int32, device=dev())
+    idx = ops.indexer_topk(g["qi"], g["w"], g["kic"], pos0, w.m, w.topk, max_pos=w.ctx - 1,
+                           qi_scale=g.get("qi_scale"), kic_scale=g.get("kic_scale"),
+                           qk_dtype=w.qk_dtype)
+    torch.cuda.synchronize()
+    return x, idx.cpu().numpy()
+
+
+def _check_decode(w, x, idx):
+    qi = _dequant(x, "qi", w.qk_dtype)
+    kic = _dequant(x, "kic", w.qk_dtype)
+    exact = 0
+    for b in range(w.B):
+        exact += _check_rows(idx[b], qi[b], f64(x["w"][b]), kic[b], [w.ctx - 1], w.m, w.topk)[0]
+    return exact
+
+
+@pytest.mark.parametrize("qk", ["bf16", "fp8", "fp4"])
+def test_decode_small(qk):
+    w = configs.HYBRID_1M_FP8.with_(ctx=65536 * 4, B=2, qk_dtype=qk, topk=2048)
+    x, idx = _decode(w)
+    assert _check_decode(w, x, idx) >= w.B - 1
+
+
+def test_decode_csa_128k_full():
+    w = configs.CSA_DECODE_128K
+    x, idx = _decode(w)
+    assert _check_decode(w, x, idx) >= w.B - 2
+
+
+@pytest.mark.parametrize("qk", ["fp8", "fp4"])
+def test_decode_hybrid_1m_full(qk):
+    w = configs.HYBRID_1M_FP8.with_(qk_dtype=qk)
+    x, idx = _decode(w)
+    assert _check_decode(w, x, idx) >= w.B - 1
+
+
+def test_padding_when_fewer_eligible_than_k():
+    w = configs.CSA_DECODE_128K.with_(ctx=4 * 1000, B=3, topk=4096)
+    x, idx = _decode(w)
+    assert np.all(idx[:, 0, :1000] == np.arange(1000)) and np.all(idx[:, 0, 1000:] == -1)
+
+
+def test_ragged_positions_per_sequence():
+    # sequences at different positions: each row sees its own eligible prefix
+    w = configs.CSA_DECODE_128K.with_(ctx=4 * 3000, B=3, topk=256)
+    x = inputs.make_inputs(w)
+    g = {k: v.to(dev()) for k, v in x.items()}
+    pos = [4 * 3000 - 1, 4 * 700 + 2, 5]
+    pos0 = torch.tensor(pos, dtype=torch.int32, device=dev())
+    idx = ops.indexer_topk(g["qi"], g["w"], g["kic"], pos0, 4, 256, max_pos=max(pos))
+    idx = idx.cpu().numpy()
+    for b in range(3):
+        _check_rows(idx[b], f64(x["qi"][b]), f64(x["w"][b]), f64(x["kic"][b]), [pos[b]], 4, 256)
