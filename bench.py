@@ -1,0 +1,257 @@
+"""Throughput of the CSA/HCA hot path on one MI355X.
+
+Default workload: one decode step of a hybrid CSA + HCA layer pair at a
+1,048,576-token context, batch 8 (one query token per sequence):
+  CSA: 262,144 compressed entries (m=4), lightning indexer with FP8 E4M3 keys
+       and queries (per-row fp32 scales, 4 heads x 64), top-2048, sliding
+       window 128, sink, 64 query heads sharing one KV head, d=128;
+  HCA: 8,192 entries (m'=128), dense over completed blocks, sink.
+A step = csa_indexer_topk -> csa_sparse_attend -> hca_attend on inputs already
+resident in HBM.  Inputs are seeded synthetic tensors; several copies rotate
+so consecutive steps do not hit the 256 MB last-level cache.
+
+Prints one JSON line.  `value` is query tokens per second for the step
+(batch / step time); `roofline` reports the dominant kernel's algorithmic
+bytes over its event-timed average launch duration against 8 TB/s;
+`cpu_baseline` times the fp64 oracle on the same inputs on host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import multiprocessing as mp
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "CSA/HCA query-tokens/s at 128K & 1M ctx; % of HBM BW (decode) / MFMA peak"
+
+_CPU_DATA = None      # inherited by forked oracle workers
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="hybrid_1m_fp8")
+    p.add_argument("--rotate", type=int, default=3, help="input copies cycled through")
+    p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    p.add_argument("--graph", type=int, default=1, help="replay the step as a HIP graph")
+    p.add_argument("--cpu-workers", type=int, default=0)
+    return p.parse_args()
+
+
+# ----------------------------------------------------------------------------
+# algorithmic bytes per launch (what the method must move; see DESIGN notes)
+# ----------------------------------------------------------------------------
+def algorithmic_bytes(w):
+    B, H, d = w.B, w.H, w.d
+    qk_row = {"fp8": w.dI + 4, "fp4": w.dI // 2 + w.dI // 32, "bf16": 2 * w.dI}[w.qk_dtype]
+    q_in = {"fp8": w.HI * (w.dI + 4), "fp4": w.HI * (w.dI // 2 + w.dI // 32),
+            "bf16": w.HI * 2 * w.dI}[w.qk_dtype] + 4 * w.HI
+    nk_csa = w.topk + w.window
+    return {
+        "indexer_score": B * (w.Nc * qk_row + q_in),
+        "indexer_zero": 0,
+        "indexer_split": 0,
+        "indexer_topk": B * w.topk * 4,
+        "attend_csa": B * (nk_csa * 2 * d * 2 + 2 * H * d * 2),
+        "attend_hca": B * (w.Nc_hca * 2 * d * 2 + 2 * H * d * 2),
+    }
+
+
+# ----------------------------------------------------------------------------
+# oracle CPU baseline (forked workers, one sequence each, single-threaded BLAS)
+# ----------------------------------------------------------------------------
+def _oracle_one(b):
+    from threadpoolctl import threadpool_limits
+    import oracle
+    from oracle import formats
+    x, w = _CPU_DATA
+    with threadpool_limits(1):
+        f = lambda t: t.double().numpy()  # noqa: E731
+        if w.qk_dtype == "fp8":
+            qi = formats.dequant_fp8_rows(x["qi"][b].numpy(), x["qi_scale"][b].numpy())
+            kic = formats.dequant_fp8_rows(x["kic"][b].numpy(), x["kic_scale"][b].numpy())
+        elif w.qk_dtype == "fp4":
+            qi = formats.dequant_fp4_blocks(x["qi"][b].numpy(), x["qi_scale"][b].numpy())
+            kic = formats.dequant_fp4_blocks(x["kic"][b].numpy(), x["kic_scale"][b].numpy())
+        else:
+            qi, kic = f(x["qi"][b]), f(x["kic"][b])
+        t = w.ctx - 1
+        ne = (t + 1) // w.m
+        sc = oracle.csa.indexer_scores(qi, f(x["w"][b]), kic[:ne])[0]
+        idx = oracle.csa.topk(sc, ne, w.topk)[None, :]
+        o1, _ = oracle.csa.sparse_attend(f(x["q"][b]), f(x["kc"][b]), f(x["vc"][b]), idx,
+                                         f(x["kw"][b]), f(x["vw"][b]), w.ctx - w.window, [t],
+                                         w.window, f(x["sink"]), w.scale)
+        o2, _ = oracle.hca.hca_attend(f(x["q_hca"][b]), f(x["kc_hca"][b]), f(x["vc_hca"][b]),
+                                      w.m_hca, [t], f(x["sink_hca"]), w.scale)
+    return b, o1, o2
+
+
+def cpu_baseline(x, w, workers):
+    global _CPU_DATA
+    _CPU_DATA = (x, w)
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(workers) as pool:
+        res = pool.map(_oracle_one, range(w.B))
+    dt = time.perf_counter() - t0
+    _CPU_DATA = None
+    outs = {b: (o1, o2) for b, o1, o2 in res}
+    return dt, outs
+
+
+# ----------------------------------------------------------------------------
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
+              "multi-GPU path: every box here has a single MI355X.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from synth import configs, inputs
+
+    w = configs.get(args.workload)
+    assert w.mode == "decode" and w.has_csa and w.has_hca, "bench drives the hybrid decode step"
+    t_gen = time.perf_counter()
+    x = inputs.make_inputs(w)
+    t_gen = time.perf_counter() - t_gen
+
+    cpu = None
+    ref = None
+    if not args.no_cpu:
+        try:
+            ncores = len(os.sched_getaffinity(0))
+        except AttributeError:
+            ncores = os.cpu_count() or 1
+        workers = args.cpu_workers or max(1, min(w.B, ncores, 16))
+        dt, ref = cpu_baseline(x, w, workers)
+        cpu = {"value": round(w.B / dt, 3), "unit": "query-tokens/s", "cores": workers,
+               "kind": "oracle",
+               "sample": f"one full decode step of {args.workload} (all {w.B} sequences: "
+                         f"fp64 indexer over {w.Nc} entries, top-{w.topk}, CSA + HCA attention), "
+                         f"{dt:.1f} s wall on {workers} processes x 1 BLAS thread"}
+
+    from sparse_attention_17_amd import _lib as L
+    from sparse_attention_17_amd import ops
+
+    dev = torch.device("cuda:0")
+    lib = L.load()
+    base = {k: v.to(dev) for k, v in x.items()}
+    sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(args.rotate - 1)]
+    pos0 = torch.full((w.B,), w.ctx - 1, dtype=torch.int32, device=dev)
+    rp0 = torch.full((w.B,), w.ctx - w.window, dtype=torch.int32, device=dev)
+    qk = w.qk_dtype
+
+    def step(g):
+        idx = ops.indexer_topk(g["qi"], g["w"], g["kic"], pos0, w.m, w.topk, max_pos=w.ctx - 1,
+                               qi_scale=g.get("qi_scale"), kic_scale=g.get("kic_scale"),
+                               qk_dtype=qk)
+        o1 = ops.sparse_attend(g["q"], g["kc"], g["vc"], idx, pos0, w.ctx - 1, w.window,
+                               kw=g["kw"], vw=g["vw"], raw_pos0=rp0, sink=g["sink"])
+        o2 = ops.hca_attend(g["q_hca"], g["kc_hca"], g["vc_hca"], w.m_hca, pos0, w.ctx - 1,
+                            sink=g["sink_hca"])
+        return o1, o2
+
+    # warm-up, then optional graph capture of one step per input copy
+    for i in range(args.warmup):
+        step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    runners = []
+    if args.graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for g in sets:
+                step(g)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        for g in sets:
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                outs = step(g)
+            runners.append((gr.replay, outs))
+        for r, _ in runners:
+            r()
+        torch.cuda.synchronize()
+    else:
+        runners = [((lambda g=g: step(g)), None) for g in sets]
+
+    # timed region
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(args.steps):
+        runners[i % len(runners)][0]()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # per-kernel launch durations from library-recorded hipEvents (eager steps)
+    lib.csa_profile_reset()
+    lib.csa_profile_enable(1)
+    nprof = 30
+    for i in range(nprof):
+        step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    lib.csa_profile_enable(0)
+    import ctypes as C
+    kern = {}
+    for name in ("indexer_zero", "indexer_score", "indexer_split", "indexer_topk", "attend_csa",
+                 "attend_hca", "attend_combine"):
+        n, t = C.c_int(0), C.c_double(0)
+        if lib.csa_profile_query(name.encode(), C.byref(n), C.byref(t)) == 0:
+            kern[name] = t.value / n.value * 1e3          # us per launch
+    lib.csa_profile_reset()
+
+    alg = algorithmic_bytes(w)
+    dom = max((k for k in alg if k in kern), key=lambda k: kern[k])
+    achieved = alg[dom] / (kern[dom] * 1e-6) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
+            "bytes_per_launch": alg[dom], "us_per_launch": round(kern[dom], 2)}
+    step_bytes = sum(alg.values())
+
+    # parity of the GPU step against the oracle outputs (when the baseline ran)
+    parity = None
+    if ref is not None:
+        o1, o2 = runners[0][1] if args.graph else step(sets[0])
+        torch.cuda.synchronize()
+        e1m = max(float(np.abs(o1[b].double().cpu().numpy() - ref[b][0]).max()) for b in range(w.B))
+        e2m = max(float(np.abs(o2[b].double().cpu().numpy() - ref[b][1]).max()) for b in range(w.B))
+        parity = {"csa_max_abs": e1m, "hca_max_abs": e2m, "tol": 2e-2,
+                  "ok": bool(e1m <= 2e-2 and e2m <= 2e-2)}
+
+    line = {
+        "metric": METRIC, "value": round(w.B / (ms * 1e-3), 1), "unit": "query-tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}_decode", "batch": w.B, "context": w.ctx,
+                   "csa_m": w.m, "csa_entries": w.Nc, "topk": w.topk, "window": w.window,
+                   "indexer": f"{w.qk_dtype} {w.HI}x{w.dI}", "hca_m": w.m_hca,
+                   "hca_entries": w.Nc_hca, "heads": w.H, "head_dim": w.d,
+                   "graph": bool(args.graph), "rotating_copies": args.rotate},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels_us": {k: round(v, 2) for k, v in kern.items()},
+        "step_algorithmic_bytes": step_bytes,
+        "step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "parity_vs_oracle": parity,
+        "input_gen_s": round(t_gen, 1),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -177,6 +177,21 @@ csa_status_t hca_attend(const void *q, const void *kc, const void *vc, int m_pri
                         void *out, float *lse_out,
                         void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Launch timing, for measurement tools (not part of any computation).
+ * While enabled, every kernel launch made by the library is bracketed by a
+ * pair of hipEvents recorded on that launch's stream.  csa_profile_query
+ * waits for the recorded events of `kernel` and returns (0) the number of
+ * launches and their summed GPU duration in milliseconds, or 1 if none were
+ * recorded, -1 on a HIP error.  Kernel names: "compress", "indexer_zero",
+ * "indexer_score", "indexer_split", "indexer_topk", "attend_csa", "attend_hca",
+ * "attend_combine".
+ * csa_profile_reset forgets all records (events are kept for reuse).
+ */
+void csa_profile_enable(int on);
+void csa_profile_reset(void);
+int csa_profile_query(const char *kernel, int *count, double *total_ms);
+
 #ifdef __cplusplus
 }
 #endif

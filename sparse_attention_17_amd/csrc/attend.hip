@@ -45,9 +45,14 @@ __host__ __device__ __forceinline__ int hca_ne(int pos, int mp, int cap) {
 template <typename T>
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <typename T, int D, int NW, bool SPARSE>
-__global__ __launch_bounds__(NW * 64) void attend_kernel(AttendArgs a, AttnGeom gm) {
+// RW row-waves (32 query rows each) x KG key groups (KG=2: each wave of a pair
+// takes one 32-key half of every 64-key tile; the two partial softmax states
+// are merged in LDS at the end).
+template <typename T, int D, int RW, int KG, bool SPARSE>
+__global__ __launch_bounds__(RW * KG * 64) void attend_kernel(AttendArgs a, AttnGeom gm) {
+  constexpr int NW = RW * KG;
   constexpr int NT = NW * 64;
+  constexpr int NSUB = 2 / KG;                 // 32-key sub-tiles per wave per tile
   constexpr int VEC = 16 / sizeof(T);          // elements per 16-byte chunk
   constexpr int KPAD = VEC;                    // Ks row padding (16 bytes)
   constexpr int VPAD = 4;                      // Vt row padding (elements)
@@ -64,6 +69,7 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(AttendArgs a, AttnGeom 
   __shared__ int s_nsel;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rw = wave % RW, kg = wave / RW;
   const int half = lane >> 5, col = lane & 31;
   const int b = blockIdx.z, split = blockIdx.y;
   const int t0 = blockIdx.x * gm.TT;
@@ -76,17 +82,24 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(AttendArgs a, AttnGeom 
   int ncomp;
   if constexpr (SPARSE) {
     // compact the valid selected entries of this (single) token into LDS
+    // each thread owns a contiguous run of the index row, loaded in one round
     const int32_t* ir = a.idx + ((size_t)b * a.Tq + t0) * a.topk;
-    uint32_t base = 0;
-    for (int c0 = 0; c0 < a.topk; c0 += NT) {
-      const int i = c0 + tid;
-      const int e = i < a.topk ? ir[i] : -1;
-      const uint32_t ok = (e >= 0 && e < a.Nc_cap) ? 1u : 0u;
-      uint32_t tot;
-      const uint32_t pos = block_excl_scan<NT>(ok, scan_sm, &tot);
-      if (ok) sel[base + pos] = e;
-      base += tot;
+    constexpr int RUN = (4096 + NT - 1) / NT;      // topk <= 4096
+    const int i0 = tid * RUN;
+    int ev[RUN];
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int q = 0; q < RUN; ++q) {
+      const int i = i0 + q;
+      ev[q] = i < a.topk ? ir[i] : -1;
     }
+#pragma unroll
+    for (int q = 0; q < RUN; ++q) cnt += (ev[q] >= 0 && ev[q] < a.Nc_cap) ? 1u : 0u;
+    uint32_t base;
+    uint32_t pos = block_excl_scan<NT>(cnt, scan_sm, &base);
+#pragma unroll
+    for (int q = 0; q < RUN; ++q)
+      if (ev[q] >= 0 && ev[q] < a.Nc_cap) sel[pos++] = ev[q];
     if (tid == 0) s_nsel = (int)base;
     __syncthreads();
     ncomp = s_nsel;
@@ -100,7 +113,7 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(AttendArgs a, AttnGeom 
   const int kend = min(nkeys, kbeg + gm.kps);
 
   // ---- this lane's query row ----
-  const int qr = wave * 32 + col;
+  const int qr = rw * 32 + col;
   const int tt = qr / a.H, hq = qr % a.H;
   const int tq = t0 + tt;
   const bool qvalid = (tt < gm.TT) && (tq < a.Tq);
@@ -146,55 +159,86 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(AttendArgs a, AttnGeom 
     }
   };
 
-  for (int s0 = kbeg; s0 < kend; s0 += KT) {
-    // ---- stage K (row-major) and V (transposed) ----
-    constexpr int KCH = D / VEC;                         // 16-byte chunks per row
-    for (int c = tid; c < KT * KCH; c += NT) {
+  // ---- staging: all global loads of a tile are issued into registers first
+  // (so they are in flight together), then written to LDS: K row-major, V
+  // transposed.  The next tile's loads are issued before the current tile is
+  // computed.
+  constexpr int KCH = D / VEC;                               // 16-byte chunks per row
+  constexpr int KLD = (KT * KCH + NT - 1) / NT;              // K chunks per thread
+  constexpr int VTOT = (KT / 4) * KCH;                       // V tasks: 4 keys x 16 bytes
+  constexpr int VTK = (VTOT + NT - 1) / NT;
+  u32x4 kreg[KLD];
+  u32x4 vreg[VTK][4];
+  auto stage_load = [&](int s0) {
+#pragma unroll
+    for (int i = 0; i < KLD; ++i) {
+      const int c = tid + i * NT;
       const int kk = c / KCH, ch = c % KCH;
       const T *kp, *vp;
       key_src(s0 + kk, kp, vp);
-      u32x4 val = {0, 0, 0, 0};
-      if (kp) val = *reinterpret_cast<const u32x4*>(kp + ch * VEC);
-      *reinterpret_cast<u32x4*>(Ks + kk * KS + ch * VEC) = val;
+      kreg[i] = u32x4{0, 0, 0, 0};
+      if (kp && c < KT * KCH) kreg[i] = *reinterpret_cast<const u32x4*>(kp + ch * VEC);
     }
-    for (int c = tid; c < (KT / 4) * KCH; c += NT) {
+#pragma unroll
+    for (int i = 0; i < VTK; ++i) {
+      const int c = tid + i * NT;
       const int kg = c / KCH, ch = c % KCH;
-      T rows[4][VEC];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const T *kp, *vp;
         key_src(s0 + kg * 4 + u, kp, vp);
-        u32x4 val = {0, 0, 0, 0};
-        if (vp) val = *reinterpret_cast<const u32x4*>(vp + ch * VEC);
-        *reinterpret_cast<u32x4*>(rows[u]) = val;
+        vreg[i][u] = u32x4{0, 0, 0, 0};
+        if (vp && c < VTOT) vreg[i][u] = *reinterpret_cast<const u32x4*>(vp + ch * VEC);
       }
+    }
+  };
+  auto stage_store = [&]() {
+#pragma unroll
+    for (int i = 0; i < KLD; ++i) {
+      const int c = tid + i * NT;
+      if (c < KT * KCH) *reinterpret_cast<u32x4*>(Ks + (c / KCH) * KS + (c % KCH) * VEC) = kreg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VTK; ++i) {
+      const int c = tid + i * NT;
+      if (c >= VTOT) continue;
+      const int kg = c / KCH, ch = c % KCH;
+      const T* rows = reinterpret_cast<const T*>(vreg[i]);      // [4][VEC]
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
-        T four[4] = {rows[0][e], rows[1][e], rows[2][e], rows[3][e]};
+        T four[4] = {rows[e], rows[VEC + e], rows[2 * VEC + e], rows[3 * VEC + e]};
         T* dst = Vt + (ch * VEC + e) * VS + kg * 4;
         if constexpr (sizeof(T) == 2) *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<uint2*>(four);
         else *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<u32x4*>(four);
       }
     }
-    __syncthreads();
+  };
 
-    // ---- S^T = K Q^T for two 32-key sub-tiles ----
-    f32x16 st[2];
+  if (kbeg < kend) stage_load(kbeg);
+  for (int s0 = kbeg; s0 < kend; s0 += KT) {
+    stage_store();
+    __syncthreads();
+    if (s0 + KT < kend) stage_load(s0 + KT);
+
+    // ---- S^T = K Q^T for this wave's 32-key sub-tiles ----
+    f32x16 st[NSUB];
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
+    for (int si = 0; si < NSUB; ++si) {
+      const int sub = KG == 2 ? kg : si;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) st[sub][r] = 0.f;
+      for (int r = 0; r < 16; ++r) st[si][r] = 0.f;
 #pragma unroll
       for (int s = 0; s < DSTEP; ++s) {
         Frag<T> kf;
         frag_load(kf, Ks + (sub * 32 + col) * KS + 16 * s + 8 * half);
-        mma32(st[sub], kf, qf[s]);
+        mma32(st[si], kf, qf[s]);
       }
     }
     // ---- mask, online softmax ----
     float mt = -INFINITY;
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
+    for (int si = 0; si < NSUB; ++si) {
+      const int sub = KG == 2 ? kg : si;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int s = s0 + sub * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
@@ -206,8 +250,8 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(AttendArgs a, AttnGeom 
         } else if (ok && !SPARSE) {
           ok = s < q_ne;
         }
-        const float x = ok ? st[sub][r] * gm.scale_log2 : -INFINITY;
-        st[sub][r] = x;
+        const float x = ok ? st[si][r] * gm.scale_log2 : -INFINITY;
+        st[si][r] = x;
         mt = fmaxf(mt, x);
       }
     }
@@ -216,17 +260,17 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(AttendArgs a, AttnGeom 
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     const float alpha = fexp2<T>(m_run - m_use);
     float psum = 0.f;
-    Frag<T> pf[2][2];
+    Frag<T> pf[NSUB][2];
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
+    for (int si = 0; si < NSUB; ++si) {
       float pv[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        pv[r] = fexp2<T>(st[sub][r] - m_use);
+        pv[r] = fexp2<T>(st[si][r] - m_use);
         psum += pv[r];
       }
-      frag_from_f32(pf[sub][0], pv);
-      frag_from_f32(pf[sub][1], pv + 8);
+      frag_from_f32(pf[si][0], pv);
+      frag_from_f32(pf[si][1], pv + 8);
     }
     l_run = l_run * alpha + psum;
     m_run = m_new;
@@ -240,7 +284,8 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(AttendArgs a, AttnGeom 
     for (int i = 0; i < DVT; ++i) {
       const T* vrow = Vt + (i * 32 + col) * VS;
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
+      for (int si = 0; si < NSUB; ++si) {
+        const int sub = KG == 2 ? kg : si;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           const int kb = sub * 32 + 16 * ks + 4 * half;
@@ -256,11 +301,36 @@ __global__ __launch_bounds__(NW * 64) void attend_kernel(AttendArgs a, AttnGeom 
             fv[0] = lo[0]; fv[1] = lo[1]; fv[2] = lo[2]; fv[3] = lo[3];
             fv[4] = hi[0]; fv[5] = hi[1]; fv[6] = hi[2]; fv[7] = hi[3];
           }
-          mma32(o[i], vf, pf[sub][ks]);
+          mma32(o[i], vf, pf[si][ks]);
         }
       }
     }
     __syncthreads();
+  }
+
+  // ---- merge the two key groups (their staging area is free now) ----
+  if constexpr (KG == 2) {
+    float* mb = reinterpret_cast<float*>(smem_raw) + (size_t)(rw * 64 + lane) * (DVT * 16 + 2);
+    if (kg == 1) {
+#pragma unroll
+      for (int i = 0; i < DVT; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mb[i * 16 + r] = o[i][r];
+      mb[DVT * 16] = m_run;
+      mb[DVT * 16 + 1] = l_run;
+    }
+    __syncthreads();
+    if (kg == 1) return;
+    const float m1 = mb[DVT * 16], l1 = mb[DVT * 16 + 1];
+    const float M = fmaxf(m_run, m1);
+    const float Mu = (M == -INFINITY) ? 0.f : M;
+    const float c0 = fexp2<T>(m_run - Mu), c1 = fexp2<T>(m1 - Mu);
+#pragma unroll
+    for (int i = 0; i < DVT; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[i][r] = o[i][r] * c0 + mb[i * 16 + r] * c1;
+    l_run = l_run * c0 + l1 * c1;
+    m_run = M;
   }
 
   // ---- epilogue ----
@@ -320,25 +390,29 @@ __global__ __launch_bounds__(256) void combine_kernel(AttendArgs a, int nsplit) 
   const float* pl = pm + (size_t)nsplit * rows_total;
   const int h = (int)(row % a.H);
   const float s2 = a.sink ? a.sink[h] * LOG2E : -INFINITY;
-  float M = s2;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pm[s * rows_total + row]);
+  float mloc = -INFINITY;
+  for (int s = lane; s < nsplit; s += 64) mloc = fmaxf(mloc, pm[s * rows_total + row]);
+  const float M = fmaxf(wave_max(mloc), s2);
   constexpr int PER = D / 64;
   float acc[PER];
 #pragma unroll
   for (int u = 0; u < PER; ++u) acc[u] = 0.f;
-  float Z = 0.f, lse = -INFINITY;
+  float lse = -INFINITY, inv = 0.f;
   if (M != -INFINITY) {
-    Z = __builtin_amdgcn_exp2f(s2 - M);
+    float zl = 0.f;
+    for (int s = lane; s < nsplit; s += 64)
+      zl += pl[s * rows_total + row] * __builtin_amdgcn_exp2f(pm[s * rows_total + row] - M);
+    const float Z = wave_sum(zl) + __builtin_amdgcn_exp2f(s2 - M);
+#pragma unroll 4
     for (int s = 0; s < nsplit; ++s) {
-      const float ms = pm[s * rows_total + row];
-      const float c = __builtin_amdgcn_exp2f(ms - M);
-      Z += pl[s * rows_total + row] * c;
+      const float c = __builtin_amdgcn_exp2f(pm[s * rows_total + row] - M);
+      const float* src = po + (s * rows_total + row) * D + lane * PER;
 #pragma unroll
-      for (int u = 0; u < PER; ++u) acc[u] += po[(s * rows_total + row) * D + lane * PER + u] * c;
+      for (int u = 0; u < PER; ++u) acc[u] = fmaf(src[u], c, acc[u]);
     }
     lse = (M + __log2f(Z)) * LN2;
+    inv = 1.f / Z;
   }
-  const float inv = (M != -INFINITY) ? 1.f / Z : 0.f;
   T* orow = reinterpret_cast<T*>(a.out) + row * D;
 #pragma unroll
   for (int u = 0; u < PER; ++u) orow[lane * PER + u] = from_f32<T>(acc[u] * inv);
@@ -348,7 +422,7 @@ __global__ __launch_bounds__(256) void combine_kernel(AttendArgs a, int nsplit) 
 // ---------------------------------- host -----------------------------------
 static int keys_per_split(bool sparse, int Tq) {
   if (Tq != 1) return INT_MAX / 2;
-  return sparse ? 128 : 512;
+  return sparse ? 128 : 256;
 }
 
 static int tokens_per_tile(bool sparse, int H, int Tq) {
@@ -371,32 +445,40 @@ size_t attend_workspace(bool sparse, int B, int Tq, int H, int d, int topk, int 
   return (size_t)ns * B * Tq * H * (d + 2) * sizeof(float);
 }
 
-template <typename T, int D, int NW, bool SPARSE>
+template <typename T, int D, int RW, int KG, bool SPARSE>
 static hipError_t launch4(const AttendArgs& a, const AttnGeom& gm, hipStream_t st) {
   constexpr int KS = D + 16 / sizeof(T);
   constexpr int VS = KT + 4;
-  const size_t lds = (size_t)(KT * KS + D * VS) * sizeof(T) + (SPARSE ? (size_t)a.topk * 4 : 0);
-  auto kfn = attend_kernel<T, D, NW, SPARSE>;
+  size_t lds = (size_t)(KT * KS + D * VS) * sizeof(T) + (SPARSE ? (size_t)a.topk * 4 : 0);
+  if (KG == 2) lds = std::max(lds, (size_t)RW * 64 * ((D / 32) * 16 + 2) * sizeof(float));
+  auto kfn = attend_kernel<T, D, RW, KG, SPARSE>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
   dim3 grid((a.Tq + gm.TT - 1) / gm.TT, gm.nsplit, a.B);
-  hipLaunchKernelGGL(kfn, grid, dim3(NW * 64), lds, st, a, gm);
+  {
+    ProfScope ps(SPARSE ? "attend_csa" : "attend_hca", st);
+    hipLaunchKernelGGL(kfn, grid, dim3(RW * KG * 64), lds, st, a, gm);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || gm.nsplit <= 1) return e;
   const size_t rows = (size_t)a.B * a.Tq * a.H;
+  ProfScope ps("attend_combine", st);
   hipLaunchKernelGGL((combine_kernel<T, D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st,
                      a, gm.nsplit);
   return hipGetLastError();
 }
 
+// Row-waves cover the tile's (token, head) rows; tiles of at most 64 rows get
+// a second key group so that four waves share every staged tile.
 template <typename T, int D, bool SPARSE>
 static hipError_t launch3(const AttendArgs& a, const AttnGeom& gm, hipStream_t st) {
   const int rows = gm.TT * a.H;
-  if (rows <= 32) return launch4<T, D, 1, SPARSE>(a, gm, st);
-  if (rows <= 64) return launch4<T, D, 2, SPARSE>(a, gm, st);
-  return launch4<T, D, 4, SPARSE>(a, gm, st);
+  if (rows <= 32) return launch4<T, D, 1, 2, SPARSE>(a, gm, st);
+  if (rows <= 64) return launch4<T, D, 2, 2, SPARSE>(a, gm, st);
+  if (rows <= 96) return launch4<T, D, 3, 1, SPARSE>(a, gm, st);
+  return launch4<T, D, 4, 1, SPARSE>(a, gm, st);
 }
 
 template <typename T, int D>

@@ -140,6 +140,7 @@ static hipError_t launch_t(const CompressArgs& a, hipStream_t st) {
   const int Nc = a.T / a.m;
   if (Nc == 0 || a.B == 0) return hipSuccess;
   dim3 grid((Nc + 3) / 4, a.B);
+  ProfScope ps("compress", st);
   hipLaunchKernelGGL((compress_kernel<T, D, DI>), grid, dim3(256), 0, st,
                      (const T*)a.k, (const T*)a.v, (const T*)a.ki, a.gate, a.pos_bias,
                      a.T, a.m, Nc, a.Nc_cap, (T*)a.kc, (T*)a.vc, (T*)a.kic);

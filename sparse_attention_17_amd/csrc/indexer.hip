@@ -7,57 +7,77 @@
 // then the k largest I[t,.] with equal scores going to the lower j, emitted
 // ascending by j and padded with -1.
 //
-// Score kernel: the (token, head) rows of qI form the MFMA A operand (16 rows
-// = 16/HI tokens), compressed indexer keys form B (16 entries per MFMA), so the
-// 16x16 accumulator hands every lane the HI head dots of one token for one
-// entry: ReLU and the head weighting happen in-lane.  FP8/FP4 codes are widened
-// exactly to bf16 in registers (E4M3 and E2M1 x E8M0 values are all bf16
-// values); products are exact and accumulate in fp32.
+// Scores (MFMA 16x16x32: bf16, fp32 as 8 x 16x16x4, FP8 E4M3 natively; FP4
+// codes times their E8M0 block scale are widened exactly to bf16):
+//   * prefill tile kernel: (token, head) rows of qI form the A operand (16
+//     rows = 16/HI tokens) and 16 entries form B, so each lane receives the HI
+//     head dots of one token for one entry and applies ReLU + head weights
+//     in-lane;
+//   * decode row kernel: one query row; its HI head rows are placed at a
+//     different row block for each of 16/HI entry tiles accumulated into one
+//     16x16 tile, so all 64 lanes finish one score per 64 entries (HI=4).  It
+//     also builds a 12-bit radix histogram of the row's score keys.
+// Scores are >= 0 (+0 for ReLU'd zeros), so their fp32 bit patterns order like
+// the values.
 //
-// Top-k kernel: one workgroup per query row.  The scores are non-negative
-// (+0 for ReLU'd zeros), so their fp32 bit patterns order like the values and
-// an 11/11/10-bit radix select finds the k-th largest key tau and how many
-// entries equal to tau are needed; a chunked, index-ordered compaction then
-// takes every key > tau and the lowest-indexed keys == tau, which yields the
-// ascending index list directly.
+// Top-k:
+//   * rows that fit in LDS: one workgroup per row runs an 11/11/10-bit radix
+//     select for the k-th largest key tau and the count of ties needed, then an
+//     index-ordered compaction keeps keys > tau and the lowest-indexed keys
+//     == tau, which is already ascending;
+//   * long rows (decode over 32K-262K entries): the histogram gives the bin of
+//     tau; a many-workgroup pass writes every index whose key lies above that
+//     bin straight to the selection and collects the bin's (key, index) pairs;
+//     one workgroup per row then resolves the bin exactly in LDS (radix on the
+//     low 20 bits, lowest index among ties) and sorts the k indices.  A row
+//     whose boundary bin overflows the candidate buffer falls back to the
+//     exact single-workgroup select over the stored scores.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace csa {
 
-static constexpr int SCORE_WG_ENTRIES = 256;   // 4 waves x 4 tiles x 16 entries
+static constexpr int SCORE_WG_ENTRIES = 256;   // prefill tile kernel: 4 waves x 4 tiles x 16
+static constexpr int ROW_CHUNK = 2048;         // decode row kernel: entries per workgroup
+static constexpr int H1_BITS = 12;             // first radix digit (key bits 20..31)
+static constexpr int H1_BINS = 1 << H1_BITS;
+static constexpr int CAND_G = 16384;           // boundary-bin candidates kept per row
+static constexpr int CAND_L = 8192;            // candidates resolved in LDS
+static constexpr int TOPK_NT = 512;
+static constexpr int TOPK_LDS_KEYS = 12288;
 
 __host__ __device__ __forceinline__ int nc_pad(int Nc_cap) { return (Nc_cap + 63) & ~63; }
 
 // ---------------- operand loaders: 8 k-values -> one fragment --------------
-// qk element encodings
+struct Frag8 { uint64_t v; };                   // 8 FP8 codes
 template <int QK> struct QkTraits;
-template <> struct QkTraits<QK_F32> { using Elem = float; using F = Frag<float>; };
-template <> struct QkTraits<QK_BF16> { using Elem = bf16; using F = Frag<bf16>; };
-template <> struct QkTraits<QK_FP8> { using Elem = uint8_t; using F = Frag<bf16>; };
-template <> struct QkTraits<QK_FP4> { using Elem = uint8_t; using F = Frag<bf16>; };
+template <> struct QkTraits<QK_F32> { using F = Frag<float>; };
+template <> struct QkTraits<QK_BF16> { using F = Frag<bf16>; };
+template <> struct QkTraits<QK_FP8> { using F = Frag8; };
+template <> struct QkTraits<QK_FP4> { using F = Frag<bf16>; };
 
-// E4M3 code -> bf16 bits (exact).
-__device__ __forceinline__ uint32_t e4m3_to_bf16_bits(uint32_t c) {
-  const uint32_t s = (c & 0x80u) << 8;
-  const uint32_t em = c & 0x7Fu;
-  const uint32_t e = em >> 3;
-  // normal: exponent e-7 -> bf16 exponent e+120; mantissa 3 bits -> top of 7
-  const uint32_t nrm = (em << 4) + (120u << 7);
-  // subnormal: (c & 7) * 2^-9, exact in fp32
-  const uint32_t sub = __float_as_uint((float)(em & 7u) * 0.001953125f) >> 16;
-  return s | (e ? nrm : sub);
+__device__ __forceinline__ void frag_zero(Frag8& f) { f.v = 0; }
+__device__ __forceinline__ void mma16(f32x4& c, const Frag8& a, const Frag8& b) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)a.v, (long)b.v, c, 0, 0, 0);
 }
-// E2M1 code (low 4 bits) times 2^(E-127) -> fp32 (exact).
+
+// E2M1 code (low 4 bits) -> fp32 value.
 __device__ __forceinline__ float e2m1_val(uint32_t c) {
   const uint32_t e = (c >> 1) & 3u, f = c & 1u;
   float mag = e ? (1.f + 0.5f * (float)f) * (float)(1u << e) * 0.5f : 0.5f * (float)f;
   return (c & 8u) ? -mag : mag;
 }
+// E8M0 code -> 2^(E-127) (E = 0 gives the subnormal 2^-127).
+__device__ __forceinline__ float e8m0_val(uint32_t e) {
+  return e ? __uint_as_float(e << 23) : __uint_as_float(0x00400000u);
+}
 
-// Load the fragment for a row of `dI` k-values: elements k0 .. k0+7.
-// FP8: `row` points at the codes of the row (scale applied by the caller).
-// FP4: `row` points at packed codes; `sc` at the row's E8M0 scales.
+// Fragment of elements k0 .. k0+7 of a row.  FP4: `row` points at packed codes
+// and `sc` at the row's E8M0 scales; the FP8 per-row scale is applied later.
+// The score kernels give lane group g (lanes 16g..16g+15) the elements
+// 8*(g*KC + c) .. +7 for k-chunk c, so a lane's operand bytes are contiguous;
+// the MFMA reduction is over all k, so any such relabelling shared by both
+// operands gives the same dot product.
 template <int QK>
 __device__ __forceinline__ void load_qk_frag(typename QkTraits<QK>::F& f, const void* row,
                                              const uint8_t* sc, int k0) {
@@ -66,16 +86,10 @@ __device__ __forceinline__ void load_qk_frag(typename QkTraits<QK>::F& f, const 
   } else if constexpr (QK == QK_BF16) {
     frag_load(f, reinterpret_cast<const bf16*>(row) + k0);
   } else if constexpr (QK == QK_FP8) {
-    const uint2 c = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(row) + k0);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const uint32_t w = i ? c.y : c.x;
-      f.v[2 * i] = e4m3_to_bf16_bits(w & 0xFF) | (e4m3_to_bf16_bits((w >> 8) & 0xFF) << 16);
-      f.v[2 * i + 1] = e4m3_to_bf16_bits((w >> 16) & 0xFF) | (e4m3_to_bf16_bits(w >> 24) << 16);
-    }
+    f.v = *reinterpret_cast<const uint64_t*>(reinterpret_cast<const uint8_t*>(row) + k0);
   } else {
     const uint32_t c = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(row) + k0 / 2);
-    const float scl = __uint_as_float((uint32_t)sc[k0 / 32] << 23);   // 2^(E-127)
+    const float scl = e8m0_val(sc[k0 / 32]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t byte = (c >> (8 * i)) & 0xFF;
@@ -86,16 +100,47 @@ __device__ __forceinline__ void load_qk_frag(typename QkTraits<QK>::F& f, const 
   }
 }
 
-template <int QK> __device__ __forceinline__ size_t qk_row_bytes(int dI) {
+template <int QK> __host__ __device__ __forceinline__ size_t qk_row_bytes(int dI) {
   if constexpr (QK == QK_F32) return (size_t)dI * 4;
   else if constexpr (QK == QK_BF16) return (size_t)dI * 2;
   else if constexpr (QK == QK_FP8) return (size_t)dI;
   else return (size_t)dI / 2;
 }
 
-// ---------------------------------- scores ---------------------------------
+__device__ __forceinline__ int row_len(const IndexerArgs& a, int b, int t) {
+  return max(0, min((a.pos0[b] + t + 1) / a.m, a.Nc_cap));
+}
+
+// Workspace carve-up for the long-row path (per query row):
+//   scores [rows][ldo] f32 | hist [rows][4096] u32 | cnt [rows][4] u32 |
+//   sel [rows][topk] u32 | cand [rows][CAND_G][2] u32
+struct LongWs {
+  float* scores;
+  uint32_t *hist, *cnt, *sel, *cand;
+};
+__host__ __device__ __forceinline__ LongWs long_ws(void* ws, int rows, int Nc_cap, int topk) {
+  LongWs w;
+  char* p = reinterpret_cast<char*>(ws);
+  w.scores = reinterpret_cast<float*>(p);
+  p += (size_t)rows * nc_pad(Nc_cap) * 4;
+  w.hist = reinterpret_cast<uint32_t*>(p);
+  p += (size_t)rows * H1_BINS * 4;
+  w.cnt = reinterpret_cast<uint32_t*>(p);
+  p += (size_t)rows * 4 * 4;
+  w.sel = reinterpret_cast<uint32_t*>(p);
+  p += (size_t)rows * ((topk + 3) & ~3) * 4;
+  w.cand = reinterpret_cast<uint32_t*>(p);
+  return w;
+}
+static size_t long_ws_bytes(int rows, int Nc_cap, int topk) {
+  return (size_t)rows * ((size_t)nc_pad(Nc_cap) * 4 + H1_BINS * 4 + 16 +
+                         (size_t)((topk + 3) & ~3) * 4 + (size_t)CAND_G * 8);
+}
+static bool use_long_path(int Tq, int Nc_cap) { return Tq <= 4 && Nc_cap > TOPK_LDS_KEYS; }
+
+// --------------------------- prefill score tile ----------------------------
 template <int QK, int DI, int HI>
-__global__ __launch_bounds__(256) void score_kernel(IndexerArgs a) {
+__global__ __launch_bounds__(256) void score_tile_kernel(IndexerArgs a) {
   constexpr int TT = 16 / HI;        // tokens per workgroup
   constexpr int KC = DI / 32;        // 32-wide k chunks
   using F = typename QkTraits<QK>::F;
@@ -103,13 +148,10 @@ __global__ __launch_bounds__(256) void score_kernel(IndexerArgs a) {
   const int b = blockIdx.z;
   const int t0 = blockIdx.y * TT;
   const int e_wg = blockIdx.x * SCORE_WG_ENTRIES;
-  const int pos_first = a.pos0[b] + t0;
   const int t_last = min(t0 + TT, a.Tq) - 1;
-  const int ne_max = min((a.pos0[b] + t_last + 1) / a.m, a.Nc_cap);
+  const int ne_max = row_len(a, b, t_last);
   if (e_wg >= ne_max) return;
-  (void)pos_first;
 
-  // A operand: query rows (token, head)
   const int r = lane & 15, g = lane >> 4;
   const int tq = t0 + r / HI, hq = r % HI;
   F qa[KC];
@@ -119,10 +161,9 @@ __global__ __launch_bounds__(256) void score_kernel(IndexerArgs a) {
   if constexpr (QK == QK_FP4) qsc = reinterpret_cast<const uint8_t*>(a.qi_scale) + qrow * (DI / 32);
 #pragma unroll
   for (int c = 0; c < KC; ++c) {
-    if (tq < a.Tq) load_qk_frag<QK>(qa[c], qptr, qsc, 32 * c + 8 * g);
+    if (tq < a.Tq) load_qk_frag<QK>(qa[c], qptr, qsc, 8 * (g * KC + c));
     else frag_zero(qa[c]);
   }
-  // per-lane output rows 4g..4g+3 -> (token, head) weights (FP8: x query scale)
   float wr[4];
   int trow[4];
 #pragma unroll
@@ -145,7 +186,7 @@ __global__ __launch_bounds__(256) void score_kernel(IndexerArgs a) {
   for (int tile = 0; tile < 4; ++tile) {
     const int e0 = e_wg + (wave * 4 + tile) * 16;
     if (e0 >= ne_max) break;
-    const int e = e0 + r;                      // B operand column / output column
+    const int e = e0 + r;
     const bool ev = e < ne_max;
     const size_t krow = (size_t)b * a.Nc_cap + (ev ? e : 0);
     const char* kptr = reinterpret_cast<const char*>(a.kic) + krow * qk_row_bytes<QK>(DI);
@@ -155,12 +196,11 @@ __global__ __launch_bounds__(256) void score_kernel(IndexerArgs a) {
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
       F kb;
-      load_qk_frag<QK>(kb, kptr, ksc, 32 * c + 8 * g);
+      load_qk_frag<QK>(kb, kptr, ksc, 8 * (g * KC + c));
       mma16(acc, qa[c], kb);
     }
     float cs = 1.f;
     if constexpr (QK == QK_FP8) cs = reinterpret_cast<const float*>(a.kic_scale)[krow];
-    // acc[i] = dot of row 4g+i with entry e
     float s[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -171,50 +211,158 @@ __global__ __launch_bounds__(256) void score_kernel(IndexerArgs a) {
     for (int u = 0; u < 4 / HI; ++u) {
       const int t = trow[u * HI];
       if (t < a.Tq && ev) {
-        const int ne = min((a.pos0[b] + t + 1) / a.m, a.Nc_cap);
-        if (e < ne) ws[((size_t)b * a.Tq + t) * ldo + e] = s[u] * cs + 0.f;
+        if (e < row_len(a, b, t)) ws[((size_t)b * a.Tq + t) * ldo + e] = s[u] * cs + 0.f;
       }
     }
   }
 }
 
-// ---------------------------------- top-k ----------------------------------
-static constexpr int TOPK_NT = 512;
-static constexpr int TOPK_LDS_KEYS = 12288;
+// ---------------------------- decode score row -----------------------------
+template <int QK, int DI, int HI>
+__global__ __launch_bounds__(256) void score_row_kernel(IndexerArgs a) {
+  constexpr int KC = DI / 32;
+  constexpr int TPC = 16 / HI;        // 16-entry tiles accumulated into one 16x16 tile
+  constexpr int EPC = 16 * TPC;       // entries per accumulator (64 for HI=4)
+  constexpr int SPL = 4 / HI;         // scores per lane per accumulator
+  using F = typename QkTraits<QK>::F;
+  __shared__ uint32_t hist[H1_BINS];
 
-struct TopkSmem {
-  uint32_t hist[2048];
-  uint32_t scan[TOPK_NT / 64];
-  uint32_t bin, above;
-};
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = blockIdx.y;
+  const int b = row / a.Tq, t = row % a.Tq;
+  const int n = row_len(a, b, t);
+  const int c0 = blockIdx.x * ROW_CHUNK;
+  if (c0 >= n) return;
+  const int c1 = min(n, c0 + ROW_CHUNK);
+  LongWs L = long_ws(a.ws, a.B * a.Tq, a.Nc_cap, a.topk);
+  for (int i = threadIdx.x; i < H1_BINS; i += 256) hist[i] = 0;
 
-// Locate, scanning from the top bin down, the bin where the running count
-// first reaches `need`; writes the bin and the count strictly above it.
-__device__ void find_bin(TopkSmem& sm, int nbins, uint32_t need) {
-  const int per = nbins / TOPK_NT;              // 4 or 2 bins per thread
+  // A operands: for tile u the query's HI head rows sit at rows u*HI .. u*HI+HI-1
+  const int r = lane & 15, g = lane >> 4;
+  const int hq = r % HI, uq = r / HI;
+  const size_t qrow = ((size_t)b * a.Tq + t) * HI + hq;
+  const char* qptr = reinterpret_cast<const char*>(a.qi) + qrow * qk_row_bytes<QK>(DI);
+  const uint8_t* qsc = nullptr;
+  if constexpr (QK == QK_FP4) qsc = reinterpret_cast<const uint8_t*>(a.qi_scale) + qrow * (DI / 32);
+  F qv[KC];
+#pragma unroll
+  for (int c = 0; c < KC; ++c) load_qk_frag<QK>(qv[c], qptr, qsc, 8 * (g * KC + c));
+  F qa[TPC][KC];
+#pragma unroll
+  for (int u = 0; u < TPC; ++u)
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      if (u == uq) qa[u][c] = qv[c];
+      else frag_zero(qa[u][c]);
+    }
+  // weights of the head rows this lane receives: rows 4g+i -> head (4g+i) % HI
+  float wr[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const size_t wi = ((size_t)b * a.Tq + t) * HI + ((4 * g + i) % HI);
+    float wv = a.w[wi];
+    if constexpr (QK == QK_FP8) wv *= reinterpret_cast<const float*>(a.qi_scale)[wi];
+    wr[i] = wv;
+  }
+  __syncthreads();
+
+  const size_t rb = qk_row_bytes<QK>(DI);
+  const char* kbase = reinterpret_cast<const char*>(a.kic) + (size_t)b * a.Nc_cap * rb;
+  const uint8_t* sbase = nullptr;
+  if constexpr (QK == QK_FP4) sbase = reinterpret_cast<const uint8_t*>(a.kic_scale) + (size_t)b * a.Nc_cap * (DI / 32);
+  const float* fsc = nullptr;
+  if constexpr (QK == QK_FP8) fsc = reinterpret_cast<const float*>(a.kic_scale) + (size_t)b * a.Nc_cap;
+  float* srow = L.scores + (size_t)row * nc_pad(a.Nc_cap);
+
+  auto load_group = [&](int e0, F (&kb)[TPC][KC]) {
+#pragma unroll
+    for (int u = 0; u < TPC; ++u) {
+      const int e = min(e0 + 16 * u + r, c1 - 1);
+#pragma unroll
+      for (int c = 0; c < KC; ++c)
+        load_qk_frag<QK>(kb[u][c], kbase + (size_t)e * rb,
+                         QK == QK_FP4 ? sbase + (size_t)e * (DI / 32) : nullptr, 8 * (g * KC + c));
+    }
+  };
+
+  F kb[TPC][KC];
+  int e0 = c0 + wave * EPC;
+  if (e0 < c1) load_group(e0, kb);
+#pragma unroll 1
+  for (; e0 < c1; e0 += 4 * EPC) {
+    F cur[TPC][KC];
+#pragma unroll
+    for (int u = 0; u < TPC; ++u)
+#pragma unroll
+      for (int c = 0; c < KC; ++c) cur[u][c] = kb[u][c];
+    if (e0 + 4 * EPC < c1) load_group(e0 + 4 * EPC, kb);      // prefetch the next group
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < TPC; ++u)
+#pragma unroll
+      for (int c = 0; c < KC; ++c) mma16(acc, qa[u][c], cur[u][c]);
+#pragma unroll
+    for (int s = 0; s < SPL; ++s) {
+      const int u = (4 * g) / HI + s;
+      const int e = e0 + 16 * u + r;
+      float sc = 0.f;
+#pragma unroll
+      for (int h = 0; h < HI; ++h) {
+        const float x = acc[s * HI + h];
+        sc = fmaf(wr[s * HI + h], x > 0.f ? x : 0.f, sc);
+      }
+      if (e < c1) {
+        if constexpr (QK == QK_FP8) sc *= fsc[e];
+        sc += 0.f;
+        srow[e] = sc;
+        atomicAdd(&hist[__float_as_uint(sc) >> (32 - H1_BITS)], 1u);
+      }
+    }
+  }
+  __syncthreads();
+  uint32_t* gh = L.hist + (size_t)row * H1_BINS;
+  for (int i = threadIdx.x; i < H1_BINS; i += 256) {
+    const uint32_t v = hist[i];
+    if (v) atomicAdd(&gh[i], v);
+  }
+}
+
+// --------------------------- shared select helpers --------------------------
+// Scanning bins from the top down, find the bin where the running count first
+// reaches `need`; out[0] = bin, out[1] = count strictly above it.
+template <int NT>
+__device__ void find_bin(const uint32_t* hist, int nbins, uint32_t need, uint32_t* scan,
+                         uint32_t* out) {
+  const int per = nbins / NT;
   const int tid = threadIdx.x;
-  const int hi = nbins - tid * per;             // my bins: [hi-per, hi), scanned top-down
+  const int hi = nbins - tid * per;
   uint32_t local = 0;
-  for (int i = 0; i < per; ++i) local += sm.hist[hi - 1 - i];
+  for (int i = 0; i < per; ++i) local += hist[hi - 1 - i];
   uint32_t tot;
-  const uint32_t excl = block_excl_scan<TOPK_NT>(local, sm.scan, &tot);
+  const uint32_t excl = block_excl_scan<NT>(local, scan, &tot);
   if (excl < need && excl + local >= need) {
     uint32_t cum = excl;
     for (int i = 0; i < per; ++i) {
-      const uint32_t h = sm.hist[hi - 1 - i];
-      if (cum + h >= need) { sm.bin = hi - 1 - i; sm.above = cum; break; }
+      const uint32_t h = hist[hi - 1 - i];
+      if (cum + h >= need) { out[0] = hi - 1 - i; out[1] = cum; break; }
       cum += h;
     }
   }
   __syncthreads();
 }
 
-template <bool LDS_ROW>
+struct TopkSmem {
+  uint32_t hist[2048];
+  uint32_t scan[TOPK_NT / 64];
+  uint32_t res[2];
+};
+
+// Exact select of one row whose keys are in `row` (LDS or global), n > k.
 __device__ void select_row(TopkSmem& sm, const uint32_t* __restrict__ row, int n, int k,
                            int32_t* __restrict__ idx_out, float* __restrict__ score_out) {
   const int tid = threadIdx.x;
   uint32_t prefix = 0, pmask = 0, need = (uint32_t)k;
-  if (tid == 0) { sm.bin = 0; sm.above = 0; }
+  if (tid == 0) { sm.res[0] = 0; sm.res[1] = 0; }
 #pragma unroll 1
   for (int p = 0; p < 3; ++p) {
     const int sh = p == 0 ? 21 : (p == 1 ? 10 : 0);
@@ -226,14 +374,13 @@ __device__ void select_row(TopkSmem& sm, const uint32_t* __restrict__ row, int n
       if ((key & pmask) == prefix) atomicAdd(&sm.hist[(key >> sh) & (nb - 1)], 1u);
     }
     __syncthreads();
-    find_bin(sm, nb, need);
-    prefix |= sm.bin << sh;
+    find_bin<TOPK_NT>(sm.hist, nb, need, sm.scan, sm.res);
+    prefix |= sm.res[0] << sh;
     pmask |= (uint32_t)(nb - 1) << sh;
-    need -= sm.above;
+    need -= sm.res[1];
     __syncthreads();
   }
   const uint32_t tau = prefix, need_eq = need;
-
   uint32_t base = 0, eq_seen = 0;
 #pragma unroll 1
   for (int c0 = 0; c0 < n; c0 += TOPK_NT) {
@@ -256,72 +403,388 @@ __device__ void select_row(TopkSmem& sm, const uint32_t* __restrict__ row, int n
   }
 }
 
-__global__ __launch_bounds__(TOPK_NT) void topk_kernel(IndexerArgs a) {
+__device__ __forceinline__ void write_all_eligible(int n, int k, const uint32_t* src,
+                                                   int32_t* idx, float* sco, int nt) {
+  for (int i = threadIdx.x; i < k; i += nt) {
+    idx[i] = i < n ? i : -1;
+    if (sco) sco[i] = i < n ? __uint_as_float(src[i]) : -INFINITY;
+  }
+}
+
+// ------------------------- per-row LDS top-k kernel -------------------------
+__global__ __launch_bounds__(TOPK_NT) void topk_row_kernel(IndexerArgs a) {
   __shared__ TopkSmem sm;
   __shared__ uint32_t rowbuf[TOPK_LDS_KEYS];
   const int t = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int n = max(0, min((a.pos0[b] + t + 1) / a.m, a.Nc_cap));
+  const int n = row_len(a, b, t);
   const size_t orow = ((size_t)b * a.Tq + t) * a.topk;
   int32_t* idx = a.idx_out + orow;
   float* sco = a.score_out ? a.score_out + orow : nullptr;
   const uint32_t* src =
       reinterpret_cast<const uint32_t*>(a.ws) + ((size_t)b * a.Tq + t) * nc_pad(a.Nc_cap);
   if (n <= a.topk) {
-    for (int i = tid; i < a.topk; i += TOPK_NT) {
-      idx[i] = i < n ? i : -1;
-      if (sco) sco[i] = i < n ? __uint_as_float(src[i]) : -INFINITY;
-    }
+    write_all_eligible(n, a.topk, src, idx, sco, TOPK_NT);
     return;
   }
   if (n <= TOPK_LDS_KEYS) {
-    for (int i = tid; i < n; i += TOPK_NT) rowbuf[i] = src[i];
+    for (int i = threadIdx.x; i < n; i += TOPK_NT) rowbuf[i] = src[i];
     __syncthreads();
-    select_row<true>(sm, rowbuf, n, a.topk, idx, sco);
+    select_row(sm, rowbuf, n, a.topk, idx, sco);
   } else {
-    select_row<false>(sm, src, n, a.topk, idx, sco);
+    select_row(sm, src, n, a.topk, idx, sco);
+  }
+}
+
+// ------------------------------ long-row path ------------------------------
+__global__ __launch_bounds__(256) void long_zero_kernel(IndexerArgs a) {
+  LongWs L = long_ws(a.ws, a.B * a.Tq, a.Nc_cap, a.topk);
+  const size_t row = blockIdx.x;
+  for (int i = threadIdx.x; i < H1_BINS; i += 256) L.hist[row * H1_BINS + i] = 0;
+  if (threadIdx.x < 4) L.cnt[row * 4 + threadIdx.x] = 0;
+}
+
+// Wave-aggregated append: returns this lane's slot (meaningful where pred).
+__device__ __forceinline__ uint32_t wave_append(bool pred, uint32_t* counter) {
+  const uint64_t m = __ballot(pred);
+  if (!m) return 0;
+  const int lane = threadIdx.x & 63;
+  const int leader = __ffsll((unsigned long long)m) - 1;
+  uint32_t base = 0;
+  if (lane == leader) base = atomicAdd(counter, (uint32_t)__popcll(m));
+  base = __shfl(base, leader, 64);
+  return base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
+}
+
+__global__ __launch_bounds__(256) void long_split_kernel(IndexerArgs a) {
+  __shared__ uint32_t hist[H1_BINS];
+  __shared__ uint32_t scan[4];
+  __shared__ uint32_t res[2];
+  const int row = blockIdx.y;
+  const int b = row / a.Tq, t = row % a.Tq;
+  const int n = row_len(a, b, t);
+  const int c0 = blockIdx.x * ROW_CHUNK;
+  if (n <= a.topk || c0 >= n) return;
+  const int c1 = min(n, c0 + ROW_CHUNK);
+  LongWs L = long_ws(a.ws, a.B * a.Tq, a.Nc_cap, a.topk);
+  {
+    const u32x4* gh = reinterpret_cast<const u32x4*>(L.hist + (size_t)row * H1_BINS);
+    u32x4 hv[H1_BINS / 1024];
+#pragma unroll
+    for (int i = 0; i < H1_BINS / 1024; ++i) hv[i] = gh[threadIdx.x + 256 * i];
+#pragma unroll
+    for (int i = 0; i < H1_BINS / 1024; ++i) reinterpret_cast<u32x4*>(hist)[threadIdx.x + 256 * i] = hv[i];
+  }
+  if (threadIdx.x == 0) { res[0] = 0; res[1] = 0; }
+  __syncthreads();
+  find_bin<256>(hist, H1_BINS, (uint32_t)a.topk, scan, res);
+  const uint32_t b1 = res[0];
+  const uint32_t* keys = reinterpret_cast<const uint32_t*>(L.scores) + (size_t)row * nc_pad(a.Nc_cap);
+  uint32_t* cnt = L.cnt + row * 4;
+  uint32_t* sel = L.sel + (size_t)row * a.topk;
+  uint32_t* cand = L.cand + (size_t)row * CAND_G * 2;
+  // each thread owns 16 consecutive keys of the chunk (4 x 16-byte loads in flight)
+  constexpr int PER = ROW_CHUNK / 256;
+  const int base = c0 + threadIdx.x * PER;
+  uint32_t kv[PER];
+#pragma unroll
+  for (int q = 0; q < PER / 4; ++q) {
+    const int i = base + 4 * q;
+    u32x4 v = {0, 0, 0, 0};
+    if (i + 3 < c1) v = *reinterpret_cast<const u32x4*>(keys + i);
+    else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = (i + u < c1) ? keys[i + u] : 0u;
+    }
+    kv[4 * q] = v[0]; kv[4 * q + 1] = v[1]; kv[4 * q + 2] = v[2]; kv[4 * q + 3] = v[3];
+  }
+  // per-workgroup aggregation: one block scan, one global atomic per counter
+  uint32_t na = 0, nb = 0;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const uint32_t d = kv[q] >> (32 - H1_BITS);
+    const bool valid = base + q < c1;
+    na += (valid && d > b1) ? 1u : 0u;
+    nb += (valid && d == b1) ? 1u : 0u;
+  }
+  uint32_t tot;
+  const uint32_t pref = block_excl_scan<256>((na << 16) | nb, scan, &tot);
+  __shared__ uint32_t gbase[2];
+  if (threadIdx.x == 0) {
+    gbase[0] = (tot >> 16) ? atomicAdd(&cnt[0], tot >> 16) : 0u;
+    gbase[1] = (tot & 0xFFFFu) ? atomicAdd(&cnt[1], tot & 0xFFFFu) : 0u;
+  }
+  __syncthreads();
+  uint32_t pa = gbase[0] + (pref >> 16), pb = gbase[1] + (pref & 0xFFFFu);
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int i = base + q;
+    const uint32_t key = kv[q];
+    const uint32_t d = key >> (32 - H1_BITS);
+    if (i < c1 && d > b1) {
+      if (pa < (uint32_t)a.topk) sel[pa] = (uint32_t)i;
+      ++pa;
+    } else if (i < c1 && d == b1) {
+      if (pb < (uint32_t)CAND_G) {
+        cand[2 * pb] = key;
+        cand[2 * pb + 1] = (uint32_t)i;
+      } else {
+        cnt[2] = 1u;                                  // overflow: exact fallback
+      }
+      ++pb;
+    }
+  }
+}
+
+static constexpr int BITMAP_WORDS = 8192;       // ascending output through a bitmap for n <= 262144
+
+struct FinalSmem {
+  uint32_t ckey[CAND_L];
+  uint32_t cidx[CAND_L];
+  uint32_t outv[4096];
+  uint32_t bits[BITMAP_WORDS];
+  uint32_t hist[1024];
+  uint32_t scan[TOPK_NT / 64];
+  uint32_t res[2];
+  uint32_t neq;
+};
+
+__global__ __launch_bounds__(TOPK_NT) void long_final_kernel(IndexerArgs a) {
+  extern __shared__ __align__(16) unsigned char fsm_raw[];
+  FinalSmem& sm = *reinterpret_cast<FinalSmem*>(fsm_raw);
+  const int row = blockIdx.x;
+  const int b = row / a.Tq, t = row % a.Tq;
+  const int tid = threadIdx.x;
+  const int n = row_len(a, b, t);
+  const int k = a.topk;
+  LongWs L = long_ws(a.ws, a.B * a.Tq, a.Nc_cap, a.topk);
+  const uint32_t* keys = reinterpret_cast<const uint32_t*>(L.scores) + (size_t)row * nc_pad(a.Nc_cap);
+  int32_t* idx = a.idx_out + (size_t)row * k;
+  float* sco = a.score_out ? a.score_out + (size_t)row * k : nullptr;
+  if (n <= k) {
+    write_all_eligible(n, k, keys, idx, sco, TOPK_NT);
+    return;
+  }
+  const uint32_t nsel = L.cnt[row * 4 + 0];
+  const uint32_t ncand = L.cnt[row * 4 + 1];
+  const bool ovf = L.cnt[row * 4 + 2] != 0;
+  if (ovf || ncand > (uint32_t)CAND_L || nsel > (uint32_t)k || (uint32_t)k - nsel > ncand) {
+    TopkSmem& ts = *reinterpret_cast<TopkSmem*>(fsm_raw);
+    select_row(ts, keys, n, k, idx, sco);
+    return;
+  }
+  const uint32_t need = (uint32_t)k - nsel;
+  const uint32_t* cand = L.cand + (size_t)row * CAND_G * 2;
+  {
+    // all loads of a round are issued before any LDS store
+    constexpr int R = CAND_L / TOPK_NT;                 // 16 pairs per thread at most
+    uint2 cv[R];
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      const uint32_t i = tid + q * TOPK_NT;
+      cv[q] = i < ncand ? reinterpret_cast<const uint2*>(cand)[i] : uint2{0u, 0u};
+    }
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      const uint32_t i = tid + q * TOPK_NT;
+      if (i < ncand) { sm.ckey[i] = cv[q].x; sm.cidx[i] = cv[q].y; }
+    }
+    const uint32_t* sel = L.sel + (size_t)row * k;
+    constexpr int RS = 4096 / TOPK_NT;
+    uint32_t sv[RS];
+#pragma unroll
+    for (int q = 0; q < RS; ++q) {
+      const uint32_t i = tid + q * TOPK_NT;
+      sv[q] = i < nsel ? sel[i] : 0xFFFFFFFFu;
+    }
+#pragma unroll
+    for (int q = 0; q < RS; ++q) sm.outv[tid + q * TOPK_NT] = sv[q];
+  }
+  if (tid == 0) { sm.res[0] = 0; sm.res[1] = 0; sm.neq = 0; }
+  __syncthreads();
+  // resolve the boundary bin: two 10-bit digits below the 12-bit prefix
+  uint32_t prefix = 0, pmask = 0, rem = need;
+#pragma unroll 1
+  for (int p = 0; p < 2; ++p) {
+    const int sh = p == 0 ? 10 : 0;
+    for (int i = tid; i < 1024; i += TOPK_NT) sm.hist[i] = 0;
+    __syncthreads();
+    for (uint32_t i = tid; i < ncand; i += TOPK_NT) {
+      const uint32_t low = sm.ckey[i] & 0xFFFFFu;
+      if ((low & pmask) == prefix) atomicAdd(&sm.hist[(low >> sh) & 1023u], 1u);
+    }
+    __syncthreads();
+    find_bin<TOPK_NT>(sm.hist, 1024, rem, sm.scan, sm.res);
+    prefix |= sm.res[0] << sh;
+    pmask |= 1023u << sh;
+    rem -= sm.res[1];
+    __syncthreads();
+  }
+  // candidates with low bits > prefix are taken; among those == prefix the
+  // `rem` lowest indices are taken
+  uint32_t neq_local = 0;
+  for (uint32_t i = tid; i < ncand; i += TOPK_NT) neq_local += ((sm.ckey[i] & 0xFFFFFu) == prefix);
+  atomicAdd(&sm.neq, neq_local);
+  __syncthreads();
+  const uint32_t neq = sm.neq;
+  if (tid == 0) sm.res[0] = nsel;                     // running output count
+  __syncthreads();
+  for (uint32_t i = tid; i < ncand; i += TOPK_NT) {
+    const uint32_t low = sm.ckey[i] & 0xFFFFFu;
+    bool take = low > prefix;
+    if (low == prefix) {
+      if (neq == rem) {
+        take = true;
+      } else {                                         // rank among the ties by index
+        uint32_t rank = 0;
+        for (uint32_t j = 0; j < ncand; ++j)
+          rank += ((sm.ckey[j] & 0xFFFFFu) == prefix) && (sm.cidx[j] < sm.cidx[i]);
+        take = rank < rem;
+      }
+    }
+    if (take) {
+      const uint32_t pos = atomicAdd(&sm.res[0], 1u);
+      if (pos < (uint32_t)k) sm.outv[pos] = sm.cidx[i];
+    }
+  }
+  __syncthreads();
+  const uint32_t nout = min(sm.res[0], (uint32_t)k);
+  if (n <= BITMAP_WORDS * 32) {
+    // ascending order: set one bit per selected index, then a prefix popcount
+    const int nw = (n + 31) / 32;
+    for (int i = tid; i < nw; i += TOPK_NT) sm.bits[i] = 0u;
+    __syncthreads();
+    for (uint32_t i = tid; i < nout; i += TOPK_NT) {
+      const uint32_t j = sm.outv[i];
+      if (j < (uint32_t)n) atomicOr(&sm.bits[j >> 5], 1u << (j & 31));
+    }
+    __syncthreads();
+    constexpr int WPT = BITMAP_WORDS / TOPK_NT;        // words per thread
+    const int w0 = tid * WPT;
+    uint32_t cntb = 0;
+#pragma unroll
+    for (int q = 0; q < WPT; ++q) cntb += (w0 + q < nw) ? (uint32_t)__popc(sm.bits[w0 + q]) : 0u;
+    uint32_t totb;
+    uint32_t pos = block_excl_scan<TOPK_NT>(cntb, sm.scan, &totb);
+#pragma unroll
+    for (int q = 0; q < WPT; ++q) {
+      if (w0 + q >= nw) break;
+      uint32_t word = sm.bits[w0 + q];
+      while (word) {
+        const int bit = __ffs(word) - 1;
+        word &= word - 1;
+        const uint32_t j = (uint32_t)(w0 + q) * 32u + (uint32_t)bit;
+        if (pos < (uint32_t)k) {
+          idx[pos] = (int32_t)j;
+          if (sco) sco[pos] = __uint_as_float(keys[j]);
+        }
+        ++pos;
+      }
+    }
+    for (uint32_t i = totb + tid; i < (uint32_t)k; i += TOPK_NT) {
+      idx[i] = -1;
+      if (sco) sco[i] = -INFINITY;
+    }
+    return;
+  }
+  // bitonic sort of the k selected indices (padded to a power of two)
+  int np2 = 1;
+  while (np2 < k) np2 <<= 1;
+  for (int size = 2; size <= np2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < np2 / 2; i += TOPK_NT) {
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool asc = ((lo & size) == 0);
+        const uint32_t x = sm.outv[lo], y = sm.outv[hi];
+        if ((x > y) == asc) { sm.outv[lo] = y; sm.outv[hi] = x; }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = tid; i < k; i += TOPK_NT) {
+    const uint32_t j = sm.outv[i];
+    const bool ok = j < (uint32_t)n;
+    idx[i] = ok ? (int32_t)j : -1;
+    if (sco) sco[i] = ok ? __uint_as_float(keys[j]) : -INFINITY;
   }
 }
 
 // --------------------------------- launch ----------------------------------
 size_t indexer_workspace(int B, int Tq, int Nc_cap, int HI, int dI, int topk, int qk) {
-  (void)HI; (void)dI; (void)topk; (void)qk;
+  (void)HI; (void)dI; (void)qk;
+  if (use_long_path(Tq, Nc_cap)) return long_ws_bytes(B * Tq, Nc_cap, topk);
   return (size_t)B * Tq * nc_pad(Nc_cap) * sizeof(float);
 }
 
 template <int QK, int DI, int HI>
-static void launch_scores(const IndexerArgs& a, hipStream_t st) {
-  const int TT = 16 / HI;
+static void launch_scores(const IndexerArgs& a, hipStream_t st, bool long_path) {
   const int ne_ub = std::min((a.max_pos + 1) / a.m, a.Nc_cap);
-  dim3 grid((ne_ub + SCORE_WG_ENTRIES - 1) / SCORE_WG_ENTRIES, (a.Tq + TT - 1) / TT, a.B);
-  if (grid.x == 0) return;
-  hipLaunchKernelGGL((score_kernel<QK, DI, HI>), grid, dim3(256), 0, st, a);
+  if (ne_ub <= 0) return;
+  if (long_path) {
+    dim3 grid((ne_ub + ROW_CHUNK - 1) / ROW_CHUNK, a.B * a.Tq);
+    ProfScope ps("indexer_score", st);
+    hipLaunchKernelGGL((score_row_kernel<QK, DI, HI>), grid, dim3(256), 0, st, a);
+  } else {
+    const int TT = 16 / HI;
+    dim3 grid((ne_ub + SCORE_WG_ENTRIES - 1) / SCORE_WG_ENTRIES, (a.Tq + TT - 1) / TT, a.B);
+    ProfScope ps("indexer_score", st);
+    hipLaunchKernelGGL((score_tile_kernel<QK, DI, HI>), grid, dim3(256), 0, st, a);
+  }
 }
 
 template <int QK, int DI>
-static void launch_scores_hi(const IndexerArgs& a, hipStream_t st) {
-  if (a.HI == 1) launch_scores<QK, DI, 1>(a, st);
-  else if (a.HI == 2) launch_scores<QK, DI, 2>(a, st);
-  else launch_scores<QK, DI, 4>(a, st);
+static void launch_scores_hi(const IndexerArgs& a, hipStream_t st, bool lp) {
+  if (a.HI == 1) launch_scores<QK, DI, 1>(a, st, lp);
+  else if (a.HI == 2) launch_scores<QK, DI, 2>(a, st, lp);
+  else launch_scores<QK, DI, 4>(a, st, lp);
 }
 
 template <int QK>
-static void launch_scores_di(const IndexerArgs& a, hipStream_t st) {
-  if (a.dI == 32) launch_scores_hi<QK, 32>(a, st);
-  else launch_scores_hi<QK, 64>(a, st);
+static void launch_scores_di(const IndexerArgs& a, hipStream_t st, bool lp) {
+  if (a.dI == 32) launch_scores_hi<QK, 32>(a, st, lp);
+  else launch_scores_hi<QK, 64>(a, st, lp);
 }
 
 hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t st) {
   if (a.B == 0 || a.Tq == 0) return hipSuccess;
+  const bool lp = use_long_path(a.Tq, a.Nc_cap);
+  const int rows = a.B * a.Tq;
+  if (lp) {
+    ProfScope ps("indexer_zero", st);
+    hipLaunchKernelGGL(long_zero_kernel, dim3(rows), dim3(256), 0, st, a);
+  }
   switch (a.qk) {
-    case QK_F32: launch_scores_di<QK_F32>(a, st); break;
-    case QK_BF16: launch_scores_di<QK_BF16>(a, st); break;
-    case QK_FP8: launch_scores_di<QK_FP8>(a, st); break;
-    case QK_FP4: launch_scores_di<QK_FP4>(a, st); break;
+    case QK_F32: launch_scores_di<QK_F32>(a, st, lp); break;
+    case QK_BF16: launch_scores_di<QK_BF16>(a, st, lp); break;
+    case QK_FP8: launch_scores_di<QK_FP8>(a, st, lp); break;
+    case QK_FP4: launch_scores_di<QK_FP4>(a, st, lp); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_kernel, dim3(a.Tq, a.B), dim3(TOPK_NT), 0, st, a);
+  if (!lp) {
+    ProfScope ps("indexer_topk", st);
+    hipLaunchKernelGGL(topk_row_kernel, dim3(a.Tq, a.B), dim3(TOPK_NT), 0, st, a);
+    return hipGetLastError();
+  }
+  const int ne_ub = std::min((a.max_pos + 1) / a.m, a.Nc_cap);
+  {
+    ProfScope ps("indexer_split", st);
+    hipLaunchKernelGGL(long_split_kernel,
+                       dim3((std::max(ne_ub, 1) + ROW_CHUNK - 1) / ROW_CHUNK, rows), dim3(256), 0,
+                       st, a);
+  }
+  static bool attr_set = false;
+  const size_t lds = sizeof(FinalSmem);
+  if (!attr_set) {
+    e = hipFuncSetAttribute((const void*)long_final_kernel,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  {
+    ProfScope ps("indexer_topk", st);
+    hipLaunchKernelGGL(long_final_kernel, dim3(rows), dim3(TOPK_NT), lds, st, a);
+  }
   return hipGetLastError();
 }
 

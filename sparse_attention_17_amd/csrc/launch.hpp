@@ -7,6 +7,20 @@
 
 namespace csa {
 
+// Brackets one kernel launch with hipEvents when launch timing is enabled
+// (csa_profile_enable); a no-op otherwise.
+class ProfScope {
+ public:
+  ProfScope(const char* name, hipStream_t st);
+  ~ProfScope();
+  ProfScope(const ProfScope&) = delete;
+  ProfScope& operator=(const ProfScope&) = delete;
+
+ private:
+  hipStream_t st_;
+  long idx_;
+};
+
 struct CompressArgs {
   const void *k, *v, *ki;
   const float *gate, *pos_bias;

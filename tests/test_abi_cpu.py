@@ -125,7 +125,7 @@ def test_hca_validation(lib):
     assert _hca(lib, window=16) == L.INVALID_ARGUMENT          # window without a raw buffer
     assert _hca(lib, H=0) == L.UNSUPPORTED
     need = lib.hca_attend_workspace(16, 1, 64, 128, 8192, 128, 0)
-    assert need == 16 * 16 * 64 * 130 * 4                      # 16 splits of 512 entries
+    assert need == 32 * 16 * 64 * 130 * 4                      # 32 splits of 256 entries
     assert _hca(lib, ws=FAKE, ws_bytes=need - 1) == L.WORKSPACE_TOO_SMALL
     assert _hca(lib, B=0) == L.OK
 

@@ -133,3 +133,39 @@ def test_ragged_positions_per_sequence():
     idx = idx.cpu().numpy()
     for b in range(3):
         _check_rows(idx[b], f64(x["qi"][b]), f64(x["w"][b]), f64(x["kic"][b]), [pos[b]], 4, 256)
+
+
+def test_long_rows_all_tied_fall_back_exactly():
+    # every score is 0: the boundary bin holds the whole row, which overflows the
+    # candidate buffer; the exact fallback must return the lowest indices
+    w = configs.CSA_DECODE_128K.with_(B=2)
+    x = inputs.make_inputs(w)
+    g = {k: v.to(dev()) for k, v in x.items()}
+    pos0 = torch.full((w.B,), w.ctx - 1, dtype=torch.int32, device=dev())
+    idx, sc = ops.indexer_topk(g["qi"], g["w"], torch.zeros_like(g["kic"]), pos0, w.m, w.topk,
+                               max_pos=w.ctx - 1, return_scores=True)
+    assert torch.equal(idx.cpu(), torch.arange(w.topk, dtype=torch.int32).expand(w.B, 1, -1))
+    assert torch.all(sc == 0)
+
+
+def test_long_rows_boundary_ties_take_lowest_indices():
+    # 100 distinct key rows repeated over 32768 entries: every score value has
+    # ~330 copies, so the k-th value is tied and the lowest indices must win
+    w = configs.CSA_DECODE_128K.with_(B=2, topk=1000)
+    x = inputs.make_inputs(w)
+    base = x["kic"][:, :100]
+    kic = base.repeat(1, w.Nc // 100 + 1, 1)[:, :w.Nc].contiguous()
+    g = {k: v.to(dev()) for k, v in x.items()}
+    pos0 = torch.full((w.B,), w.ctx - 1, dtype=torch.int32, device=dev())
+    idx = ops.indexer_topk(g["qi"], g["w"], kic.to(dev()), pos0, w.m, w.topk, max_pos=w.ctx - 1)
+    idx = idx.cpu().numpy()
+    for b in range(w.B):
+        sc = oracle.csa.indexer_scores(f64(x["qi"][b]), f64(x["w"][b]), f64(kic[b]))[0]
+        assert check_topk_row(idx[b, 0], sc, w.Nc, w.topk, band_rel=0.0)
+
+
+def test_fp32_and_bf16_long_rows():
+    for qk in ("bf16",):
+        w = configs.CSA_DECODE_128K.with_(B=3, ctx=4 * 20000, qk_dtype=qk, topk=777)
+        x, idx = _decode(w)
+        assert _check_decode(w, x, idx) >= w.B - 1
