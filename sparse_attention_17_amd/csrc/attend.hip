@@ -64,7 +64,8 @@ __global__ __launch_bounds__(RW * KG * 64) void attend_kernel(AttendArgs a, Attn
   extern __shared__ __align__(16) unsigned char smem_raw[];
   T* Ks = reinterpret_cast<T*>(smem_raw);
   T* Vt = Ks + KT * KS;
-  int* sel = reinterpret_cast<int*>(Vt + D * VS);
+  T* Qs = Vt + D * VS;                         // [RW*32][KS] query rows of the tile
+  int* sel = reinterpret_cast<int*>(Qs + RW * 32 * KS);
   __shared__ uint32_t scan_sm[NW];
   __shared__ int s_nsel;
 
@@ -120,13 +121,17 @@ __global__ __launch_bounds__(RW * KG * 64) void attend_kernel(AttendArgs a, Attn
   const int qpos = p0 + tq;
   const int q_ne = SPARSE ? ncomp : hca_ne(qpos, a.m_prime, a.Nc_cap);
   const int q_wlo = max(0, qpos - a.window + 1);
-  Frag<T> qf[DSTEP];
+  // stage the tile's query rows in LDS (read back per MFMA step)
   {
-    const T* qrow = reinterpret_cast<const T*>(a.q) + (((size_t)b * a.Tq + tq) * a.H + hq) * D;
-#pragma unroll
-    for (int s = 0; s < DSTEP; ++s) {
-      if (qvalid) frag_load(qf[s], qrow + 16 * s + 8 * half);
-      else frag_zero(qf[s]);
+    constexpr int QCH = D * sizeof(T) / 16;
+    for (int c = tid; c < RW * 32 * QCH; c += NT) {
+      const int r = c / QCH, ch = c % QCH;
+      const int ttr = r / a.H, hr = r % a.H, tqr = t0 + ttr;
+      u32x4 v = {0, 0, 0, 0};
+      if (ttr < gm.TT && tqr < a.Tq)
+        v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(a.q) +
+                                            (((size_t)b * a.Tq + tqr) * a.H + hr) * D + ch * (16 / sizeof(T)));
+      *reinterpret_cast<u32x4*>(Qs + r * KS + ch * (16 / sizeof(T))) = v;
     }
   }
 
@@ -229,9 +234,10 @@ __global__ __launch_bounds__(RW * KG * 64) void attend_kernel(AttendArgs a, Attn
       for (int r = 0; r < 16; ++r) st[si][r] = 0.f;
 #pragma unroll
       for (int s = 0; s < DSTEP; ++s) {
-        Frag<T> kf;
+        Frag<T> kf, qf;
         frag_load(kf, Ks + (sub * 32 + col) * KS + 16 * s + 8 * half);
-        mma32(st[si], kf, qf[s]);
+        frag_load(qf, Qs + (rw * 32 + col) * KS + 16 * s + 8 * half);
+        mma32(st[si], kf, qf);
       }
     }
     // ---- mask, online softmax ----
@@ -449,7 +455,7 @@ template <typename T, int D, int RW, int KG, bool SPARSE>
 static hipError_t launch4(const AttendArgs& a, const AttnGeom& gm, hipStream_t st) {
   constexpr int KS = D + 16 / sizeof(T);
   constexpr int VS = KT + 4;
-  size_t lds = (size_t)(KT * KS + D * VS) * sizeof(T) + (SPARSE ? (size_t)a.topk * 4 : 0);
+  size_t lds = (size_t)(KT * KS + D * VS + RW * 32 * KS) * sizeof(T) + (SPARSE ? (size_t)a.topk * 4 : 0);
   if (KG == 2) lds = std::max(lds, (size_t)RW * 64 * ((D / 32) * 16 + 2) * sizeof(float));
   auto kfn = attend_kernel<T, D, RW, KG, SPARSE>;
   if (lds > 65536) {

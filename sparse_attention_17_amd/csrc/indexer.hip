@@ -41,9 +41,9 @@ static constexpr int SCORE_WG_ENTRIES = 256;   // prefill tile kernel: 4 waves x
 static constexpr int ROW_CHUNK = 2048;         // decode row kernel: entries per workgroup
 static constexpr int H1_BITS = 12;             // first radix digit (key bits 20..31)
 static constexpr int H1_BINS = 1 << H1_BITS;
-static constexpr int CAND_G = 16384;           // boundary-bin candidates kept per row
-static constexpr int CAND_L = 8192;            // candidates resolved in LDS
 static constexpr int TOPK_NT = 512;
+// long-row final select: threads per row
+static constexpr int SEL_NT = 1024;
 static constexpr int TOPK_LDS_KEYS = 12288;
 
 __host__ __device__ __forceinline__ int nc_pad(int Nc_cap) { return (Nc_cap + 63) & ~63; }
@@ -111,32 +111,62 @@ __device__ __forceinline__ int row_len(const IndexerArgs& a, int b, int t) {
   return max(0, min((a.pos0[b] + t + 1) / a.m, a.Nc_cap));
 }
 
-// Workspace carve-up for the long-row path (per query row):
-//   scores [rows][ldo] f32 | hist [rows][4096] u32 | cnt [rows][4] u32 |
-//   sel [rows][topk] u32 | cand [rows][CAND_G][2] u32
+// Workspace carve-up for the long-row path (per query row; nch = row chunks):
+//   scores [rows][ldo] f32 | hist [rows][4096] u32 | ccnt [rows][nch][2] u32 |
+//   csel [rows][nch][ROW_CHUNK] u32 | ccand [rows][nch][ROW_CHUNK][2] u32
+// Every split workgroup owns one chunk's slots, so no atomics are needed.
 struct LongWs {
   float* scores;
-  uint32_t *hist, *cnt, *sel, *cand;
+  uint32_t *hist, *ccnt, *csel, *ccand;
+  int nch;
 };
+__host__ __device__ __forceinline__ int row_chunks(int Nc_cap) { return (Nc_cap + ROW_CHUNK - 1) / ROW_CHUNK; }
 __host__ __device__ __forceinline__ LongWs long_ws(void* ws, int rows, int Nc_cap, int topk) {
+  (void)topk;
   LongWs w;
+  w.nch = row_chunks(Nc_cap);
   char* p = reinterpret_cast<char*>(ws);
   w.scores = reinterpret_cast<float*>(p);
   p += (size_t)rows * nc_pad(Nc_cap) * 4;
   w.hist = reinterpret_cast<uint32_t*>(p);
   p += (size_t)rows * H1_BINS * 4;
-  w.cnt = reinterpret_cast<uint32_t*>(p);
-  p += (size_t)rows * 4 * 4;
-  w.sel = reinterpret_cast<uint32_t*>(p);
-  p += (size_t)rows * ((topk + 3) & ~3) * 4;
-  w.cand = reinterpret_cast<uint32_t*>(p);
+  w.ccnt = reinterpret_cast<uint32_t*>(p);
+  p += (size_t)rows * ((w.nch * 2 + 3) & ~3) * 4;
+  w.csel = reinterpret_cast<uint32_t*>(p);
+  p += (size_t)rows * w.nch * ROW_CHUNK * 4;
+  w.ccand = reinterpret_cast<uint32_t*>(p);
   return w;
 }
 static size_t long_ws_bytes(int rows, int Nc_cap, int topk) {
-  return (size_t)rows * ((size_t)nc_pad(Nc_cap) * 4 + H1_BINS * 4 + 16 +
-                         (size_t)((topk + 3) & ~3) * 4 + (size_t)CAND_G * 8);
+  (void)topk;
+  const int nch = row_chunks(Nc_cap);
+  return (size_t)rows * ((size_t)nc_pad(Nc_cap) * 4 + H1_BINS * 4 + (size_t)((nch * 2 + 3) & ~3) * 4 +
+                         (size_t)nch * ROW_CHUNK * 12);
 }
 static bool use_long_path(int Tq, int Nc_cap) { return Tq <= 4 && Nc_cap > TOPK_LDS_KEYS; }
+
+// Scanning bins from the top down, find the bin where the running count first
+// reaches `need`; out[0] = bin, out[1] = count strictly above it.
+template <int NT>
+__device__ void find_bin(const uint32_t* hist, int nbins, uint32_t need, uint32_t* scan,
+                         uint32_t* out) {
+  const int per = nbins / NT;
+  const int tid = threadIdx.x;
+  const int hi = nbins - tid * per;
+  uint32_t local = 0;
+  for (int i = 0; i < per; ++i) local += hist[hi - 1 - i];
+  uint32_t tot;
+  const uint32_t excl = block_excl_scan<NT>(local, scan, &tot);
+  if (excl < need && excl + local >= need) {
+    uint32_t cum = excl;
+    for (int i = 0; i < per; ++i) {
+      const uint32_t h = hist[hi - 1 - i];
+      if (cum + h >= need) { out[0] = hi - 1 - i; out[1] = cum; break; }
+      cum += h;
+    }
+  }
+  __syncthreads();
+}
 
 // --------------------------- prefill score tile ----------------------------
 template <int QK, int DI, int HI>
@@ -274,7 +304,9 @@ __global__ __launch_bounds__(256) void score_row_kernel(IndexerArgs a) {
   if constexpr (QK == QK_FP8) fsc = reinterpret_cast<const float*>(a.kic_scale) + (size_t)b * a.Nc_cap;
   float* srow = L.scores + (size_t)row * nc_pad(a.Nc_cap);
 
-  auto load_group = [&](int e0, F (&kb)[TPC][KC]) {
+  // one group = EPC entries: the B fragments plus (FP8) the per-entry scales of
+  // the entries this lane will score
+  auto load_group = [&](int e0, F (&kb)[TPC][KC], float (&ks)[SPL]) {
 #pragma unroll
     for (int u = 0; u < TPC; ++u) {
       const int e = min(e0 + 16 * u + r, c1 - 1);
@@ -283,19 +315,28 @@ __global__ __launch_bounds__(256) void score_row_kernel(IndexerArgs a) {
         load_qk_frag<QK>(kb[u][c], kbase + (size_t)e * rb,
                          QK == QK_FP4 ? sbase + (size_t)e * (DI / 32) : nullptr, 8 * (g * KC + c));
     }
+#pragma unroll
+    for (int s = 0; s < SPL; ++s) {
+      if constexpr (QK == QK_FP8) ks[s] = fsc[min(e0 + 16 * ((4 * g) / HI + s) + r, c1 - 1)];
+      else ks[s] = 1.f;
+    }
   };
 
   F kb[TPC][KC];
+  float kscl[SPL];
   int e0 = c0 + wave * EPC;
-  if (e0 < c1) load_group(e0, kb);
+  if (e0 < c1) load_group(e0, kb, kscl);
 #pragma unroll 1
   for (; e0 < c1; e0 += 4 * EPC) {
     F cur[TPC][KC];
+    float cscl[SPL];
 #pragma unroll
     for (int u = 0; u < TPC; ++u)
 #pragma unroll
       for (int c = 0; c < KC; ++c) cur[u][c] = kb[u][c];
-    if (e0 + 4 * EPC < c1) load_group(e0 + 4 * EPC, kb);      // prefetch the next group
+#pragma unroll
+    for (int s = 0; s < SPL; ++s) cscl[s] = kscl[s];
+    if (e0 + 4 * EPC < c1) load_group(e0 + 4 * EPC, kb, kscl);      // prefetch the next group
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < TPC; ++u)
@@ -312,7 +353,7 @@ __global__ __launch_bounds__(256) void score_row_kernel(IndexerArgs a) {
         sc = fmaf(wr[s * HI + h], x > 0.f ? x : 0.f, sc);
       }
       if (e < c1) {
-        if constexpr (QK == QK_FP8) sc *= fsc[e];
+        if constexpr (QK == QK_FP8) sc *= cscl[s];
         sc += 0.f;
         srow[e] = sc;
         atomicAdd(&hist[__float_as_uint(sc) >> (32 - H1_BITS)], 1u);
@@ -328,37 +369,16 @@ __global__ __launch_bounds__(256) void score_row_kernel(IndexerArgs a) {
 }
 
 // --------------------------- shared select helpers --------------------------
-// Scanning bins from the top down, find the bin where the running count first
-// reaches `need`; out[0] = bin, out[1] = count strictly above it.
 template <int NT>
-__device__ void find_bin(const uint32_t* hist, int nbins, uint32_t need, uint32_t* scan,
-                         uint32_t* out) {
-  const int per = nbins / NT;
-  const int tid = threadIdx.x;
-  const int hi = nbins - tid * per;
-  uint32_t local = 0;
-  for (int i = 0; i < per; ++i) local += hist[hi - 1 - i];
-  uint32_t tot;
-  const uint32_t excl = block_excl_scan<NT>(local, scan, &tot);
-  if (excl < need && excl + local >= need) {
-    uint32_t cum = excl;
-    for (int i = 0; i < per; ++i) {
-      const uint32_t h = hist[hi - 1 - i];
-      if (cum + h >= need) { out[0] = hi - 1 - i; out[1] = cum; break; }
-      cum += h;
-    }
-  }
-  __syncthreads();
-}
-
 struct TopkSmem {
   uint32_t hist[2048];
-  uint32_t scan[TOPK_NT / 64];
+  uint32_t scan[NT / 64];
   uint32_t res[2];
 };
 
 // Exact select of one row whose keys are in `row` (LDS or global), n > k.
-__device__ void select_row(TopkSmem& sm, const uint32_t* __restrict__ row, int n, int k,
+template <int NT>
+__device__ void select_row(TopkSmem<NT>& sm, const uint32_t* __restrict__ row, int n, int k,
                            int32_t* __restrict__ idx_out, float* __restrict__ score_out) {
   const int tid = threadIdx.x;
   uint32_t prefix = 0, pmask = 0, need = (uint32_t)k;
@@ -367,14 +387,14 @@ __device__ void select_row(TopkSmem& sm, const uint32_t* __restrict__ row, int n
   for (int p = 0; p < 3; ++p) {
     const int sh = p == 0 ? 21 : (p == 1 ? 10 : 0);
     const int nb = p == 2 ? 1024 : 2048;
-    for (int i = tid; i < nb; i += TOPK_NT) sm.hist[i] = 0;
+    for (int i = tid; i < nb; i += NT) sm.hist[i] = 0;
     __syncthreads();
-    for (int i = tid; i < n; i += TOPK_NT) {
+    for (int i = tid; i < n; i += NT) {
       const uint32_t key = row[i];
       if ((key & pmask) == prefix) atomicAdd(&sm.hist[(key >> sh) & (nb - 1)], 1u);
     }
     __syncthreads();
-    find_bin<TOPK_NT>(sm.hist, nb, need, sm.scan, sm.res);
+    find_bin<NT>(sm.hist, nb, need, sm.scan, sm.res);
     prefix |= sm.res[0] << sh;
     pmask |= (uint32_t)(nb - 1) << sh;
     need -= sm.res[1];
@@ -383,16 +403,16 @@ __device__ void select_row(TopkSmem& sm, const uint32_t* __restrict__ row, int n
   const uint32_t tau = prefix, need_eq = need;
   uint32_t base = 0, eq_seen = 0;
 #pragma unroll 1
-  for (int c0 = 0; c0 < n; c0 += TOPK_NT) {
+  for (int c0 = 0; c0 < n; c0 += NT) {
     const int i = c0 + tid;
     const uint32_t key = i < n ? row[i] : 0u;
     const uint32_t is_gt = (i < n && key > tau) ? 1u : 0u;
     const uint32_t is_eq = (i < n && key == tau) ? 1u : 0u;
     uint32_t tot_eq;
-    const uint32_t eq_x = block_excl_scan<TOPK_NT>(is_eq, sm.scan, &tot_eq);
+    const uint32_t eq_x = block_excl_scan<NT>(is_eq, sm.scan, &tot_eq);
     const uint32_t take = is_gt | ((is_eq && eq_seen + eq_x < need_eq) ? 1u : 0u);
     uint32_t tot_take;
-    const uint32_t pos = block_excl_scan<TOPK_NT>(take, sm.scan, &tot_take);
+    const uint32_t pos = block_excl_scan<NT>(take, sm.scan, &tot_take);
     if (take && base + pos < (uint32_t)k) {
       idx_out[base + pos] = i;
       if (score_out) score_out[base + pos] = __uint_as_float(key);
@@ -413,7 +433,7 @@ __device__ __forceinline__ void write_all_eligible(int n, int k, const uint32_t*
 
 // ------------------------- per-row LDS top-k kernel -------------------------
 __global__ __launch_bounds__(TOPK_NT) void topk_row_kernel(IndexerArgs a) {
-  __shared__ TopkSmem sm;
+  __shared__ TopkSmem<TOPK_NT> sm;
   __shared__ uint32_t rowbuf[TOPK_LDS_KEYS];
   const int t = blockIdx.x, b = blockIdx.y;
   const int n = row_len(a, b, t);
@@ -429,62 +449,40 @@ __global__ __launch_bounds__(TOPK_NT) void topk_row_kernel(IndexerArgs a) {
   if (n <= TOPK_LDS_KEYS) {
     for (int i = threadIdx.x; i < n; i += TOPK_NT) rowbuf[i] = src[i];
     __syncthreads();
-    select_row(sm, rowbuf, n, a.topk, idx, sco);
+    select_row<TOPK_NT>(sm, rowbuf, n, a.topk, idx, sco);
   } else {
-    select_row(sm, src, n, a.topk, idx, sco);
+    select_row<TOPK_NT>(sm, src, n, a.topk, idx, sco);
   }
 }
 
 // ------------------------------ long-row path ------------------------------
 __global__ __launch_bounds__(256) void long_zero_kernel(IndexerArgs a) {
   LongWs L = long_ws(a.ws, a.B * a.Tq, a.Nc_cap, a.topk);
-  const size_t row = blockIdx.x;
-  for (int i = threadIdx.x; i < H1_BINS; i += 256) L.hist[row * H1_BINS + i] = 0;
-  if (threadIdx.x < 4) L.cnt[row * 4 + threadIdx.x] = 0;
+  u32x4* h = reinterpret_cast<u32x4*>(L.hist + (size_t)blockIdx.x * H1_BINS);
+  for (int i = threadIdx.x; i < H1_BINS / 4; i += 256) h[i] = u32x4{0, 0, 0, 0};
 }
 
-// Wave-aggregated append: returns this lane's slot (meaningful where pred).
-__device__ __forceinline__ uint32_t wave_append(bool pred, uint32_t* counter) {
-  const uint64_t m = __ballot(pred);
-  if (!m) return 0;
-  const int lane = threadIdx.x & 63;
-  const int leader = __ffsll((unsigned long long)m) - 1;
-  uint32_t base = 0;
-  if (lane == leader) base = atomicAdd(counter, (uint32_t)__popcll(m));
-  base = __shfl(base, leader, 64);
-  return base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
-}
+static constexpr int CAND_L = 8192;            // boundary-bin candidates resolved in LDS
+static constexpr int BITMAP_WORDS = 8192;      // ascending output through a bitmap for n <= 262144
 
+// Split pass over one chunk of one long row: find the bin b1 holding the k-th
+// largest key from the row histogram, then write the chunk's indices with keys
+// above b1 and its (key, index) pairs inside b1 to the chunk's own slots.
 __global__ __launch_bounds__(256) void long_split_kernel(IndexerArgs a) {
   __shared__ uint32_t hist[H1_BINS];
   __shared__ uint32_t scan[4];
   __shared__ uint32_t res[2];
-  const int row = blockIdx.y;
+  const int row = blockIdx.y, chunk = blockIdx.x;
   const int b = row / a.Tq, t = row % a.Tq;
   const int n = row_len(a, b, t);
-  const int c0 = blockIdx.x * ROW_CHUNK;
+  const int c0 = chunk * ROW_CHUNK;
   if (n <= a.topk || c0 >= n) return;
   const int c1 = min(n, c0 + ROW_CHUNK);
   LongWs L = long_ws(a.ws, a.B * a.Tq, a.Nc_cap, a.topk);
-  {
-    const u32x4* gh = reinterpret_cast<const u32x4*>(L.hist + (size_t)row * H1_BINS);
-    u32x4 hv[H1_BINS / 1024];
-#pragma unroll
-    for (int i = 0; i < H1_BINS / 1024; ++i) hv[i] = gh[threadIdx.x + 256 * i];
-#pragma unroll
-    for (int i = 0; i < H1_BINS / 1024; ++i) reinterpret_cast<u32x4*>(hist)[threadIdx.x + 256 * i] = hv[i];
-  }
-  if (threadIdx.x == 0) { res[0] = 0; res[1] = 0; }
-  __syncthreads();
-  find_bin<256>(hist, H1_BINS, (uint32_t)a.topk, scan, res);
-  const uint32_t b1 = res[0];
   const uint32_t* keys = reinterpret_cast<const uint32_t*>(L.scores) + (size_t)row * nc_pad(a.Nc_cap);
-  uint32_t* cnt = L.cnt + row * 4;
-  uint32_t* sel = L.sel + (size_t)row * a.topk;
-  uint32_t* cand = L.cand + (size_t)row * CAND_G * 2;
-  // each thread owns 16 consecutive keys of the chunk (4 x 16-byte loads in flight)
   constexpr int PER = ROW_CHUNK / 256;
   const int base = c0 + threadIdx.x * PER;
+  // issue the chunk's key loads and the histogram loads together
   uint32_t kv[PER];
 #pragma unroll
   for (int q = 0; q < PER / 4; ++q) {
@@ -497,7 +495,18 @@ __global__ __launch_bounds__(256) void long_split_kernel(IndexerArgs a) {
     }
     kv[4 * q] = v[0]; kv[4 * q + 1] = v[1]; kv[4 * q + 2] = v[2]; kv[4 * q + 3] = v[3];
   }
-  // per-workgroup aggregation: one block scan, one global atomic per counter
+  {
+    const u32x4* gh = reinterpret_cast<const u32x4*>(L.hist + (size_t)row * H1_BINS);
+    u32x4 hv[H1_BINS / 1024];
+#pragma unroll
+    for (int i = 0; i < H1_BINS / 1024; ++i) hv[i] = gh[threadIdx.x + 256 * i];
+#pragma unroll
+    for (int i = 0; i < H1_BINS / 1024; ++i) reinterpret_cast<u32x4*>(hist)[threadIdx.x + 256 * i] = hv[i];
+  }
+  if (threadIdx.x == 0) { res[0] = 0; res[1] = 0; }
+  __syncthreads();
+  find_bin<256>(hist, H1_BINS, (uint32_t)a.topk, scan, res);
+  const uint32_t b1 = res[0];
   uint32_t na = 0, nb = 0;
 #pragma unroll
   for (int q = 0; q < PER; ++q) {
@@ -508,49 +517,47 @@ __global__ __launch_bounds__(256) void long_split_kernel(IndexerArgs a) {
   }
   uint32_t tot;
   const uint32_t pref = block_excl_scan<256>((na << 16) | nb, scan, &tot);
-  __shared__ uint32_t gbase[2];
-  if (threadIdx.x == 0) {
-    gbase[0] = (tot >> 16) ? atomicAdd(&cnt[0], tot >> 16) : 0u;
-    gbase[1] = (tot & 0xFFFFu) ? atomicAdd(&cnt[1], tot & 0xFFFFu) : 0u;
-  }
-  __syncthreads();
-  uint32_t pa = gbase[0] + (pref >> 16), pb = gbase[1] + (pref & 0xFFFFu);
+  uint32_t* csel = L.csel + ((size_t)row * L.nch + chunk) * ROW_CHUNK;
+  uint32_t* ccand = L.ccand + ((size_t)row * L.nch + chunk) * ROW_CHUNK * 2;
+  uint32_t pa = pref >> 16, pb = pref & 0xFFFFu;
 #pragma unroll
   for (int q = 0; q < PER; ++q) {
     const int i = base + q;
-    const uint32_t key = kv[q];
-    const uint32_t d = key >> (32 - H1_BITS);
+    const uint32_t d = kv[q] >> (32 - H1_BITS);
     if (i < c1 && d > b1) {
-      if (pa < (uint32_t)a.topk) sel[pa] = (uint32_t)i;
-      ++pa;
+      csel[pa++] = (uint32_t)i;
     } else if (i < c1 && d == b1) {
-      if (pb < (uint32_t)CAND_G) {
-        cand[2 * pb] = key;
-        cand[2 * pb + 1] = (uint32_t)i;
-      } else {
-        cnt[2] = 1u;                                  // overflow: exact fallback
-      }
+      ccand[2 * pb] = kv[q];
+      ccand[2 * pb + 1] = (uint32_t)i;
       ++pb;
     }
   }
+  if (threadIdx.x == 0) {
+    uint32_t* cc = L.ccnt + (size_t)row * ((L.nch * 2 + 3) & ~3) + 2 * chunk;
+    cc[0] = tot >> 16;
+    cc[1] = tot & 0xFFFFu;
+  }
 }
 
-static constexpr int BITMAP_WORDS = 8192;       // ascending output through a bitmap for n <= 262144
+static constexpr int MAX_CHUNKS = 1024;        // rows up to 2M entries use the gather path
 
-struct FinalSmem {
+struct SelectSmem {
   uint32_t ckey[CAND_L];
   uint32_t cidx[CAND_L];
   uint32_t outv[4096];
   uint32_t bits[BITMAP_WORDS];
   uint32_t hist[1024];
-  uint32_t scan[TOPK_NT / 64];
+  uint32_t off[2][MAX_CHUNKS + 1];             // exclusive prefix of the chunk counts
+  uint32_t scan[SEL_NT / 64];
   uint32_t res[2];
-  uint32_t neq;
+  uint32_t neq, fallback;
 };
 
-__global__ __launch_bounds__(TOPK_NT) void long_final_kernel(IndexerArgs a) {
-  extern __shared__ __align__(16) unsigned char fsm_raw[];
-  FinalSmem& sm = *reinterpret_cast<FinalSmem*>(fsm_raw);
+// Final pass of one long row: gather the chunks' lists, resolve the boundary
+// bin on the low 20 key bits (lowest index wins ties), emit ascending indices.
+__global__ __launch_bounds__(SEL_NT) void long_final_kernel(IndexerArgs a) {
+  extern __shared__ __align__(16) unsigned char ssm_raw[];
+  SelectSmem& sm = *reinterpret_cast<SelectSmem*>(ssm_raw);
   const int row = blockIdx.x;
   const int b = row / a.Tq, t = row % a.Tq;
   const int tid = threadIdx.x;
@@ -561,80 +568,112 @@ __global__ __launch_bounds__(TOPK_NT) void long_final_kernel(IndexerArgs a) {
   int32_t* idx = a.idx_out + (size_t)row * k;
   float* sco = a.score_out ? a.score_out + (size_t)row * k : nullptr;
   if (n <= k) {
-    write_all_eligible(n, k, keys, idx, sco, TOPK_NT);
+    write_all_eligible(n, k, keys, idx, sco, SEL_NT);
     return;
   }
-  const uint32_t nsel = L.cnt[row * 4 + 0];
-  const uint32_t ncand = L.cnt[row * 4 + 1];
-  const bool ovf = L.cnt[row * 4 + 2] != 0;
-  if (ovf || ncand > (uint32_t)CAND_L || nsel > (uint32_t)k || (uint32_t)k - nsel > ncand) {
-    TopkSmem& ts = *reinterpret_cast<TopkSmem*>(fsm_raw);
-    select_row(ts, keys, n, k, idx, sco);
-    return;
-  }
-  const uint32_t need = (uint32_t)k - nsel;
-  const uint32_t* cand = L.cand + (size_t)row * CAND_G * 2;
+  const int nch = (n + ROW_CHUNK - 1) / ROW_CHUNK;
+  if (tid == 0) { sm.neq = 0; sm.fallback = nch > MAX_CHUNKS; }
+  // chunk counts -> exclusive offsets (one block scan per list)
   {
-    // all loads of a round are issued before any LDS store
-    constexpr int R = CAND_L / TOPK_NT;                 // 16 pairs per thread at most
-    uint2 cv[R];
-#pragma unroll
-    for (int q = 0; q < R; ++q) {
-      const uint32_t i = tid + q * TOPK_NT;
-      cv[q] = i < ncand ? reinterpret_cast<const uint2*>(cand)[i] : uint2{0u, 0u};
+    const uint32_t* cc = L.ccnt + (size_t)row * ((L.nch * 2 + 3) & ~3);
+    uint32_t c_sel = 0, c_cand = 0;
+    if (tid < nch && tid < MAX_CHUNKS) { c_sel = cc[2 * tid]; c_cand = cc[2 * tid + 1]; }
+    uint32_t tot_sel, tot_cand;
+    const uint32_t o_sel = block_excl_scan<SEL_NT>(c_sel, sm.scan, &tot_sel);
+    const uint32_t o_cand = block_excl_scan<SEL_NT>(c_cand, sm.scan, &tot_cand);
+    if (tid < MAX_CHUNKS) { sm.off[0][tid] = o_sel; sm.off[1][tid] = o_cand; }
+    if (tid == 0) {
+      sm.off[0][MAX_CHUNKS] = tot_sel;
+      sm.off[1][MAX_CHUNKS] = tot_cand;
+      if (tot_sel >= (uint32_t)k || tot_cand > (uint32_t)CAND_L || (uint32_t)k - tot_sel > tot_cand)
+        sm.fallback = 1;
     }
-#pragma unroll
-    for (int q = 0; q < R; ++q) {
-      const uint32_t i = tid + q * TOPK_NT;
-      if (i < ncand) { sm.ckey[i] = cv[q].x; sm.cidx[i] = cv[q].y; }
-    }
-    const uint32_t* sel = L.sel + (size_t)row * k;
-    constexpr int RS = 4096 / TOPK_NT;
-    uint32_t sv[RS];
-#pragma unroll
-    for (int q = 0; q < RS; ++q) {
-      const uint32_t i = tid + q * TOPK_NT;
-      sv[q] = i < nsel ? sel[i] : 0xFFFFFFFFu;
-    }
-#pragma unroll
-    for (int q = 0; q < RS; ++q) sm.outv[tid + q * TOPK_NT] = sv[q];
   }
-  if (tid == 0) { sm.res[0] = 0; sm.res[1] = 0; sm.neq = 0; }
   __syncthreads();
+  if (sm.fallback) {                                           // exact, slow, rare
+    TopkSmem<SEL_NT>& ts = *reinterpret_cast<TopkSmem<SEL_NT>*>(ssm_raw);
+    __syncthreads();
+    select_row<SEL_NT>(ts, keys, n, k, idx, sco);
+    return;
+  }
+  const uint32_t nsel = sm.off[0][MAX_CHUNKS], ncand = sm.off[1][MAX_CHUNKS];
+  // gather: list position p lives in the chunk c with off[c] <= p < off[c+1]
+  auto chunk_of = [&](int list, uint32_t p) {
+    int lo = 0, hi = nch - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (sm.off[list][mid] <= p) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  };
+  {
+    constexpr int R = 4;                                      // 4 x 1024 >= k
+    uint32_t sv[R];
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      const uint32_t p = tid + q * SEL_NT;
+      sv[q] = 0xFFFFFFFFu;
+      if (p < nsel) {
+        const int c = chunk_of(0, p);
+        sv[q] = L.csel[((size_t)row * L.nch + c) * ROW_CHUNK + (p - sm.off[0][c])];
+      }
+    }
+    constexpr int RC = CAND_L / SEL_NT;
+    uint2 cv[RC];
+#pragma unroll
+    for (int q = 0; q < RC; ++q) {
+      const uint32_t p = tid + q * SEL_NT;
+      cv[q] = uint2{0u, 0u};
+      if (p < ncand) {
+        const int c = chunk_of(1, p);
+        cv[q] = reinterpret_cast<const uint2*>(L.ccand + ((size_t)row * L.nch + c) * ROW_CHUNK * 2)[p - sm.off[1][c]];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < R; ++q) sm.outv[tid + q * SEL_NT] = sv[q];
+#pragma unroll
+    for (int q = 0; q < RC; ++q) {
+      const uint32_t p = tid + q * SEL_NT;
+      if (p < ncand) { sm.ckey[p] = cv[q].x; sm.cidx[p] = cv[q].y; }
+    }
+  }
+  if (tid == 0) { sm.res[0] = 0; sm.res[1] = 0; }
+  __syncthreads();
+  const uint32_t need = (uint32_t)k - nsel;
   // resolve the boundary bin: two 10-bit digits below the 12-bit prefix
   uint32_t prefix = 0, pmask = 0, rem = need;
 #pragma unroll 1
   for (int p = 0; p < 2; ++p) {
     const int sh = p == 0 ? 10 : 0;
-    for (int i = tid; i < 1024; i += TOPK_NT) sm.hist[i] = 0;
+    for (int i = tid; i < 1024; i += SEL_NT) sm.hist[i] = 0;
     __syncthreads();
-    for (uint32_t i = tid; i < ncand; i += TOPK_NT) {
+    for (uint32_t i = tid; i < ncand; i += SEL_NT) {
       const uint32_t low = sm.ckey[i] & 0xFFFFFu;
       if ((low & pmask) == prefix) atomicAdd(&sm.hist[(low >> sh) & 1023u], 1u);
     }
     __syncthreads();
-    find_bin<TOPK_NT>(sm.hist, 1024, rem, sm.scan, sm.res);
+    find_bin<SEL_NT>(sm.hist, 1024, rem, sm.scan, sm.res);
     prefix |= sm.res[0] << sh;
     pmask |= 1023u << sh;
     rem -= sm.res[1];
     __syncthreads();
   }
-  // candidates with low bits > prefix are taken; among those == prefix the
-  // `rem` lowest indices are taken
+  // take candidates whose low bits exceed the prefix, and the `rem` lowest
+  // indices among those equal to it
   uint32_t neq_local = 0;
-  for (uint32_t i = tid; i < ncand; i += TOPK_NT) neq_local += ((sm.ckey[i] & 0xFFFFFu) == prefix);
-  atomicAdd(&sm.neq, neq_local);
+  for (uint32_t i = tid; i < ncand; i += SEL_NT) neq_local += ((sm.ckey[i] & 0xFFFFFu) == prefix);
+  if (neq_local) atomicAdd(&sm.neq, neq_local);
   __syncthreads();
   const uint32_t neq = sm.neq;
-  if (tid == 0) sm.res[0] = nsel;                     // running output count
+  if (tid == 0) sm.res[0] = nsel;                              // running output count
   __syncthreads();
-  for (uint32_t i = tid; i < ncand; i += TOPK_NT) {
+  for (uint32_t i = tid; i < ncand; i += SEL_NT) {
     const uint32_t low = sm.ckey[i] & 0xFFFFFu;
     bool take = low > prefix;
     if (low == prefix) {
       if (neq == rem) {
         take = true;
-      } else {                                         // rank among the ties by index
+      } else {
         uint32_t rank = 0;
         for (uint32_t j = 0; j < ncand; ++j)
           rank += ((sm.ckey[j] & 0xFFFFFu) == prefix) && (sm.cidx[j] < sm.cidx[i]);
@@ -648,23 +687,23 @@ __global__ __launch_bounds__(TOPK_NT) void long_final_kernel(IndexerArgs a) {
   }
   __syncthreads();
   const uint32_t nout = min(sm.res[0], (uint32_t)k);
+  // ascending output
   if (n <= BITMAP_WORDS * 32) {
-    // ascending order: set one bit per selected index, then a prefix popcount
     const int nw = (n + 31) / 32;
-    for (int i = tid; i < nw; i += TOPK_NT) sm.bits[i] = 0u;
+    for (int i = tid; i < nw; i += SEL_NT) sm.bits[i] = 0u;
     __syncthreads();
-    for (uint32_t i = tid; i < nout; i += TOPK_NT) {
+    for (uint32_t i = tid; i < nout; i += SEL_NT) {
       const uint32_t j = sm.outv[i];
       if (j < (uint32_t)n) atomicOr(&sm.bits[j >> 5], 1u << (j & 31));
     }
     __syncthreads();
-    constexpr int WPT = BITMAP_WORDS / TOPK_NT;        // words per thread
+    constexpr int WPT = BITMAP_WORDS / SEL_NT;
     const int w0 = tid * WPT;
     uint32_t cntb = 0;
 #pragma unroll
     for (int q = 0; q < WPT; ++q) cntb += (w0 + q < nw) ? (uint32_t)__popc(sm.bits[w0 + q]) : 0u;
     uint32_t totb;
-    uint32_t pos = block_excl_scan<TOPK_NT>(cntb, sm.scan, &totb);
+    uint32_t pos = block_excl_scan<SEL_NT>(cntb, sm.scan, &totb);
 #pragma unroll
     for (int q = 0; q < WPT; ++q) {
       if (w0 + q >= nw) break;
@@ -680,28 +719,28 @@ __global__ __launch_bounds__(TOPK_NT) void long_final_kernel(IndexerArgs a) {
         ++pos;
       }
     }
-    for (uint32_t i = totb + tid; i < (uint32_t)k; i += TOPK_NT) {
+    for (uint32_t i = totb + tid; i < (uint32_t)k; i += SEL_NT) {
       idx[i] = -1;
       if (sco) sco[i] = -INFINITY;
     }
     return;
   }
-  // bitonic sort of the k selected indices (padded to a power of two)
+  // longer rows: bitonic sort of the k selected indices (padded to a power of two)
   int np2 = 1;
   while (np2 < k) np2 <<= 1;
   for (int size = 2; size <= np2; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < np2 / 2; i += TOPK_NT) {
-        const int lo = 2 * i - (i & (stride - 1));
-        const int hi = lo + stride;
-        const bool asc = ((lo & size) == 0);
-        const uint32_t x = sm.outv[lo], y = sm.outv[hi];
-        if ((x > y) == asc) { sm.outv[lo] = y; sm.outv[hi] = x; }
+      for (int i = tid; i < np2 / 2; i += SEL_NT) {
+        const int l2 = 2 * i - (i & (stride - 1));
+        const int h2 = l2 + stride;
+        const bool asc = ((l2 & size) == 0);
+        const uint32_t x = sm.outv[l2], y = sm.outv[h2];
+        if ((x > y) == asc) { sm.outv[l2] = y; sm.outv[h2] = x; }
       }
       __syncthreads();
     }
   }
-  for (int i = tid; i < k; i += TOPK_NT) {
+  for (int i = tid; i < k; i += SEL_NT) {
     const uint32_t j = sm.outv[i];
     const bool ok = j < (uint32_t)n;
     idx[i] = ok ? (int32_t)j : -1;
@@ -769,12 +808,11 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t st) {
   const int ne_ub = std::min((a.max_pos + 1) / a.m, a.Nc_cap);
   {
     ProfScope ps("indexer_split", st);
-    hipLaunchKernelGGL(long_split_kernel,
-                       dim3((std::max(ne_ub, 1) + ROW_CHUNK - 1) / ROW_CHUNK, rows), dim3(256), 0,
-                       st, a);
+    hipLaunchKernelGGL(long_split_kernel, dim3(row_chunks(std::max(ne_ub, 1)), rows), dim3(256),
+                       0, st, a);
   }
   static bool attr_set = false;
-  const size_t lds = sizeof(FinalSmem);
+  const size_t lds = sizeof(SelectSmem);
   if (!attr_set) {
     e = hipFuncSetAttribute((const void*)long_final_kernel,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -783,7 +821,7 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t st) {
   }
   {
     ProfScope ps("indexer_topk", st);
-    hipLaunchKernelGGL(long_final_kernel, dim3(rows), dim3(TOPK_NT), lds, st, a);
+    hipLaunchKernelGGL(long_final_kernel, dim3(rows), dim3(SEL_NT), lds, st, a);
   }
   return hipGetLastError();
 }
