@@ -45,6 +45,8 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     p.add_argument("--graph", type=int, default=1, help="replay the step as a HIP graph")
     p.add_argument("--cpu-workers", type=int, default=0)
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="first run three 256 MiB device copies (known traffic for counter scaling)")
     return p.parse_args()
 
 
@@ -147,6 +149,13 @@ def main():
 
     dev = torch.device("cuda:0")
     lib = L.load()
+    if args.copy_calibration:
+        src = torch.ones(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     base = {k: v.to(dev) for k, v in x.items()}
     sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(args.rotate - 1)]
     pos0 = torch.full((w.B,), w.ctx - 1, dtype=torch.int32, device=dev)

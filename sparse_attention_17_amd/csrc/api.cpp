@@ -2,7 +2,7 @@
 // thread-local error text, and dispatch to the gfx950 kernels.  Every entry
 // point checks its arguments before touching the device; on any error it
 // returns a status and launches nothing.
-#include "../../include/csa_mi355x.h"
+#include "csa_mi355x.h"
 
 #include <hip/hip_runtime.h>
 

@@ -322,21 +322,8 @@ __global__ __launch_bounds__(256) void score_row_kernel(IndexerArgs a) {
     }
   };
 
-  F kb[TPC][KC];
-  float kscl[SPL];
-  int e0 = c0 + wave * EPC;
-  if (e0 < c1) load_group(e0, kb, kscl);
-#pragma unroll 1
-  for (; e0 < c1; e0 += 4 * EPC) {
-    F cur[TPC][KC];
-    float cscl[SPL];
-#pragma unroll
-    for (int u = 0; u < TPC; ++u)
-#pragma unroll
-      for (int c = 0; c < KC; ++c) cur[u][c] = kb[u][c];
-#pragma unroll
-    for (int s = 0; s < SPL; ++s) cscl[s] = kscl[s];
-    if (e0 + 4 * EPC < c1) load_group(e0 + 4 * EPC, kb, kscl);      // prefetch the next group
+  // process one group: MFMAs, ReLU + head weights, store, histogram
+  auto process = [&](int e0, const F (&cur)[TPC][KC], const float (&cscl)[SPL]) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < TPC; ++u)
@@ -358,6 +345,128 @@ __global__ __launch_bounds__(256) void score_row_kernel(IndexerArgs a) {
         srow[e] = sc;
         atomicAdd(&hist[__float_as_uint(sc) >> (32 - H1_BITS)], 1u);
       }
+    }
+  };
+
+  // two groups in flight per wave (ping-pong register buffers)
+  constexpr int STRIDE = 4 * EPC;
+  F kbA[TPC][KC], kbB[TPC][KC];
+  float ksA[SPL], ksB[SPL];
+  int e0 = c0 + wave * EPC;
+  if (e0 < c1) load_group(e0, kbA, ksA);
+  if (e0 + STRIDE < c1) load_group(e0 + STRIDE, kbB, ksB);
+#pragma unroll 1
+  for (; e0 < c1; e0 += 2 * STRIDE) {
+    process(e0, kbA, ksA);
+    if (e0 + 2 * STRIDE < c1) load_group(e0 + 2 * STRIDE, kbA, ksA);
+    if (e0 + STRIDE < c1) {
+      process(e0 + STRIDE, kbB, ksB);
+      if (e0 + 3 * STRIDE < c1) load_group(e0 + 3 * STRIDE, kbB, ksB);
+    }
+  }
+  __syncthreads();
+  uint32_t* gh = L.hist + (size_t)row * H1_BINS;
+  for (int i = threadIdx.x; i < H1_BINS; i += 256) {
+    const uint32_t v = hist[i];
+    if (v) atomicAdd(&gh[i], v);
+  }
+}
+
+// ------------------------ decode score row, native FP4 ------------------------
+// v_mfma_scale_f32_16x16x128_f8f6f4 with E2M1 operands: lane (c = l%16,
+// kb = l/16) supplies 32 FP4 values (16 bytes) of column c / row c for the
+// k-block kb and the E8M0 scale of that block.  An entry has DI/32 blocks, so
+// one 128-deep k column holds 4/(DI/32) entries; the query's four head rows are
+// placed, per entry slot p, at rows 4p..4p+3 and only in the k-blocks of that
+// slot, so the accumulator gives lane group g the four head dots of entry
+// e0 + 16g + c, exactly as in the generic decode kernel.
+template <int DI>
+__global__ __launch_bounds__(256) void score_row_fp4_kernel(IndexerArgs a) {
+  constexpr int HI = 4;
+  constexpr int KBE = DI / 32;                 // k-blocks per entry
+  constexpr int EPCOL = 4 / KBE;               // entries per 128-deep column
+  constexpr int NM = KBE;                      // MFMAs per 64 entries
+  constexpr int EPC = 64;
+  constexpr int RB = DI / 2;                   // bytes per packed row
+  __shared__ uint32_t hist[H1_BINS];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = blockIdx.y;
+  const int b = row / a.Tq, t = row % a.Tq;
+  const int n = row_len(a, b, t);
+  const int c0 = blockIdx.x * ROW_CHUNK;
+  if (c0 >= n) return;
+  const int c1 = min(n, c0 + ROW_CHUNK);
+  LongWs L = long_ws(a.ws, a.B * a.Tq, a.Nc_cap, a.topk);
+  for (int i = threadIdx.x; i < H1_BINS; i += 256) hist[i] = 0;
+
+  const int c = lane & 15, kb = lane >> 4;
+  const int half = kb % KBE;
+  // A operands: row r = 4p + h holds q_h in the k-blocks of entry slot p
+  i32x8 qa[NM];
+  int qs[NM];
+  {
+    const int h = c % 4, p = c / 4;
+    const size_t qrow = ((size_t)b * a.Tq + t) * HI + h;
+    const u32x4 qv = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(a.qi) + qrow * RB + 16 * half);
+    const int qsv = reinterpret_cast<const uint8_t*>(a.qi_scale)[qrow * KBE + half];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const bool on = (m * EPCOL + kb / KBE) == p;
+      qa[m] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+      if (on) { qa[m][0] = qv[0]; qa[m][1] = qv[1]; qa[m][2] = qv[2]; qa[m][3] = qv[3]; }
+      qs[m] = on ? qsv : 127;
+    }
+  }
+  float wr[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) wr[i] = a.w[((size_t)b * a.Tq + t) * HI + i];
+  __syncthreads();
+
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.kic) + (size_t)b * a.Nc_cap * RB;
+  const uint8_t* sbase = reinterpret_cast<const uint8_t*>(a.kic_scale) + (size_t)b * a.Nc_cap * KBE;
+  float* srow = L.scores + (size_t)row * nc_pad(a.Nc_cap);
+
+  auto load_group = [&](int e0, u32x4 (&kv)[NM], int (&ks)[NM]) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const int e = min(e0 + 16 * (m * EPCOL + kb / KBE) + c, c1 - 1);
+      kv[m] = *reinterpret_cast<const u32x4*>(kbase + (size_t)e * RB + 16 * half);
+      ks[m] = sbase[(size_t)e * KBE + half];
+    }
+  };
+  auto process = [&](int e0, const u32x4 (&kv)[NM], const int (&ks)[NM]) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const i32x8 bv = i32x8{(int)kv[m][0], (int)kv[m][1], (int)kv[m][2], (int)kv[m][3], 0, 0, 0, 0};
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[m], bv, acc, 4, 4, 0, qs[m], 0, ks[m]);
+    }
+    const int e = e0 + lane;
+    float sc = 0.f;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const float x = acc[h];
+      sc = fmaf(wr[h], x > 0.f ? x : 0.f, sc);
+    }
+    if (e < c1) {
+      sc += 0.f;
+      srow[e] = sc;
+      atomicAdd(&hist[__float_as_uint(sc) >> (32 - H1_BITS)], 1u);
+    }
+  };
+  constexpr int STRIDE = 4 * EPC;
+  u32x4 kvA[NM], kvB[NM];
+  int ksA[NM], ksB[NM];
+  int e0 = c0 + wave * EPC;
+  if (e0 < c1) load_group(e0, kvA, ksA);
+  if (e0 + STRIDE < c1) load_group(e0 + STRIDE, kvB, ksB);
+#pragma unroll 1
+  for (; e0 < c1; e0 += 2 * STRIDE) {
+    process(e0, kvA, ksA);
+    if (e0 + 2 * STRIDE < c1) load_group(e0 + 2 * STRIDE, kvA, ksA);
+    if (e0 + STRIDE < c1) {
+      process(e0 + STRIDE, kvB, ksB);
+      if (e0 + 3 * STRIDE < c1) load_group(e0 + 3 * STRIDE, kvB, ksB);
     }
   }
   __syncthreads();
@@ -762,7 +871,10 @@ static void launch_scores(const IndexerArgs& a, hipStream_t st, bool long_path) 
   if (long_path) {
     dim3 grid((ne_ub + ROW_CHUNK - 1) / ROW_CHUNK, a.B * a.Tq);
     ProfScope ps("indexer_score", st);
-    hipLaunchKernelGGL((score_row_kernel<QK, DI, HI>), grid, dim3(256), 0, st, a);
+    if constexpr (QK == QK_FP4 && HI == 4)
+      hipLaunchKernelGGL((score_row_fp4_kernel<DI>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((score_row_kernel<QK, DI, HI>), grid, dim3(256), 0, st, a);
   } else {
     const int TT = 16 / HI;
     dim3 grid((ne_ub + SCORE_WG_ENTRIES - 1) / SCORE_WG_ENTRIES, (a.Tq + TT - 1) / TT, a.B);
