@@ -146,6 +146,13 @@ __global__ __launch_bounds__(RW * KG * 64) void attend_kernel(AttendArgs a, Attn
   const T* vcb = reinterpret_cast<const T*>(a.vc) + (size_t)b * a.Nc_cap * D;
   const T* kwb = a.kw ? reinterpret_cast<const T*>(a.kw) + (size_t)b * a.R * D : nullptr;
   const T* vwb = a.vw ? reinterpret_cast<const T*>(a.vw) + (size_t)b * a.R * D : nullptr;
+  // Facts that let whole tiles skip per-element masking (wave-uniform):
+  // every window row is present in the raw buffer, and the smallest number of
+  // compressed entries visible to any valid row of this wave.
+  const bool win_ok = nwin == 0 || (kwb != nullptr && wlo - rp0 >= 0 && wlo + nwin - 1 - rp0 < a.R);
+  int wave_min_ne = qvalid ? q_ne : INT_MAX;
+#pragma unroll
+  for (int o2 = 32; o2 > 0; o2 >>= 1) wave_min_ne = min(wave_min_ne, __shfl_xor(wave_min_ne, o2, 64));
 
   // source row of key slot s (nullptr = absent)
   auto key_src = [&](int s, const T*& kp, const T*& vp) {
@@ -228,43 +235,62 @@ __global__ __launch_bounds__(RW * KG * 64) void attend_kernel(AttendArgs a, Attn
     // ---- S^T = K Q^T for this wave's 32-key sub-tiles ----
     f32x16 st[NSUB];
 #pragma unroll
-    for (int si = 0; si < NSUB; ++si) {
-      const int sub = KG == 2 ? kg : si;
+    for (int si = 0; si < NSUB; ++si)
 #pragma unroll
       for (int r = 0; r < 16; ++r) st[si][r] = 0.f;
 #pragma unroll
-      for (int s = 0; s < DSTEP; ++s) {
-        Frag<T> kf, qf;
+    for (int s = 0; s < DSTEP; ++s) {
+      Frag<T> qf;
+      frag_load(qf, Qs + (rw * 32 + col) * KS + 16 * s + 8 * half);
+#pragma unroll
+      for (int si = 0; si < NSUB; ++si) {
+        const int sub = KG == 2 ? kg : si;
+        Frag<T> kf;
         frag_load(kf, Ks + (sub * 32 + col) * KS + 16 * s + 8 * half);
-        frag_load(qf, Qs + (rw * 32 + col) * KS + 16 * s + 8 * half);
         mma32(st[si], kf, qf);
       }
     }
-    // ---- mask, online softmax ----
+    // ---- mask (only tiles that reach a boundary), online softmax ----
+    const int t_end = s0 + KT;
+    const bool full = t_end <= kend &&
+                      (SPARSE ? (t_end <= ncomp || win_ok) : (t_end <= ncomp && t_end <= wave_min_ne));
     float mt = -INFINITY;
 #pragma unroll
     for (int si = 0; si < NSUB; ++si) {
       const int sub = KG == 2 ? kg : si;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int s = s0 + sub * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        bool ok = qvalid && s < kend;
-        if (ok && s >= ncomp) {
-          const int p = wlo + (s - ncomp);
-          ok = (p - rp0 >= 0) && (p - rp0 < a.R) && (kwb != nullptr);   // row present
-          if (!SPARSE) ok = ok && p >= q_wlo && p <= qpos;
-        } else if (ok && !SPARSE) {
-          ok = s < q_ne;
+        float x = st[si][r] * gm.scale_log2;
+        if (!full) {
+          const int s = s0 + sub * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          bool ok = qvalid && s < kend;
+          if (ok && s >= ncomp) {
+            const int p = wlo + (s - ncomp);
+            ok = (p - rp0 >= 0) && (p - rp0 < a.R) && (kwb != nullptr);   // row present
+            if (!SPARSE) ok = ok && p >= q_wlo && p <= qpos;
+          } else if (ok && !SPARSE) {
+            ok = s < q_ne;
+          }
+          x = ok ? x : -INFINITY;
         }
-        const float x = ok ? st[si][r] * gm.scale_log2 : -INFINITY;
         st[si][r] = x;
         mt = fmaxf(mt, x);
       }
     }
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float m_new = fmaxf(m_run, mt);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fexp2<T>(m_run - m_use);
+    // The reference max only moves when a lane's tile max exceeds it by more
+    // than 8 (log2 units): P stays <= 2^8 and most tiles skip the O rescale.
+    if (__any(mt > m_run + 8.f)) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = (m_new == -INFINITY) ? 1.f : fexp2<T>(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < DVT; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     float psum = 0.f;
     Frag<T> pf[NSUB][2];
 #pragma unroll
@@ -278,12 +304,7 @@ __global__ __launch_bounds__(RW * KG * 64) void attend_kernel(AttendArgs a, Attn
       frag_from_f32(pf[si][0], pv);
       frag_from_f32(pf[si][1], pv + 8);
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int i = 0; i < DVT; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
+    l_run += psum;
 
     // ---- O^T += V^T P^T ----
 #pragma unroll

@@ -18,10 +18,13 @@ __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(bf16 v) { return __uint_as_float((uint32_t)v.x << 16); }
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
-// fp32 -> bf16, round to nearest even (inputs are finite).
+// fp32 -> bf16, round to nearest even (gfx950 v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
 }
 template <typename T> __device__ __forceinline__ T from_f32(float f);
 template <> __device__ __forceinline__ float from_f32<float>(float f) { return f; }
@@ -55,8 +58,7 @@ __device__ __forceinline__ void frag_zero(Frag<float>& f) {
 // Build a fragment from 8 fp32 values (bf16: round to nearest even).
 __device__ __forceinline__ void frag_from_f32(Frag<bf16>& f, const float* x) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    f.v[i] = f32_to_bf16_bits(x[2 * i]) | (f32_to_bf16_bits(x[2 * i + 1]) << 16);
+  for (int i = 0; i < 4; ++i) f.v[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
 }
 __device__ __forceinline__ void frag_from_f32(Frag<float>& f, const float* x) {
 #pragma unroll
