@@ -7,8 +7,10 @@
 // then the k largest I[t,.] with equal scores going to the lower j, emitted
 // ascending by j and padded with -1.
 //
-// Scores (MFMA 16x16x32: bf16, fp32 as 8 x 16x16x4, FP8 E4M3 natively; FP4
-// codes times their E8M0 block scale are widened exactly to bf16):
+// Scores (MFMA 16x16x32: bf16, fp32 as 8 x 16x16x4; FP8 E4M3 codes, and FP4
+// codes times their E8M0 block scale, are widened exactly to bf16 first — the
+// native FP8 MFMA accumulates with a few 1e-5 relative error, which would put
+// FP8 rows outside a 1e-6 tie band, while bf16 products accumulate in fp32):
 //   * prefill tile kernel: (token, head) rows of qI form the A operand (16
 //     rows = 16/HI tokens) and 16 entries form B, so each lane receives the HI
 //     head dots of one token for one entry and applies ReLU + head weights
@@ -49,16 +51,18 @@ static constexpr int TOPK_LDS_KEYS = 12288;
 __host__ __device__ __forceinline__ int nc_pad(int Nc_cap) { return (Nc_cap + 63) & ~63; }
 
 // ---------------- operand loaders: 8 k-values -> one fragment --------------
-struct Frag8 { uint64_t v; };                   // 8 FP8 codes
 template <int QK> struct QkTraits;
 template <> struct QkTraits<QK_F32> { using F = Frag<float>; };
 template <> struct QkTraits<QK_BF16> { using F = Frag<bf16>; };
-template <> struct QkTraits<QK_FP8> { using F = Frag8; };
+template <> struct QkTraits<QK_FP8> { using F = Frag<bf16>; };
 template <> struct QkTraits<QK_FP4> { using F = Frag<bf16>; };
 
-__device__ __forceinline__ void frag_zero(Frag8& f) { f.v = 0; }
-__device__ __forceinline__ void mma16(f32x4& c, const Frag8& a, const Frag8& b) {
-  c = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)a.v, (long)b.v, c, 0, 0, 0);
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// Two E4M3 codes (bytes 0-1, or 2-3 if HIGH_HALF) -> two packed bf16.  Every E4M3
+// value is a bf16 value, so the widening is exact.
+template <bool HIGH_HALF>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16(uint32_t c) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, 1.0f, HIGH_HALF));
 }
 
 // E2M1 code (low 4 bits) -> fp32 value.
@@ -86,7 +90,9 @@ __device__ __forceinline__ void load_qk_frag(typename QkTraits<QK>::F& f, const 
   } else if constexpr (QK == QK_BF16) {
     frag_load(f, reinterpret_cast<const bf16*>(row) + k0);
   } else if constexpr (QK == QK_FP8) {
-    f.v = *reinterpret_cast<const uint64_t*>(reinterpret_cast<const uint8_t*>(row) + k0);
+    const uint2 c = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(row) + k0);
+    f.v = u32x4{e4m3x2_to_bf16<false>(c.x), e4m3x2_to_bf16<true>(c.x),
+                e4m3x2_to_bf16<false>(c.y), e4m3x2_to_bf16<true>(c.y)};
   } else {
     const uint32_t c = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(row) + k0 / 2);
     const float scl = e8m0_val(sc[k0 / 32]);
@@ -857,6 +863,357 @@ __global__ __launch_bounds__(SEL_NT) void long_final_kernel(IndexerArgs a) {
   }
 }
 
+// --------------------------- fused prefill path ----------------------------
+// One workgroup (8 waves) per FQ consecutive query tokens.  Scores never reach
+// HBM: the eligible indexer keys are streamed twice (from L2) and the scores
+// recomputed on MFMA each time.
+//   pass 1: an 11-bit radix histogram of each token's score keys in LDS (bits
+//           30..20 — bit 31 is the sign, always 0 here — as two 16-bit counters
+//           per word); two tokens per wave then find the bin b1 holding the
+//           k-th largest key and the count above it;
+//   pass 2: entries whose digit is above b1 set their bit in the token's LDS
+//           selection bitmap, entries inside b1 append (key, index) to the
+//           token's candidate slots;
+//   resolve: per token, a radix select over the low 20 bits of the candidates
+//           (lowest index among equal keys) marks the remaining winners in the
+//           bitmap, which is then written out as the ascending index list.
+// A token whose boundary bin overflows its candidate slots is rescored into the
+// workspace and selected by the exact block-wide select.
+static constexpr int FQ = 16;                  // query tokens per workgroup
+static constexpr int FNT = 512;                // threads per workgroup
+static constexpr int FNW = FNT / 64;
+static constexpr int FK = 512;                 // largest top-k on this path
+static constexpr int FCAP = 512;               // boundary-bin candidates per token
+static constexpr int FMAXN = 8192;             // largest eligible row on this path
+static constexpr int FBM = FMAXN / 32;         // bitmap words per token
+// Histogram rows are padded with one word after every 32 (pass 1) or 16
+// (resolve) so that the per-lane bin ranges of the top-down scan fall in
+// distinct LDS banks.
+static constexpr int HROW = 1024 + 1024 / 32;  // pass-1 row: 2048 bins as 16-bit pairs
+static constexpr int SROW = 1024 + 1024 / 16;  // resolve row: 1024 bins
+__device__ __forceinline__ int hpad(int w) { return w + (w >> 5); }
+__device__ __forceinline__ int spad(int w) { return w + (w >> 4); }
+
+struct FusedSmem {
+  union {
+    uint32_t hist[FQ + 1][HROW];               // bin i: word hpad(i & 1023), half i >> 10;
+                                               // row FQ absorbs ineligible entries
+    uint32_t cand[FQ][FCAP][2];                // (key, index)
+  } u;
+  uint32_t bm[FQ][FBM];
+  uint32_t scr[FNW][SROW];                     // per-wave radix scratch; fallback select
+  uint32_t ncand[FQ], b1[FQ], above[FQ], fb[FQ];
+};
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Wave-level: scanning nb bins from the top down, the bin where the running
+// count first reaches `need` (>= 1, <= total) and the count strictly above it.
+template <typename Cnt>
+__device__ __forceinline__ void wave_find_bin(int nb, uint32_t need, Cnt cnt, uint32_t& bin,
+                                              uint32_t& above) {
+  const int lane = threadIdx.x & 63;
+  const int per = nb / 64;
+  const int hi = nb - lane * per;
+  uint32_t local = 0;
+  for (int i = 0; i < per; ++i) local += cnt(hi - 1 - i);
+  const uint32_t incl = wave_incl_scan(local);
+  const uint32_t excl = incl - local;
+  const bool mine = excl < need && incl >= need;
+  uint32_t bb = 0, ab = 0;
+  if (mine) {
+    uint32_t cum = excl;
+    for (int i = 0; i < per; ++i) {
+      const uint32_t h = cnt(hi - 1 - i);
+      if (cum + h >= need) { bb = hi - 1 - i; ab = cum; break; }
+      cum += h;
+    }
+  }
+  const uint64_t m = __ballot(mine);
+  const int src = m ? __ffsll((unsigned long long)m) - 1 : 0;
+  bin = __shfl(bb, src, 64);
+  above = __shfl(ab, src, 64);
+}
+
+template <int QK, int DI, int HI>
+__global__ __launch_bounds__(FNT) void fused_prefill_kernel(IndexerArgs a) {
+  constexpr int KC = DI / 32;
+  constexpr int NRT = HI;                      // 16-row tiles of (token, head) rows
+  constexpr int SPL = 4 / HI;                  // scores per lane per row tile
+  constexpr int TPW = FQ / FNW;                // tokens resolved per wave
+  using F = typename QkTraits<QK>::F;
+  extern __shared__ __align__(16) unsigned char fsm_raw[];
+  FusedSmem& sm = *reinterpret_cast<FusedSmem*>(fsm_raw);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int b = blockIdx.y, t0 = blockIdx.x * FQ;
+  const int nt = min(FQ, a.Tq - t0);
+  const int k = a.topk;
+  const int ne_max = row_len(a, b, t0 + nt - 1);
+  const size_t rb = qk_row_bytes<QK>(DI);
+
+  // A operands: row 16 rt + r of the tiles is token (16 rt + r) / HI, head (16 rt + r) % HI
+  F qa[NRT][KC];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+    const int tt = (16 * rt + r) / HI, h = (16 * rt + r) % HI;
+    const size_t qrow = ((size_t)b * a.Tq + t0 + tt) * HI + h;
+    const char* qptr = reinterpret_cast<const char*>(a.qi) + qrow * rb;
+    const uint8_t* qsc = QK == QK_FP4 ? reinterpret_cast<const uint8_t*>(a.qi_scale) + qrow * (DI / 32) : nullptr;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      if (tt < nt) load_qk_frag<QK>(qa[rt][c], qptr, qsc, 8 * (g * KC + c));
+      else frag_zero(qa[rt][c]);
+    }
+  }
+  // accumulator rows of lane group g in tile rt: 16 rt + 4g + i -> token (16 rt + 4g + i) / HI
+  float wr[NRT][4];
+  int tok[NRT][SPL], tne[NRT][SPL];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = 16 * rt + 4 * g + i;
+      const int tt = rr / HI, h = rr % HI;
+      float wv = 0.f;
+      if (tt < nt) {
+        const size_t wi = ((size_t)b * a.Tq + t0 + tt) * HI + h;
+        wv = a.w[wi];
+        if constexpr (QK == QK_FP8) wv *= reinterpret_cast<const float*>(a.qi_scale)[wi];
+      }
+      wr[rt][i] = wv;
+    }
+#pragma unroll
+    for (int sp = 0; sp < SPL; ++sp) {
+      const int tt = (16 * rt + 4 * g) / HI + sp;
+      tok[rt][sp] = tt;
+      tne[rt][sp] = tt < nt ? row_len(a, b, t0 + tt) : 0;
+    }
+  }
+  for (int i = tid; i < (FQ + 1) * HROW; i += FNT) (&sm.u.hist[0][0])[i] = 0u;
+  for (int i = tid; i < FQ * FBM; i += FNT) (&sm.bm[0][0])[i] = 0u;
+  if (tid < FQ) { sm.ncand[tid] = 0; sm.fb[tid] = 0; sm.b1[tid] = 0; sm.above[tid] = 0; }
+  __syncthreads();
+
+  const char* kbase = reinterpret_cast<const char*>(a.kic) + (size_t)b * a.Nc_cap * rb;
+  const uint8_t* sbase = QK == QK_FP4 ? reinterpret_cast<const uint8_t*>(a.kic_scale) + (size_t)b * a.Nc_cap * (DI / 32) : nullptr;
+  const float* fsc = QK == QK_FP8 ? reinterpret_cast<const float*>(a.kic_scale) + (size_t)b * a.Nc_cap : nullptr;
+
+  // Scores of entries e0 + 16 wave + r (e0 steps by 16 FNW) for every row tile;
+  // f(rt, sp, entry, key, eligible) is called for each.  All MFMAs of an entry
+  // tile issue before the epilogue reads their results.
+  auto pass = [&](auto&& f) {
+    F kb[KC];
+    float ks = 1.f;
+    auto load = [&](int e0) {
+      const int e = min(e0 + 16 * wave + r, ne_max - 1);
+#pragma unroll
+      for (int c = 0; c < KC; ++c)
+        load_qk_frag<QK>(kb[c], kbase + (size_t)e * rb, QK == QK_FP4 ? sbase + (size_t)e * (DI / 32) : nullptr,
+                         8 * (g * KC + c));
+      if constexpr (QK == QK_FP8) ks = fsc[e];
+    };
+    if (ne_max > 0) load(0);
+#pragma unroll 1
+    for (int e0 = 0; e0 < ne_max; e0 += 16 * FNW) {
+      F cur[KC];
+#pragma unroll
+      for (int c = 0; c < KC; ++c) cur[c] = kb[c];
+      const float cks = ks;
+      if (e0 + 16 * FNW < ne_max) load(e0 + 16 * FNW);
+      const int e = e0 + 16 * wave + r;
+      f32x4 acc[NRT];
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) {
+        acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < KC; ++c) mma16(acc[rt], qa[rt][c], cur[c]);
+      }
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) {
+#pragma unroll
+        for (int sp = 0; sp < SPL; ++sp) {
+          // scores are sums of non-negative terms starting from +0, so never -0
+          float sc = 0.f;
+#pragma unroll
+          for (int h = 0; h < HI; ++h) {
+            const float x = __int_as_float(max(__float_as_int(acc[rt][sp * HI + h]), 0));   // ReLU
+            sc = fmaf(wr[rt][sp * HI + h], x, sc);
+          }
+          if constexpr (QK == QK_FP8) sc *= cks;
+          f(rt, sp, e, __float_as_uint(sc), e < tne[rt][sp]);
+        }
+      }
+    }
+  };
+
+  // ---- pass 1: per-token histograms of key bits 30..20 ----
+  pass([&](int rt, int sp, int e, uint32_t key, bool ok) {
+    const uint32_t bin = key >> 20;
+    atomicAdd(&sm.u.hist[ok ? tok[rt][sp] : FQ][hpad(bin & 1023u)], 1u << ((bin >> 10) << 4));
+  });
+  __syncthreads();
+  for (int j = 0; j < TPW; ++j) {
+    const int tt = TPW * wave + j;
+    if (tt >= nt || row_len(a, b, t0 + tt) <= k) continue;
+    const uint32_t* hrow = sm.u.hist[tt];
+    uint32_t bin, ab;
+    wave_find_bin(2048, (uint32_t)k,
+                  [&](int i) { return (hrow[hpad(i & 1023)] >> ((i >> 10) << 4)) & 0xFFFFu; }, bin, ab);
+    if (lane == 0) { sm.b1[tt] = bin; sm.above[tt] = ab; }
+  }
+  __syncthreads();
+  uint32_t tb1[NRT][SPL];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+    for (int sp = 0; sp < SPL; ++sp) tb1[rt][sp] = tne[rt][sp] > k ? sm.b1[tok[rt][sp]] : 0xFFFFFFFFu;
+  __syncthreads();                                           // histograms become candidate slots
+  // ---- pass 2: bits above b1, candidates inside b1 ----
+  pass([&](int rt, int sp, int e, uint32_t key, bool ok) {
+    const uint32_t d = key >> 20;
+    if (ok && d >= tb1[rt][sp]) {
+      const int tt = tok[rt][sp];
+      if (d > tb1[rt][sp]) {
+        atomicOr(&sm.bm[tt][e >> 5], 1u << (e & 31));
+      } else {
+        const uint32_t slot = atomicAdd(&sm.ncand[tt], 1u);
+        if (slot < (uint32_t)FCAP) { sm.u.cand[tt][slot][0] = key; sm.u.cand[tt][slot][1] = (uint32_t)e; }
+      }
+    }
+  });
+  __syncthreads();
+  // ---- resolve the boundary bin, write ascending lists ----
+  uint32_t* scr = sm.scr[wave];
+  for (int j = 0; j < TPW; ++j) {
+    const int tt = TPW * wave + j;
+    if (tt >= nt) break;
+    const int ne = row_len(a, b, t0 + tt);
+    int32_t* idx = a.idx_out + ((size_t)b * a.Tq + t0 + tt) * k;
+    if (ne <= k) {
+      for (int i = lane; i < k; i += 64) idx[i] = i < ne ? i : -1;
+      continue;
+    }
+    const uint32_t ncand = sm.ncand[tt];
+    uint32_t rem = (uint32_t)k - sm.above[tt];
+    if (ncand > (uint32_t)FCAP || rem > ncand) {
+      if (lane == 0) sm.fb[tt] = 1u;
+      continue;
+    }
+    const uint32_t(*cand)[2] = sm.u.cand[tt];
+    uint32_t prefix = 0, pmask = 0;
+    for (int p = 0; p < 2; ++p) {
+      const int sh = p == 0 ? 10 : 0;
+      for (int i = lane; i < SROW; i += 64) scr[i] = 0u;
+      wave_sync();
+      for (uint32_t i = lane; i < ncand; i += 64) {
+        const uint32_t low = cand[i][0] & 0xFFFFFu;
+        if ((low & pmask) == prefix) atomicAdd(&scr[spad((low >> sh) & 1023u)], 1u);
+      }
+      wave_sync();
+      uint32_t bin, ab;
+      wave_find_bin(1024, rem, [&](int i) { return scr[spad(i)]; }, bin, ab);
+      prefix |= bin << sh;
+      pmask |= 1023u << sh;
+      rem -= ab;
+      wave_sync();
+    }
+    // rem keys equal to the threshold's low bits remain to be taken
+    uint32_t neq = 0;
+    for (uint32_t i = lane; i < ncand; i += 64) neq += (cand[i][0] & 0xFFFFFu) == prefix;
+    neq = (uint32_t)wave_sum((float)neq);
+    for (uint32_t i = lane; i < ncand; i += 64) {
+      const uint32_t low = cand[i][0] & 0xFFFFFu;
+      bool take = low > prefix;
+      if (low == prefix) {
+        if (neq == rem) {
+          take = true;
+        } else {
+          uint32_t rank = 0;
+          for (uint32_t q = 0; q < ncand; ++q)
+            rank += ((cand[q][0] & 0xFFFFFu) == prefix) && (cand[q][1] < cand[i][1]);
+          take = rank < rem;
+        }
+      }
+      if (take) atomicOr(&sm.bm[tt][cand[i][1] >> 5], 1u << (cand[i][1] & 31));
+    }
+    wave_sync();
+    constexpr int WPL = FBM / 64;                           // bitmap words per lane
+    const int nw = (ne + 31) / 32;
+    uint32_t words[WPL];
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int q = 0; q < WPL; ++q) {
+      const int w = lane * WPL + q;
+      words[q] = w < nw ? sm.bm[tt][w] : 0u;
+      cnt += (uint32_t)__popc(words[q]);
+    }
+    uint32_t pos = wave_incl_scan(cnt) - cnt;
+#pragma unroll
+    for (int q = 0; q < WPL; ++q) {
+      uint32_t word = words[q];
+      while (word) {
+        const int bit = __ffs(word) - 1;
+        word &= word - 1;
+        if (pos < (uint32_t)k) idx[pos] = (lane * WPL + q) * 32 + bit;
+        ++pos;
+      }
+    }
+    const uint32_t tot = __shfl(pos, 63, 64);
+    for (uint32_t i = tot + lane; i < (uint32_t)k; i += 64) idx[i] = -1;
+    wave_sync();
+  }
+  __syncthreads();
+  // ---- exact fallback for tokens whose boundary bin overflowed ----
+  for (int tt = 0; tt < nt; ++tt) {
+    if (!sm.fb[tt]) continue;                                // uniform: LDS after a barrier
+    const int ne = row_len(a, b, t0 + tt);
+    float* srow = reinterpret_cast<float*>(a.ws) + ((size_t)b * a.Tq + t0 + tt) * nc_pad(a.Nc_cap);
+    pass([&](int rt, int sp, int e, uint32_t key, bool ok) {
+      if (ok && tok[rt][sp] == tt) srow[e] = __uint_as_float(key);
+    });
+    __syncthreads();
+    TopkSmem<FNT>& ts = *reinterpret_cast<TopkSmem<FNT>*>(&sm.scr[0][0]);
+    select_row<FNT>(ts, reinterpret_cast<const uint32_t*>(srow), ne, k,
+                    a.idx_out + ((size_t)b * a.Tq + t0 + tt) * k, nullptr);
+    __syncthreads();
+  }
+}
+
+static bool use_fused_prefill(const IndexerArgs& a) {
+  return a.Tq > 4 && a.topk <= FK && a.Nc_cap <= FMAXN && a.score_out == nullptr;
+}
+
+template <int QK, int DI, int HI>
+static hipError_t launch_fused(const IndexerArgs& a, hipStream_t st) {
+  static bool attr_set = false;
+  const size_t lds = sizeof(FusedSmem);
+  auto kfn = fused_prefill_kernel<QK, DI, HI>;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  ProfScope ps("indexer_fused", st);
+  hipLaunchKernelGGL(kfn, dim3((a.Tq + FQ - 1) / FQ, a.B), dim3(FNT), lds, st, a);
+  return hipGetLastError();
+}
+
+template <int QK, int DI>
+static hipError_t launch_fused_hi(const IndexerArgs& a, hipStream_t st) {
+  if (a.HI == 1) return launch_fused<QK, DI, 1>(a, st);
+  if (a.HI == 2) return launch_fused<QK, DI, 2>(a, st);
+  return launch_fused<QK, DI, 4>(a, st);
+}
+
+template <int QK>
+static hipError_t launch_fused_di(const IndexerArgs& a, hipStream_t st) {
+  return a.dI == 32 ? launch_fused_hi<QK, 32>(a, st) : launch_fused_hi<QK, 64>(a, st);
+}
+
 // --------------------------------- launch ----------------------------------
 size_t indexer_workspace(int B, int Tq, int Nc_cap, int HI, int dI, int topk, int qk) {
   (void)HI; (void)dI; (void)qk;
@@ -898,6 +1255,14 @@ static void launch_scores_di(const IndexerArgs& a, hipStream_t st, bool lp) {
 
 hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t st) {
   if (a.B == 0 || a.Tq == 0) return hipSuccess;
+  if (use_fused_prefill(a)) {
+    switch (a.qk) {
+      case QK_F32: return launch_fused_di<QK_F32>(a, st);
+      case QK_BF16: return launch_fused_di<QK_BF16>(a, st);
+      case QK_FP8: return launch_fused_di<QK_FP8>(a, st);
+      case QK_FP4: return launch_fused_di<QK_FP4>(a, st);
+    }
+  }
   const bool lp = use_long_path(a.Tq, a.Nc_cap);
   const int rows = a.B * a.Tq;
   if (lp) {

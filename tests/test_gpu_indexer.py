@@ -9,7 +9,7 @@ import oracle
 from helpers import check_topk_row, dev, f64
 from oracle import formats
 from sparse_attention_17_amd import ops
-from synth import configs, inputs
+from synth import configs, inputs, quant
 
 pytestmark = pytest.mark.gpu
 
@@ -169,3 +169,93 @@ def test_fp32_and_bf16_long_rows():
         w = configs.CSA_DECODE_128K.with_(B=3, ctx=4 * 20000, qk_dtype=qk, topk=777)
         x, idx = _decode(w)
         assert _check_decode(w, x, idx) >= w.B - 1
+
+
+# ---- prefill rows through the fused score+select kernel (no scores returned) ----
+
+def _prefill_raw(B, Tq, HI, dI, Nc_cap, qk, wid):
+    """Seeded qI / w / KIc for prefill rows that start at arbitrary positions."""
+    qi = inputs.normal(wid, "qi", (B, Tq, HI, dI))
+    kic = inputs.normal(wid, "kic", (B, Nc_cap, dI))
+    wl = inputs.normal(wid, "wlog", (B, Tq, HI), scaled_by_last=False)
+    x = {"w": torch.softmax(wl, dim=-1)}
+    for name, v in (("qi", qi), ("kic", kic)):
+        if qk == "fp8":
+            x[name], x[name + "_scale"] = quant.quant_fp8_rows(v)
+        elif qk == "fp4":
+            x[name], x[name + "_scale"] = quant.quant_fp4_blocks(v)
+        else:
+            x[name] = inputs.to_dtype(v, qk)
+    return x
+
+
+def _check_all_prefill(x, idx, pos0, m, k, qk, band_rel=None):
+    qi = _dequant(x, "qi", qk)
+    kic = _dequant(x, "kic", qk)
+    w64 = f64(x["w"])
+    for b in range(idx.shape[0]):
+        for t in range(idx.shape[1]):
+            ne = min((pos0[b] + t + 1) // m, kic.shape[1])
+            sc = oracle.csa.indexer_scores(qi[b, t:t + 1], w64[b, t:t + 1], kic[b, :ne])[0]
+            kw = {} if band_rel is None else {"band_rel": band_rel}
+            check_topk_row(idx[b, t], sc, ne, k, **kw)
+
+
+def test_tiny_f32_fused_equals_score_then_select():
+    # the same rows through both prefill paths: fp32 sets must be identical
+    w = configs.TINY
+    x, kic, (idx_a, _) = _prefill(w, return_scores=True)
+    g = {k: v.to(dev()) for k, v in x.items()}
+    pos0 = torch.zeros(w.B, dtype=torch.int32, device=dev())
+    idx_b = ops.indexer_topk(g["qi"], g["w"], kic, pos0, w.m, w.topk, max_pos=w.ctx - 1)
+    assert torch.equal(idx_a, idx_b)
+
+
+@pytest.mark.parametrize("qk,HI,dI,k", [("bf16", 2, 64, 128), ("fp8", 4, 64, 300),
+                                        ("fp4", 1, 64, 64), ("f32", 4, 32, 512)])
+def test_prefill_ragged_positions_and_tail(qk, HI, dI, k):
+    # Tq not a multiple of the 16-token tile, sequences at different offsets
+    B, Tq, Nc_cap, m = 2, 1000, 1024, 4
+    pos = [3000, 17]
+    x = _prefill_raw(B, Tq, HI, dI, Nc_cap, qk, 90 + HI)
+    g = {n: v.to(dev()) for n, v in x.items()}
+    pos0 = torch.tensor(pos, dtype=torch.int32, device=dev())
+    idx = ops.indexer_topk(g["qi"], g["w"], g["kic"], pos0, m, k, max_pos=pos[0] + Tq - 1,
+                           qi_scale=g.get("qi_scale"), kic_scale=g.get("kic_scale"),
+                           qk_dtype=qk)
+    _check_all_prefill(x, idx.cpu().numpy(), pos, m, k, qk)
+
+
+def test_prefill_all_tied_rows():
+    # every score is 0: rows with up to 512 eligible entries resolve the tied
+    # boundary bin in LDS, longer rows overflow it and take the exact fallback;
+    # both must return the lowest indices
+    w = configs.CSA_PREFILL_32K.with_(ctx=4096, Tq=4096, topk=100)
+    x = inputs.make_inputs(w)
+    g = {k: v.to(dev()) for k, v in x.items()}
+    kic = torch.zeros(w.B, w.Nc, w.dI, dtype=torch.bfloat16, device=dev())
+    pos0 = torch.zeros(w.B, dtype=torch.int32, device=dev())
+    idx = ops.indexer_topk(g["qi"], g["w"], kic, pos0, w.m, w.topk, max_pos=w.ctx - 1).cpu()
+    for t in range(w.Tq):
+        ne = (t + 1) // w.m
+        n = min(ne, w.topk)
+        assert torch.equal(idx[0, t, :n], torch.arange(n, dtype=torch.int32)), t
+        assert torch.all(idx[0, t, n:] == -1), t
+
+
+def test_prefill_boundary_ties_take_lowest_indices():
+    # 7 distinct key rows repeated: every score value has ~ne/7 copies, so the
+    # k-th value is tied in every row; the lowest tied indices must win
+    w = configs.CSA_PREFILL_32K.with_(ctx=4096, Tq=4096, topk=200, HI=2)
+    x = inputs.make_inputs(w)
+    g = {k: v.to(dev()) for k, v in x.items()}
+    base = inputs.normal(95, "kic", (w.B, 7, w.dI)).to(torch.bfloat16)
+    kic = base.repeat(1, w.Nc // 7 + 1, 1)[:, :w.Nc].contiguous()
+    pos0 = torch.zeros(w.B, dtype=torch.int32, device=dev())
+    idx = ops.indexer_topk(g["qi"], g["w"], kic.to(dev()), pos0, w.m, w.topk,
+                           max_pos=w.ctx - 1).cpu().numpy()
+    qi, w64, k64 = f64(x["qi"][0]), f64(x["w"][0]), f64(kic[0])
+    for t in list(range(790, 830)) + list(range(2040, 2060)) + list(range(4060, 4096)):
+        ne = (t + 1) // w.m
+        sc = oracle.csa.indexer_scores(qi[t:t + 1], w64[t:t + 1], k64[:ne])[0]
+        assert check_topk_row(idx[0, t], sc, ne, w.topk, band_rel=0.0), t
