@@ -171,6 +171,13 @@ static csa_status_t check_attend_common(const void* q, const void* kc, const voi
           "max_pos (%d) must be >= Tq-1 and < 2^30", max_pos);
   REQUIRE((long long)B * Tq * H * d < kMaxElems && (long long)B * Nc_cap * d < kMaxElems,
           CSA_INVALID_ARGUMENT, "tensor too large");
+  {
+    // the kernels address one sequence's rows with 32-bit byte offsets
+    const long long eb = dt == CSA_F32 ? 4 : 2;
+    REQUIRE((long long)Tq * H * d * eb < (1LL << 31) && (long long)Nc_cap * d * eb < (1LL << 31) &&
+                (window == 0 || (long long)R * d * eb < (1LL << 31)),
+            CSA_INVALID_ARGUMENT, "one sequence's q, cache or raw rows exceed 2 GiB");
+  }
   if (B == 0 || Tq == 0) return ok();
   REQUIRE_PTR(q, "q");
   REQUIRE_PTR(kc, "kc");

@@ -47,8 +47,10 @@ __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(
 
 // RW row-waves (32 query rows each) x KG key groups (KG=2: each wave of a pair
 // takes one 32-key half of every 64-key tile; the two partial softmax states
-// are merged in LDS at the end).
-template <typename T, int D, int RW, int KG, bool SPARSE>
+// are merged in LDS at the end).  PF key tiles are in flight ahead of the one
+// being computed (PF=2 for split decode, whose workgroups hold two tiles: all
+// of a workgroup's keys are then requested at once).
+template <typename T, int D, int RW, int KG, bool SPARSE, int PF>
 __global__ __launch_bounds__(RW * KG * 64) void attend_kernel(AttendArgs a, AttnGeom gm) {
   constexpr int NW = RW * KG;
   constexpr int NT = NW * 64;
@@ -79,38 +81,79 @@ __global__ __launch_bounds__(RW * KG * 64) void attend_kernel(AttendArgs a, Attn
   const int pos_first = p0 + t0, pos_last = p0 + tl;
   const int rp0 = a.raw_pos0 ? a.raw_pos0[b] : 0;
 
-  // ---- the tile's key list: [compressed part][window part] ----
-  int ncomp;
-  if constexpr (SPARSE) {
-    // compact the valid selected entries of this (single) token into LDS
-    // each thread owns a contiguous run of the index row, loaded in one round
-    const int32_t* ir = a.idx + ((size_t)b * a.Tq + t0) * a.topk;
-    constexpr int RUN = (4096 + NT - 1) / NT;      // topk <= 4096
-    const int i0 = tid * RUN;
-    int ev[RUN];
-    uint32_t cnt = 0;
+  // Buffer resources: a load outside a buffer's range returns zeros, so absent
+  // keys, padding rows and masked slots are fetched without branches (which
+  // also keeps every load of a tile in flight together).
+  constexpr uint32_t OOB = 0x80000000u;                      // offset past every range
+  constexpr uint32_t ROWB = D * sizeof(T);
+  auto rsrc = [](const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+  };
+
+  // ---- the tile's query rows: loads issued first, written to LDS once the
+  // first key tiles are requested ----
+  constexpr int QCH = D * sizeof(T) / 16;
+  constexpr int QLD = (RW * 32 * QCH + NT - 1) / NT;
+  u32x4 qreg[QLD];
+  {
+    const __amdgpu_buffer_rsrc_t rq =
+        rsrc(reinterpret_cast<const T*>(a.q) + (size_t)b * a.Tq * a.H * D, (uint32_t)a.Tq * a.H * ROWB);
 #pragma unroll
-    for (int q = 0; q < RUN; ++q) {
-      const int i = i0 + q;
-      ev[q] = i < a.topk ? ir[i] : -1;
+    for (int i = 0; i < QLD; ++i) {
+      const int c = tid + i * NT;
+      const int r = c / QCH, ch = c % QCH;
+      const int ttr = r / a.H, hr = r % a.H, tqr = t0 + ttr;
+      const bool ok = c < RW * 32 * QCH && ttr < gm.TT && tqr < a.Tq;
+      const uint32_t off = ok ? (uint32_t)(tqr * a.H + hr) * ROWB + ch * 16 : OOB;
+      qreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
     }
+  }
+
+  // ---- the tile's key list: [compressed part][window part] ----
+  const int kbeg = split * gm.kps;
+  int ncomp, sel_base = 0;
+  if constexpr (SPARSE) {
+    const int32_t* ir = a.idx + ((size_t)b * a.Tq + t0) * a.topk;
+    const __amdgpu_buffer_rsrc_t ri = rsrc(ir, (uint32_t)a.topk * 4);
+    if (gm.nsplit > 1) {
+      // split decode: this workgroup's own slots of the index row; slots whose
+      // entry is invalid are masked out later
+      ncomp = a.topk;
+      sel_base = kbeg;
+      const int ns = max(0, min(gm.kps, a.topk - kbeg));
+      for (int i = tid; i < ns; i += NT)
+        sel[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(ri, (uint32_t)(kbeg + i) * 4, 0, 0);
+      __syncthreads();
+    } else {
+      // one workgroup per token: compact the valid entries into LDS; each
+      // thread owns a contiguous run of the index row, loaded in one round
+      constexpr int RUN = (4096 + NT - 1) / NT;      // topk <= 4096
+      const int i0 = tid * RUN;
+      int ev[RUN];
+      uint32_t cnt = 0;
 #pragma unroll
-    for (int q = 0; q < RUN; ++q) cnt += (ev[q] >= 0 && ev[q] < a.Nc_cap) ? 1u : 0u;
-    uint32_t base;
-    uint32_t pos = block_excl_scan<NT>(cnt, scan_sm, &base);
+      for (int q = 0; q < RUN; ++q) {
+        const int i = i0 + q;
+        const int v = (int)__builtin_amdgcn_raw_buffer_load_b32(ri, i < a.topk ? (uint32_t)i * 4 : OOB, 0, 0);
+        ev[q] = i < a.topk ? v : -1;
+      }
 #pragma unroll
-    for (int q = 0; q < RUN; ++q)
-      if (ev[q] >= 0 && ev[q] < a.Nc_cap) sel[pos++] = ev[q];
-    if (tid == 0) s_nsel = (int)base;
-    __syncthreads();
-    ncomp = s_nsel;
+      for (int q = 0; q < RUN; ++q) cnt += (ev[q] >= 0 && ev[q] < a.Nc_cap) ? 1u : 0u;
+      uint32_t base;
+      uint32_t pos = block_excl_scan<NT>(cnt, scan_sm, &base);
+#pragma unroll
+      for (int q = 0; q < RUN; ++q)
+        if (ev[q] >= 0 && ev[q] < a.Nc_cap) sel[pos++] = ev[q];
+      if (tid == 0) s_nsel = (int)base;
+      __syncthreads();
+      ncomp = s_nsel;
+    }
   } else {
     ncomp = hca_ne(pos_last, a.m_prime, a.Nc_cap);
   }
   const int wlo = a.window > 0 ? max(0, pos_first - a.window + 1) : 0;
   const int nwin = a.window > 0 ? pos_last - wlo + 1 : 0;
   const int nkeys = ncomp + nwin;
-  const int kbeg = split * gm.kps;
   const int kend = min(nkeys, kbeg + gm.kps);
 
   // ---- this lane's query row ----
@@ -121,19 +164,6 @@ __global__ __launch_bounds__(RW * KG * 64) void attend_kernel(AttendArgs a, Attn
   const int qpos = p0 + tq;
   const int q_ne = SPARSE ? ncomp : hca_ne(qpos, a.m_prime, a.Nc_cap);
   const int q_wlo = max(0, qpos - a.window + 1);
-  // stage the tile's query rows in LDS (read back per MFMA step)
-  {
-    constexpr int QCH = D * sizeof(T) / 16;
-    for (int c = tid; c < RW * 32 * QCH; c += NT) {
-      const int r = c / QCH, ch = c % QCH;
-      const int ttr = r / a.H, hr = r % a.H, tqr = t0 + ttr;
-      u32x4 v = {0, 0, 0, 0};
-      if (ttr < gm.TT && tqr < a.Tq)
-        v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const T*>(a.q) +
-                                            (((size_t)b * a.Tq + tqr) * a.H + hr) * D + ch * (16 / sizeof(T)));
-      *reinterpret_cast<u32x4*>(Qs + r * KS + ch * (16 / sizeof(T))) = v;
-    }
-  }
 
   f32x16 o[DVT];
 #pragma unroll
@@ -154,57 +184,65 @@ __global__ __launch_bounds__(RW * KG * 64) void attend_kernel(AttendArgs a, Attn
 #pragma unroll
   for (int o2 = 32; o2 > 0; o2 >>= 1) wave_min_ne = min(wave_min_ne, __shfl_xor(wave_min_ne, o2, 64));
 
-  // source row of key slot s (nullptr = absent)
-  auto key_src = [&](int s, const T*& kp, const T*& vp) {
-    kp = vp = nullptr;
-    if (s < kbeg || s >= kend) return;
-    if (s < ncomp) {
-      const int e = SPARSE ? sel[s] : s;
-      kp = kcb + (size_t)e * D;
-      vp = vcb + (size_t)e * D;
-    } else {
-      const int r = wlo + (s - ncomp) - rp0;
-      if (r >= 0 && r < a.R && kwb) {
-        kp = kwb + (size_t)r * D;
-        vp = vwb + (size_t)r * D;
-      }
-    }
+  // byte offset of key slot s's row in the compressed / window buffers (OOB =
+  // not there)
+  const __amdgpu_buffer_rsrc_t rkc = rsrc(kcb, (uint32_t)a.Nc_cap * ROWB);
+  const __amdgpu_buffer_rsrc_t rvc = rsrc(vcb, (uint32_t)a.Nc_cap * ROWB);
+  const __amdgpu_buffer_rsrc_t rkw = rsrc(kwb, kwb ? (uint32_t)a.R * ROWB : 0u);
+  const __amdgpu_buffer_rsrc_t rvw = rsrc(vwb, vwb ? (uint32_t)a.R * ROWB : 0u);
+  auto comp_off = [&](int s) -> uint32_t {
+    if (s < kbeg || s >= kend || s >= ncomp) return OOB;
+    const int e = SPARSE ? sel[s - sel_base] : s;
+    return (e >= 0 && e < a.Nc_cap) ? (uint32_t)e * ROWB : OOB;
+  };
+  auto win_off = [&](int s) -> uint32_t {
+    if (s < kbeg || s >= kend || s < ncomp) return OOB;
+    const int r = wlo + (s - ncomp) - rp0;
+    return (r >= 0 && r < a.R) ? (uint32_t)r * ROWB : OOB;
   };
 
   // ---- staging: all global loads of a tile are issued into registers first
   // (so they are in flight together), then written to LDS: K row-major, V
-  // transposed.  The next tile's loads are issued before the current tile is
-  // computed.
+  // transposed.  Tiles that hold only compressed or only window keys read one
+  // buffer; the tile that straddles both ORs the two (one of them is zero).
   constexpr int KCH = D / VEC;                               // 16-byte chunks per row
   constexpr int KLD = (KT * KCH + NT - 1) / NT;              // K chunks per thread
   constexpr int VTOT = (KT / 4) * KCH;                       // V tasks: 4 keys x 16 bytes
   constexpr int VTK = (VTOT + NT - 1) / NT;
-  u32x4 kreg[KLD];
-  u32x4 vreg[VTK][4];
-  auto stage_load = [&](int s0) {
+  u32x4 kregA[KLD], vregA[VTK][4];
+  u32x4 kregB[PF == 2 ? KLD : 1], vregB[PF == 2 ? VTK : 1][4];
+  auto ld = [](const __amdgpu_buffer_rsrc_t& r, uint32_t off, uint32_t ch) -> u32x4 {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off == OOB ? OOB : off + ch * 16, 0, 0));
+  };
+  auto stage_load = [&](auto& kreg, auto& vreg, int s0) {
+    // per-tile source: compressed keys only, window keys only, or both (the
+    // one tile that straddles the boundary); each branch issues its loads back
+    // to back
+    auto load_all = [&](auto&& fetch) {
 #pragma unroll
-    for (int i = 0; i < KLD; ++i) {
-      const int c = tid + i * NT;
-      const int kk = c / KCH, ch = c % KCH;
-      const T *kp, *vp;
-      key_src(s0 + kk, kp, vp);
-      kreg[i] = u32x4{0, 0, 0, 0};
-      if (kp && c < KT * KCH) kreg[i] = *reinterpret_cast<const u32x4*>(kp + ch * VEC);
-    }
-#pragma unroll
-    for (int i = 0; i < VTK; ++i) {
-      const int c = tid + i * NT;
-      const int kg = c / KCH, ch = c % KCH;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const T *kp, *vp;
-        key_src(s0 + kg * 4 + u, kp, vp);
-        vreg[i][u] = u32x4{0, 0, 0, 0};
-        if (vp && c < VTOT) vreg[i][u] = *reinterpret_cast<const u32x4*>(vp + ch * VEC);
+      for (int i = 0; i < KLD; ++i) {
+        const int c = tid + i * NT;
+        kreg[i] = fetch(true, c < KT * KCH ? s0 + c / KCH : INT_MAX / 2, c % KCH);
       }
+#pragma unroll
+      for (int i = 0; i < VTK; ++i) {
+        const int c = tid + i * NT;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          vreg[i][u] = fetch(false, c < VTOT ? s0 + (c / KCH) * 4 + u : INT_MAX / 2, c % KCH);
+      }
+    };
+    if (s0 + KT <= ncomp || nwin == 0) {
+      load_all([&](bool k, int s, int ch) { return ld(k ? rkc : rvc, comp_off(s), ch); });
+    } else if (s0 >= ncomp) {
+      load_all([&](bool k, int s, int ch) { return ld(k ? rkw : rvw, win_off(s), ch); });
+    } else {
+      load_all([&](bool k, int s, int ch) {
+        return ld(k ? rkc : rvc, comp_off(s), ch) | ld(k ? rkw : rvw, win_off(s), ch);
+      });
     }
   };
-  auto stage_store = [&]() {
+  auto stage_store = [&](const auto& kreg, const auto& vreg) {
 #pragma unroll
     for (int i = 0; i < KLD; ++i) {
       const int c = tid + i * NT;
@@ -226,12 +264,18 @@ __global__ __launch_bounds__(RW * KG * 64) void attend_kernel(AttendArgs a, Attn
     }
   };
 
-  if (kbeg < kend) stage_load(kbeg);
-  for (int s0 = kbeg; s0 < kend; s0 += KT) {
-    stage_store();
-    __syncthreads();
-    if (s0 + KT < kend) stage_load(s0 + KT);
+  if (kbeg < kend) stage_load(kregA, vregA, kbeg);
+  if constexpr (PF == 2) {
+    if (kbeg + KT < kend) stage_load(kregB, vregB, kbeg + KT);
+  }
+#pragma unroll
+  for (int i = 0; i < QLD; ++i) {
+    const int c = tid + i * NT;
+    if (c < RW * 32 * QCH)
+      *reinterpret_cast<u32x4*>(Qs + (c / QCH) * KS + (c % QCH) * (16 / sizeof(T))) = qreg[i];
+  }
 
+  auto tile = [&](int s0) {
     // ---- S^T = K Q^T for this wave's 32-key sub-tiles ----
     f32x16 st[NSUB];
 #pragma unroll
@@ -252,8 +296,16 @@ __global__ __launch_bounds__(RW * KG * 64) void attend_kernel(AttendArgs a, Attn
     }
     // ---- mask (only tiles that reach a boundary), online softmax ----
     const int t_end = s0 + KT;
+    bool comp_ok = true;                       // every compressed slot of the tile holds an entry
+    if constexpr (SPARSE) {
+      if (sel_base > 0 || gm.nsplit > 1) {
+        const int sl = s0 + lane;
+        const int e = sl < min(t_end, ncomp) ? sel[sl - sel_base] : 0;
+        comp_ok = __all(e >= 0 && e < a.Nc_cap);
+      }
+    }
     const bool full = t_end <= kend &&
-                      (SPARSE ? (t_end <= ncomp || win_ok) : (t_end <= ncomp && t_end <= wave_min_ne));
+                      (SPARSE ? comp_ok && (t_end <= ncomp || win_ok) : (t_end <= ncomp && t_end <= wave_min_ne));
     float mt = -INFINITY;
 #pragma unroll
     for (int si = 0; si < NSUB; ++si) {
@@ -268,8 +320,13 @@ __global__ __launch_bounds__(RW * KG * 64) void attend_kernel(AttendArgs a, Attn
             const int p = wlo + (s - ncomp);
             ok = (p - rp0 >= 0) && (p - rp0 < a.R) && (kwb != nullptr);   // row present
             if (!SPARSE) ok = ok && p >= q_wlo && p <= qpos;
-          } else if (ok && !SPARSE) {
-            ok = s < q_ne;
+          } else if (ok) {
+            if constexpr (SPARSE) {
+              const int e = sel[s - sel_base];
+              ok = e >= 0 && e < a.Nc_cap;
+            } else {
+              ok = s < q_ne;
+            }
           }
           x = ok ? x : -INFINITY;
         }
@@ -332,7 +389,29 @@ __global__ __launch_bounds__(RW * KG * 64) void attend_kernel(AttendArgs a, Attn
         }
       }
     }
-    __syncthreads();
+  };
+  if constexpr (PF == 2) {
+    for (int s0 = kbeg; s0 < kend; s0 += 2 * KT) {
+      stage_store(kregA, vregA);
+      __syncthreads();
+      if (s0 + 2 * KT < kend) stage_load(kregA, vregA, s0 + 2 * KT);
+      tile(s0);
+      __syncthreads();
+      if (s0 + KT >= kend) break;
+      stage_store(kregB, vregB);
+      __syncthreads();
+      if (s0 + 3 * KT < kend) stage_load(kregB, vregB, s0 + 3 * KT);
+      tile(s0 + KT);
+      __syncthreads();
+    }
+  } else {
+    for (int s0 = kbeg; s0 < kend; s0 += KT) {
+      stage_store(kregA, vregA);
+      __syncthreads();
+      if (s0 + KT < kend) stage_load(kregA, vregA, s0 + KT);
+      tile(s0);
+      __syncthreads();
+    }
   }
 
   // ---- merge the two key groups (their staging area is free now) ----
@@ -405,9 +484,13 @@ __global__ __launch_bounds__(RW * KG * 64) void attend_kernel(AttendArgs a, Attn
   if (a.lse && half == 0) a.lse[grow] = lse;
 }
 
-// Merge split partials in fixed split order (one wave per query row).
+// Merge split partials in fixed split order (one wave per query row).  The
+// partials of CB splits are requested together; a running maximum rescales
+// the sums between batches, so the result depends only on the split list.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void combine_kernel(AttendArgs a, int nsplit) {
+  constexpr int PER = D / 64;
+  constexpr int CB = 32;
   const int lane = threadIdx.x & 63;
   const size_t rows_total = (size_t)a.B * a.Tq * a.H;
   const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -417,26 +500,39 @@ __global__ __launch_bounds__(256) void combine_kernel(AttendArgs a, int nsplit) 
   const float* pl = pm + (size_t)nsplit * rows_total;
   const int h = (int)(row % a.H);
   const float s2 = a.sink ? a.sink[h] * LOG2E : -INFINITY;
-  float mloc = -INFINITY;
-  for (int s = lane; s < nsplit; s += 64) mloc = fmaxf(mloc, pm[s * rows_total + row]);
-  const float M = fmaxf(wave_max(mloc), s2);
-  constexpr int PER = D / 64;
+  float M = s2, Z = 0.f;
   float acc[PER];
 #pragma unroll
   for (int u = 0; u < PER; ++u) acc[u] = 0.f;
+  for (int s0 = 0; s0 < nsplit; s0 += CB) {
+    float v[CB][PER];
+    const float mv = lane < CB && s0 + lane < nsplit ? pm[(s0 + lane) * rows_total + row] : -INFINITY;
+    const float lv = lane < CB && s0 + lane < nsplit ? pl[(s0 + lane) * rows_total + row] : 0.f;
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+      const float* src = po + ((s0 + j) * rows_total + row) * D + lane * PER;
+#pragma unroll
+      for (int u = 0; u < PER; ++u) v[j][u] = s0 + j < nsplit ? src[u] : 0.f;
+    }
+    const float M_new = fmaxf(M, wave_max(mv));
+    if (M_new == -INFINITY) continue;
+    const float r = __builtin_amdgcn_exp2f(M - M_new);      // M = -inf -> 0
+    Z *= r;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) acc[u] *= r;
+    const float cl = __builtin_amdgcn_exp2f(mv - M_new);     // this lane's split weight
+    Z += wave_sum(lv * cl);
+#pragma unroll
+    for (int j = 0; j < CB; ++j) {
+      const float c = __shfl(cl, j, 64);
+#pragma unroll
+      for (int u = 0; u < PER; ++u) acc[u] = fmaf(v[j][u], c, acc[u]);
+    }
+    M = M_new;
+  }
   float lse = -INFINITY, inv = 0.f;
   if (M != -INFINITY) {
-    float zl = 0.f;
-    for (int s = lane; s < nsplit; s += 64)
-      zl += pl[s * rows_total + row] * __builtin_amdgcn_exp2f(pm[s * rows_total + row] - M);
-    const float Z = wave_sum(zl) + __builtin_amdgcn_exp2f(s2 - M);
-#pragma unroll 4
-    for (int s = 0; s < nsplit; ++s) {
-      const float c = __builtin_amdgcn_exp2f(pm[s * rows_total + row] - M);
-      const float* src = po + (s * rows_total + row) * D + lane * PER;
-#pragma unroll
-      for (int u = 0; u < PER; ++u) acc[u] = fmaf(src[u], c, acc[u]);
-    }
+    Z += __builtin_amdgcn_exp2f(s2 - M);
     lse = (M + __log2f(Z)) * LN2;
     inv = 1.f / Z;
   }
@@ -472,13 +568,13 @@ size_t attend_workspace(bool sparse, int B, int Tq, int H, int d, int topk, int 
   return (size_t)ns * B * Tq * H * (d + 2) * sizeof(float);
 }
 
-template <typename T, int D, int RW, int KG, bool SPARSE>
-static hipError_t launch4(const AttendArgs& a, const AttnGeom& gm, hipStream_t st) {
+template <typename T, int D, int RW, int KG, bool SPARSE, int PF>
+static hipError_t launch5(const AttendArgs& a, const AttnGeom& gm, hipStream_t st) {
   constexpr int KS = D + 16 / sizeof(T);
   constexpr int VS = KT + 4;
   size_t lds = (size_t)(KT * KS + D * VS + RW * 32 * KS) * sizeof(T) + (SPARSE ? (size_t)a.topk * 4 : 0);
   if (KG == 2) lds = std::max(lds, (size_t)RW * 64 * ((D / 32) * 16 + 2) * sizeof(float));
-  auto kfn = attend_kernel<T, D, RW, KG, SPARSE>;
+  auto kfn = attend_kernel<T, D, RW, KG, SPARSE, PF>;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -495,6 +591,11 @@ static hipError_t launch4(const AttendArgs& a, const AttnGeom& gm, hipStream_t s
   hipLaunchKernelGGL((combine_kernel<T, D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st,
                      a, gm.nsplit);
   return hipGetLastError();
+}
+
+template <typename T, int D, int RW, int KG, bool SPARSE>
+static hipError_t launch4(const AttendArgs& a, const AttnGeom& gm, hipStream_t st) {
+  return gm.nsplit > 1 ? launch5<T, D, RW, KG, SPARSE, 2>(a, gm, st) : launch5<T, D, RW, KG, SPARSE, 1>(a, gm, st);
 }
 
 // Row-waves cover the tile's (token, head) rows; tiles of at most 64 rows get
