@@ -61,8 +61,6 @@ def algorithmic_bytes(w):
     nk_csa = w.topk + w.window
     return {
         "indexer_score": B * (w.Nc * qk_row + q_in),
-        "indexer_zero": 0,
-        "indexer_split": 0,
         "indexer_topk": B * w.topk * 4,
         "attend_csa": B * (nk_csa * 2 * d * 2 + 2 * H * d * 2),
         "attend_hca": B * (w.Nc_hca * 2 * d * 2 + 2 * H * d * 2),
@@ -216,7 +214,7 @@ def main():
     lib.csa_profile_enable(0)
     import ctypes as C
     kern = {}
-    for name in ("indexer_zero", "indexer_score", "indexer_split", "indexer_topk", "attend_csa",
+    for name in ("indexer_score", "indexer_topk", "attend_csa",
                  "attend_hca", "attend_combine"):
         n, t = C.c_int(0), C.c_double(0)
         if lib.csa_profile_query(name.encode(), C.byref(n), C.byref(t)) == 0:

@@ -116,7 +116,8 @@ csa_status_t csa_compress(const void *k, const void *v, const void *ki,
  *   score_out [B, Tq, topk] fp32 scores aligned with idx_out (-inf where
  *             idx_out is -1), or NULL
  *   qk_dt ∈ {F32, BF16, FP8_E4M3, FP4_E2M1}; dI ∈ {32, 64}; HI ∈ {1, 2, 4};
- *   1 <= topk <= 4096.  Scores accumulate in fp32; ReLU yields +0.
+ *   1 <= topk <= 4096; 1 <= Nc_cap <= 2^23.  FP8/FP4 codes are widened
+ *   exactly to bf16 and scores accumulate in fp32; ReLU yields +0.
  */
 size_t csa_indexer_topk_workspace(int B, int Tq, int Nc_cap, int HI, int dI, int topk,
                                   csa_dtype_t qk_dt);
@@ -183,9 +184,10 @@ csa_status_t hca_attend(const void *q, const void *kc, const void *vc, int m_pri
  * pair of hipEvents recorded on that launch's stream.  csa_profile_query
  * waits for the recorded events of `kernel` and returns (0) the number of
  * launches and their summed GPU duration in milliseconds, or 1 if none were
- * recorded, -1 on a HIP error.  Kernel names: "compress", "indexer_zero",
- * "indexer_score", "indexer_split", "indexer_topk", "attend_csa", "attend_hca",
- * "attend_combine".
+ * recorded, -1 on a HIP error.  Kernel names: "compress", "indexer_score"
+ * (decode scores and per-chunk cut), "indexer_topk" (row select),
+ * "indexer_fused" (prefill scores and select in one kernel), "attend_csa",
+ * "attend_hca", "attend_combine".
  * csa_profile_reset forgets all records (events are kept for reuse).
  */
 void csa_profile_enable(int on);

@@ -112,6 +112,7 @@ csa_status_t csa_indexer_topk(const void* qi, const void* qi_scale, const float*
                               void* workspace, size_t workspace_bytes, void* stream) {
   REQUIRE(B >= 0 && Tq >= 0, CSA_INVALID_ARGUMENT, "B and Tq must be >= 0");
   REQUIRE(Nc_cap >= 1, CSA_INVALID_ARGUMENT, "Nc_cap must be >= 1");
+  REQUIRE(Nc_cap <= (1 << 23), CSA_UNSUPPORTED, "Nc_cap (%d) above 2^23 entries is not supported", Nc_cap);
   REQUIRE(m >= 1, CSA_INVALID_ARGUMENT, "m must be >= 1");
   REQUIRE(topk >= 1 && topk <= 4096, CSA_INVALID_ARGUMENT, "topk must be in [1, 4096] (got %d)", topk);
   REQUIRE(qk_dt == CSA_F32 || qk_dt == CSA_BF16 || qk_dt == CSA_FP8_E4M3 || qk_dt == CSA_FP4_E2M1,

@@ -40,12 +40,14 @@
 namespace csa {
 
 static constexpr int SCORE_WG_ENTRIES = 256;   // prefill tile kernel: 4 waves x 4 tiles x 16
-static constexpr int ROW_CHUNK = 2048;         // decode row kernel: entries per workgroup
+static constexpr int ROW_CHUNK = 2048;         // long-row select: entries per split workgroup
+#ifndef CSA_SCORE_CHUNK
+#define CSA_SCORE_CHUNK 2048
+#endif
+static constexpr int SCORE_CHUNK = CSA_SCORE_CHUNK;   // decode score kernels: entries per workgroup
 static constexpr int H1_BITS = 12;             // first radix digit (key bits 20..31)
 static constexpr int H1_BINS = 1 << H1_BITS;
 static constexpr int TOPK_NT = 512;
-// long-row final select: threads per row
-static constexpr int SEL_NT = 1024;
 static constexpr int TOPK_LDS_KEYS = 12288;
 
 __host__ __device__ __forceinline__ int nc_pad(int Nc_cap) { return (Nc_cap + 63) & ~63; }
@@ -106,6 +108,45 @@ __device__ __forceinline__ void load_qk_frag(typename QkTraits<QK>::F& f, const 
   }
 }
 
+// Split form of load_qk_frag: `load_raw` only issues the loads (so several
+// groups can be in flight), `widen` builds the fragment when it is needed.
+template <int QK> struct RawFrag { typename QkTraits<QK>::F f; };
+template <> struct RawFrag<QK_FP8> { uint2 c; };
+template <> struct RawFrag<QK_FP4> { uint32_t c; uint32_t s; };
+template <int QK>
+__device__ __forceinline__ void load_raw(RawFrag<QK>& r, const void* row, const uint8_t* sc, int k0) {
+  if constexpr (QK == QK_FP8) {
+    r.c = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(row) + k0);
+  } else if constexpr (QK == QK_FP4) {
+    r.c = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(row) + k0 / 2);
+    r.s = sc[k0 / 32];
+  } else {
+    load_qk_frag<QK>(r.f, row, sc, k0);
+  }
+}
+template <int QK>
+__device__ __forceinline__ typename QkTraits<QK>::F widen(const RawFrag<QK>& r) {
+  if constexpr (QK == QK_FP8) {
+    typename QkTraits<QK>::F f;
+    f.v = u32x4{e4m3x2_to_bf16<false>(r.c.x), e4m3x2_to_bf16<true>(r.c.x),
+                e4m3x2_to_bf16<false>(r.c.y), e4m3x2_to_bf16<true>(r.c.y)};
+    return f;
+  } else if constexpr (QK == QK_FP4) {
+    typename QkTraits<QK>::F f;
+    const float scl = e8m0_val(r.s);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t byte = (r.c >> (8 * i)) & 0xFF;
+      const uint32_t lo = __float_as_uint(e2m1_val(byte & 0xF) * scl) >> 16;
+      const uint32_t hi = __float_as_uint(e2m1_val(byte >> 4) * scl) >> 16;
+      f.v[i] = lo | (hi << 16);
+    }
+    return f;
+  } else {
+    return r.f;
+  }
+}
+
 template <int QK> __host__ __device__ __forceinline__ size_t qk_row_bytes(int dI) {
   if constexpr (QK == QK_F32) return (size_t)dI * 4;
   else if constexpr (QK == QK_BF16) return (size_t)dI * 2;
@@ -117,38 +158,45 @@ __device__ __forceinline__ int row_len(const IndexerArgs& a, int b, int t) {
   return max(0, min((a.pos0[b] + t + 1) / a.m, a.Nc_cap));
 }
 
-// Workspace carve-up for the long-row path (per query row; nch = row chunks):
-//   scores [rows][ldo] f32 | hist [rows][4096] u32 | ccnt [rows][nch][2] u32 |
-//   csel [rows][nch][ROW_CHUNK] u32 | ccand [rows][nch][ROW_CHUNK][2] u32
-// Every split workgroup owns one chunk's slots, so no atomics are needed.
+// Workspace carve-up for the long-row path (per query row; nch = score chunks):
+//   scores [rows][ldo] f32 | meta [rows][nch][2] u32 (kept count, cut) |
+//   cand [rows][nch * SCORE_CHUNK][2] u32 (key, entry), chunk c's kept entries
+//   at slots c * cap ..  (cap = the row's per-chunk capacity)
+// Every score workgroup owns one chunk's slots, so no atomics are needed.
 struct LongWs {
   float* scores;
-  uint32_t *hist, *ccnt, *csel, *ccand;
+  uint32_t *meta, *cand;
   int nch;
 };
-__host__ __device__ __forceinline__ int row_chunks(int Nc_cap) { return (Nc_cap + ROW_CHUNK - 1) / ROW_CHUNK; }
-__host__ __device__ __forceinline__ LongWs long_ws(void* ws, int rows, int Nc_cap, int topk) {
-  (void)topk;
+__host__ __device__ __forceinline__ int row_chunks(int Nc_cap) { return (Nc_cap + SCORE_CHUNK - 1) / SCORE_CHUNK; }
+__host__ __device__ __forceinline__ LongWs long_ws(void* ws, int rows, int Nc_cap) {
   LongWs w;
   w.nch = row_chunks(Nc_cap);
   char* p = reinterpret_cast<char*>(ws);
   w.scores = reinterpret_cast<float*>(p);
   p += (size_t)rows * nc_pad(Nc_cap) * 4;
-  w.hist = reinterpret_cast<uint32_t*>(p);
-  p += (size_t)rows * H1_BINS * 4;
-  w.ccnt = reinterpret_cast<uint32_t*>(p);
+  w.meta = reinterpret_cast<uint32_t*>(p);
   p += (size_t)rows * ((w.nch * 2 + 3) & ~3) * 4;
-  w.csel = reinterpret_cast<uint32_t*>(p);
-  p += (size_t)rows * w.nch * ROW_CHUNK * 4;
-  w.ccand = reinterpret_cast<uint32_t*>(p);
+  w.cand = reinterpret_cast<uint32_t*>(p);
   return w;
 }
-static size_t long_ws_bytes(int rows, int Nc_cap, int topk) {
-  (void)topk;
+static size_t long_ws_bytes(int rows, int Nc_cap) {
   const int nch = row_chunks(Nc_cap);
-  return (size_t)rows * ((size_t)nc_pad(Nc_cap) * 4 + H1_BINS * 4 + (size_t)((nch * 2 + 3) & ~3) * 4 +
-                         (size_t)nch * ROW_CHUNK * 12);
+  return (size_t)rows * ((size_t)nc_pad(Nc_cap) * 4 + (size_t)((nch * 2 + 3) & ~3) * 4 +
+                         (size_t)nch * SCORE_CHUNK * 8);
 }
+// Entries each score chunk keeps for the row select: about four times the
+// chunk's expected share of the top k, as a power of two in [32, SCORE_CHUNK].
+// A chunk stores every entry whose 12-bit digit is at least the digit of its
+// kc-th largest key (its "cut"), up to chunk_cap of them.
+__host__ __device__ __forceinline__ int chunk_keep(int k, int n) {
+  const long long want = (4LL * k * SCORE_CHUNK + n - 1) / n;
+  int kc = 32;
+  while (kc < want && kc < SCORE_CHUNK) kc <<= 1;
+  return kc;
+}
+__host__ __device__ __forceinline__ int chunk_cap(int kc) { return kc * 2 < SCORE_CHUNK ? kc * 2 : SCORE_CHUNK; }
+static constexpr uint32_t CUT_ALL = 0xFFFFFFFFu;   // the chunk kept every entry
 static bool use_long_path(int Tq, int Nc_cap) { return Tq <= 4 && Nc_cap > TOPK_LDS_KEYS; }
 
 // Scanning bins from the top down, find the bin where the running count first
@@ -172,6 +220,51 @@ __device__ void find_bin(const uint32_t* hist, int nbins, uint32_t need, uint32_
     }
   }
   __syncthreads();
+}
+
+// End of a decode score workgroup: keep the chunk's entries at or above its
+// cut, in index order, in the chunk's candidate slots.  The cut is the 20-bit
+// key prefix (key >> 12) of the chunk's kc-th largest key, found from the
+// 12-bit digit histogram and a second 8-bit histogram inside that digit, so
+// few entries beyond kc share it.  sk holds the chunk's nloc keys, hist their
+// 12-bit digit histogram (256 threads; hist is reused).
+__device__ void chunk_cut(const IndexerArgs& a, const LongWs& L, int row, int chunk, int n, int c0,
+                          int nloc, const uint32_t* sk, uint32_t* hist, uint32_t* scan,
+                          uint32_t* res) {
+  constexpr int PER = SCORE_CHUNK / 256;
+  const int kc = chunk_keep(a.topk, n), cap = chunk_cap(kc);
+  const int i0 = threadIdx.x * PER;
+  uint32_t cut = 0;
+  const bool dropped = nloc > kc;                            // uniform
+  if (dropped) {
+    find_bin<256>(hist, H1_BINS, (uint32_t)kc, scan, res);
+    const uint32_t d1 = res[0], above = res[1];
+    hist[threadIdx.x] = 0;                                   // find_bin ended with a barrier
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < PER; ++q)
+      if (i0 + q < nloc && (sk[i0 + q] >> 20) == d1) atomicAdd(&hist[(sk[i0 + q] >> 12) & 255u], 1u);
+    __syncthreads();
+    find_bin<256>(hist, 256, (uint32_t)kc - above, scan, res);
+    cut = (d1 << 8) | res[0];
+  }
+  uint32_t keep = 0;
+#pragma unroll
+  for (int q = 0; q < PER; ++q)
+    if (i0 + q < nloc && (sk[i0 + q] >> 12) >= cut) keep |= 1u << q;
+  uint32_t tot;
+  uint32_t pos = block_excl_scan<256>((uint32_t)__popc(keep), scan, &tot);
+  uint2* cd = reinterpret_cast<uint2*>(L.cand) + (size_t)row * L.nch * SCORE_CHUNK + (size_t)chunk * cap;
+#pragma unroll
+  for (int q = 0; q < PER; ++q)
+    if ((keep >> q) & 1u) {
+      if (pos < (uint32_t)cap) cd[pos] = uint2{sk[i0 + q], (uint32_t)(c0 + i0 + q)};
+      ++pos;
+    }
+  if (threadIdx.x == 0) {
+    L.meta[((size_t)row * L.nch + chunk) * 2] = tot;
+    L.meta[((size_t)row * L.nch + chunk) * 2 + 1] = dropped ? cut : CUT_ALL;
+  }
 }
 
 // --------------------------- prefill score tile ----------------------------
@@ -262,15 +355,17 @@ __global__ __launch_bounds__(256) void score_row_kernel(IndexerArgs a) {
   constexpr int SPL = 4 / HI;         // scores per lane per accumulator
   using F = typename QkTraits<QK>::F;
   __shared__ uint32_t hist[H1_BINS];
+  __shared__ uint32_t sk[SCORE_CHUNK];
+  __shared__ uint32_t cut_scan[4], cut_res[2];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = blockIdx.y;
   const int b = row / a.Tq, t = row % a.Tq;
   const int n = row_len(a, b, t);
-  const int c0 = blockIdx.x * ROW_CHUNK;
+  const int c0 = blockIdx.x * SCORE_CHUNK;
   if (c0 >= n) return;
-  const int c1 = min(n, c0 + ROW_CHUNK);
-  LongWs L = long_ws(a.ws, a.B * a.Tq, a.Nc_cap, a.topk);
+  const int c1 = min(n, c0 + SCORE_CHUNK);
+  LongWs L = long_ws(a.ws, a.B * a.Tq, a.Nc_cap);
   for (int i = threadIdx.x; i < H1_BINS; i += 256) hist[i] = 0;
 
   // A operands: for tile u the query's HI head rows sit at rows u*HI .. u*HI+HI-1
@@ -312,14 +407,15 @@ __global__ __launch_bounds__(256) void score_row_kernel(IndexerArgs a) {
 
   // one group = EPC entries: the B fragments plus (FP8) the per-entry scales of
   // the entries this lane will score
-  auto load_group = [&](int e0, F (&kb)[TPC][KC], float (&ks)[SPL]) {
+  using R = RawFrag<QK>;
+  auto load_group = [&](int e0, R (&kb)[TPC][KC], float (&ks)[SPL]) {
 #pragma unroll
     for (int u = 0; u < TPC; ++u) {
       const int e = min(e0 + 16 * u + r, c1 - 1);
 #pragma unroll
       for (int c = 0; c < KC; ++c)
-        load_qk_frag<QK>(kb[u][c], kbase + (size_t)e * rb,
-                         QK == QK_FP4 ? sbase + (size_t)e * (DI / 32) : nullptr, 8 * (g * KC + c));
+        load_raw<QK>(kb[u][c], kbase + (size_t)e * rb,
+                     QK == QK_FP4 ? sbase + (size_t)e * (DI / 32) : nullptr, 8 * (g * KC + c));
     }
 #pragma unroll
     for (int s = 0; s < SPL; ++s) {
@@ -329,12 +425,12 @@ __global__ __launch_bounds__(256) void score_row_kernel(IndexerArgs a) {
   };
 
   // process one group: MFMAs, ReLU + head weights, store, histogram
-  auto process = [&](int e0, const F (&cur)[TPC][KC], const float (&cscl)[SPL]) {
+  auto process = [&](int e0, const R (&cur)[TPC][KC], const float (&cscl)[SPL]) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < TPC; ++u)
 #pragma unroll
-      for (int c = 0; c < KC; ++c) mma16(acc, qa[u][c], cur[u][c]);
+      for (int c = 0; c < KC; ++c) mma16(acc, qa[u][c], widen<QK>(cur[u][c]));
 #pragma unroll
     for (int s = 0; s < SPL; ++s) {
       const int u = (4 * g) / HI + s;
@@ -349,33 +445,30 @@ __global__ __launch_bounds__(256) void score_row_kernel(IndexerArgs a) {
         if constexpr (QK == QK_FP8) sc *= cscl[s];
         sc += 0.f;
         srow[e] = sc;
+        sk[e - c0] = __float_as_uint(sc);
         atomicAdd(&hist[__float_as_uint(sc) >> (32 - H1_BITS)], 1u);
       }
     }
   };
 
-  // two groups in flight per wave (ping-pong register buffers)
+  // DEPTH groups in flight per wave; the chunk's groups are fully unrolled
+  // and branch-free (loads clamp to the chunk, stores are masked), so the
+  // loads of later groups stay in flight while earlier ones are scored
   constexpr int STRIDE = 4 * EPC;
-  F kbA[TPC][KC], kbB[TPC][KC];
-  float ksA[SPL], ksB[SPL];
-  int e0 = c0 + wave * EPC;
-  if (e0 < c1) load_group(e0, kbA, ksA);
-  if (e0 + STRIDE < c1) load_group(e0 + STRIDE, kbB, ksB);
-#pragma unroll 1
-  for (; e0 < c1; e0 += 2 * STRIDE) {
-    process(e0, kbA, ksA);
-    if (e0 + 2 * STRIDE < c1) load_group(e0 + 2 * STRIDE, kbA, ksA);
-    if (e0 + STRIDE < c1) {
-      process(e0 + STRIDE, kbB, ksB);
-      if (e0 + 3 * STRIDE < c1) load_group(e0 + 3 * STRIDE, kbB, ksB);
-    }
+  constexpr int NG = (SCORE_CHUNK + STRIDE - 1) / STRIDE;
+  constexpr int DEPTH = NG < 3 ? NG : 3;
+  R kb[DEPTH][TPC][KC];
+  float ks[DEPTH][SPL];
+  const int ew = c0 + wave * EPC;
+#pragma unroll
+  for (int j = 0; j < DEPTH; ++j) load_group(ew + j * STRIDE, kb[j], ks[j]);
+#pragma unroll
+  for (int j = 0; j < NG; ++j) {
+    process(ew + j * STRIDE, kb[j % DEPTH], ks[j % DEPTH]);
+    if (j + DEPTH < NG) load_group(ew + (j + DEPTH) * STRIDE, kb[j % DEPTH], ks[j % DEPTH]);
   }
   __syncthreads();
-  uint32_t* gh = L.hist + (size_t)row * H1_BINS;
-  for (int i = threadIdx.x; i < H1_BINS; i += 256) {
-    const uint32_t v = hist[i];
-    if (v) atomicAdd(&gh[i], v);
-  }
+  if (n > a.topk) chunk_cut(a, L, row, blockIdx.x, n, c0, c1 - c0, sk, hist, cut_scan, cut_res);
 }
 
 // ------------------------ decode score row, native FP4 ------------------------
@@ -395,14 +488,16 @@ __global__ __launch_bounds__(256) void score_row_fp4_kernel(IndexerArgs a) {
   constexpr int EPC = 64;
   constexpr int RB = DI / 2;                   // bytes per packed row
   __shared__ uint32_t hist[H1_BINS];
+  __shared__ uint32_t sk[SCORE_CHUNK];
+  __shared__ uint32_t cut_scan[4], cut_res[2];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = blockIdx.y;
   const int b = row / a.Tq, t = row % a.Tq;
   const int n = row_len(a, b, t);
-  const int c0 = blockIdx.x * ROW_CHUNK;
+  const int c0 = blockIdx.x * SCORE_CHUNK;
   if (c0 >= n) return;
-  const int c1 = min(n, c0 + ROW_CHUNK);
-  LongWs L = long_ws(a.ws, a.B * a.Tq, a.Nc_cap, a.topk);
+  const int c1 = min(n, c0 + SCORE_CHUNK);
+  LongWs L = long_ws(a.ws, a.B * a.Tq, a.Nc_cap);
   for (int i = threadIdx.x; i < H1_BINS; i += 256) hist[i] = 0;
 
   const int c = lane & 15, kb = lane >> 4;
@@ -457,6 +552,7 @@ __global__ __launch_bounds__(256) void score_row_fp4_kernel(IndexerArgs a) {
     if (e < c1) {
       sc += 0.f;
       srow[e] = sc;
+      sk[e - c0] = __float_as_uint(sc);
       atomicAdd(&hist[__float_as_uint(sc) >> (32 - H1_BITS)], 1u);
     }
   };
@@ -476,11 +572,7 @@ __global__ __launch_bounds__(256) void score_row_fp4_kernel(IndexerArgs a) {
     }
   }
   __syncthreads();
-  uint32_t* gh = L.hist + (size_t)row * H1_BINS;
-  for (int i = threadIdx.x; i < H1_BINS; i += 256) {
-    const uint32_t v = hist[i];
-    if (v) atomicAdd(&gh[i], v);
-  }
+  if (n > a.topk) chunk_cut(a, L, row, blockIdx.x, n, c0, c1 - c0, sk, hist, cut_scan, cut_res);
 }
 
 // --------------------------- shared select helpers --------------------------
@@ -571,295 +663,208 @@ __global__ __launch_bounds__(TOPK_NT) void topk_row_kernel(IndexerArgs a) {
 }
 
 // ------------------------------ long-row path ------------------------------
-__global__ __launch_bounds__(256) void long_zero_kernel(IndexerArgs a) {
-  LongWs L = long_ws(a.ws, a.B * a.Tq, a.Nc_cap, a.topk);
-  u32x4* h = reinterpret_cast<u32x4*>(L.hist + (size_t)blockIdx.x * H1_BINS);
-  for (int i = threadIdx.x; i < H1_BINS / 4; i += 256) h[i] = u32x4{0, 0, 0, 0};
-}
+// One workgroup per query row picks the row's k largest keys among the
+// chunks' candidates.  Candidate slot (chunk c, j) holds the j-th kept entry
+// of chunk c; slots in (c, j) order are in ascending entry order, so the
+// lowest-index rule among equal keys is slot order and the output needs no
+// sort.  The pick is exact when every chunk's dropped entries lie below the
+// selected threshold tau (tau >= cut << 12) and no chunk overflowed its slots;
+// otherwise the row is selected exactly from the stored scores.
+static constexpr int PICK_NT = 1024;
+static constexpr int PICK_NW = PICK_NT / 64;
+static constexpr int PICK_MAXCH = 4096;        // rows up to 8M entries
+static constexpr int PICK_PER = 32;            // candidate slots per thread (registers)
+static constexpr int PICK_SLOTS = PICK_PER * PICK_NT;
+static constexpr int PICK_BINS = 4096;         // 12-bit radix digits
 
-static constexpr int CAND_L = 8192;            // boundary-bin candidates resolved in LDS
-static constexpr int BITMAP_WORDS = 8192;      // ascending output through a bitmap for n <= 262144
-
-// Split pass over one chunk of one long row: find the bin b1 holding the k-th
-// largest key from the row histogram, then write the chunk's indices with keys
-// above b1 and its (key, index) pairs inside b1 to the chunk's own slots.
-__global__ __launch_bounds__(256) void long_split_kernel(IndexerArgs a) {
-  __shared__ uint32_t hist[H1_BINS];
-  __shared__ uint32_t scan[4];
-  __shared__ uint32_t res[2];
-  const int row = blockIdx.y, chunk = blockIdx.x;
-  const int b = row / a.Tq, t = row % a.Tq;
-  const int n = row_len(a, b, t);
-  const int c0 = chunk * ROW_CHUNK;
-  if (n <= a.topk || c0 >= n) return;
-  const int c1 = min(n, c0 + ROW_CHUNK);
-  LongWs L = long_ws(a.ws, a.B * a.Tq, a.Nc_cap, a.topk);
-  const uint32_t* keys = reinterpret_cast<const uint32_t*>(L.scores) + (size_t)row * nc_pad(a.Nc_cap);
-  constexpr int PER = ROW_CHUNK / 256;
-  const int base = c0 + threadIdx.x * PER;
-  // issue the chunk's key loads and the histogram loads together
-  uint32_t kv[PER];
-#pragma unroll
-  for (int q = 0; q < PER / 4; ++q) {
-    const int i = base + 4 * q;
-    u32x4 v = {0, 0, 0, 0};
-    if (i + 3 < c1) v = *reinterpret_cast<const u32x4*>(keys + i);
-    else {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = (i + u < c1) ? keys[i + u] : 0u;
-    }
-    kv[4 * q] = v[0]; kv[4 * q + 1] = v[1]; kv[4 * q + 2] = v[2]; kv[4 * q + 3] = v[3];
-  }
-  {
-    const u32x4* gh = reinterpret_cast<const u32x4*>(L.hist + (size_t)row * H1_BINS);
-    u32x4 hv[H1_BINS / 1024];
-#pragma unroll
-    for (int i = 0; i < H1_BINS / 1024; ++i) hv[i] = gh[threadIdx.x + 256 * i];
-#pragma unroll
-    for (int i = 0; i < H1_BINS / 1024; ++i) reinterpret_cast<u32x4*>(hist)[threadIdx.x + 256 * i] = hv[i];
-  }
-  if (threadIdx.x == 0) { res[0] = 0; res[1] = 0; }
-  __syncthreads();
-  find_bin<256>(hist, H1_BINS, (uint32_t)a.topk, scan, res);
-  const uint32_t b1 = res[0];
-  uint32_t na = 0, nb = 0;
-#pragma unroll
-  for (int q = 0; q < PER; ++q) {
-    const uint32_t d = kv[q] >> (32 - H1_BITS);
-    const bool valid = base + q < c1;
-    na += (valid && d > b1) ? 1u : 0u;
-    nb += (valid && d == b1) ? 1u : 0u;
-  }
-  uint32_t tot;
-  const uint32_t pref = block_excl_scan<256>((na << 16) | nb, scan, &tot);
-  uint32_t* csel = L.csel + ((size_t)row * L.nch + chunk) * ROW_CHUNK;
-  uint32_t* ccand = L.ccand + ((size_t)row * L.nch + chunk) * ROW_CHUNK * 2;
-  uint32_t pa = pref >> 16, pb = pref & 0xFFFFu;
-#pragma unroll
-  for (int q = 0; q < PER; ++q) {
-    const int i = base + q;
-    const uint32_t d = kv[q] >> (32 - H1_BITS);
-    if (i < c1 && d > b1) {
-      csel[pa++] = (uint32_t)i;
-    } else if (i < c1 && d == b1) {
-      ccand[2 * pb] = kv[q];
-      ccand[2 * pb + 1] = (uint32_t)i;
-      ++pb;
-    }
-  }
-  if (threadIdx.x == 0) {
-    uint32_t* cc = L.ccnt + (size_t)row * ((L.nch * 2 + 3) & ~3) + 2 * chunk;
-    cc[0] = tot >> 16;
-    cc[1] = tot & 0xFFFFu;
-  }
-}
-
-static constexpr int MAX_CHUNKS = 1024;        // rows up to 2M entries use the gather path
-
-struct SelectSmem {
-  uint32_t ckey[CAND_L];
-  uint32_t cidx[CAND_L];
-  uint32_t outv[4096];
-  uint32_t bits[BITMAP_WORDS];
-  uint32_t hist[1024];
-  uint32_t off[2][MAX_CHUNKS + 1];             // exclusive prefix of the chunk counts
-  uint32_t scan[SEL_NT / 64];
+struct PickSmem {
+  uint32_t hist[2][PICK_BINS];                 // alternating digit histograms
+  uint32_t ccnt[PICK_MAXCH];
+  uint32_t bm_gt[PICK_SLOTS / 32];             // output bitmaps over slots
+  uint32_t bm_eq[PICK_SLOTS / 32];
+  uint32_t wv[4][PICK_NW];                     // per-wave partials
   uint32_t res[2];
-  uint32_t neq, fallback;
 };
 
-// Final pass of one long row: gather the chunks' lists, resolve the boundary
-// bin on the low 20 key bits (lowest index wins ties), emit ascending indices.
-__global__ __launch_bounds__(SEL_NT) void long_final_kernel(IndexerArgs a) {
-  extern __shared__ __align__(16) unsigned char ssm_raw[];
-  SelectSmem& sm = *reinterpret_cast<SelectSmem*>(ssm_raw);
+// Slot s of a row holds (key, entry) of the (s mod cap)-th kept entry of chunk
+// s / cap; the row's slots are nch * cap long.  Thread tid holds slots
+// q * PICK_NT + tid (coalesced loads); the ordered output goes through LDS
+// bitmaps over the slots.
+__global__ __launch_bounds__(PICK_NT) void long_pick_kernel(IndexerArgs a) {
+  __shared__ PickSmem sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = blockIdx.x;
   const int b = row / a.Tq, t = row % a.Tq;
-  const int tid = threadIdx.x;
   const int n = row_len(a, b, t);
   const int k = a.topk;
-  LongWs L = long_ws(a.ws, a.B * a.Tq, a.Nc_cap, a.topk);
-  const uint32_t* keys = reinterpret_cast<const uint32_t*>(L.scores) + (size_t)row * nc_pad(a.Nc_cap);
+  const LongWs L = long_ws(a.ws, a.B * a.Tq, a.Nc_cap);
   int32_t* idx = a.idx_out + (size_t)row * k;
   float* sco = a.score_out ? a.score_out + (size_t)row * k : nullptr;
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(L.scores) + (size_t)row * nc_pad(a.Nc_cap);
   if (n <= k) {
-    write_all_eligible(n, k, keys, idx, sco, SEL_NT);
+    write_all_eligible(n, k, src, idx, sco, PICK_NT);
     return;
   }
-  const int nch = (n + ROW_CHUNK - 1) / ROW_CHUNK;
-  if (tid == 0) { sm.neq = 0; sm.fallback = nch > MAX_CHUNKS; }
-  // chunk counts -> exclusive offsets (one block scan per list)
-  {
-    const uint32_t* cc = L.ccnt + (size_t)row * ((L.nch * 2 + 3) & ~3);
-    uint32_t c_sel = 0, c_cand = 0;
-    if (tid < nch && tid < MAX_CHUNKS) { c_sel = cc[2 * tid]; c_cand = cc[2 * tid + 1]; }
-    uint32_t tot_sel, tot_cand;
-    const uint32_t o_sel = block_excl_scan<SEL_NT>(c_sel, sm.scan, &tot_sel);
-    const uint32_t o_cand = block_excl_scan<SEL_NT>(c_cand, sm.scan, &tot_cand);
-    if (tid < MAX_CHUNKS) { sm.off[0][tid] = o_sel; sm.off[1][tid] = o_cand; }
-    if (tid == 0) {
-      sm.off[0][MAX_CHUNKS] = tot_sel;
-      sm.off[1][MAX_CHUNKS] = tot_cand;
-      if (tot_sel >= (uint32_t)k || tot_cand > (uint32_t)CAND_L || (uint32_t)k - tot_sel > tot_cand)
-        sm.fallback = 1;
-    }
+  const int nch = (n + SCORE_CHUNK - 1) / SCORE_CHUNK;
+  const int cap = chunk_cap(chunk_keep(k, n));
+  const int lg = 31 - __clz(cap);                            // cap is a power of two
+  const uint32_t* meta = L.meta + (size_t)row * L.nch * 2;
+  const uint2* cand = reinterpret_cast<const uint2*>(L.cand) + (size_t)row * L.nch * SCORE_CHUNK;
+  const int nslot = nch << lg;
+  const int per = (nslot + PICK_NT - 1) / PICK_NT;
+  constexpr uint2 EMPTY = {0u, 0xFFFFFFFFu};
+  auto slot_addr = [&](int s) { return (size_t)s; };         // slots are dense: chunk c at c * cap
+
+  // ---- 1. chunk counts and this thread's candidate slots, requested together ----
+  int bad = per > PICK_PER;
+  uint2 kv[PICK_PER];
+#pragma unroll
+  for (int q = 0; q < PICK_PER; ++q) kv[q] = cand[slot_addr(min(q * PICK_NT + tid, max(nslot - 1, 0)))];
+  uint32_t part = 0;
+  for (int c = tid; c < nch; c += PICK_NT) {
+    const uint32_t m0 = meta[2 * c];
+    sm.ccnt[c] = min(m0, (uint32_t)cap);
+    bad |= m0 > (uint32_t)cap;
+    part += min(m0, (uint32_t)cap);
   }
+  for (int i = tid; i < PICK_SLOTS / 32; i += PICK_NT) { sm.bm_gt[i] = 0; sm.bm_eq[i] = 0; }
   __syncthreads();
-  if (sm.fallback) {                                           // exact, slow, rare
-    TopkSmem<SEL_NT>& ts = *reinterpret_cast<TopkSmem<SEL_NT>*>(ssm_raw);
-    __syncthreads();
-    select_row<SEL_NT>(ts, keys, n, k, idx, sco);
-    return;
+#pragma unroll
+  for (int q = 0; q < PICK_PER; ++q) {
+    const int s = q * PICK_NT + tid;
+    if (q >= per || s >= nslot || (s & (cap - 1)) >= (int)sm.ccnt[s >> lg]) kv[q] = EMPTY;
   }
-  const uint32_t nsel = sm.off[0][MAX_CHUNKS], ncand = sm.off[1][MAX_CHUNKS];
-  // gather: list position p lives in the chunk c with off[c] <= p < off[c+1]
-  auto chunk_of = [&](int list, uint32_t p) {
-    int lo = 0, hi = nch - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (sm.off[list][mid] <= p) lo = mid; else hi = mid - 1;
-    }
-    return lo;
-  };
-  {
-    constexpr int R = 4;                                      // 4 x 1024 >= k
-    uint32_t sv[R];
+
+  // ---- 2. candidate total, key range, overflow: one block reduction ----
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0;
 #pragma unroll
-    for (int q = 0; q < R; ++q) {
-      const uint32_t p = tid + q * SEL_NT;
-      sv[q] = 0xFFFFFFFFu;
-      if (p < nsel) {
-        const int c = chunk_of(0, p);
-        sv[q] = L.csel[((size_t)row * L.nch + c) * ROW_CHUNK + (p - sm.off[0][c])];
-      }
-    }
-    constexpr int RC = CAND_L / SEL_NT;
-    uint2 cv[RC];
+  for (int q = 0; q < PICK_PER; ++q)
+    if (kv[q].y != EMPTY.y) { kmin = min(kmin, kv[q].x); kmax = max(kmax, kv[q].x); }
 #pragma unroll
-    for (int q = 0; q < RC; ++q) {
-      const uint32_t p = tid + q * SEL_NT;
-      cv[q] = uint2{0u, 0u};
-      if (p < ncand) {
-        const int c = chunk_of(1, p);
-        cv[q] = reinterpret_cast<const uint2*>(L.ccand + ((size_t)row * L.nch + c) * ROW_CHUNK * 2)[p - sm.off[1][c]];
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < R; ++q) sm.outv[tid + q * SEL_NT] = sv[q];
-#pragma unroll
-    for (int q = 0; q < RC; ++q) {
-      const uint32_t p = tid + q * SEL_NT;
-      if (p < ncand) { sm.ckey[p] = cv[q].x; sm.cidx[p] = cv[q].y; }
-    }
+  for (int o = 32; o > 0; o >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+    part += (uint32_t)__shfl_xor((int)part, o, 64);
+    bad |= __shfl_xor(bad, o, 64);
   }
-  if (tid == 0) { sm.res[0] = 0; sm.res[1] = 0; }
+  if (lane == 0) { sm.wv[0][wave] = part; sm.wv[1][wave] = kmin; sm.wv[2][wave] = kmax; sm.wv[3][wave] = bad; }
+  for (int i = tid; i < PICK_BINS; i += PICK_NT) sm.hist[0][i] = 0;
   __syncthreads();
-  const uint32_t need = (uint32_t)k - nsel;
-  // resolve the boundary bin: two 10-bit digits below the 12-bit prefix
-  uint32_t prefix = 0, pmask = 0, rem = need;
+  uint32_t total = 0;
+  kmin = 0xFFFFFFFFu; kmax = 0; bad = 0;
+#pragma unroll
+  for (int w = 0; w < PICK_NW; ++w) {
+    total += sm.wv[0][w];
+    kmin = min(kmin, sm.wv[1][w]);
+    kmax = max(kmax, sm.wv[2][w]);
+    bad |= sm.wv[3][w];
+  }
+  bad |= total < (uint32_t)k;
+
+  // ---- 3. exact radix select of the k-th largest candidate key ----
+  // The candidates are the tops of their chunks and share leading bits, so
+  // the 12-bit digits start at the highest bit where the smallest and largest
+  // key differ; that spreads them over the bins.
+  uint32_t tau = kmin, need = (uint32_t)k;
+  if (!bad && kmin != kmax) {
+    const int top = 31 - __clz((int)(kmin ^ kmax));
+    uint32_t prefix = top >= 31 ? 0u : (kmin & ~((2u << top) - 1u));
+    uint32_t pmask = top >= 31 ? 0u : ~((2u << top) - 1u);
+    int buf = 0;
 #pragma unroll 1
-  for (int p = 0; p < 2; ++p) {
-    const int sh = p == 0 ? 10 : 0;
-    for (int i = tid; i < 1024; i += SEL_NT) sm.hist[i] = 0;
-    __syncthreads();
-    for (uint32_t i = tid; i < ncand; i += SEL_NT) {
-      const uint32_t low = sm.ckey[i] & 0xFFFFFu;
-      if ((low & pmask) == prefix) atomicAdd(&sm.hist[(low >> sh) & 1023u], 1u);
-    }
-    __syncthreads();
-    find_bin<SEL_NT>(sm.hist, 1024, rem, sm.scan, sm.res);
-    prefix |= sm.res[0] << sh;
-    pmask |= 1023u << sh;
-    rem -= sm.res[1];
-    __syncthreads();
-  }
-  // take candidates whose low bits exceed the prefix, and the `rem` lowest
-  // indices among those equal to it
-  uint32_t neq_local = 0;
-  for (uint32_t i = tid; i < ncand; i += SEL_NT) neq_local += ((sm.ckey[i] & 0xFFFFFu) == prefix);
-  if (neq_local) atomicAdd(&sm.neq, neq_local);
-  __syncthreads();
-  const uint32_t neq = sm.neq;
-  if (tid == 0) sm.res[0] = nsel;                              // running output count
-  __syncthreads();
-  for (uint32_t i = tid; i < ncand; i += SEL_NT) {
-    const uint32_t low = sm.ckey[i] & 0xFFFFFu;
-    bool take = low > prefix;
-    if (low == prefix) {
-      if (neq == rem) {
-        take = true;
-      } else {
-        uint32_t rank = 0;
-        for (uint32_t j = 0; j < ncand; ++j)
-          rank += ((sm.ckey[j] & 0xFFFFFu) == prefix) && (sm.cidx[j] < sm.cidx[i]);
-        take = rank < rem;
-      }
-    }
-    if (take) {
-      const uint32_t pos = atomicAdd(&sm.res[0], 1u);
-      if (pos < (uint32_t)k) sm.outv[pos] = sm.cidx[i];
-    }
-  }
-  __syncthreads();
-  const uint32_t nout = min(sm.res[0], (uint32_t)k);
-  // ascending output
-  if (n <= BITMAP_WORDS * 32) {
-    const int nw = (n + 31) / 32;
-    for (int i = tid; i < nw; i += SEL_NT) sm.bits[i] = 0u;
-    __syncthreads();
-    for (uint32_t i = tid; i < nout; i += SEL_NT) {
-      const uint32_t j = sm.outv[i];
-      if (j < (uint32_t)n) atomicOr(&sm.bits[j >> 5], 1u << (j & 31));
-    }
-    __syncthreads();
-    constexpr int WPT = BITMAP_WORDS / SEL_NT;
-    const int w0 = tid * WPT;
-    uint32_t cntb = 0;
+    for (int hi = top; hi >= 0; hi -= 12) {
+      const int sh = hi >= 11 ? hi - 11 : 0;
+      const int nb = 1 << (hi - sh + 1);
+      const int nbs = max(nb, PICK_NT);                       // bins scanned
+      uint32_t* hist = sm.hist[buf];
+      for (int i = tid; i < PICK_BINS; i += PICK_NT) sm.hist[buf ^ 1][i] = 0;   // next pass's buffer
 #pragma unroll
-    for (int q = 0; q < WPT; ++q) cntb += (w0 + q < nw) ? (uint32_t)__popc(sm.bits[w0 + q]) : 0u;
-    uint32_t totb;
-    uint32_t pos = block_excl_scan<SEL_NT>(cntb, sm.scan, &totb);
-#pragma unroll
-    for (int q = 0; q < WPT; ++q) {
-      if (w0 + q >= nw) break;
-      uint32_t word = sm.bits[w0 + q];
-      while (word) {
-        const int bit = __ffs(word) - 1;
-        word &= word - 1;
-        const uint32_t j = (uint32_t)(w0 + q) * 32u + (uint32_t)bit;
-        if (pos < (uint32_t)k) {
-          idx[pos] = (int32_t)j;
-          if (sco) sco[pos] = __uint_as_float(keys[j]);
-        }
-        ++pos;
-      }
-    }
-    for (uint32_t i = totb + tid; i < (uint32_t)k; i += SEL_NT) {
-      idx[i] = -1;
-      if (sco) sco[i] = -INFINITY;
-    }
-    return;
-  }
-  // longer rows: bitonic sort of the k selected indices (padded to a power of two)
-  int np2 = 1;
-  while (np2 < k) np2 <<= 1;
-  for (int size = 2; size <= np2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < np2 / 2; i += SEL_NT) {
-        const int l2 = 2 * i - (i & (stride - 1));
-        const int h2 = l2 + stride;
-        const bool asc = ((l2 & size) == 0);
-        const uint32_t x = sm.outv[l2], y = sm.outv[h2];
-        if ((x > y) == asc) { sm.outv[l2] = y; sm.outv[h2] = x; }
+      for (int q = 0; q < PICK_PER; ++q) {
+        const uint2 v = kv[q];
+        if (v.y != EMPTY.y && (v.x & pmask) == prefix) atomicAdd(&hist[(v.x >> sh) & (nb - 1)], 1u);
       }
       __syncthreads();
+      // top-down scan: thread tid owns bins [nbs - pb*(tid+1), nbs - pb*tid)
+      const int pb = nbs / PICK_NT;
+      const int hb = nbs - pb * tid;
+      uint32_t local = 0;
+      for (int i = 0; i < pb; ++i) local += hist[hb - 1 - i];
+      const uint32_t incl = wave_incl_scan(local);
+      if (lane == 63) sm.wv[0][wave] = incl;
+      __syncthreads();
+      uint32_t before = incl - local;
+      for (int w = 0; w < wave; ++w) before += sm.wv[0][w];
+      if (before < need && before + local >= need) {
+        uint32_t cum = before;
+        for (int i = 0; i < pb; ++i) {
+          const uint32_t h = hist[hb - 1 - i];
+          if (cum + h >= need) { sm.res[0] = (uint32_t)(hb - 1 - i); sm.res[1] = cum; break; }
+          cum += h;
+        }
+      }
+      __syncthreads();
+      prefix |= sm.res[0] << sh;
+      pmask |= (uint32_t)(nb - 1) << sh;
+      need -= sm.res[1];
+      buf ^= 1;
+    }
+    tau = prefix;
+  }
+  // the chunks' dropped entries must all lie below tau
+  int unsafe = bad;
+  if (!bad)
+    for (int c = tid; c < nch; c += PICK_NT) {
+      const uint32_t cut = meta[2 * c + 1];
+      unsafe |= cut != CUT_ALL && tau < (cut << 12);
+    }
+  // mark keys > tau and keys == tau in the slot bitmaps
+  if (!unsafe) {
+#pragma unroll
+    for (int q = 0; q < PICK_PER; ++q) {
+      const uint2 v = kv[q];
+      const int s = q * PICK_NT + tid;
+      if (v.y == EMPTY.y) continue;
+      if (v.x > tau) atomicOr(&sm.bm_gt[s >> 5], 1u << (s & 31));
+      else if (v.x == tau) atomicOr(&sm.bm_eq[s >> 5], 1u << (s & 31));
     }
   }
-  for (int i = tid; i < k; i += SEL_NT) {
-    const uint32_t j = sm.outv[i];
-    const bool ok = j < (uint32_t)n;
-    idx[i] = ok ? (int32_t)j : -1;
-    if (sco) sco[i] = ok ? __uint_as_float(keys[j]) : -INFINITY;
+  if (__syncthreads_or(unsafe)) {
+    select_row<PICK_NT>(*reinterpret_cast<TopkSmem<PICK_NT>*>(&sm.hist[0][0]), src, n, k, idx, sco);
+    return;
+  }
+
+  // ---- 4. output in slot order (= ascending entry order): thread tid owns
+  // the contiguous slots [32 tid, 32 tid + 32): keys > tau, and the first
+  // `need` keys == tau over the whole row ----
+  const uint32_t wgt = tid < PICK_SLOTS / 32 ? sm.bm_gt[tid] : 0u;
+  const uint32_t weq = tid < PICK_SLOTS / 32 ? sm.bm_eq[tid] : 0u;
+  const uint64_t pk = ((uint64_t)__popc(wgt) << 32) | (uint32_t)__popc(weq);
+  uint64_t inc = pk;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint64_t y = ((uint64_t)(uint32_t)__shfl_up((int)(uint32_t)(inc >> 32), o, 64) << 32) |
+                       (uint32_t)__shfl_up((int)(uint32_t)inc, o, 64);
+    if (lane >= o) inc += y;
+  }
+  if (lane == 63) { sm.wv[1][wave] = (uint32_t)(inc >> 32); sm.wv[2][wave] = (uint32_t)inc; }
+  __syncthreads();
+  uint32_t gt_before = (uint32_t)((inc - pk) >> 32), eq_before = (uint32_t)(inc - pk);
+  for (int w = 0; w < wave; ++w) { gt_before += sm.wv[1][w]; eq_before += sm.wv[2][w]; }
+  uint32_t pos = gt_before + min(eq_before, need);
+  uint32_t e_seen = eq_before;
+  uint32_t take = wgt;
+  for (uint32_t m = weq; m; m &= m - 1) {
+    const int bit = __ffs(m) - 1;
+    if (e_seen++ < need) take |= 1u << bit;
+  }
+  for (; take; take &= take - 1) {
+    const int s = tid * 32 + __ffs(take) - 1;
+    const uint2 v = cand[slot_addr(s)];
+    if (pos < (uint32_t)k) {
+      idx[pos] = (int32_t)v.y;
+      if (sco) sco[pos] = __uint_as_float(v.x);
+    }
+    ++pos;
   }
 }
 
@@ -1006,20 +1011,20 @@ __global__ __launch_bounds__(FNT) void fused_prefill_kernel(IndexerArgs a) {
   // f(rt, sp, entry, key, eligible) is called for each.  All MFMAs of an entry
   // tile issue before the epilogue reads their results.
   auto pass = [&](auto&& f) {
-    F kb[KC];
+    RawFrag<QK> kb[KC];
     float ks = 1.f;
     auto load = [&](int e0) {
       const int e = min(e0 + 16 * wave + r, ne_max - 1);
 #pragma unroll
       for (int c = 0; c < KC; ++c)
-        load_qk_frag<QK>(kb[c], kbase + (size_t)e * rb, QK == QK_FP4 ? sbase + (size_t)e * (DI / 32) : nullptr,
-                         8 * (g * KC + c));
+        load_raw<QK>(kb[c], kbase + (size_t)e * rb, QK == QK_FP4 ? sbase + (size_t)e * (DI / 32) : nullptr,
+                     8 * (g * KC + c));
       if constexpr (QK == QK_FP8) ks = fsc[e];
     };
     if (ne_max > 0) load(0);
 #pragma unroll 1
     for (int e0 = 0; e0 < ne_max; e0 += 16 * FNW) {
-      F cur[KC];
+      RawFrag<QK> cur[KC];
 #pragma unroll
       for (int c = 0; c < KC; ++c) cur[c] = kb[c];
       const float cks = ks;
@@ -1030,7 +1035,7 @@ __global__ __launch_bounds__(FNT) void fused_prefill_kernel(IndexerArgs a) {
       for (int rt = 0; rt < NRT; ++rt) {
         acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < KC; ++c) mma16(acc[rt], qa[rt][c], cur[c]);
+        for (int c = 0; c < KC; ++c) mma16(acc[rt], qa[rt][c], widen<QK>(cur[c]));
       }
 #pragma unroll
       for (int rt = 0; rt < NRT; ++rt) {
@@ -1217,7 +1222,7 @@ static hipError_t launch_fused_di(const IndexerArgs& a, hipStream_t st) {
 // --------------------------------- launch ----------------------------------
 size_t indexer_workspace(int B, int Tq, int Nc_cap, int HI, int dI, int topk, int qk) {
   (void)HI; (void)dI; (void)qk;
-  if (use_long_path(Tq, Nc_cap)) return long_ws_bytes(B * Tq, Nc_cap, topk);
+  if (use_long_path(Tq, Nc_cap)) return long_ws_bytes(B * Tq, Nc_cap);
   return (size_t)B * Tq * nc_pad(Nc_cap) * sizeof(float);
 }
 
@@ -1226,7 +1231,7 @@ static void launch_scores(const IndexerArgs& a, hipStream_t st, bool long_path) 
   const int ne_ub = std::min((a.max_pos + 1) / a.m, a.Nc_cap);
   if (ne_ub <= 0) return;
   if (long_path) {
-    dim3 grid((ne_ub + ROW_CHUNK - 1) / ROW_CHUNK, a.B * a.Tq);
+    dim3 grid((ne_ub + SCORE_CHUNK - 1) / SCORE_CHUNK, a.B * a.Tq);
     ProfScope ps("indexer_score", st);
     if constexpr (QK == QK_FP4 && HI == 4)
       hipLaunchKernelGGL((score_row_fp4_kernel<DI>), grid, dim3(256), 0, st, a);
@@ -1264,11 +1269,6 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t st) {
     }
   }
   const bool lp = use_long_path(a.Tq, a.Nc_cap);
-  const int rows = a.B * a.Tq;
-  if (lp) {
-    ProfScope ps("indexer_zero", st);
-    hipLaunchKernelGGL(long_zero_kernel, dim3(rows), dim3(256), 0, st, a);
-  }
   switch (a.qk) {
     case QK_F32: launch_scores_di<QK_F32>(a, st, lp); break;
     case QK_BF16: launch_scores_di<QK_BF16>(a, st, lp); break;
@@ -1277,29 +1277,9 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (!lp) {
-    ProfScope ps("indexer_topk", st);
-    hipLaunchKernelGGL(topk_row_kernel, dim3(a.Tq, a.B), dim3(TOPK_NT), 0, st, a);
-    return hipGetLastError();
-  }
-  const int ne_ub = std::min((a.max_pos + 1) / a.m, a.Nc_cap);
-  {
-    ProfScope ps("indexer_split", st);
-    hipLaunchKernelGGL(long_split_kernel, dim3(row_chunks(std::max(ne_ub, 1)), rows), dim3(256),
-                       0, st, a);
-  }
-  static bool attr_set = false;
-  const size_t lds = sizeof(SelectSmem);
-  if (!attr_set) {
-    e = hipFuncSetAttribute((const void*)long_final_kernel,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  {
-    ProfScope ps("indexer_topk", st);
-    hipLaunchKernelGGL(long_final_kernel, dim3(rows), dim3(SEL_NT), lds, st, a);
-  }
+  ProfScope ps("indexer_topk", st);
+  if (lp) hipLaunchKernelGGL(long_pick_kernel, dim3(a.B * a.Tq), dim3(PICK_NT), 0, st, a);
+  else hipLaunchKernelGGL(topk_row_kernel, dim3(a.Tq, a.B), dim3(TOPK_NT), 0, st, a);
   return hipGetLastError();
 }
 
