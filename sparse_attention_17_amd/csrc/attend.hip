@@ -51,7 +51,7 @@ __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(
 // being computed (PF=2 for split decode, whose workgroups hold two tiles: all
 // of a workgroup's keys are then requested at once).
 template <typename T, int D, int RW, int KG, bool SPARSE, int PF>
-__global__ __launch_bounds__(RW * KG * 64) void attend_kernel(AttendArgs a, AttnGeom gm) {
+__global__ __launch_bounds__(RW * KG * 64) __attribute__((amdgpu_waves_per_eu(PF == 1 ? 2 : 1))) void attend_kernel(AttendArgs a, AttnGeom gm) {
   constexpr int NW = RW * KG;
   constexpr int NT = NW * 64;
   constexpr int NSUB = 2 / KG;                 // 32-key sub-tiles per wave per tile

@@ -185,17 +185,20 @@ static size_t long_ws_bytes(int rows, int Nc_cap) {
   return (size_t)rows * ((size_t)nc_pad(Nc_cap) * 4 + (size_t)((nch * 2 + 3) & ~3) * 4 +
                          (size_t)nch * SCORE_CHUNK * 8);
 }
-// Entries each score chunk keeps for the row select: about four times the
-// chunk's expected share of the top k, as a power of two in [32, SCORE_CHUNK].
-// A chunk stores every entry whose 12-bit digit is at least the digit of its
-// kc-th largest key (its "cut"), up to chunk_cap of them.
-__host__ __device__ __forceinline__ int chunk_keep(int k, int n) {
+// Candidate slots per chunk for the row select: a power of two in
+// [32, SCORE_CHUNK] near four times the chunk's expected share of the top k;
+// the chunk keeps its kc = 3/4 of that (three times its share) largest keys
+// plus whatever shares the kc-th key's 20-bit prefix, up to the slots.
+__host__ __device__ __forceinline__ int chunk_cap_n(int k, int n) {
   const long long want = (4LL * k * SCORE_CHUNK + n - 1) / n;
-  int kc = 32;
-  while (kc < want && kc < SCORE_CHUNK) kc <<= 1;
-  return kc;
+  int cap = 32;
+  while (cap < want && cap < SCORE_CHUNK) cap <<= 1;
+  return cap;
 }
-__host__ __device__ __forceinline__ int chunk_cap(int kc) { return kc * 2 < SCORE_CHUNK ? kc * 2 : SCORE_CHUNK; }
+__host__ __device__ __forceinline__ int chunk_keep(int k, int n) {
+  const int cap = chunk_cap_n(k, n);
+  return cap < SCORE_CHUNK ? cap - cap / 4 : SCORE_CHUNK;
+}
 static constexpr uint32_t CUT_ALL = 0xFFFFFFFFu;   // the chunk kept every entry
 static bool use_long_path(int Tq, int Nc_cap) { return Tq <= 4 && Nc_cap > TOPK_LDS_KEYS; }
 
@@ -232,7 +235,7 @@ __device__ void chunk_cut(const IndexerArgs& a, const LongWs& L, int row, int ch
                           int nloc, const uint32_t* sk, uint32_t* hist, uint32_t* scan,
                           uint32_t* res) {
   constexpr int PER = SCORE_CHUNK / 256;
-  const int kc = chunk_keep(a.topk, n), cap = chunk_cap(kc);
+  const int kc = chunk_keep(a.topk, n), cap = chunk_cap_n(a.topk, n);
   const int i0 = threadIdx.x * PER;
   uint32_t cut = 0;
   const bool dropped = nloc > kc;                            // uniform
@@ -706,7 +709,7 @@ __global__ __launch_bounds__(PICK_NT) void long_pick_kernel(IndexerArgs a) {
     return;
   }
   const int nch = (n + SCORE_CHUNK - 1) / SCORE_CHUNK;
-  const int cap = chunk_cap(chunk_keep(k, n));
+  const int cap = chunk_cap_n(k, n);
   const int lg = 31 - __clz(cap);                            // cap is a power of two
   const uint32_t* meta = L.meta + (size_t)row * L.nch * 2;
   const uint2* cand = reinterpret_cast<const uint2*>(L.cand) + (size_t)row * L.nch * SCORE_CHUNK;
@@ -719,7 +722,8 @@ __global__ __launch_bounds__(PICK_NT) void long_pick_kernel(IndexerArgs a) {
   int bad = per > PICK_PER;
   uint2 kv[PICK_PER];
 #pragma unroll
-  for (int q = 0; q < PICK_PER; ++q) kv[q] = cand[slot_addr(min(q * PICK_NT + tid, max(nslot - 1, 0)))];
+  for (int q = 0; q < PICK_PER; ++q)
+    if (q < per) kv[q] = cand[slot_addr(min(q * PICK_NT + tid, max(nslot - 1, 0)))];
   uint32_t part = 0;
   for (int c = tid; c < nch; c += PICK_NT) {
     const uint32_t m0 = meta[2 * c];
@@ -739,7 +743,7 @@ __global__ __launch_bounds__(PICK_NT) void long_pick_kernel(IndexerArgs a) {
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0;
 #pragma unroll
   for (int q = 0; q < PICK_PER; ++q)
-    if (kv[q].y != EMPTY.y) { kmin = min(kmin, kv[q].x); kmax = max(kmax, kv[q].x); }
+    if (q < per && kv[q].y != EMPTY.y) { kmin = min(kmin, kv[q].x); kmax = max(kmax, kv[q].x); }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
@@ -781,7 +785,8 @@ __global__ __launch_bounds__(PICK_NT) void long_pick_kernel(IndexerArgs a) {
 #pragma unroll
       for (int q = 0; q < PICK_PER; ++q) {
         const uint2 v = kv[q];
-        if (v.y != EMPTY.y && (v.x & pmask) == prefix) atomicAdd(&hist[(v.x >> sh) & (nb - 1)], 1u);
+        if (q < per && v.y != EMPTY.y && (v.x & pmask) == prefix)
+          atomicAdd(&hist[(v.x >> sh) & (nb - 1)], 1u);
       }
       __syncthreads();
       // top-down scan: thread tid owns bins [nbs - pb*(tid+1), nbs - pb*tid)
@@ -823,7 +828,7 @@ __global__ __launch_bounds__(PICK_NT) void long_pick_kernel(IndexerArgs a) {
     for (int q = 0; q < PICK_PER; ++q) {
       const uint2 v = kv[q];
       const int s = q * PICK_NT + tid;
-      if (v.y == EMPTY.y) continue;
+      if (q >= per || v.y == EMPTY.y) continue;
       if (v.x > tau) atomicOr(&sm.bm_gt[s >> 5], 1u << (s & 31));
       else if (v.x == tau) atomicOr(&sm.bm_eq[s >> 5], 1u << (s & 31));
     }
