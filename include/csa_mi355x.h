@@ -147,6 +147,7 @@ csa_status_t csa_indexer_topk(const void *qi, const void *qi_scale, const float 
  *             max(0, t-W+1) .. t (its own token included)
  *   sink      [H] fp32 sink logits, or NULL for no sink
  *   lse_out   [B, Tq, H] fp32 natural-log denominators (incl. sink), or NULL
+ *   softmax_scale  sigma > 0 (finite); logits are sigma * q.k
  *   dt ∈ {F32, BF16}; d ∈ {64, 128}; 1 <= H <= 128; topk <= 4096.
  */
 size_t csa_sparse_attend_workspace(int B, int Tq, int H, int d, int topk, int window);

@@ -203,6 +203,8 @@ csa_status_t csa_sparse_attend(const void* q, const void* kc, const void* vc, co
                                int Nc_cap, csa_dtype_t dt, void* out, float* lse_out,
                                void* workspace, size_t workspace_bytes, void* stream) {
   REQUIRE(topk >= 1 && topk <= 4096, CSA_INVALID_ARGUMENT, "topk must be in [1, 4096] (got %d)", topk);
+  REQUIRE(softmax_scale > 0.f && softmax_scale < 1e30f, CSA_INVALID_ARGUMENT,
+          "softmax_scale must be positive and finite (got %g)", (double)softmax_scale);
   csa_status_t st = check_attend_common(q, kc, vc, kw, vw, raw_pos0, R, window, pos0, max_pos,
                                         sink, B, Tq, H, d, Nc_cap, dt, out, lse_out);
   if (st != CSA_OK || B == 0 || Tq == 0) return st;
@@ -228,6 +230,8 @@ csa_status_t hca_attend(const void* q, const void* kc, const void* vc, int m_pri
                         void* out, float* lse_out, void* workspace, size_t workspace_bytes,
                         void* stream) {
   REQUIRE(m_prime >= 1, CSA_INVALID_ARGUMENT, "m_prime must be >= 1");
+  REQUIRE(softmax_scale > 0.f && softmax_scale < 1e30f, CSA_INVALID_ARGUMENT,
+          "softmax_scale must be positive and finite (got %g)", (double)softmax_scale);
   csa_status_t st = check_attend_common(q, kc, vc, kw, vw, raw_pos0, R, window, pos0, max_pos,
                                         sink, B, Tq, H, d, Nc_cap, dt, out, lse_out);
   if (st != CSA_OK || B == 0 || Tq == 0) return st;

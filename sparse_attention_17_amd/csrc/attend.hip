@@ -312,7 +312,7 @@ __global__ __launch_bounds__(RW * KG * 64) __attribute__((amdgpu_waves_per_eu(PF
       const int sub = KG == 2 ? kg : si;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float x = st[si][r] * gm.scale_log2;
+        float x = st[si][r];                   // raw q.k; the scale is applied in the exponent
         if (!full) {
           const int s = s0 + sub * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
           bool ok = qvalid && s < kend;
@@ -334,7 +334,7 @@ __global__ __launch_bounds__(RW * KG * 64) __attribute__((amdgpu_waves_per_eu(PF
         mt = fmaxf(mt, x);
       }
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * gm.scale_log2;   // scale > 0 keeps the order
     // The reference max only moves when a lane's tile max exceeds it by more
     // than 8 (log2 units): P stays <= 2^8 and most tiles skip the O rescale.
     if (__any(mt > m_run + 8.f)) {
@@ -355,7 +355,7 @@ __global__ __launch_bounds__(RW * KG * 64) __attribute__((amdgpu_waves_per_eu(PF
       float pv[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        pv[r] = fexp2<T>(st[si][r] - m_use);
+        pv[r] = fexp2<T>(fmaf(st[si][r], gm.scale_log2, -m_use));
         psum += pv[r];
       }
       frag_from_f32(pf[si][0], pv);

@@ -105,6 +105,8 @@ def test_sparse_attend_validation(lib):
     assert _sparse(lib, R=0) == L.INVALID_ARGUMENT
     assert _sparse(lib, dt=L.FP4_E2M1) == L.UNSUPPORTED
     assert _sparse(lib, max_pos=-5) == L.INVALID_ARGUMENT
+    assert _sparse(lib, scale=C.c_float(0.0)) == L.INVALID_ARGUMENT      # the scale must be > 0
+    assert _sparse(lib, scale=C.c_float(-0.1)) == L.INVALID_ARGUMENT
     need = lib.csa_sparse_attend_workspace(2, 1, 64, 128, 64, 128)
     assert need > 0                                          # one decode token: split-KV partials
     assert _sparse(lib, ws=FAKE, ws_bytes=need - 1) == L.WORKSPACE_TOO_SMALL
@@ -124,6 +126,7 @@ def test_hca_validation(lib):
     assert _hca(lib, m_prime=0) == L.INVALID_ARGUMENT
     assert _hca(lib, window=16) == L.INVALID_ARGUMENT          # window without a raw buffer
     assert _hca(lib, H=0) == L.UNSUPPORTED
+    assert _hca(lib, scale=C.c_float(float("inf"))) == L.INVALID_ARGUMENT
     need = lib.hca_attend_workspace(16, 1, 64, 128, 8192, 128, 0)
     assert need == 32 * 16 * 64 * 130 * 4                      # 32 splits of 256 entries
     assert _hca(lib, ws=FAKE, ws_bytes=need - 1) == L.WORKSPACE_TOO_SMALL
