@@ -45,6 +45,12 @@ __host__ __device__ __forceinline__ int hca_ne(int pos, int mp, int cap) {
 template <typename T>
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Position of the 4-key block kb (0..15) in row `dim` of the transposed V
+// tile: blocks are XOR-swizzled by the row's 8-dim group so that the staging
+// stores (one 4-key block for each of 8 consecutive dims per lane, lanes 8
+// dims apart) spread over the LDS banks; the MFMA operand reads apply the same map.
+__device__ __forceinline__ int vt_block(int dim, int kb) { return kb ^ ((dim >> 3) & 15); }
+
 // RW row-waves (32 query rows each) x KG key groups (KG=2: each wave of a pair
 // takes one 32-key half of every 64-key tile; the two partial softmax states
 // are merged in LDS at the end).  PF key tiles are in flight ahead of the one
@@ -257,7 +263,7 @@ __global__ __launch_bounds__(RW * KG * 64) __attribute__((amdgpu_waves_per_eu(PF
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
         T four[4] = {rows[e], rows[VEC + e], rows[2 * VEC + e], rows[3 * VEC + e]};
-        T* dst = Vt + (ch * VEC + e) * VS + kg * 4;
+        T* dst = Vt + (ch * VEC + e) * VS + vt_block(ch * VEC + e, kg) * 4;
         if constexpr (sizeof(T) == 2) *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<uint2*>(four);
         else *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<u32x4*>(four);
       }
@@ -372,15 +378,15 @@ __global__ __launch_bounds__(RW * KG * 64) __attribute__((amdgpu_waves_per_eu(PF
         const int sub = KG == 2 ? kg : si;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const int kb = sub * 32 + 16 * ks + 4 * half;
+          const int kb = sub * 32 + 16 * ks + 4 * half;    // first of keys kb..kb+3, kb+8..kb+11
           Frag<T> vf;
           if constexpr (sizeof(T) == 2) {
-            const uint2 lo = *reinterpret_cast<const uint2*>(vrow + kb);
-            const uint2 hi = *reinterpret_cast<const uint2*>(vrow + kb + 8);
+            const uint2 lo = *reinterpret_cast<const uint2*>(vrow + vt_block(i * 32 + col, kb / 4) * 4);
+            const uint2 hi = *reinterpret_cast<const uint2*>(vrow + vt_block(i * 32 + col, kb / 4 + 2) * 4);
             vf.v = u32x4{lo.x, lo.y, hi.x, hi.y};
           } else {
-            const f32x4 lo = *reinterpret_cast<const f32x4*>(vrow + kb);
-            const f32x4 hi = *reinterpret_cast<const f32x4*>(vrow + kb + 8);
+            const f32x4 lo = *reinterpret_cast<const f32x4*>(vrow + vt_block(i * 32 + col, kb / 4) * 4);
+            const f32x4 hi = *reinterpret_cast<const f32x4*>(vrow + vt_block(i * 32 + col, kb / 4 + 2) * 4);
             float* fv = reinterpret_cast<float*>(&vf);
             fv[0] = lo[0]; fv[1] = lo[1]; fv[2] = lo[2]; fv[3] = lo[3];
             fv[4] = hi[0]; fv[5] = hi[1]; fv[6] = hi[2]; fv[7] = hi[3];
