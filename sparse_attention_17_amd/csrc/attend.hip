@@ -72,8 +72,7 @@ __global__ __launch_bounds__(RW * KG * 64) __attribute__((amdgpu_waves_per_eu(PF
   extern __shared__ __align__(16) unsigned char smem_raw[];
   T* Ks = reinterpret_cast<T*>(smem_raw);
   T* Vt = Ks + KT * KS;
-  T* Qs = Vt + D * VS;                         // [RW*32][KS] query rows of the tile
-  int* sel = reinterpret_cast<int*>(Qs + RW * 32 * KS);
+  int* sel = reinterpret_cast<int*>(Vt + D * VS);
   __shared__ uint32_t scan_sm[NW];
   __shared__ int s_nsel;
 
@@ -96,22 +95,27 @@ __global__ __launch_bounds__(RW * KG * 64) __attribute__((amdgpu_waves_per_eu(PF
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
   };
 
-  // ---- the tile's query rows: loads issued first, written to LDS once the
-  // first key tiles are requested ----
-  constexpr int QCH = D * sizeof(T) / 16;
-  constexpr int QLD = (RW * 32 * QCH + NT - 1) / NT;
-  u32x4 qreg[QLD];
+  // ---- this wave's query fragments: loaded once into registers, issued
+  // before anything else ----
+  Frag<T> qfr[DSTEP];
   {
     const __amdgpu_buffer_rsrc_t rq =
         rsrc(reinterpret_cast<const T*>(a.q) + (size_t)b * a.Tq * a.H * D, (uint32_t)a.Tq * a.H * ROWB);
+    const int r = rw * 32 + col;
+    const int ttr = r / a.H, hr = r % a.H, tqr = t0 + ttr;
+    const bool ok = ttr < gm.TT && tqr < a.Tq;
+    const uint32_t base = (uint32_t)(tqr * a.H + hr) * ROWB + 8 * half * sizeof(T);
 #pragma unroll
-    for (int i = 0; i < QLD; ++i) {
-      const int c = tid + i * NT;
-      const int r = c / QCH, ch = c % QCH;
-      const int ttr = r / a.H, hr = r % a.H, tqr = t0 + ttr;
-      const bool ok = c < RW * 32 * QCH && ttr < gm.TT && tqr < a.Tq;
-      const uint32_t off = ok ? (uint32_t)(tqr * a.H + hr) * ROWB + ch * 16 : OOB;
-      qreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+    for (int s = 0; s < DSTEP; ++s) {
+      const uint32_t off = base + 16 * s * sizeof(T);
+      if constexpr (sizeof(T) == 2) {
+        qfr[s].v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, ok ? off : OOB, 0, 0));
+      } else {
+        const f32x4 lo = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, ok ? off : OOB, 0, 0));
+        const f32x4 hi = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, ok ? off + 16 : OOB, 0, 0));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { qfr[s].v[i] = lo[i]; qfr[s].v[4 + i] = hi[i]; }
+      }
     }
   }
 
@@ -274,12 +278,6 @@ __global__ __launch_bounds__(RW * KG * 64) __attribute__((amdgpu_waves_per_eu(PF
   if constexpr (PF == 2) {
     if (kbeg + KT < kend) stage_load(kregB, vregB, kbeg + KT);
   }
-#pragma unroll
-  for (int i = 0; i < QLD; ++i) {
-    const int c = tid + i * NT;
-    if (c < RW * 32 * QCH)
-      *reinterpret_cast<u32x4*>(Qs + (c / QCH) * KS + (c % QCH) * (16 / sizeof(T))) = qreg[i];
-  }
 
   auto tile = [&](int s0) {
     // ---- S^T = K Q^T for this wave's 32-key sub-tiles ----
@@ -290,14 +288,12 @@ __global__ __launch_bounds__(RW * KG * 64) __attribute__((amdgpu_waves_per_eu(PF
       for (int r = 0; r < 16; ++r) st[si][r] = 0.f;
 #pragma unroll
     for (int s = 0; s < DSTEP; ++s) {
-      Frag<T> qf;
-      frag_load(qf, Qs + (rw * 32 + col) * KS + 16 * s + 8 * half);
 #pragma unroll
       for (int si = 0; si < NSUB; ++si) {
         const int sub = KG == 2 ? kg : si;
         Frag<T> kf;
         frag_load(kf, Ks + (sub * 32 + col) * KS + 16 * s + 8 * half);
-        mma32(st[si], kf, qf);
+        mma32(st[si], kf, qfr[s]);
       }
     }
     // ---- mask (only tiles that reach a boundary), online softmax ----
@@ -578,7 +574,7 @@ template <typename T, int D, int RW, int KG, bool SPARSE, int PF>
 static hipError_t launch5(const AttendArgs& a, const AttnGeom& gm, hipStream_t st) {
   constexpr int KS = D + 16 / sizeof(T);
   constexpr int VS = KT + 4;
-  size_t lds = (size_t)(KT * KS + D * VS + RW * 32 * KS) * sizeof(T) + (SPARSE ? (size_t)a.topk * 4 : 0);
+  size_t lds = (size_t)(KT * KS + D * VS) * sizeof(T) + (SPARSE ? (size_t)a.topk * 4 : 0);
   if (KG == 2) lds = std::max(lds, (size_t)RW * 64 * ((D / 32) * 16 + 2) * sizeof(float));
   auto kfn = attend_kernel<T, D, RW, KG, SPARSE, PF>;
   if (lds > 65536) {
