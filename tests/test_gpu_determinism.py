@@ -1,0 +1,101 @@
+"""Determinism and batch invariance of the whole path on the GPU: repeated
+launches give bitwise identical results, and a sequence's outputs do not
+depend on the batch it runs in (split-KV decode splits by key count only, and
+every merge runs in a fixed order).  Also: index lists with holes."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import assert_close, dev, f64
+from sparse_attention_17_amd import ops
+from synth import configs, inputs
+
+pytestmark = pytest.mark.gpu
+
+# 65536 CSA entries per sequence (the long-row select path), 2048 HCA entries
+W = configs.HYBRID_1M_FP8.with_(ctx=4 * 65536, B=4)
+
+
+def _decode_step(x, w):
+    g = {k: v.to(dev()) for k, v in x.items()}
+    B = g["q"].shape[0]
+    pos0 = torch.full((B,), w.ctx - 1, dtype=torch.int32, device=dev())
+    rp0 = torch.full((B,), w.ctx - w.window, dtype=torch.int32, device=dev())
+    idx = ops.indexer_topk(g["qi"], g["w"], g["kic"], pos0, w.m, w.topk, max_pos=w.ctx - 1,
+                           qi_scale=g.get("qi_scale"), kic_scale=g.get("kic_scale"),
+                           qk_dtype=w.qk_dtype)
+    o1, l1 = ops.sparse_attend(g["q"], g["kc"], g["vc"], idx, pos0, w.ctx - 1, w.window,
+                               kw=g["kw"], vw=g["vw"], raw_pos0=rp0, sink=g["sink"],
+                               return_lse=True)
+    o2, l2 = ops.hca_attend(g["q_hca"], g["kc_hca"], g["vc_hca"], w.m_hca, pos0, w.ctx - 1,
+                            sink=g["sink_hca"], return_lse=True)
+    torch.cuda.synchronize()
+    return [t.cpu() for t in (idx, o1, l1, o2, l2)]
+
+
+def _same(a, b):
+    return all(torch.equal(u.view(torch.uint8) if u.dtype == torch.bfloat16 else u,
+                           v.view(torch.uint8) if v.dtype == torch.bfloat16 else v)
+               for u, v in zip(a, b))
+
+
+def test_decode_repeats_are_bitwise_identical():
+    x = inputs.make_inputs(W)
+    ref = _decode_step(x, W)
+    for _ in range(5):
+        assert _same(ref, _decode_step(x, W))
+
+
+def test_decode_batch_invariance():
+    x = inputs.make_inputs(W)
+    full = _decode_step(x, W)
+    for b in (0, 3):
+        xb = {k: (v[b:b + 1].contiguous() if v.dim() >= 2 and v.shape[0] == W.B else v)
+              for k, v in x.items()}
+        one = _decode_step(xb, W.with_(B=1))
+        assert _same([t[b:b + 1] for t in full], one), f"sequence {b} differs at batch 1"
+
+
+def test_prefill_repeats_are_bitwise_identical():
+    w = configs.CSA_PREFILL_32K.with_(ctx=4096, Tq=4096)
+    x = inputs.make_inputs(w)
+    g = {k: v.to(dev()) for k, v in x.items()}
+    pos0 = torch.zeros(w.B, dtype=torch.int32, device=dev())
+
+    def run():
+        kc, vc, kic = ops.compress(g["k"], g["v"], g["ki"], g["g"], w.m)
+        idx = ops.indexer_topk(g["qi"], g["w"], kic, pos0, w.m, w.topk, max_pos=w.ctx - 1)
+        o = ops.sparse_attend(g["q"], kc, vc, idx, pos0, w.ctx - 1, w.window, kw=g["k"],
+                              vw=g["v"], raw_pos0=pos0, sink=g["sink"])
+        kh, vh, _ = ops.compress(g["k"], g["v"], None, g["g"], 32)    # an HCA-style m'=32 pooling
+        oh = ops.hca_attend(g["q"], kh, vh, 32, pos0, w.ctx - 1, sink=g["sink"])
+        torch.cuda.synchronize()
+        return [t.cpu() for t in (kc, vc, kic, idx, o, kh, vh, oh)]
+
+    ref = run()
+    for _ in range(3):
+        assert _same(ref, run())
+
+
+def test_decode_index_lists_with_holes():
+    # invalid entries (-1) anywhere in the list, not only as trailing padding
+    w = configs.CSA_DECODE_128K.with_(ctx=4 * 6000, B=2, topk=1024)
+    x = inputs.make_inputs(w, peaky=True)
+    rng = np.random.default_rng(11)
+    idx = np.stack([np.sort(rng.choice(6000, 1024, replace=False)) for _ in range(2)])
+    idx = idx[:, None, :].astype(np.int32)
+    idx[rng.random(idx.shape) < 0.3] = -1
+    g = {k: v.to(dev()) for k, v in x.items()}
+    pos0 = torch.full((w.B,), w.ctx - 1, dtype=torch.int32, device=dev())
+    rp0 = torch.full((w.B,), w.ctx - w.window, dtype=torch.int32, device=dev())
+    out, lse = ops.sparse_attend(g["q"], g["kc"], g["vc"], torch.from_numpy(idx).to(dev()), pos0,
+                                 w.ctx - 1, w.window, kw=g["kw"], vw=g["vw"], raw_pos0=rp0,
+                                 sink=g["sink"], return_lse=True)
+    torch.cuda.synchronize()
+    for b in range(w.B):
+        ro, rl = oracle.csa.sparse_attend(f64(x["q"][b]), f64(x["kc"][b]), f64(x["vc"][b]),
+                                          idx[b], f64(x["kw"][b]), f64(x["vw"][b]),
+                                          w.ctx - w.window, [w.ctx - 1], w.window,
+                                          f64(x["sink"]), w.scale)
+        assert_close(out[b], ro, w.dtype, f"out[{b}]", lse[b], rl)
