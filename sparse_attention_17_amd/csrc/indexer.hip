@@ -44,7 +44,15 @@ static constexpr int ROW_CHUNK = 2048;         // long-row select: entries per s
 #ifndef CSA_SCORE_CHUNK
 #define CSA_SCORE_CHUNK 2048
 #endif
-static constexpr int SCORE_CHUNK = CSA_SCORE_CHUNK;   // decode score kernels: entries per workgroup
+static constexpr int SCORE_CHUNK = CSA_SCORE_CHUNK;   // decode score kernels: entries per chunk
+#ifndef CSA_SCORE_CPW
+#define CSA_SCORE_CPW 1
+#endif
+static constexpr int SCORE_CPW = CSA_SCORE_CPW;       // chunks per score_row_kernel workgroup
+#ifndef CSA_SCORE_DEPTH
+#define CSA_SCORE_DEPTH 3
+#endif
+static constexpr int SCORE_DEPTH = CSA_SCORE_DEPTH;   // entry groups in flight per wave
 static constexpr int H1_BITS = 12;             // first radix digit (key bits 20..31)
 static constexpr int H1_BINS = 1 << H1_BITS;
 static constexpr int TOPK_NT = 512;
@@ -225,38 +233,89 @@ __device__ void find_bin(const uint32_t* hist, int nbins, uint32_t need, uint32_
   __syncthreads();
 }
 
-// End of a decode score workgroup: keep the chunk's entries at or above its
-// cut, in index order, in the chunk's candidate slots.  The cut is the 20-bit
-// key prefix (key >> 12) of the chunk's kc-th largest key, found from the
-// 12-bit digit histogram and a second 8-bit histogram inside that digit, so
-// few entries beyond kc share it.  sk holds the chunk's nloc keys, hist their
-// 12-bit digit histogram (256 threads; hist is reused).
+// Top-down search within a wave: given cnt(i) for bins [0, nb) (nb = 64*per),
+// the bin where the running count from the top first reaches `need`, and the
+// count strictly above it (all lanes get the result).
+template <typename Cnt>
+__device__ __forceinline__ void wave_top_bin(int per, uint32_t need, Cnt cnt, uint32_t& bin,
+                                             uint32_t& above) {
+  const int lane = threadIdx.x & 63;
+  const int hi = 64 * per - lane * per;
+  uint32_t local = 0;
+  for (int i = 0; i < per; ++i) local += cnt(hi - 1 - i);
+  const uint32_t incl = wave_incl_scan(local);
+  const uint32_t excl = incl - local;
+  const bool mine = excl < need && incl >= need;
+  uint32_t bb = 0, ab = 0;
+  if (mine) {
+    uint32_t cum = excl;
+    for (int i = 0; i < per; ++i) {
+      const uint32_t h = cnt(hi - 1 - i);
+      if (cum + h >= need) { bb = hi - 1 - i; ab = cum; break; }
+      cum += h;
+    }
+  }
+  const uint64_t m = __ballot(mine);
+  const int src = m ? __ffsll((unsigned long long)m) - 1 : 0;
+  bin = __shfl(bb, src, 64);
+  above = __shfl(ab, src, 64);
+}
+
+// End of a decode score workgroup (256 threads): keep the chunk's entries at
+// or above its cut, in index order, in the chunk's candidate slots.  The cut
+// is the 20-bit key prefix (key >> 12) of the chunk's kc-th largest key: its
+// 12-bit digit comes from the digit histogram (every thread first sums 16
+// bins, then each wave scans those sums), the next 8 bits from a histogram of
+// the entries inside that digit.  Every wave finds the cut by itself, so the
+// whole step needs three barriers.  sk holds the chunk's nloc keys, hist
+// their 12-bit digit histogram; cw is 256 + 256 + 4 words of scratch.
 __device__ void chunk_cut(const IndexerArgs& a, const LongWs& L, int row, int chunk, int n, int c0,
-                          int nloc, const uint32_t* sk, uint32_t* hist, uint32_t* scan,
-                          uint32_t* res) {
+                          int nloc, const uint32_t* sk, const uint32_t* hist, uint32_t* cw) {
   constexpr int PER = SCORE_CHUNK / 256;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kc = chunk_keep(a.topk, n), cap = chunk_cap_n(a.topk, n);
-  const int i0 = threadIdx.x * PER;
+  const int i0 = tid * PER;
+  uint32_t* part = cw;                                       // 256 sums of 16 digit bins
+  uint32_t* h8 = cw + 256;                                   // second-level histogram
+  uint32_t* wtot = cw + 512;                                 // per-wave counts
   uint32_t cut = 0;
   const bool dropped = nloc > kc;                            // uniform
   if (dropped) {
-    find_bin<256>(hist, H1_BINS, (uint32_t)kc, scan, res);
-    const uint32_t d1 = res[0], above = res[1];
-    hist[threadIdx.x] = 0;                                   // find_bin ended with a barrier
+    uint32_t sum = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sum += hist[16 * tid + i];
+    part[tid] = sum;
+    h8[tid] = 0;
     __syncthreads();
+    uint32_t grp, above;
+    wave_top_bin(4, (uint32_t)kc, [&](int i) { return part[i]; }, grp, above);
+    uint32_t d1, above1;
+    wave_top_bin(1, (uint32_t)kc - above, [&](int i) { return i < 16 ? hist[16 * grp + i] : 0u; }, d1, above1);
+    d1 += 16 * grp;
+    above += above1;
 #pragma unroll
     for (int q = 0; q < PER; ++q)
-      if (i0 + q < nloc && (sk[i0 + q] >> 20) == d1) atomicAdd(&hist[(sk[i0 + q] >> 12) & 255u], 1u);
+      if (i0 + q < nloc && (sk[i0 + q] >> 20) == d1) atomicAdd(&h8[(sk[i0 + q] >> 12) & 255u], 1u);
     __syncthreads();
-    find_bin<256>(hist, 256, (uint32_t)kc - above, scan, res);
-    cut = (d1 << 8) | res[0];
+    uint32_t d2, above2;
+    wave_top_bin(4, (uint32_t)kc - above, [&](int i) { return h8[i]; }, d2, above2);
+    cut = (d1 << 8) | d2;
   }
   uint32_t keep = 0;
 #pragma unroll
   for (int q = 0; q < PER; ++q)
     if (i0 + q < nloc && (sk[i0 + q] >> 12) >= cut) keep |= 1u << q;
-  uint32_t tot;
-  uint32_t pos = block_excl_scan<256>((uint32_t)__popc(keep), scan, &tot);
+  const uint32_t cnt = (uint32_t)__popc(keep);
+  const uint32_t incl = wave_incl_scan(cnt);
+  if (lane == 63) wtot[wave] = incl;
+  __syncthreads();
+  uint32_t pos = incl - cnt, tot = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t v = wtot[w];
+    pos += w < wave ? v : 0u;
+    tot += v;
+  }
   uint2* cd = reinterpret_cast<uint2*>(L.cand) + (size_t)row * L.nch * SCORE_CHUNK + (size_t)chunk * cap;
 #pragma unroll
   for (int q = 0; q < PER; ++q)
@@ -264,7 +323,7 @@ __device__ void chunk_cut(const IndexerArgs& a, const LongWs& L, int row, int ch
       if (pos < (uint32_t)cap) cd[pos] = uint2{sk[i0 + q], (uint32_t)(c0 + i0 + q)};
       ++pos;
     }
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     L.meta[((size_t)row * L.nch + chunk) * 2] = tot;
     L.meta[((size_t)row * L.nch + chunk) * 2 + 1] = dropped ? cut : CUT_ALL;
   }
@@ -359,17 +418,15 @@ __global__ __launch_bounds__(256) void score_row_kernel(IndexerArgs a) {
   using F = typename QkTraits<QK>::F;
   __shared__ uint32_t hist[H1_BINS];
   __shared__ uint32_t sk[SCORE_CHUNK];
-  __shared__ uint32_t cut_scan[4], cut_res[2];
+  __shared__ uint32_t cut_ws[516];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = blockIdx.y;
   const int b = row / a.Tq, t = row % a.Tq;
   const int n = row_len(a, b, t);
-  const int c0 = blockIdx.x * SCORE_CHUNK;
-  if (c0 >= n) return;
-  const int c1 = min(n, c0 + SCORE_CHUNK);
+  const int chunk0 = blockIdx.x * SCORE_CPW;
+  if (chunk0 * SCORE_CHUNK >= n) return;
   LongWs L = long_ws(a.ws, a.B * a.Tq, a.Nc_cap);
-  for (int i = threadIdx.x; i < H1_BINS; i += 256) hist[i] = 0;
 
   // A operands: for tile u the query's HI head rows sit at rows u*HI .. u*HI+HI-1
   const int r = lane & 15, g = lane >> 4;
@@ -398,7 +455,6 @@ __global__ __launch_bounds__(256) void score_row_kernel(IndexerArgs a) {
     if constexpr (QK == QK_FP8) wv *= reinterpret_cast<const float*>(a.qi_scale)[wi];
     wr[i] = wv;
   }
-  __syncthreads();
 
   const size_t rb = qk_row_bytes<QK>(DI);
   const char* kbase = reinterpret_cast<const char*>(a.kic) + (size_t)b * a.Nc_cap * rb;
@@ -408,10 +464,10 @@ __global__ __launch_bounds__(256) void score_row_kernel(IndexerArgs a) {
   if constexpr (QK == QK_FP8) fsc = reinterpret_cast<const float*>(a.kic_scale) + (size_t)b * a.Nc_cap;
   float* srow = L.scores + (size_t)row * nc_pad(a.Nc_cap);
 
-  // one group = EPC entries: the B fragments plus (FP8) the per-entry scales of
-  // the entries this lane will score
+  // one group = EPC entries of the chunk ending at c1: the B fragments plus
+  // (FP8) the per-entry scales of the entries this lane will score
   using R = RawFrag<QK>;
-  auto load_group = [&](int e0, R (&kb)[TPC][KC], float (&ks)[SPL]) {
+  auto load_group = [&](int e0, int c1, R (&kb)[TPC][KC], float (&ks)[SPL]) {
 #pragma unroll
     for (int u = 0; u < TPC; ++u) {
       const int e = min(e0 + 16 * u + r, c1 - 1);
@@ -427,8 +483,9 @@ __global__ __launch_bounds__(256) void score_row_kernel(IndexerArgs a) {
     }
   };
 
-  // process one group: MFMAs, ReLU + head weights, store, histogram
-  auto process = [&](int e0, const R (&cur)[TPC][KC], const float (&cscl)[SPL]) {
+  // process one group of the chunk [c0, c1): MFMAs, ReLU + head weights, store,
+  // chunk key copy and histogram
+  auto process = [&](int e0, int c0, int c1, const R (&cur)[TPC][KC], const float (&cscl)[SPL]) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < TPC; ++u)
@@ -454,24 +511,44 @@ __global__ __launch_bounds__(256) void score_row_kernel(IndexerArgs a) {
     }
   };
 
-  // DEPTH groups in flight per wave; the chunk's groups are fully unrolled
-  // and branch-free (loads clamp to the chunk, stores are masked), so the
-  // loads of later groups stay in flight while earlier ones are scored
+  // DEPTH groups in flight per wave; a chunk's groups are fully unrolled and
+  // branch-free (loads clamp to the chunk, stores are masked).  A workgroup
+  // scores SCORE_CPW consecutive chunks and requests the next chunk's first
+  // groups before cutting the current one, so the cut overlaps those loads.
   constexpr int STRIDE = 4 * EPC;
   constexpr int NG = (SCORE_CHUNK + STRIDE - 1) / STRIDE;
-  constexpr int DEPTH = NG < 3 ? NG : 3;
+  constexpr int DEPTH = NG < SCORE_DEPTH ? NG : SCORE_DEPTH;
   R kb[DEPTH][TPC][KC];
   float ks[DEPTH][SPL];
-  const int ew = c0 + wave * EPC;
+  {
+    const int c0 = chunk0 * SCORE_CHUNK, c1 = min(n, c0 + SCORE_CHUNK);
 #pragma unroll
-  for (int j = 0; j < DEPTH; ++j) load_group(ew + j * STRIDE, kb[j], ks[j]);
-#pragma unroll
-  for (int j = 0; j < NG; ++j) {
-    process(ew + j * STRIDE, kb[j % DEPTH], ks[j % DEPTH]);
-    if (j + DEPTH < NG) load_group(ew + (j + DEPTH) * STRIDE, kb[j % DEPTH], ks[j % DEPTH]);
+    for (int j = 0; j < DEPTH; ++j) load_group(c0 + wave * EPC + j * STRIDE, c1, kb[j], ks[j]);
   }
-  __syncthreads();
-  if (n > a.topk) chunk_cut(a, L, row, blockIdx.x, n, c0, c1 - c0, sk, hist, cut_scan, cut_res);
+#pragma unroll 1
+  for (int ci = 0; ci < SCORE_CPW; ++ci) {
+    const int chunk = chunk0 + ci;
+    const int c0 = chunk * SCORE_CHUNK;
+    if (c0 >= n) break;                                      // uniform
+    const int c1 = min(n, c0 + SCORE_CHUNK);
+    for (int i = threadIdx.x; i < H1_BINS; i += 256) hist[i] = 0;
+    __syncthreads();
+    const int ew = c0 + wave * EPC;
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+      process(ew + j * STRIDE, c0, c1, kb[j % DEPTH], ks[j % DEPTH]);
+      if (j + DEPTH < NG) load_group(ew + (j + DEPTH) * STRIDE, c1, kb[j % DEPTH], ks[j % DEPTH]);
+    }
+    __syncthreads();
+    const int n0 = c0 + SCORE_CHUNK;                         // the next chunk
+    if (ci + 1 < SCORE_CPW && n0 < n) {
+      const int n1 = min(n, n0 + SCORE_CHUNK);
+#pragma unroll
+      for (int j = 0; j < DEPTH; ++j) load_group(n0 + wave * EPC + j * STRIDE, n1, kb[j], ks[j]);
+    }
+    if (n > a.topk) chunk_cut(a, L, row, chunk, n, c0, c1 - c0, sk, hist, cut_ws);
+    __syncthreads();                                         // hist and sk are reused
+  }
 }
 
 // ------------------------ decode score row, native FP4 ------------------------
@@ -492,7 +569,7 @@ __global__ __launch_bounds__(256) void score_row_fp4_kernel(IndexerArgs a) {
   constexpr int RB = DI / 2;                   // bytes per packed row
   __shared__ uint32_t hist[H1_BINS];
   __shared__ uint32_t sk[SCORE_CHUNK];
-  __shared__ uint32_t cut_scan[4], cut_res[2];
+  __shared__ uint32_t cut_ws[516];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = blockIdx.y;
   const int b = row / a.Tq, t = row % a.Tq;
@@ -575,7 +652,7 @@ __global__ __launch_bounds__(256) void score_row_fp4_kernel(IndexerArgs a) {
     }
   }
   __syncthreads();
-  if (n > a.topk) chunk_cut(a, L, row, blockIdx.x, n, c0, c1 - c0, sk, hist, cut_scan, cut_res);
+  if (n > a.topk) chunk_cut(a, L, row, blockIdx.x, n, c0, c1 - c0, sk, hist, cut_ws);
 }
 
 // --------------------------- shared select helpers --------------------------
@@ -1236,12 +1313,13 @@ static void launch_scores(const IndexerArgs& a, hipStream_t st, bool long_path) 
   const int ne_ub = std::min((a.max_pos + 1) / a.m, a.Nc_cap);
   if (ne_ub <= 0) return;
   if (long_path) {
-    dim3 grid((ne_ub + SCORE_CHUNK - 1) / SCORE_CHUNK, a.B * a.Tq);
+    const int nch = (ne_ub + SCORE_CHUNK - 1) / SCORE_CHUNK;
     ProfScope ps("indexer_score", st);
     if constexpr (QK == QK_FP4 && HI == 4)
-      hipLaunchKernelGGL((score_row_fp4_kernel<DI>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((score_row_fp4_kernel<DI>), dim3(nch, a.B * a.Tq), dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((score_row_kernel<QK, DI, HI>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((score_row_kernel<QK, DI, HI>), dim3((nch + SCORE_CPW - 1) / SCORE_CPW, a.B * a.Tq),
+                         dim3(256), 0, st, a);
   } else {
     const int TT = 16 / HI;
     dim3 grid((ne_ub + SCORE_WG_ENTRIES - 1) / SCORE_WG_ENTRIES, (a.Tq + TT - 1) / TT, a.B);
