@@ -753,18 +753,22 @@ __global__ __launch_bounds__(TOPK_NT) void topk_row_kernel(IndexerArgs a) {
 static constexpr int PICK_NT = 1024;
 static constexpr int PICK_NW = PICK_NT / 64;
 static constexpr int PICK_MAXCH = 4096;        // rows up to 8M entries
-static constexpr int PICK_PER = 32;            // candidate slots per thread (registers)
+static constexpr int PICK_PER = 30;            // candidate slots per thread (registers)
 static constexpr int PICK_SLOTS = PICK_PER * PICK_NT;
+static constexpr int PICK_STASH = 16384;       // slots whose selected entry is kept in LDS
 static constexpr int PICK_BINS = 4096;         // 12-bit radix digits
 
 struct PickSmem {
   uint32_t hist[2][PICK_BINS];                 // alternating digit histograms
-  uint32_t ccnt[PICK_MAXCH];
+  uint32_t ccnt[PICK_MAXCH];                   // kept count per chunk (clamped to cap)
+  uint32_t ccut[PICK_MAXCH];                   // cut key prefix per chunk
   uint32_t bm_gt[PICK_SLOTS / 32];             // output bitmaps over slots
   uint32_t bm_eq[PICK_SLOTS / 32];
+  uint32_t sel[PICK_STASH];                    // entry index of selected slots
   uint32_t wv[4][PICK_NW];                     // per-wave partials
   uint32_t res[2];
 };
+static_assert(sizeof(TopkSmem<PICK_NT>) <= sizeof(PickSmem), "fallback select aliases PickSmem");
 
 // Slot s of a row holds (key, entry) of the (s mod cap)-th kept entry of chunk
 // s / cap; the row's slots are nch * cap long.  Thread tid holds slots
@@ -775,12 +779,35 @@ __global__ __launch_bounds__(PICK_NT) void long_pick_kernel(IndexerArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = blockIdx.x;
   const int b = row / a.Tq, t = row % a.Tq;
-  const int n = row_len(a, b, t);
   const int k = a.topk;
   const LongWs L = long_ws(a.ws, a.B * a.Tq, a.Nc_cap);
   int32_t* idx = a.idx_out + (size_t)row * k;
   float* sco = a.score_out ? a.score_out + (size_t)row * k : nullptr;
   const uint32_t* src = reinterpret_cast<const uint32_t*>(L.scores) + (size_t)row * nc_pad(a.Nc_cap);
+  const uint2* meta = reinterpret_cast<const uint2*>(L.meta) + (size_t)row * L.nch;
+  const uint2* cand = reinterpret_cast<const uint2*>(L.cand) + (size_t)row * L.nch * SCORE_CHUNK;
+  constexpr uint2 EMPTY = {0u, 0xFFFFFFFFu};
+
+  // ---- 1. chunk records and this thread's candidate slots, requested together ----
+  // The slot geometry (cap, chunks) follows from the row length, which needs
+  // pos0; the loads are first issued for the geometry of the last query
+  // position allowed by max_pos (the decode case) and redone only when the
+  // row's own geometry turns out to differ.  Every load stays inside the
+  // row's workspace: nch * cap <= L.nch * SCORE_CHUNK.
+  uint2 kv[PICK_PER], mc0;                                   // mc0: record of chunk tid
+  auto load_all = [&](int nch_, int nslot_, int per_) {
+#pragma unroll
+    for (int q = 0; q < PICK_PER; ++q)
+      if (q < per_) kv[q] = cand[min(q * PICK_NT + tid, max(nslot_ - 1, 0))];
+    mc0 = meta[min(tid, nch_ - 1)];
+  };
+  const int n_hi = max(0, min((a.max_pos + 1) / a.m, a.Nc_cap));
+  const int cap_s = chunk_cap_n(k, max(n_hi, 1));
+  const int nch_s = min((n_hi + SCORE_CHUNK - 1) / SCORE_CHUNK, min(L.nch, PICK_MAXCH));
+  const int nslot_s = nch_s * cap_s;
+  const int per_s = min((nslot_s + PICK_NT - 1) / PICK_NT, PICK_PER);
+  if (n_hi > k) load_all(nch_s, nslot_s, per_s);
+  const int n = row_len(a, b, t);
   if (n <= k) {
     write_all_eligible(n, k, src, idx, sco, PICK_NT);
     return;
@@ -788,32 +815,27 @@ __global__ __launch_bounds__(PICK_NT) void long_pick_kernel(IndexerArgs a) {
   const int nch = (n + SCORE_CHUNK - 1) / SCORE_CHUNK;
   const int cap = chunk_cap_n(k, n);
   const int lg = 31 - __clz(cap);                            // cap is a power of two
-  const uint32_t* meta = L.meta + (size_t)row * L.nch * 2;
-  const uint2* cand = reinterpret_cast<const uint2*>(L.cand) + (size_t)row * L.nch * SCORE_CHUNK;
   const int nslot = nch << lg;
   const int per = (nslot + PICK_NT - 1) / PICK_NT;
-  constexpr uint2 EMPTY = {0u, 0xFFFFFFFFu};
-  auto slot_addr = [&](int s) { return (size_t)s; };         // slots are dense: chunk c at c * cap
+  int bad = per > PICK_PER || nch > PICK_MAXCH;
+  if (!bad && (n_hi <= k || cap != cap_s || nch > nch_s))    // uniform
+    load_all(nch, nslot, per);
 
-  // ---- 1. chunk counts and this thread's candidate slots, requested together ----
-  int bad = per > PICK_PER;
-  uint2 kv[PICK_PER];
-#pragma unroll
-  for (int q = 0; q < PICK_PER; ++q)
-    if (q < per) kv[q] = cand[slot_addr(min(q * PICK_NT + tid, max(nslot - 1, 0)))];
   uint32_t part = 0;
-  for (int c = tid; c < nch; c += PICK_NT) {
-    const uint32_t m0 = meta[2 * c];
-    sm.ccnt[c] = min(m0, (uint32_t)cap);
-    bad |= m0 > (uint32_t)cap;
-    part += min(m0, (uint32_t)cap);
-  }
+  if (!bad)
+    for (int c = tid; c < nch; c += PICK_NT) {
+      const uint2 r = c == tid ? mc0 : meta[c];
+      sm.ccnt[c] = min(r.x, (uint32_t)cap);
+      sm.ccut[c] = r.y;
+      bad |= r.x > (uint32_t)cap;
+      part += min(r.x, (uint32_t)cap);
+    }
   for (int i = tid; i < PICK_SLOTS / 32; i += PICK_NT) { sm.bm_gt[i] = 0; sm.bm_eq[i] = 0; }
   __syncthreads();
 #pragma unroll
   for (int q = 0; q < PICK_PER; ++q) {
     const int s = q * PICK_NT + tid;
-    if (q >= per || s >= nslot || (s & (cap - 1)) >= (int)sm.ccnt[s >> lg]) kv[q] = EMPTY;
+    if (q >= per || s >= nslot || bad || (s & (cap - 1)) >= (int)sm.ccnt[s >> lg]) kv[q] = EMPTY;
   }
 
   // ---- 2. candidate total, key range, overflow: one block reduction ----
@@ -896,18 +918,19 @@ __global__ __launch_bounds__(PICK_NT) void long_pick_kernel(IndexerArgs a) {
   int unsafe = bad;
   if (!bad)
     for (int c = tid; c < nch; c += PICK_NT) {
-      const uint32_t cut = meta[2 * c + 1];
+      const uint32_t cut = sm.ccut[c];
       unsafe |= cut != CUT_ALL && tau < (cut << 12);
     }
-  // mark keys > tau and keys == tau in the slot bitmaps
+  // mark keys > tau and keys == tau in the slot bitmaps; keep their entries
   if (!unsafe) {
 #pragma unroll
     for (int q = 0; q < PICK_PER; ++q) {
       const uint2 v = kv[q];
       const int s = q * PICK_NT + tid;
-      if (q >= per || v.y == EMPTY.y) continue;
+      if (q >= per || v.y == EMPTY.y || v.x < tau) continue;
+      if (s < PICK_STASH) sm.sel[s] = v.y;
       if (v.x > tau) atomicOr(&sm.bm_gt[s >> 5], 1u << (s & 31));
-      else if (v.x == tau) atomicOr(&sm.bm_eq[s >> 5], 1u << (s & 31));
+      else atomicOr(&sm.bm_eq[s >> 5], 1u << (s & 31));
     }
   }
   if (__syncthreads_or(unsafe)) {
@@ -941,10 +964,9 @@ __global__ __launch_bounds__(PICK_NT) void long_pick_kernel(IndexerArgs a) {
   }
   for (; take; take &= take - 1) {
     const int s = tid * 32 + __ffs(take) - 1;
-    const uint2 v = cand[slot_addr(s)];
     if (pos < (uint32_t)k) {
-      idx[pos] = (int32_t)v.y;
-      if (sco) sco[pos] = __uint_as_float(v.x);
+      idx[pos] = (int32_t)(s < PICK_STASH ? sm.sel[s] : cand[s].y);
+      if (sco) sco[pos] = __uint_as_float(cand[s].x);
     }
     ++pos;
   }

@@ -135,6 +135,28 @@ def test_ragged_positions_per_sequence():
         _check_rows(idx[b], f64(x["qi"][b]), f64(x["w"][b]), f64(x["kic"][b]), [pos[b]], 4, 256)
 
 
+@pytest.mark.parametrize("qk", ["bf16", "fp8"])
+def test_long_rows_ragged_positions(qk):
+    # long rows at different positions: rows whose chunk count and per-chunk
+    # slot capacity differ from those of the last allowed position, and a row
+    # with fewer eligible entries than k
+    w = configs.CSA_DECODE_128K.with_(ctx=4 * 40000, B=4, topk=1024, qk_dtype=qk)
+    x = inputs.make_inputs(w)
+    g = {k: v.to(dev()) for k, v in x.items()}
+    pos = [4 * 40000 - 1, 4 * 20000 + 1, 4 * 13000, 4 * 900 + 3]
+    pos0 = torch.tensor(pos, dtype=torch.int32, device=dev())
+    idx = ops.indexer_topk(g["qi"], g["w"], g["kic"], pos0, w.m, w.topk, max_pos=max(pos),
+                           qi_scale=g.get("qi_scale"), kic_scale=g.get("kic_scale"),
+                           qk_dtype=qk).cpu().numpy()
+    qi = _dequant(x, "qi", qk)
+    kic = _dequant(x, "kic", qk)
+    exact = 0
+    for b in range(w.B):
+        exact += _check_rows(idx[b], qi[b], f64(x["w"][b]), kic[b], [pos[b]], w.m, w.topk)[0]
+    assert exact >= w.B - 1
+    assert np.all(idx[3, 0, :901] == np.arange(901)) and np.all(idx[3, 0, 901:] == -1)
+
+
 def test_long_rows_all_tied_fall_back_exactly():
     # every score is 0: the boundary bin holds the whole row, which overflows the
     # candidate buffer; the exact fallback must return the lowest indices
