@@ -50,6 +50,8 @@ def parse():
     p.add_argument("--graph", type=int, default=0, help="replay the step as a HIP graph")
     p.add_argument("--overlap", type=int, default=0,
                    help="run the HCA branch on a second stream, concurrently with the CSA chain")
+    p.add_argument("--pair", type=int, default=1,
+                   help="run CSA and HCA attention through csa_hybrid_attend (one launch)")
     p.add_argument("--cpu-workers", type=int, default=0)
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run three 256 MiB device copies (known traffic for counter scaling)")
@@ -164,6 +166,7 @@ def algorithmic_bytes(w):
         "indexer_topk": B * w.topk * 4,
         "attend_csa": B * (nk_csa * 2 * d * 2 + 2 * H * d * 2),
         "attend_hca": B * (w.Nc_hca * 2 * d * 2 + 2 * H * d * 2),
+        "attend_pair": B * ((nk_csa + w.Nc_hca) * 2 * d * 2 + 4 * H * d * 2),
     }
 
 
@@ -285,11 +288,18 @@ def main():
         idx = ops.indexer_topk(g["qi"], g["w"], g["kic"], pos0, w.m, w.topk, max_pos=w.ctx - 1,
                                qi_scale=g.get("qi_scale"), kic_scale=g.get("kic_scale"),
                                qk_dtype=qk)
-        o1 = ops.sparse_attend(g["q"], g["kc"], g["vc"], idx, pos0, w.ctx - 1, w.window,
-                               kw=g["kw"], vw=g["vw"], raw_pos0=rp0, sink=g["sink"])
+        csa = dict(q=g["q"], kc=g["kc"], vc=g["vc"], idx=idx, pos0=pos0, max_pos=w.ctx - 1,
+                   window=w.window, kw=g["kw"], vw=g["vw"], raw_pos0=rp0, sink=g["sink"])
         if overlap:
+            o1 = ops.sparse_attend(**csa)
             cur.wait_stream(side)
+        elif args.pair:
+            # both attention problems in one launch (plus one split merge)
+            o1, o2 = ops.hybrid_attend(csa, dict(q=g["q_hca"], kc=g["kc_hca"], vc=g["vc_hca"],
+                                                 m_prime=w.m_hca, pos0=pos0, max_pos=w.ctx - 1,
+                                                 sink=g["sink_hca"]))
         else:
+            o1 = ops.sparse_attend(**csa)
             o2 = hca(g)
         return o1, o2
 
@@ -341,7 +351,7 @@ def main():
     import ctypes as C
     kern = {}
     for name in ("indexer_score", "indexer_topk", "attend_csa",
-                 "attend_hca", "attend_combine"):
+                 "attend_hca", "attend_pair", "attend_combine"):
         n, t = C.c_int(0), C.c_double(0)
         if lib.csa_profile_query(name.encode(), C.byref(n), C.byref(t)) == 0:
             kern[name] = t.value / n.value * 1e3          # us per launch
@@ -354,7 +364,7 @@ def main():
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom,
             "bytes_per_launch": alg[dom], "us_per_launch": round(kern[dom], 2)}
-    step_bytes = sum(alg.values())
+    step_bytes = sum(v for k, v in alg.items() if k != "attend_pair")   # pair = csa + hca
 
     # parity of the GPU step against the oracle outputs (when the baseline ran)
     parity = None
@@ -376,6 +386,7 @@ def main():
                    "indexer": f"{w.qk_dtype} {w.HI}x{w.dI}", "hca_m": w.m_hca,
                    "hca_entries": w.Nc_hca, "heads": w.H, "head_dim": w.d,
                    "graph": bool(args.graph), "hca_branch_concurrent": bool(args.overlap),
+                   "attention_pair_launch": bool(args.pair and not args.overlap),
                    "rotating_copies": args.rotate},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -180,6 +180,38 @@ csa_status_t hca_attend(const void *q, const void *kc, const void *vc, int m_pri
                         void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * csa_hybrid_attend — the CSA attention and the HCA attention of one hybrid
+ * layer pair (hyper.ai "Method": a CSA layer and an HCA layer side by side,
+ * each with its sliding-window branch) in one call.
+ *
+ *   The first 24 arguments are those of csa_sparse_attend and the next 23
+ *   those of hca_attend (each prefixed h), with the same meaning, layout and
+ *   validation; each problem has its own workspace, sized by its own query
+ *   (csa_sparse_attend_workspace / hca_attend_workspace), and the two must not
+ *   overlap; out and hout must be different buffers.
+ *   When both problems are split decode (Tq = 1) with the same dtype, head
+ *   dim and query-head tile shape, one kernel runs the workgroups of both,
+ *   with the key lists cut into 256-key (CSA) and 384-key (HCA) splits
+ *   (longer than the separate calls' 128 and 256), and one kernel merges the
+ *   split partials of both: results then equal those of the separate calls up
+ *   to the rounding of the split merge, and, like theirs, do not depend on
+ *   the batch size.  Otherwise the two calls run one after the other on
+ *   `stream`, with bit-identical results.  An error in either part launches
+ *   nothing; the error text names the part.
+ */
+csa_status_t csa_hybrid_attend(
+    const void *q, const void *kc, const void *vc, const int32_t *idx, int topk,
+    const void *kw, const void *vw, const int32_t *raw_pos0, int R,
+    const int32_t *pos0, int max_pos, int window, const float *sink, float softmax_scale,
+    int B, int Tq, int H, int d, int Nc_cap, csa_dtype_t dt, void *out, float *lse_out,
+    void *workspace, size_t workspace_bytes,
+    const void *hq, const void *hkc, const void *hvc, int m_prime, int hNc_cap,
+    const void *hkw, const void *hvw, const int32_t *hraw_pos0, int hR, int hwindow,
+    const int32_t *hpos0, int hmax_pos, const float *hsink, float hsoftmax_scale,
+    int hB, int hTq, int hH, int hd, csa_dtype_t hdt, void *hout, float *hlse_out,
+    void *hworkspace, size_t hworkspace_bytes, void *stream);
+
+/*
  * Launch timing, for measurement tools (not part of any computation).
  * While enabled, every kernel launch made by the library is bracketed by a
  * pair of hipEvents recorded on that launch's stream.  csa_profile_query
@@ -188,7 +220,8 @@ csa_status_t hca_attend(const void *q, const void *kc, const void *vc, int m_pri
  * recorded, -1 on a HIP error.  Kernel names: "compress", "indexer_score"
  * (decode scores and per-chunk cut), "indexer_topk" (row select),
  * "indexer_fused" (prefill scores and select in one kernel), "attend_csa",
- * "attend_hca", "attend_combine".
+ * "attend_hca", "attend_pair" (both of csa_hybrid_attend in one kernel),
+ * "attend_combine".
  * csa_profile_reset forgets all records (events are kept for reuse).
  */
 void csa_profile_enable(int on);

@@ -196,12 +196,16 @@ static csa_status_t check_attend_common(const void* q, const void* kc, const voi
   return ok();
 }
 
-csa_status_t csa_sparse_attend(const void* q, const void* kc, const void* vc, const int32_t* idx,
-                               int topk, const void* kw, const void* vw, const int32_t* raw_pos0,
-                               int R, const int32_t* pos0, int max_pos, int window,
-                               const float* sink, float softmax_scale, int B, int Tq, int H, int d,
-                               int Nc_cap, csa_dtype_t dt, void* out, float* lse_out,
-                               void* workspace, size_t workspace_bytes, void* stream) {
+// Validation and argument packing shared by csa_sparse_attend and
+// csa_hybrid_attend; *empty is set when there is nothing to compute.
+static csa_status_t build_sparse(const void* q, const void* kc, const void* vc, const int32_t* idx,
+                                 int topk, const void* kw, const void* vw, const int32_t* raw_pos0,
+                                 int R, const int32_t* pos0, int max_pos, int window,
+                                 const float* sink, float softmax_scale, int B, int Tq, int H, int d,
+                                 int Nc_cap, csa_dtype_t dt, void* out, float* lse_out,
+                                 void* workspace, size_t workspace_bytes, csa::AttendArgs* a,
+                                 bool* empty) {
+  *empty = true;
   REQUIRE(topk >= 1 && topk <= 4096, CSA_INVALID_ARGUMENT, "topk must be in [1, 4096] (got %d)", topk);
   REQUIRE(softmax_scale > 0.f && softmax_scale < 1e30f, CSA_INVALID_ARGUMENT,
           "softmax_scale must be positive and finite (got %g)", (double)softmax_scale);
@@ -213,22 +217,39 @@ csa_status_t csa_sparse_attend(const void* q, const void* kc, const void* vc, co
   REQUIRE(workspace_bytes >= need, CSA_WORKSPACE_TOO_SMALL,
           "workspace holds %zu bytes, %zu needed", workspace_bytes, need);
   if (need) REQUIRE_PTR(workspace, "workspace");
-  csa::AttendArgs a{};
-  a.sparse = true; a.q = q; a.kc = kc; a.vc = vc; a.idx = idx; a.topk = topk; a.m_prime = 1;
-  a.kw = window > 0 ? kw : nullptr; a.vw = window > 0 ? vw : nullptr;
-  a.raw_pos0 = window > 0 ? raw_pos0 : nullptr; a.R = window > 0 ? R : 0; a.window = window;
-  a.pos0 = pos0; a.max_pos = max_pos; a.sink = sink; a.scale = softmax_scale;
-  a.B = B; a.Tq = Tq; a.H = H; a.d = d; a.Nc_cap = Nc_cap; a.f32 = dt == CSA_F32;
-  a.out = out; a.lse = lse_out; a.ws = workspace;
+  *a = csa::AttendArgs{};
+  a->sparse = true; a->q = q; a->kc = kc; a->vc = vc; a->idx = idx; a->topk = topk; a->m_prime = 1;
+  a->kw = window > 0 ? kw : nullptr; a->vw = window > 0 ? vw : nullptr;
+  a->raw_pos0 = window > 0 ? raw_pos0 : nullptr; a->R = window > 0 ? R : 0; a->window = window;
+  a->pos0 = pos0; a->max_pos = max_pos; a->sink = sink; a->scale = softmax_scale;
+  a->B = B; a->Tq = Tq; a->H = H; a->d = d; a->Nc_cap = Nc_cap; a->f32 = dt == CSA_F32;
+  a->out = out; a->lse = lse_out; a->ws = workspace;
+  *empty = false;
+  return ok();
+}
+
+csa_status_t csa_sparse_attend(const void* q, const void* kc, const void* vc, const int32_t* idx,
+                               int topk, const void* kw, const void* vw, const int32_t* raw_pos0,
+                               int R, const int32_t* pos0, int max_pos, int window,
+                               const float* sink, float softmax_scale, int B, int Tq, int H, int d,
+                               int Nc_cap, csa_dtype_t dt, void* out, float* lse_out,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  csa::AttendArgs a;
+  bool empty;
+  const csa_status_t st = build_sparse(q, kc, vc, idx, topk, kw, vw, raw_pos0, R, pos0, max_pos,
+                                       window, sink, softmax_scale, B, Tq, H, d, Nc_cap, dt, out,
+                                       lse_out, workspace, workspace_bytes, &a, &empty);
+  if (st != CSA_OK || empty) return st;
   return device_status(csa::launch_attend(a, (hipStream_t)stream), "csa_sparse_attend launch");
 }
 
-csa_status_t hca_attend(const void* q, const void* kc, const void* vc, int m_prime, int Nc_cap,
-                        const void* kw, const void* vw, const int32_t* raw_pos0, int R,
-                        int window, const int32_t* pos0, int max_pos, const float* sink,
-                        float softmax_scale, int B, int Tq, int H, int d, csa_dtype_t dt,
-                        void* out, float* lse_out, void* workspace, size_t workspace_bytes,
-                        void* stream) {
+static csa_status_t build_hca(const void* q, const void* kc, const void* vc, int m_prime, int Nc_cap,
+                              const void* kw, const void* vw, const int32_t* raw_pos0, int R,
+                              int window, const int32_t* pos0, int max_pos, const float* sink,
+                              float softmax_scale, int B, int Tq, int H, int d, csa_dtype_t dt,
+                              void* out, float* lse_out, void* workspace, size_t workspace_bytes,
+                              csa::AttendArgs* a, bool* empty) {
+  *empty = true;
   REQUIRE(m_prime >= 1, CSA_INVALID_ARGUMENT, "m_prime must be >= 1");
   REQUIRE(softmax_scale > 0.f && softmax_scale < 1e30f, CSA_INVALID_ARGUMENT,
           "softmax_scale must be positive and finite (got %g)", (double)softmax_scale);
@@ -239,14 +260,65 @@ csa_status_t hca_attend(const void* q, const void* kc, const void* vc, int m_pri
   REQUIRE(workspace_bytes >= need, CSA_WORKSPACE_TOO_SMALL,
           "workspace holds %zu bytes, %zu needed", workspace_bytes, need);
   if (need) REQUIRE_PTR(workspace, "workspace");
-  csa::AttendArgs a{};
-  a.sparse = false; a.q = q; a.kc = kc; a.vc = vc; a.idx = nullptr; a.topk = 0; a.m_prime = m_prime;
-  a.kw = window > 0 ? kw : nullptr; a.vw = window > 0 ? vw : nullptr;
-  a.raw_pos0 = window > 0 ? raw_pos0 : nullptr; a.R = window > 0 ? R : 0; a.window = window;
-  a.pos0 = pos0; a.max_pos = max_pos; a.sink = sink; a.scale = softmax_scale;
-  a.B = B; a.Tq = Tq; a.H = H; a.d = d; a.Nc_cap = Nc_cap; a.f32 = dt == CSA_F32;
-  a.out = out; a.lse = lse_out; a.ws = workspace;
+  *a = csa::AttendArgs{};
+  a->sparse = false; a->q = q; a->kc = kc; a->vc = vc; a->idx = nullptr; a->topk = 0; a->m_prime = m_prime;
+  a->kw = window > 0 ? kw : nullptr; a->vw = window > 0 ? vw : nullptr;
+  a->raw_pos0 = window > 0 ? raw_pos0 : nullptr; a->R = window > 0 ? R : 0; a->window = window;
+  a->pos0 = pos0; a->max_pos = max_pos; a->sink = sink; a->scale = softmax_scale;
+  a->B = B; a->Tq = Tq; a->H = H; a->d = d; a->Nc_cap = Nc_cap; a->f32 = dt == CSA_F32;
+  a->out = out; a->lse = lse_out; a->ws = workspace;
+  *empty = false;
+  return ok();
+}
+
+csa_status_t hca_attend(const void* q, const void* kc, const void* vc, int m_prime, int Nc_cap,
+                        const void* kw, const void* vw, const int32_t* raw_pos0, int R,
+                        int window, const int32_t* pos0, int max_pos, const float* sink,
+                        float softmax_scale, int B, int Tq, int H, int d, csa_dtype_t dt,
+                        void* out, float* lse_out, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  csa::AttendArgs a;
+  bool empty;
+  const csa_status_t st = build_hca(q, kc, vc, m_prime, Nc_cap, kw, vw, raw_pos0, R, window, pos0,
+                                    max_pos, sink, softmax_scale, B, Tq, H, d, dt, out, lse_out,
+                                    workspace, workspace_bytes, &a, &empty);
+  if (st != CSA_OK || empty) return st;
   return device_status(csa::launch_attend(a, (hipStream_t)stream), "hca_attend launch");
+}
+
+csa_status_t csa_hybrid_attend(
+    const void* q, const void* kc, const void* vc, const int32_t* idx, int topk, const void* kw,
+    const void* vw, const int32_t* raw_pos0, int R, const int32_t* pos0, int max_pos, int window,
+    const float* sink, float softmax_scale, int B, int Tq, int H, int d, int Nc_cap, csa_dtype_t dt,
+    void* out, float* lse_out, void* workspace, size_t workspace_bytes,
+    const void* hq, const void* hkc, const void* hvc, int m_prime, int hNc_cap, const void* hkw,
+    const void* hvw, const int32_t* hraw_pos0, int hR, int hwindow, const int32_t* hpos0,
+    int hmax_pos, const float* hsink, float hsoftmax_scale, int hB, int hTq, int hH, int hd,
+    csa_dtype_t hdt, void* hout, float* hlse_out, void* hworkspace, size_t hworkspace_bytes,
+    void* stream) {
+  csa::AttendArgs ac, ah;
+  bool ec, eh;
+  csa_status_t st = build_sparse(q, kc, vc, idx, topk, kw, vw, raw_pos0, R, pos0, max_pos, window,
+                                 sink, softmax_scale, B, Tq, H, d, Nc_cap, dt, out, lse_out,
+                                 workspace, workspace_bytes, &ac, &ec);
+  if (st != CSA_OK) return fail(st, "CSA part: %s", g_err.c_str());
+  st = build_hca(hq, hkc, hvc, m_prime, hNc_cap, hkw, hvw, hraw_pos0, hR, hwindow, hpos0, hmax_pos,
+                 hsink, hsoftmax_scale, hB, hTq, hH, hd, hdt, hout, hlse_out, hworkspace,
+                 hworkspace_bytes, &ah, &eh);
+  if (st != CSA_OK) return fail(st, "HCA part: %s", g_err.c_str());
+  if (!ec && !eh) {
+    const size_t nc = csa::attend_workspace(true, B, Tq, H, d, topk, window, Nc_cap, 1, max_pos);
+    const size_t nh = csa::attend_workspace(false, hB, hTq, hH, hd, 0, hwindow, hNc_cap, m_prime, hmax_pos);
+    const uintptr_t c0 = (uintptr_t)workspace, h0 = (uintptr_t)hworkspace;
+    REQUIRE(nc == 0 || nh == 0 || c0 + nc <= h0 || h0 + nh <= c0, CSA_INVALID_ARGUMENT,
+            "the CSA and HCA workspaces overlap");
+    REQUIRE(out != hout, CSA_INVALID_ARGUMENT, "the CSA and HCA outputs are the same buffer");
+  }
+  hipError_t e = hipSuccess;
+  if (!ec && !eh) e = csa::launch_attend_pair(ac, ah, (hipStream_t)stream);
+  else if (!ec) e = csa::launch_attend(ac, (hipStream_t)stream);
+  else if (!eh) e = csa::launch_attend(ah, (hipStream_t)stream);
+  return device_status(e, "csa_hybrid_attend launch");
 }
 
 }  // extern "C"

@@ -56,8 +56,11 @@ __device__ __forceinline__ int vt_block(int dim, int kb) { return kb ^ ((dim >> 
 // are merged in LDS at the end).  PF key tiles are in flight ahead of the one
 // being computed (PF=2 for split decode, whose workgroups hold two tiles: all
 // of a workgroup's keys are then requested at once).
+// The body takes its workgroup's coordinates (token tile bx, split by,
+// sequence bz) and the dynamic LDS block from the kernel that runs it.
 template <typename T, int D, int RW, int KG, bool SPARSE, int PF>
-__global__ __launch_bounds__(RW * KG * 64) __attribute__((amdgpu_waves_per_eu(PF == 1 ? 2 : 1))) void attend_kernel(AttendArgs a, AttnGeom gm) {
+__device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom& gm, int bx, int by,
+                                            int bz, unsigned char* smem_raw) {
   constexpr int NW = RW * KG;
   constexpr int NT = NW * 64;
   constexpr int NSUB = 2 / KG;                 // 32-key sub-tiles per wave per tile
@@ -69,7 +72,6 @@ __global__ __launch_bounds__(RW * KG * 64) __attribute__((amdgpu_waves_per_eu(PF
   constexpr int DSTEP = D / 16;                // k-steps of S^T
   constexpr int DVT = D / 32;                  // 32-wide dv tiles of O^T
 
-  extern __shared__ __align__(16) unsigned char smem_raw[];
   T* Ks = reinterpret_cast<T*>(smem_raw);
   T* Vt = Ks + KT * KS;
   int* sel = reinterpret_cast<int*>(Vt + D * VS);
@@ -79,8 +81,8 @@ __global__ __launch_bounds__(RW * KG * 64) __attribute__((amdgpu_waves_per_eu(PF
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rw = wave % RW, kg = wave / RW;
   const int half = lane >> 5, col = lane & 31;
-  const int b = blockIdx.z, split = blockIdx.y;
-  const int t0 = blockIdx.x * gm.TT;
+  const int b = bz, split = by;
+  const int t0 = bx * gm.TT;
   const int tl = min(t0 + gm.TT, a.Tq) - 1;
   const int p0 = a.pos0[b];
   const int pos_first = p0 + t0, pos_last = p0 + tl;
@@ -486,16 +488,41 @@ __global__ __launch_bounds__(RW * KG * 64) __attribute__((amdgpu_waves_per_eu(PF
   if (a.lse && half == 0) a.lse[grow] = lse;
 }
 
+template <typename T, int D, int RW, int KG, bool SPARSE, int PF>
+__global__ __launch_bounds__(RW * KG * 64) __attribute__((amdgpu_waves_per_eu(PF == 1 ? 2 : 1))) void attend_kernel(AttendArgs a, AttnGeom gm) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  attend_body<T, D, RW, KG, SPARSE, PF>(a, gm, blockIdx.x, blockIdx.y, blockIdx.z, smem_raw);
+}
+
+// The HCA and CSA attention of one layer pair in a single split-decode launch:
+// a 1-D grid whose first nb0 workgroups run the HCA problem a0 and the rest the
+// CSA problem a1 (each decomposed as its own (tile, split, sequence) grid).  The
+// HCA workgroups, which hold more keys each, are dispatched first; the CSA ones
+// fill the compute units the HCA grid leaves free.
+template <typename T, int D, int RW, int KG>
+__global__ __launch_bounds__(RW * KG * 64) __attribute__((amdgpu_waves_per_eu(1))) void attend_pair_kernel(
+    AttendArgs a0, AttnGeom g0, AttendArgs a1, AttnGeom g1, int nb0) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  int bid = blockIdx.x;
+  if (bid < nb0) {
+    const int gx = (a0.Tq + g0.TT - 1) / g0.TT;
+    attend_body<T, D, RW, KG, false, 2>(a0, g0, bid % gx, (bid / gx) % g0.nsplit, bid / (gx * g0.nsplit), smem_raw);
+  } else {
+    bid -= nb0;
+    const int gx = (a1.Tq + g1.TT - 1) / g1.TT;
+    attend_body<T, D, RW, KG, true, 2>(a1, g1, bid % gx, (bid / gx) % g1.nsplit, bid / (gx * g1.nsplit), smem_raw);
+  }
+}
+
 // Merge split partials in fixed split order (one wave per query row).  The
 // partials of CB splits are requested together; a running maximum rescales
 // the sums between batches, so the result depends only on the split list.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void combine_kernel(AttendArgs a, int nsplit) {
+__device__ __forceinline__ void combine_row(const AttendArgs& a, int nsplit, size_t row) {
   constexpr int PER = D / 64;
   constexpr int CB = 32;
   const int lane = threadIdx.x & 63;
   const size_t rows_total = (size_t)a.B * a.Tq * a.H;
-  const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows_total) return;
   const float* po = reinterpret_cast<const float*>(a.ws);
   const float* pm = po + (size_t)nsplit * rows_total * D;
@@ -507,15 +534,21 @@ __global__ __launch_bounds__(256) void combine_kernel(AttendArgs a, int nsplit) 
 #pragma unroll
   for (int u = 0; u < PER; ++u) acc[u] = 0.f;
   for (int s0 = 0; s0 < nsplit; s0 += CB) {
+    // every load is unconditional (split indices past the end repeat the last
+    // split, whose weight is then zero), so all of them are in flight together
     float v[CB][PER];
-    const float mv = lane < CB && s0 + lane < nsplit ? pm[(s0 + lane) * rows_total + row] : -INFINITY;
-    const float lv = lane < CB && s0 + lane < nsplit ? pl[(s0 + lane) * rows_total + row] : 0.f;
+    const int sl = min(s0 + (lane & (CB - 1)), nsplit - 1);
+    const bool lv_ok = lane < CB && s0 + lane < nsplit;
+    const float mraw = pm[(size_t)sl * rows_total + row];
+    const float lraw = pl[(size_t)sl * rows_total + row];
 #pragma unroll
     for (int j = 0; j < CB; ++j) {
-      const float* src = po + ((s0 + j) * rows_total + row) * D + lane * PER;
+      const float* src = po + ((size_t)min(s0 + j, nsplit - 1) * rows_total + row) * D + lane * PER;
 #pragma unroll
-      for (int u = 0; u < PER; ++u) v[j][u] = s0 + j < nsplit ? src[u] : 0.f;
+      for (int u = 0; u < PER; ++u) v[j][u] = src[u];
     }
+    const float mv = lv_ok ? mraw : -INFINITY;
+    const float lv = lv_ok ? lraw : 0.f;
     const float M_new = fmaxf(M, wave_max(mv));
     if (M_new == -INFINITY) continue;
     const float r = __builtin_amdgcn_exp2f(M - M_new);      // M = -inf -> 0
@@ -544,11 +577,29 @@ __global__ __launch_bounds__(256) void combine_kernel(AttendArgs a, int nsplit) 
   if (a.lse && lane == 0) a.lse[row] = lse;
 }
 
+template <typename T, int D>
+__global__ __launch_bounds__(256) void combine_kernel(AttendArgs a, int nsplit) {
+  combine_row<T, D>(a, nsplit, (size_t)blockIdx.x * 4 + (threadIdx.x >> 6));
+}
+
+// Both problems of a pair launch: workgroups below nb0 merge a0's rows.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void combine_pair_kernel(AttendArgs a0, int ns0, AttendArgs a1, int ns1,
+                                                           int nb0) {
+  if ((int)blockIdx.x < nb0) combine_row<T, D>(a0, ns0, (size_t)blockIdx.x * 4 + (threadIdx.x >> 6));
+  else combine_row<T, D>(a1, ns1, (size_t)(blockIdx.x - nb0) * 4 + (threadIdx.x >> 6));
+}
+
 // ---------------------------------- host -----------------------------------
 static int keys_per_split(bool sparse, int Tq) {
   if (Tq != 1) return INT_MAX / 2;
   return sparse ? 128 : 256;
 }
+
+// keys per split in a paired decode launch (gathered CSA rows take longer per
+// tile than the contiguous HCA blocks, so CSA splits are shorter)
+static constexpr int PAIR_KPS_CSA = 4 * KT;
+static constexpr int PAIR_KPS_HCA = 6 * KT;
 
 static int tokens_per_tile(bool sparse, int H, int Tq) {
   if (sparse) return 1;
@@ -570,27 +621,38 @@ size_t attend_workspace(bool sparse, int B, int Tq, int H, int d, int topk, int 
   return (size_t)ns * B * Tq * H * (d + 2) * sizeof(float);
 }
 
-template <typename T, int D, int RW, int KG, bool SPARSE, int PF>
-static hipError_t launch5(const AttendArgs& a, const AttnGeom& gm, hipStream_t st) {
+template <typename T, int D, bool SPARSE>
+static size_t attend_lds(const AttendArgs& a, int RW, int KG) {
   constexpr int KS = D + 16 / sizeof(T);
   constexpr int VS = KT + 4;
   size_t lds = (size_t)(KT * KS + D * VS) * sizeof(T) + (SPARSE ? (size_t)a.topk * 4 : 0);
   if (KG == 2) lds = std::max(lds, (size_t)RW * 64 * ((D / 32) * 16 + 2) * sizeof(float));
+  return lds;
+}
+
+template <typename K>
+static hipError_t set_lds(K kfn, size_t lds) {
+  if (lds <= 65536) return hipSuccess;
+  return hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+}
+
+static size_t partial_rows(const AttendArgs& a) { return (size_t)a.B * a.Tq * a.H; }
+
+template <typename T, int D, int RW, int KG, bool SPARSE, int PF>
+static hipError_t launch5(const AttendArgs& a, const AttnGeom& gm, hipStream_t st) {
+  const size_t lds = attend_lds<T, D, SPARSE>(a, RW, KG);
   auto kfn = attend_kernel<T, D, RW, KG, SPARSE, PF>;
-  if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
+  hipError_t e = set_lds(kfn, lds);
+  if (e != hipSuccess) return e;
   dim3 grid((a.Tq + gm.TT - 1) / gm.TT, gm.nsplit, a.B);
   {
     ProfScope ps(SPARSE ? "attend_csa" : "attend_hca", st);
     hipLaunchKernelGGL(kfn, grid, dim3(RW * KG * 64), lds, st, a, gm);
   }
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess || gm.nsplit <= 1) return e;
-  const size_t rows = (size_t)a.B * a.Tq * a.H;
   ProfScope ps("attend_combine", st);
-  hipLaunchKernelGGL((combine_kernel<T, D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st,
+  hipLaunchKernelGGL((combine_kernel<T, D>), dim3((unsigned)((partial_rows(a) + 3) / 4)), dim3(256), 0, st,
                      a, gm.nsplit);
   return hipGetLastError();
 }
@@ -602,12 +664,20 @@ static hipError_t launch4(const AttendArgs& a, const AttnGeom& gm, hipStream_t s
 
 // Row-waves cover the tile's (token, head) rows; tiles of at most 64 rows get
 // a second key group so that four waves share every staged tile.
+static void wave_shape(int rows, int* RW, int* KG) {
+  if (rows <= 32) { *RW = 1; *KG = 2; }
+  else if (rows <= 64) { *RW = 2; *KG = 2; }
+  else if (rows <= 96) { *RW = 3; *KG = 1; }
+  else { *RW = 4; *KG = 1; }
+}
+
 template <typename T, int D, bool SPARSE>
 static hipError_t launch3(const AttendArgs& a, const AttnGeom& gm, hipStream_t st) {
-  const int rows = gm.TT * a.H;
-  if (rows <= 32) return launch4<T, D, 1, 2, SPARSE>(a, gm, st);
-  if (rows <= 64) return launch4<T, D, 2, 2, SPARSE>(a, gm, st);
-  if (rows <= 96) return launch4<T, D, 3, 1, SPARSE>(a, gm, st);
+  int RW, KG;
+  wave_shape(gm.TT * a.H, &RW, &KG);
+  if (RW == 1) return launch4<T, D, 1, 2, SPARSE>(a, gm, st);
+  if (RW == 2) return launch4<T, D, 2, 2, SPARSE>(a, gm, st);
+  if (RW == 3) return launch4<T, D, 3, 1, SPARSE>(a, gm, st);
   return launch4<T, D, 4, 1, SPARSE>(a, gm, st);
 }
 
@@ -616,17 +686,85 @@ static hipError_t launch2(const AttendArgs& a, const AttnGeom& gm, hipStream_t s
   return a.sparse ? launch3<T, D, true>(a, gm, st) : launch3<T, D, false>(a, gm, st);
 }
 
-hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
-  if (a.B == 0 || a.Tq == 0) return hipSuccess;
+static AttnGeom make_geom(const AttendArgs& a, int kps_override = 0) {
   AttnGeom gm;
   gm.TT = tokens_per_tile(a.sparse, a.H, a.Tq);
-  const int kps = keys_per_split(a.sparse, a.Tq);
+  const int kps = kps_override > 0 ? kps_override : keys_per_split(a.sparse, a.Tq);
   const long nk = nkeys_upper(a.sparse, a.topk, a.window, a.Nc_cap, a.m_prime, a.max_pos);
   gm.nsplit = (int)std::max(1L, (nk + kps - 1) / kps);
   gm.kps = gm.nsplit > 1 ? kps : INT_MAX / 2;
   gm.scale_log2 = a.scale * LOG2E;
+  return gm;
+}
+
+hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
+  if (a.B == 0 || a.Tq == 0) return hipSuccess;
+  const AttnGeom gm = make_geom(a);
   if (a.f32) return a.d == 64 ? launch2<float, 64>(a, gm, st) : launch2<float, 128>(a, gm, st);
   return a.d == 64 ? launch2<bf16, 64>(a, gm, st) : launch2<bf16, 128>(a, gm, st);
+}
+
+template <typename T, int D, int RW, int KG>
+static hipError_t launch_pair4(const AttendArgs& h, const AttnGeom& gh, const AttendArgs& c,
+                               const AttnGeom& gc, hipStream_t st) {
+  const size_t lds = std::max(attend_lds<T, D, false>(h, RW, KG), attend_lds<T, D, true>(c, RW, KG));
+  auto kfn = attend_pair_kernel<T, D, RW, KG>;
+  hipError_t e = set_lds(kfn, lds);
+  if (e != hipSuccess) return e;
+  const long nbh = (long)((h.Tq + gh.TT - 1) / gh.TT) * gh.nsplit * h.B;
+  const long nbc = (long)((c.Tq + gc.TT - 1) / gc.TT) * gc.nsplit * c.B;
+  {
+    ProfScope ps("attend_pair", st);
+    hipLaunchKernelGGL(kfn, dim3((unsigned)(nbh + nbc)), dim3(RW * KG * 64), lds, st, h, gh, c, gc, (int)nbh);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // a problem left with one split wrote its output directly
+  const long cbh = gh.nsplit > 1 ? (long)((partial_rows(h) + 3) / 4) : 0;
+  const long cbc = gc.nsplit > 1 ? (long)((partial_rows(c) + 3) / 4) : 0;
+  if (cbh + cbc == 0) return hipSuccess;
+  ProfScope ps("attend_combine", st);
+  hipLaunchKernelGGL((combine_pair_kernel<T, D>), dim3((unsigned)(cbh + cbc)), dim3(256), 0, st,
+                     h, gh.nsplit, c, gc.nsplit, (int)cbh);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_pair2(const AttendArgs& h, const AttnGeom& gh, const AttendArgs& c,
+                               const AttnGeom& gc, int RW, hipStream_t st) {
+  if (RW == 1) return launch_pair4<T, D, 1, 2>(h, gh, c, gc, st);
+  if (RW == 2) return launch_pair4<T, D, 2, 2>(h, gh, c, gc, st);
+  if (RW == 3) return launch_pair4<T, D, 3, 1>(h, gh, c, gc, st);
+  return launch_pair4<T, D, 4, 1>(h, gh, c, gc, st);
+}
+
+hipError_t launch_attend_pair(const AttendArgs& csa_a, const AttendArgs& hca_a, hipStream_t st) {
+  if (csa_a.B == 0 || csa_a.Tq == 0) return launch_attend(hca_a, st);
+  if (hca_a.B == 0 || hca_a.Tq == 0) return launch_attend(csa_a, st);
+  AttnGeom gc = make_geom(csa_a), gh = make_geom(hca_a);
+  int rwc, kgc, rwh, kgh;
+  wave_shape(gc.TT * csa_a.H, &rwc, &kgc);
+  wave_shape(gh.TT * hca_a.H, &rwh, &kgh);
+  // one launch needs the same kernel shape for both (split decode, same
+  // element type, head dim and wave layout); otherwise they run one after the other
+  const bool fuse = gc.nsplit > 1 && gh.nsplit > 1 && csa_a.f32 == hca_a.f32 && csa_a.d == hca_a.d &&
+                    rwc == rwh && kgc == kgh;
+  if (!fuse) {
+    const hipError_t e = launch_attend(csa_a, st);
+    return e != hipSuccess ? e : launch_attend(hca_a, st);
+  }
+  // Longer splits than in the separate calls: the decode kernel holds one
+  // workgroup per compute unit, so fewer splits let the CSA and HCA
+  // workgroups of a decode batch run side by side instead of in two rounds.
+  // The split length depends on nothing but the problem kind, so results stay
+  // independent of the batch.
+  gc = make_geom(csa_a, PAIR_KPS_CSA);
+  gh = make_geom(hca_a, PAIR_KPS_HCA);
+  if (csa_a.f32)
+    return csa_a.d == 64 ? launch_pair2<float, 64>(hca_a, gh, csa_a, gc, rwc, st)
+                         : launch_pair2<float, 128>(hca_a, gh, csa_a, gc, rwc, st);
+  return csa_a.d == 64 ? launch_pair2<bf16, 64>(hca_a, gh, csa_a, gc, rwc, st)
+                       : launch_pair2<bf16, 128>(hca_a, gh, csa_a, gc, rwc, st);
 }
 
 }  // namespace csa

@@ -69,5 +69,8 @@ struct AttendArgs {
 size_t attend_workspace(bool sparse, int B, int Tq, int H, int d, int topk, int window,
                         int Nc_cap, int m_prime, int max_pos);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t st);
+// Both attention problems of a hybrid layer pair (csa_a sparse, hca_a dense),
+// in one launch (plus one merge launch) when their split-decode kernels share a shape.
+hipError_t launch_attend_pair(const AttendArgs& csa_a, const AttendArgs& hca_a, hipStream_t st);
 
 }  // namespace csa

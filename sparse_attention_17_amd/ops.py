@@ -134,3 +134,47 @@ def hca_attend(q, kc, vc, m_prime, pos0, max_pos, sink=None, scale=None, window=
                            R, window, _p(pos0), int(max_pos), _p(sink), float(scale), B, Tq, H, d,
                            _attn_dt(q), _p(out), _p(lse), _p(ws), nws, _stream(dev)))
     return (out, lse) if return_lse else out
+
+
+def hybrid_attend(csa, hca, return_lse=False):
+    """CSA and HCA attention of one layer pair in one library call.
+
+    `csa` holds the arguments of sparse_attend (q, kc, vc, idx, pos0, max_pos,
+    window, and optionally kw, vw, raw_pos0, sink, scale), `hca` those of
+    hca_attend (q, kc, vc, m_prime, pos0, max_pos, and optionally sink, scale,
+    window, kw, vw, raw_pos0).  Returns (csa_out, hca_out), or with return_lse
+    (csa_out, csa_lse, hca_out, hca_lse)."""
+    c = dict(kw=None, vw=None, raw_pos0=None, sink=None, scale=None)
+    c.update(csa)
+    h = dict(sink=None, scale=None, window=0, kw=None, vw=None, raw_pos0=None)
+    h.update(hca)
+    dev = _dev_check(c["q"], c["kc"], c["vc"], c["idx"], c["pos0"], c["kw"], c["vw"],
+                     c["raw_pos0"], c["sink"], h["q"], h["kc"], h["vc"], h["pos0"], h["kw"],
+                     h["vw"], h["raw_pos0"], h["sink"])
+    lib = L.load()
+    B, Tq, H, d = c["q"].shape
+    topk = c["idx"].shape[-1]
+    R = c["kw"].shape[1] if c["kw"] is not None else 0
+    scale = d ** -0.5 if c["scale"] is None else c["scale"]
+    nws = lib.csa_sparse_attend_workspace(B, Tq, H, d, topk, c["window"])
+    ws = _ws(nws, dev)
+    out = torch.empty_like(c["q"])
+    lse = torch.empty(B, Tq, H, dtype=torch.float32, device=dev) if return_lse else None
+    hB, hTq, hH, hd = h["q"].shape
+    hNc = h["kc"].shape[1]
+    hR = h["kw"].shape[1] if h["kw"] is not None else 0
+    hscale = hd ** -0.5 if h["scale"] is None else h["scale"]
+    hnws = lib.hca_attend_workspace(hB, hTq, hH, hd, hNc, h["m_prime"], h["window"])
+    hws = _ws(hnws, dev)
+    hout = torch.empty_like(h["q"])
+    hlse = torch.empty(hB, hTq, hH, dtype=torch.float32, device=dev) if return_lse else None
+    L.check(lib.csa_hybrid_attend(
+        _p(c["q"]), _p(c["kc"]), _p(c["vc"]), _p(c["idx"]), topk, _p(c["kw"]), _p(c["vw"]),
+        _p(c["raw_pos0"]), R, _p(c["pos0"]), int(c["max_pos"]), c["window"], _p(c["sink"]),
+        float(scale), B, Tq, H, d, c["kc"].shape[1], _attn_dt(c["q"]), _p(out), _p(lse), _p(ws), nws,
+        _p(h["q"]), _p(h["kc"]), _p(h["vc"]), h["m_prime"], hNc, _p(h["kw"]), _p(h["vw"]),
+        _p(h["raw_pos0"]), hR, h["window"], _p(h["pos0"]), int(h["max_pos"]), _p(h["sink"]),
+        float(hscale), hB, hTq, hH, hd, _attn_dt(h["q"]), _p(hout), _p(hlse), _p(hws), hnws,
+        _stream(dev)))
+    return (out, lse, hout, hlse) if return_lse else (out, hout)
+

@@ -133,6 +133,46 @@ def test_hca_validation(lib):
     assert _hca(lib, B=0) == L.OK
 
 
+WS_C, WS_H = 0x10000000, 0x20000000    # separate fake workspaces
+
+
+def _hybrid(lib, csa=None, hca=None):
+    c = dict(q=FAKE, kc=FAKE, vc=FAKE, idx=FAKE, topk=64, kw=FAKE, vw=FAKE, raw_pos0=FAKE, R=128,
+             pos0=FAKE, max_pos=4095, window=128, sink=None, scale=C.c_float(0.1), B=2, Tq=1,
+             H=64, d=128, Nc_cap=1024, dt=L.BF16, out=FAKE, lse=None, ws=WS_C, ws_bytes=1 << 26)
+    h = dict(q=FAKE, kc=FAKE, vc=FAKE, m_prime=128, Nc_cap=8192, kw=None, vw=None, raw_pos0=None,
+             R=0, window=0, pos0=FAKE, max_pos=(1 << 20) - 1, sink=None, scale=C.c_float(0.1),
+             B=16, Tq=1, H=64, d=128, dt=L.BF16, out=FAKE + 0x1000, lse=None, ws=WS_H,
+             ws_bytes=1 << 26)
+    c.update(csa or {})
+    h.update(hca or {})
+    return lib.csa_hybrid_attend(*c.values(), *h.values(), None)
+
+
+def test_hybrid_attend_validation(lib):
+    # each part is validated as by its own entry point; the error names the part
+    assert _hybrid(lib, csa=dict(topk=0)) == L.INVALID_ARGUMENT
+    assert lib.csa_last_error().startswith(b"CSA part: topk")
+    assert _hybrid(lib, hca=dict(m_prime=0)) == L.INVALID_ARGUMENT
+    assert lib.csa_last_error().startswith(b"HCA part: m_prime")
+    assert _hybrid(lib, hca=dict(d=96)) == L.UNSUPPORTED
+    assert _hybrid(lib, csa=dict(scale=C.c_float(0.0))) == L.INVALID_ARGUMENT
+    cn = lib.csa_sparse_attend_workspace(2, 1, 64, 128, 64, 128)
+    hn = lib.hca_attend_workspace(16, 1, 64, 128, 8192, 128, 0)
+    assert _hybrid(lib, csa=dict(ws_bytes=cn - 1)) == L.WORKSPACE_TOO_SMALL
+    assert lib.csa_last_error().startswith(b"CSA part")
+    assert _hybrid(lib, hca=dict(ws_bytes=hn - 1)) == L.WORKSPACE_TOO_SMALL
+    assert lib.csa_last_error().startswith(b"HCA part")
+    # the two workspaces must not overlap, nor the two outputs coincide
+    assert _hybrid(lib, hca=dict(ws=WS_C + cn - 16)) == L.INVALID_ARGUMENT
+    assert b"overlap" in lib.csa_last_error()
+    assert _hybrid(lib, hca=dict(ws=WS_C - hn + 16)) == L.INVALID_ARGUMENT
+    assert _hybrid(lib, hca=dict(out=FAKE)) == L.INVALID_ARGUMENT
+    assert b"same buffer" in lib.csa_last_error()
+    # both parts empty: nothing to do
+    assert _hybrid(lib, csa=dict(B=0), hca=dict(Tq=0)) == L.OK
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(L, "_lib", None)
     monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "nope.so"))
