@@ -43,13 +43,10 @@ def parse():
     p.add_argument("--workload", default="hybrid_1m_fp8")
     p.add_argument("--rotate", type=int, default=3, help="input copies cycled through")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    # Measured on MI355X: the eager step (one stream, host enqueue ~46 us/step,
+    # Measured on MI355X: the eager step (one stream, host enqueue ~40 us/step,
     # below the GPU time) runs ~7 us faster than the same step replayed as a
-    # captured HIP graph, and a second stream for the HCA branch gains nothing
-    # (eager: the extra stream switches make the host the bottleneck).
+    # captured HIP graph.
     p.add_argument("--graph", type=int, default=0, help="replay the step as a HIP graph")
-    p.add_argument("--overlap", type=int, default=0,
-                   help="run the HCA branch on a second stream, concurrently with the CSA chain")
     p.add_argument("--pair", type=int, default=1,
                    help="run CSA and HCA attention through csa_hybrid_attend (one launch)")
     p.add_argument("--cpu-workers", type=int, default=0)
@@ -268,40 +265,18 @@ def main():
     rp0 = torch.full((w.B,), w.ctx - w.window, dtype=torch.int32, device=dev)
     qk = w.qk_dtype
 
-    # The HCA branch does not depend on the CSA chain (indexer -> top-k -> sparse
-    # attention), so with --overlap it runs on a second stream (default priority)
-    # forked from and joined back to the caller's stream; in a captured graph the
-    # two branches become parallel nodes.  Its kernels then fill the CUs that the
-    # top-k select (one workgroup per sequence) leaves idle.
-    side = torch.cuda.Stream(device=dev)
-
-    def hca(g):
-        return ops.hca_attend(g["q_hca"], g["kc_hca"], g["vc_hca"], w.m_hca, pos0, w.ctx - 1,
-                              sink=g["sink_hca"])
-
-    def step(g, overlap=bool(args.overlap)):
-        if overlap:
-            cur = torch.cuda.current_stream(dev)
-            side.wait_stream(cur)
-            with torch.cuda.stream(side):
-                o2 = hca(g)
+    def step(g):
         idx = ops.indexer_topk(g["qi"], g["w"], g["kic"], pos0, w.m, w.topk, max_pos=w.ctx - 1,
                                qi_scale=g.get("qi_scale"), kic_scale=g.get("kic_scale"),
                                qk_dtype=qk)
         csa = dict(q=g["q"], kc=g["kc"], vc=g["vc"], idx=idx, pos0=pos0, max_pos=w.ctx - 1,
                    window=w.window, kw=g["kw"], vw=g["vw"], raw_pos0=rp0, sink=g["sink"])
-        if overlap:
-            o1 = ops.sparse_attend(**csa)
-            cur.wait_stream(side)
-        elif args.pair:
+        hca = dict(q=g["q_hca"], kc=g["kc_hca"], vc=g["vc_hca"], m_prime=w.m_hca, pos0=pos0,
+                   max_pos=w.ctx - 1, sink=g["sink_hca"])
+        if args.pair:
             # both attention problems in one launch (plus one split merge)
-            o1, o2 = ops.hybrid_attend(csa, dict(q=g["q_hca"], kc=g["kc_hca"], vc=g["vc_hca"],
-                                                 m_prime=w.m_hca, pos0=pos0, max_pos=w.ctx - 1,
-                                                 sink=g["sink_hca"]))
-        else:
-            o1 = ops.sparse_attend(**csa)
-            o2 = hca(g)
-        return o1, o2
+            return ops.hybrid_attend(csa, hca)
+        return ops.sparse_attend(**csa), ops.hca_attend(**hca)
 
     # warm-up, then optional graph capture of one step per input copy
     for i in range(args.warmup):
@@ -339,13 +314,12 @@ def main():
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
 
-    # per-kernel launch durations from library-recorded hipEvents (eager steps,
-    # one stream, so that no kernel shares the chip with another while timed)
+    # per-kernel launch durations from library-recorded hipEvents (eager steps)
     lib.csa_profile_reset()
     lib.csa_profile_enable(1)
     nprof = 30
     for i in range(nprof):
-        step(sets[i % len(sets)], overlap=False)
+        step(sets[i % len(sets)])
     torch.cuda.synchronize()
     lib.csa_profile_enable(0)
     import ctypes as C
@@ -385,8 +359,7 @@ def main():
                    "csa_m": w.m, "csa_entries": w.Nc, "topk": w.topk, "window": w.window,
                    "indexer": f"{w.qk_dtype} {w.HI}x{w.dI}", "hca_m": w.m_hca,
                    "hca_entries": w.Nc_hca, "heads": w.H, "head_dim": w.d,
-                   "graph": bool(args.graph), "hca_branch_concurrent": bool(args.overlap),
-                   "attention_pair_launch": bool(args.pair and not args.overlap),
+                   "graph": bool(args.graph), "attention_pair_launch": bool(args.pair),
                    "rotating_copies": args.rotate},
         "roofline": roof,
         "cpu_baseline": cpu,

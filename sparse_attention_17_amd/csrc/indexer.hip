@@ -753,8 +753,8 @@ __global__ __launch_bounds__(TOPK_NT) void topk_row_kernel(IndexerArgs a) {
 static constexpr int PICK_NT = 1024;
 static constexpr int PICK_NW = PICK_NT / 64;
 static constexpr int PICK_MAXCH = 4096;        // rows up to 8M entries
-static constexpr int PICK_PER = 30;            // candidate slots per thread (registers)
-static constexpr int PICK_SLOTS = PICK_PER * PICK_NT;
+static constexpr int PICK_MAXPER = 30;         // candidate slots per thread, largest body
+static constexpr int PICK_WORDS = PICK_MAXPER * PICK_NT / 32;
 static constexpr int PICK_STASH = 16384;       // slots whose selected entry is kept in LDS
 static constexpr int PICK_BINS = 4096;         // 12-bit radix digits
 
@@ -762,87 +762,60 @@ struct PickSmem {
   uint32_t hist[2][PICK_BINS];                 // alternating digit histograms
   uint32_t ccnt[PICK_MAXCH];                   // kept count per chunk (clamped to cap)
   uint32_t ccut[PICK_MAXCH];                   // cut key prefix per chunk
-  uint32_t bm_gt[PICK_SLOTS / 32];             // output bitmaps over slots
-  uint32_t bm_eq[PICK_SLOTS / 32];
+  uint32_t bm_gt[PICK_WORDS];                  // output bitmaps over slots
+  uint32_t bm_eq[PICK_WORDS];
   uint32_t sel[PICK_STASH];                    // entry index of selected slots
   uint32_t wv[4][PICK_NW];                     // per-wave partials
   uint32_t res[2];
 };
 static_assert(sizeof(TopkSmem<PICK_NT>) <= sizeof(PickSmem), "fallback select aliases PickSmem");
 
-// Slot s of a row holds (key, entry) of the (s mod cap)-th kept entry of chunk
-// s / cap; the row's slots are nch * cap long.  Thread tid holds slots
-// q * PICK_NT + tid (coalesced loads); the ordered output goes through LDS
-// bitmaps over the slots.
-__global__ __launch_bounds__(PICK_NT) void long_pick_kernel(IndexerArgs a) {
-  __shared__ PickSmem sm;
+struct PickRow {
+  int row, n, k, nch, cap, lg, nslot;
+  const uint2* meta;
+  const uint2* cand;
+  const uint32_t* src;
+  int32_t* idx;
+  float* sco;
+};
+
+// Select for one row whose nslot fits PER slots per thread.  Slot s holds
+// (key, entry) of the (s mod cap)-th kept entry of chunk s / cap; thread tid
+// holds slots q * PICK_NT + tid (coalesced loads).  Every loop runs exactly
+// PER times, and the output bitmaps are built from wave ballots.
+template <int PER>
+__device__ __forceinline__ void pick_body(PickSmem& sm, const PickRow& R) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int row = blockIdx.x;
-  const int b = row / a.Tq, t = row % a.Tq;
-  const int k = a.topk;
-  const LongWs L = long_ws(a.ws, a.B * a.Tq, a.Nc_cap);
-  int32_t* idx = a.idx_out + (size_t)row * k;
-  float* sco = a.score_out ? a.score_out + (size_t)row * k : nullptr;
-  const uint32_t* src = reinterpret_cast<const uint32_t*>(L.scores) + (size_t)row * nc_pad(a.Nc_cap);
-  const uint2* meta = reinterpret_cast<const uint2*>(L.meta) + (size_t)row * L.nch;
-  const uint2* cand = reinterpret_cast<const uint2*>(L.cand) + (size_t)row * L.nch * SCORE_CHUNK;
   constexpr uint2 EMPTY = {0u, 0xFFFFFFFFu};
+  const int k = R.k, cap = R.cap, lg = R.lg, nslot = R.nslot, nch = R.nch;
 
-  // ---- 1. chunk records and this thread's candidate slots, requested together ----
-  // The slot geometry (cap, chunks) follows from the row length, which needs
-  // pos0; the loads are first issued for the geometry of the last query
-  // position allowed by max_pos (the decode case) and redone only when the
-  // row's own geometry turns out to differ.  Every load stays inside the
-  // row's workspace: nch * cap <= L.nch * SCORE_CHUNK.
-  uint2 kv[PICK_PER], mc0;                                   // mc0: record of chunk tid
-  auto load_all = [&](int nch_, int nslot_, int per_) {
+  // ---- 1. candidate slots and chunk records, requested together ----
+  uint2 kv[PER];
 #pragma unroll
-    for (int q = 0; q < PICK_PER; ++q)
-      if (q < per_) kv[q] = cand[min(q * PICK_NT + tid, max(nslot_ - 1, 0))];
-    mc0 = meta[min(tid, nch_ - 1)];
-  };
-  const int n_hi = max(0, min((a.max_pos + 1) / a.m, a.Nc_cap));
-  const int cap_s = chunk_cap_n(k, max(n_hi, 1));
-  const int nch_s = min((n_hi + SCORE_CHUNK - 1) / SCORE_CHUNK, min(L.nch, PICK_MAXCH));
-  const int nslot_s = nch_s * cap_s;
-  const int per_s = min((nslot_s + PICK_NT - 1) / PICK_NT, PICK_PER);
-  if (n_hi > k) load_all(nch_s, nslot_s, per_s);
-  const int n = row_len(a, b, t);
-  if (n <= k) {
-    write_all_eligible(n, k, src, idx, sco, PICK_NT);
-    return;
-  }
-  const int nch = (n + SCORE_CHUNK - 1) / SCORE_CHUNK;
-  const int cap = chunk_cap_n(k, n);
-  const int lg = 31 - __clz(cap);                            // cap is a power of two
-  const int nslot = nch << lg;
-  const int per = (nslot + PICK_NT - 1) / PICK_NT;
-  int bad = per > PICK_PER || nch > PICK_MAXCH;
-  if (!bad && (n_hi <= k || cap != cap_s || nch > nch_s))    // uniform
-    load_all(nch, nslot, per);
-
+  for (int q = 0; q < PER; ++q) kv[q] = R.cand[min(q * PICK_NT + tid, nslot - 1)];
   uint32_t part = 0;
-  if (!bad)
-    for (int c = tid; c < nch; c += PICK_NT) {
-      const uint2 r = c == tid ? mc0 : meta[c];
-      sm.ccnt[c] = min(r.x, (uint32_t)cap);
-      sm.ccut[c] = r.y;
-      bad |= r.x > (uint32_t)cap;
-      part += min(r.x, (uint32_t)cap);
-    }
-  for (int i = tid; i < PICK_SLOTS / 32; i += PICK_NT) { sm.bm_gt[i] = 0; sm.bm_eq[i] = 0; }
-  __syncthreads();
-#pragma unroll
-  for (int q = 0; q < PICK_PER; ++q) {
-    const int s = q * PICK_NT + tid;
-    if (q >= per || s >= nslot || bad || (s & (cap - 1)) >= (int)sm.ccnt[s >> lg]) kv[q] = EMPTY;
+  int bad = 0;
+  for (int c = tid; c < nch; c += PICK_NT) {
+    const uint2 r = R.meta[c];
+    sm.ccnt[c] = min(r.x, (uint32_t)cap);
+    sm.ccut[c] = r.y;
+    bad |= r.x > (uint32_t)cap;
+    part += min(r.x, (uint32_t)cap);
   }
+  for (int i = tid; i < PICK_BINS; i += PICK_NT) sm.hist[0][i] = 0;
+  __syncthreads();
 
-  // ---- 2. candidate total, key range, overflow: one block reduction ----
+  // ---- 2. mask empty slots; candidate total, key range, overflow ----
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0;
 #pragma unroll
-  for (int q = 0; q < PICK_PER; ++q)
-    if (q < per && kv[q].y != EMPTY.y) { kmin = min(kmin, kv[q].x); kmax = max(kmax, kv[q].x); }
+  for (int q = 0; q < PER; ++q) {
+    const int s = q * PICK_NT + tid;
+    const bool ok = s < nslot && (s & (cap - 1)) < (int)sm.ccnt[min(s >> lg, PICK_MAXCH - 1)];
+    kv[q].x = ok ? kv[q].x : EMPTY.x;
+    kv[q].y = ok ? kv[q].y : EMPTY.y;
+    kmin = ok ? min(kmin, kv[q].x) : kmin;
+    kmax = ok ? max(kmax, kv[q].x) : kmax;
+  }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
@@ -851,7 +824,6 @@ __global__ __launch_bounds__(PICK_NT) void long_pick_kernel(IndexerArgs a) {
     bad |= __shfl_xor(bad, o, 64);
   }
   if (lane == 0) { sm.wv[0][wave] = part; sm.wv[1][wave] = kmin; sm.wv[2][wave] = kmax; sm.wv[3][wave] = bad; }
-  for (int i = tid; i < PICK_BINS; i += PICK_NT) sm.hist[0][i] = 0;
   __syncthreads();
   uint32_t total = 0;
   kmin = 0xFFFFFFFFu; kmax = 0; bad = 0;
@@ -882,10 +854,9 @@ __global__ __launch_bounds__(PICK_NT) void long_pick_kernel(IndexerArgs a) {
       uint32_t* hist = sm.hist[buf];
       for (int i = tid; i < PICK_BINS; i += PICK_NT) sm.hist[buf ^ 1][i] = 0;   // next pass's buffer
 #pragma unroll
-      for (int q = 0; q < PICK_PER; ++q) {
+      for (int q = 0; q < PER; ++q) {
         const uint2 v = kv[q];
-        if (q < per && v.y != EMPTY.y && (v.x & pmask) == prefix)
-          atomicAdd(&hist[(v.x >> sh) & (nb - 1)], 1u);
+        if (v.y != EMPTY.y && (v.x & pmask) == prefix) atomicAdd(&hist[(v.x >> sh) & (nb - 1)], 1u);
       }
       __syncthreads();
       // top-down scan: thread tid owns bins [nbs - pb*(tid+1), nbs - pb*tid)
@@ -921,28 +892,35 @@ __global__ __launch_bounds__(PICK_NT) void long_pick_kernel(IndexerArgs a) {
       const uint32_t cut = sm.ccut[c];
       unsafe |= cut != CUT_ALL && tau < (cut << 12);
     }
-  // mark keys > tau and keys == tau in the slot bitmaps; keep their entries
-  if (!unsafe) {
+  // slot bitmaps of keys > tau and keys == tau, one ballot per 64 slots (each
+  // word has one writer: no atomics, no clearing); selected entries kept
 #pragma unroll
-    for (int q = 0; q < PICK_PER; ++q) {
-      const uint2 v = kv[q];
-      const int s = q * PICK_NT + tid;
-      if (q >= per || v.y == EMPTY.y || v.x < tau) continue;
-      if (s < PICK_STASH) sm.sel[s] = v.y;
-      if (v.x > tau) atomicOr(&sm.bm_gt[s >> 5], 1u << (s & 31));
-      else atomicOr(&sm.bm_eq[s >> 5], 1u << (s & 31));
+  for (int q = 0; q < PER; ++q) {
+    const uint2 v = kv[q];
+    const int s = q * PICK_NT + tid;
+    const bool valid = v.y != EMPTY.y;
+    const bool gt = valid && v.x > tau, eq = valid && v.x == tau;
+    if ((gt || eq) && s < PICK_STASH) sm.sel[s] = v.y;
+    const uint64_t bg = __ballot(gt), be = __ballot(eq);
+    if (lane == 0) {
+      const int w0 = (q * PICK_NT + wave * 64) >> 5;
+      sm.bm_gt[w0] = (uint32_t)bg;
+      sm.bm_gt[w0 + 1] = (uint32_t)(bg >> 32);
+      sm.bm_eq[w0] = (uint32_t)be;
+      sm.bm_eq[w0 + 1] = (uint32_t)(be >> 32);
     }
   }
   if (__syncthreads_or(unsafe)) {
-    select_row<PICK_NT>(*reinterpret_cast<TopkSmem<PICK_NT>*>(&sm.hist[0][0]), src, n, k, idx, sco);
+    select_row<PICK_NT>(*reinterpret_cast<TopkSmem<PICK_NT>*>(&sm.hist[0][0]), R.src, R.n, k, R.idx, R.sco);
     return;
   }
 
   // ---- 4. output in slot order (= ascending entry order): thread tid owns
   // the contiguous slots [32 tid, 32 tid + 32): keys > tau, and the first
   // `need` keys == tau over the whole row ----
-  const uint32_t wgt = tid < PICK_SLOTS / 32 ? sm.bm_gt[tid] : 0u;
-  const uint32_t weq = tid < PICK_SLOTS / 32 ? sm.bm_eq[tid] : 0u;
+  constexpr int NWORDS = PER * PICK_NT / 32;
+  const uint32_t wgt = tid < NWORDS ? sm.bm_gt[tid] : 0u;
+  const uint32_t weq = tid < NWORDS ? sm.bm_eq[tid] : 0u;
   const uint64_t pk = ((uint64_t)__popc(wgt) << 32) | (uint32_t)__popc(weq);
   uint64_t inc = pk;
 #pragma unroll
@@ -965,11 +943,44 @@ __global__ __launch_bounds__(PICK_NT) void long_pick_kernel(IndexerArgs a) {
   for (; take; take &= take - 1) {
     const int s = tid * 32 + __ffs(take) - 1;
     if (pos < (uint32_t)k) {
-      idx[pos] = (int32_t)(s < PICK_STASH ? sm.sel[s] : cand[s].y);
-      if (sco) sco[pos] = __uint_as_float(cand[s].x);
+      R.idx[pos] = (int32_t)(s < PICK_STASH ? sm.sel[s] : R.cand[s].y);
+      if (R.sco) R.sco[pos] = __uint_as_float(R.cand[s].x);
     }
     ++pos;
   }
+}
+
+// One workgroup per row: the row's geometry, then the body specialised for
+// its slots per thread (a uniform branch).
+__global__ __launch_bounds__(PICK_NT) void long_pick_kernel(IndexerArgs a) {
+  __shared__ PickSmem sm;
+  PickRow R;
+  R.row = blockIdx.x;
+  const int b = R.row / a.Tq, t = R.row % a.Tq;
+  R.k = a.topk;
+  const LongWs L = long_ws(a.ws, a.B * a.Tq, a.Nc_cap);
+  R.idx = a.idx_out + (size_t)R.row * R.k;
+  R.sco = a.score_out ? a.score_out + (size_t)R.row * R.k : nullptr;
+  R.src = reinterpret_cast<const uint32_t*>(L.scores) + (size_t)R.row * nc_pad(a.Nc_cap);
+  R.meta = reinterpret_cast<const uint2*>(L.meta) + (size_t)R.row * L.nch;
+  R.cand = reinterpret_cast<const uint2*>(L.cand) + (size_t)R.row * L.nch * SCORE_CHUNK;
+  R.n = row_len(a, b, t);
+  if (R.n <= R.k) {
+    write_all_eligible(R.n, R.k, R.src, R.idx, R.sco, PICK_NT);
+    return;
+  }
+  R.nch = (R.n + SCORE_CHUNK - 1) / SCORE_CHUNK;
+  R.cap = chunk_cap_n(R.k, R.n);
+  R.lg = 31 - __clz(R.cap);                                  // cap is a power of two
+  R.nslot = R.nch << R.lg;                                   // <= L.nch * SCORE_CHUNK
+  const int per = (R.nslot + PICK_NT - 1) / PICK_NT;
+  if (per > PICK_MAXPER || R.nch > PICK_MAXCH) {
+    select_row<PICK_NT>(*reinterpret_cast<TopkSmem<PICK_NT>*>(&sm.hist[0][0]), R.src, R.n, R.k, R.idx, R.sco);
+    return;
+  }
+  if (per <= 8) pick_body<8>(sm, R);
+  else if (per <= 16) pick_body<16>(sm, R);
+  else pick_body<PICK_MAXPER>(sm, R);
 }
 
 // --------------------------- fused prefill path ----------------------------
