@@ -212,6 +212,25 @@ csa_status_t csa_hybrid_attend(
     void *hworkspace, size_t hworkspace_bytes, void *stream);
 
 /*
+ * csa_grouped_out_proj — grouped output projection after the core attention.
+ * hyper.ai "Method", CSA paragraph (the core attention is followed by a
+ * grouped output projection that keeps its cost down).  Form implemented:
+ * the H heads form G consecutive groups of H/G heads; group j's head outputs
+ * of a token, concatenated (K = (H/G) d values), are multiplied by the
+ * group's own matrix:
+ *   y[t, j*dg + n] = sum_k o[t, j*K + k] * w[j, k, n]
+ *
+ *   o  [T, H, d]   attention outputs (dt), rows of H*d values per token
+ *   w  [G, K, dg]  per-group weights (dt), row-major
+ *   y  [T, G*dg]   output (dt)
+ *   dt ∈ {F32, BF16}; G divides H; K a multiple of 64; dg a multiple of 128;
+ *   T * H * d elements under 2 GiB.  Products accumulate in fp32 on the MFMA
+ *   units; bf16 outputs are rounded to nearest even.  No workspace.
+ */
+csa_status_t csa_grouped_out_proj(const void *o, const void *w, int T, int H, int d, int G, int dg,
+                                  csa_dtype_t dt, void *y, void *stream);
+
+/*
  * Launch timing, for measurement tools (not part of any computation).
  * While enabled, every kernel launch made by the library is bracketed by a
  * pair of hipEvents recorded on that launch's stream.  csa_profile_query
@@ -221,7 +240,7 @@ csa_status_t csa_hybrid_attend(
  * (decode scores and per-chunk cut), "indexer_topk" (row select),
  * "indexer_fused" (prefill scores and select in one kernel), "attend_csa",
  * "attend_hca", "attend_pair" (both of csa_hybrid_attend in one kernel),
- * "attend_combine".
+ * "attend_combine", "out_proj".
  * csa_profile_reset forgets all records (events are kept for reuse).
  */
 void csa_profile_enable(int on);

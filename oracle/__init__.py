@@ -15,6 +15,8 @@ Sources (DeepSeek-V4 summary pages):
   * same page, HCA paragraph: compression at m' >> m, non-overlapping, dense
     attention over the compressed entries; both mechanisms carry a sliding
     window branch.
+  * same page, CSA paragraph: a grouped output projection follows the core
+    attention (``proj``).
   * same page, efficiency paragraph, and aiboss88 "Technical Principles"
     (CSA and FP4 bullets): FP4 indexer QK path, FP8 for extra dynamic range,
     sliding window plus attention sink in CSA.
@@ -28,4 +30,4 @@ than itself: format definitions and torch's own float8 decoder, closed forms
 of the pooling, brute-force sorts, and PyTorch's scaled_dot_product_attention
 in float64 for the dense special cases.
 """
-from . import formats, csa, hca  # noqa: F401
+from . import formats, csa, hca, proj  # noqa: F401

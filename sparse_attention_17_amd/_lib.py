@@ -36,6 +36,7 @@ EXPORTS = {
                                _I, _I, _I, _I, _I, _I, _P, _P, _P, _SZ,
                                _P, _P, _P, _I, _I, _P, _P, _P, _I, _I, _P, _I, _P, C.c_float,
                                _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
+    "csa_grouped_out_proj": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
     "csa_profile_enable": (None, [_I]),
     "csa_profile_reset": (None, []),
     "csa_profile_query": (_I, [C.c_char_p, C.POINTER(C.c_int), C.POINTER(C.c_double)]),

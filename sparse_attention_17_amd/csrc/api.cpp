@@ -321,4 +321,25 @@ csa_status_t csa_hybrid_attend(
   return device_status(e, "csa_hybrid_attend launch");
 }
 
+csa_status_t csa_grouped_out_proj(const void* o, const void* w, int T, int H, int d, int G, int dg,
+                                  csa_dtype_t dt, void* y, void* stream) {
+  REQUIRE(T >= 0, CSA_INVALID_ARGUMENT, "T must be >= 0");
+  REQUIRE(H >= 1 && d >= 1 && G >= 1, CSA_INVALID_ARGUMENT, "H, d and G must be >= 1");
+  REQUIRE(H % G == 0, CSA_INVALID_ARGUMENT, "G=%d must divide H=%d", G, H);
+  const long long K = (long long)(H / G) * d;
+  REQUIRE(K % 64 == 0, CSA_UNSUPPORTED, "inputs per group (H/G)*d = %lld must be a multiple of 64", K);
+  REQUIRE(dg >= 128 && dg % 128 == 0, CSA_UNSUPPORTED, "outputs per group dg=%d must be a multiple of 128", dg);
+  REQUIRE(attn_dtype_ok(dt), CSA_UNSUPPORTED, "dtype must be CSA_F32 or CSA_BF16");
+  const long long eb = dt == CSA_F32 ? 4 : 2;
+  REQUIRE((long long)T * H * d * eb < (1LL << 31), CSA_INVALID_ARGUMENT, "o exceeds 2 GiB");
+  REQUIRE((long long)G * K * dg < kMaxElems && (long long)T * G * dg < kMaxElems, CSA_INVALID_ARGUMENT,
+          "tensor too large");
+  if (T == 0) return ok();
+  REQUIRE_PTR(o, "o");
+  REQUIRE_PTR(w, "w");
+  REQUIRE_PTR(y, "y");
+  csa::ProjArgs a{o, w, y, T, G, (int)K, dg, dt == CSA_F32};
+  return device_status(csa::launch_proj(a, (hipStream_t)stream), "csa_grouped_out_proj launch");
+}
+
 }  // extern "C"

@@ -73,4 +73,12 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st);
 // in one launch (plus one merge launch) when their split-decode kernels share a shape.
 hipError_t launch_attend_pair(const AttendArgs& csa_a, const AttendArgs& hca_a, hipStream_t st);
 
+struct ProjArgs {
+  const void *o, *w;
+  void* y;
+  int T, G, K, dg;                 // tokens, groups, inputs per group ((H/G) d), outputs per group
+  bool f32;
+};
+hipError_t launch_proj(const ProjArgs& a, hipStream_t st);
+
 }  // namespace csa

@@ -178,3 +178,18 @@ def hybrid_attend(csa, hca, return_lse=False):
         _stream(dev)))
     return (out, lse, hout, hlse) if return_lse else (out, hout)
 
+
+def grouped_out_proj(o, w):
+    """Grouped output projection.  o [T, H, d]; w [G, (H/G) d, dg] -> y [T, G dg]."""
+    dev = _dev_check(o, w)
+    T, H, d = o.shape
+    G, K, dg = w.shape
+    if K * G != H * d:
+        raise ValueError("w must be [G, (H/G)*d, dg]")
+    if w.dtype != o.dtype:
+        raise ValueError("o and w must have the same dtype")
+    y = torch.empty(T, G * dg, dtype=o.dtype, device=dev)
+    lib = L.load()
+    L.check(lib.csa_grouped_out_proj(_p(o), _p(w), T, H, d, G, dg, _attn_dt(o), _p(y), _stream(dev)))
+    return y
+

@@ -22,7 +22,7 @@ from .configs import Workload
 SEED = 17
 TID = dict(q=0, k=1, v=2, ki=3, qi=4, wlog=5, g=6, g_hca=7, sink=8, kic=9, kc=10, vc=11,
            kw=12, vw=13, q_hca=14, kc_hca=15, vc_hca=16, sink_hca=17, pos_bias=18,
-           pos_bias_hca=19)
+           pos_bias_hca=19, o_attn=20, w_proj=21)
 
 
 def rng_for(wid: int, tensor: str, seed: int = SEED) -> np.random.Generator:
@@ -109,3 +109,14 @@ def _encode_qk(out: dict, name: str, x: torch.Tensor, qk_dtype: str, dt: str) ->
         out[name], out[name + "_scale"] = quant.quant_fp4_blocks(x)
     else:
         raise ValueError(qk_dtype)
+
+
+def proj_inputs(wid: int, T: int, H: int, d: int, G: int, dg: int, dtype: str, seed: int = SEED):
+    """Attention outputs o [T, H, d] ~ N(0, 1) and group weights w [G, (H/G) d, dg]
+    ~ N(0, 1/((H/G) d)) for the grouped output projection (values, no method
+    arithmetic), in the given dtype."""
+    o = normal(wid, "o_attn", (T, H, d), scaled_by_last=False, seed=seed)
+    w = normal(wid, "w_proj", (G, (H // G) * d, dg), scaled_by_last=False, seed=seed)
+    w *= np.float32(1.0 / np.sqrt((H // G) * d))
+    return to_dtype(o, dtype), to_dtype(w, dtype)
+

@@ -173,6 +173,23 @@ def test_hybrid_attend_validation(lib):
     assert _hybrid(lib, csa=dict(B=0), hca=dict(Tq=0)) == L.OK
 
 
+def _proj(lib, **kw):
+    a = dict(o=FAKE, w=FAKE, T=64, H=64, d=128, G=8, dg=1024, dt=L.BF16, y=FAKE, stream=None)
+    a.update(kw)
+    return lib.csa_grouped_out_proj(*a.values())
+
+
+def test_grouped_out_proj_validation(lib):
+    assert _proj(lib, G=3) == L.INVALID_ARGUMENT                # G must divide H
+    assert _proj(lib, H=4, d=8, G=1) == L.UNSUPPORTED           # K = 32 not a multiple of 64
+    assert _proj(lib, dg=100) == L.UNSUPPORTED
+    assert _proj(lib, dt=L.FP8_E4M3) == L.UNSUPPORTED
+    assert _proj(lib, y=None) == L.INVALID_ARGUMENT
+    assert _proj(lib, o=FAKE + 8) == L.INVALID_ARGUMENT         # misaligned
+    assert _proj(lib, T=1 << 20) == L.INVALID_ARGUMENT          # o over 2 GiB
+    assert _proj(lib, T=0) == L.OK
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(L, "_lib", None)
     monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "nope.so"))
