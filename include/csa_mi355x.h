@@ -217,11 +217,11 @@ csa_status_t csa_hybrid_attend(
  * grouped output projection that keeps its cost down).  Form implemented:
  * the H heads form G consecutive groups of H/G heads; group j's head outputs
  * of a token, concatenated (K = (H/G) d values), are multiplied by the
- * group's own matrix:
- *   y[t, j*dg + n] = sum_k o[t, j*K + k] * w[j, k, n]
+ * group's own matrix (stored one row per output, as a linear layer's weight):
+ *   y[t, j*dg + n] = sum_k o[t, j*K + k] * w[j, n, k]
  *
  *   o  [T, H, d]   attention outputs (dt), rows of H*d values per token
- *   w  [G, K, dg]  per-group weights (dt), row-major
+ *   w  [G, dg, K]  per-group weights (dt), row-major
  *   y  [T, G*dg]   output (dt)
  *   dt ∈ {F32, BF16}; G divides H; K a multiple of 64; dg a multiple of 128;
  *   T * H * d elements under 2 GiB.  Products accumulate in fp32 on the MFMA

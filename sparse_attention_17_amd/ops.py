@@ -180,12 +180,12 @@ def hybrid_attend(csa, hca, return_lse=False):
 
 
 def grouped_out_proj(o, w):
-    """Grouped output projection.  o [T, H, d]; w [G, (H/G) d, dg] -> y [T, G dg]."""
+    """Grouped output projection.  o [T, H, d]; w [G, dg, (H/G) d] -> y [T, G dg]."""
     dev = _dev_check(o, w)
     T, H, d = o.shape
-    G, K, dg = w.shape
+    G, dg, K = w.shape
     if K * G != H * d:
-        raise ValueError("w must be [G, (H/G)*d, dg]")
+        raise ValueError("w must be [G, dg, (H/G)*d]")
     if w.dtype != o.dtype:
         raise ValueError("o and w must have the same dtype")
     y = torch.empty(T, G * dg, dtype=o.dtype, device=dev)

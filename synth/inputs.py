@@ -112,11 +112,11 @@ def _encode_qk(out: dict, name: str, x: torch.Tensor, qk_dtype: str, dt: str) ->
 
 
 def proj_inputs(wid: int, T: int, H: int, d: int, G: int, dg: int, dtype: str, seed: int = SEED):
-    """Attention outputs o [T, H, d] ~ N(0, 1) and group weights w [G, (H/G) d, dg]
+    """Attention outputs o [T, H, d] ~ N(0, 1) and group weights w [G, dg, (H/G) d]
     ~ N(0, 1/((H/G) d)) for the grouped output projection (values, no method
     arithmetic), in the given dtype."""
     o = normal(wid, "o_attn", (T, H, d), scaled_by_last=False, seed=seed)
-    w = normal(wid, "w_proj", (G, (H // G) * d, dg), scaled_by_last=False, seed=seed)
+    w = normal(wid, "w_proj", (G, dg, (H // G) * d), scaled_by_last=False, seed=seed)
     w *= np.float32(1.0 / np.sqrt((H // G) * d))
     return to_dtype(o, dtype), to_dtype(w, dtype)
 
