@@ -52,6 +52,8 @@ def parse():
     p.add_argument("--cpu-workers", type=int, default=0)
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run three 256 MiB device copies (known traffic for counter scaling)")
+    p.add_argument("--suite", action="store_true",
+                   help="time every op at the other workloads' sizes (one JSON object) and exit")
     p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                         "`bench.py --copy-calibration --graph 0` into profiles/ and exit")
@@ -211,10 +213,136 @@ def cpu_baseline(x, w, workers):
 
 
 # ----------------------------------------------------------------------------
+# ----------------------------------------------------------------------------
+# per-op timings at the other workloads (prefill, 128K decode, HCA, FP4, ...)
+# ----------------------------------------------------------------------------
+def suite():
+    import ctypes as C
+    import torch
+    from synth import configs, inputs
+    from sparse_attention_17_amd import _lib as L
+    from sparse_attention_17_amd import ops
+
+    dev = torch.device("cuda:0")
+    lib = L.load()
+    res = {}
+
+    def timeit(fn, n=20, w=3):
+        for _ in range(w):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3                   # us per call
+
+    def kernels(fn, names, key, n=5):
+        lib.csa_profile_reset()
+        lib.csa_profile_enable(1)
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        lib.csa_profile_enable(0)
+        for name in names:
+            c, t = C.c_int(0), C.c_double(0)
+            if lib.csa_profile_query(name.encode(), C.byref(c), C.byref(t)) == 0:
+                res[f"{key}.{name}_us"] = t.value / c.value * 1e3
+        lib.csa_profile_reset()
+
+    # CSA prefill, 32K tokens (compress -> fused indexer/top-k -> sparse attention)
+    w = configs.CSA_PREFILL_32K
+    x = inputs.make_inputs(w)
+    g = {k: v.to(dev) for k, v in x.items()}
+    pos0 = torch.zeros(1, dtype=torch.int32, device=dev)
+    comp = lambda: ops.compress(g["k"], g["v"], g["ki"], g["g"], w.m)
+    kc, vc, kic = comp()
+    key = "csa_prefill_32k"
+    res[f"{key}.compress_us"] = timeit(comp)
+    res[f"{key}.compress_GBs"] = w.ctx * (2 * w.d + w.dI) * 2 * 1.25 / res[f"{key}.compress_us"] / 1e3
+    ind = lambda: ops.indexer_topk(g["qi"], g["w"], kic, pos0, w.m, w.topk, max_pos=w.ctx - 1)
+    idx = ind()
+    res[f"{key}.indexer_topk_us"] = timeit(ind, n=5)
+    res[f"{key}.indexer_TFLOPs"] = 6.87e10 / res[f"{key}.indexer_topk_us"] / 1e6
+    att = lambda: ops.sparse_attend(g["q"], kc, vc, idx, pos0, w.ctx - 1, w.window, kw=g["k"],
+                                    vw=g["v"], raw_pos0=pos0, sink=g["sink"])
+    res[f"{key}.sparse_attend_us"] = timeit(att, n=5)
+    res[f"{key}.attend_TFLOPs"] = 6.70e11 / res[f"{key}.sparse_attend_us"] / 1e6
+    del x, g, kc, vc, kic, idx
+
+    # grouped output projection of the 32K prefill and of an 8-token decode batch
+    for key, T in (("out_proj_32k", 32768), ("out_proj_decode8", 8)):
+        o, wp = inputs.proj_inputs(71, T, 64, 128, 8, 1024, "bf16")
+        o, wp = o.to(dev), wp.to(dev)
+        res[f"{key}.us"] = timeit(lambda: ops.grouped_out_proj(o, wp), n=10)
+        res[f"{key}.TFLOPs"] = 2.0 * T * 8192 * 1024 / res[f"{key}.us"] / 1e6
+        res[f"{key}.GBs"] = (o.numel() + wp.numel() + T * 8192) * 2 / res[f"{key}.us"] / 1e3
+        del o, wp
+
+    # CSA decode, 128K context, batch 64
+    w = configs.CSA_DECODE_128K
+    x = inputs.make_inputs(w)
+    g = {k: v.to(dev) for k, v in x.items()}
+    pos0 = torch.full((w.B,), w.ctx - 1, dtype=torch.int32, device=dev)
+    rp0 = torch.full((w.B,), w.ctx - w.window, dtype=torch.int32, device=dev)
+    ind = lambda: ops.indexer_topk(g["qi"], g["w"], g["kic"], pos0, w.m, w.topk, max_pos=w.ctx - 1)
+    idx = ind()
+    att = lambda: ops.sparse_attend(g["q"], g["kc"], g["vc"], idx, pos0, w.ctx - 1, w.window,
+                                    kw=g["kw"], vw=g["vw"], raw_pos0=rp0, sink=g["sink"])
+    key = "csa_decode_128k"
+    res[f"{key}.indexer_topk_us"] = timeit(ind)
+    res[f"{key}.sparse_attend_us"] = timeit(att)
+    kernels(lambda: (ind(), att()), ("indexer_score", "indexer_topk", "attend_csa", "attend_combine"), key)
+    res[f"{key}.indexer_score_GBs"] = w.B * w.Nc * w.dI * 2 / res[f"{key}.indexer_score_us"] / 1e3
+    del x, g, idx
+
+    # HCA at 1M context: decode batch 16 and a 4096-query prefill chunk
+    for w in (configs.HCA_1M_DECODE, configs.HCA_1M_PREFILL):
+        x = inputs.make_inputs(w)
+        g = {k: v.to(dev) for k, v in x.items()}
+        pos0 = torch.full((w.B,), w.ctx - w.Tq, dtype=torch.int32, device=dev)
+        fn = lambda: ops.hca_attend(g["q_hca"], g["kc_hca"], g["vc_hca"], w.m_hca, pos0, w.ctx - 1,
+                                    sink=g["sink_hca"])
+        key = w.name
+        res[f"{key}.hca_us"] = timeit(fn, n=20 if w.Tq == 1 else 5)
+        if w.Tq == 1:
+            res[f"{key}.GBs"] = w.B * (w.Nc_hca * w.d * 2 * 2 + 2 * w.H * w.d * 2) / res[f"{key}.hca_us"] / 1e3
+        else:
+            res[f"{key}.TFLOPs"] = 1.097e12 / res[f"{key}.hca_us"] / 1e6
+        del x, g
+
+    # hybrid 1M decode with the FP4 indexer
+    w = configs.HYBRID_1M_FP4
+    x = inputs.make_inputs(w)
+    g = {k: v.to(dev) for k, v in x.items()}
+    pos0 = torch.full((w.B,), w.ctx - 1, dtype=torch.int32, device=dev)
+    ind = lambda: ops.indexer_topk(g["qi"], g["w"], g["kic"], pos0, w.m, w.topk, max_pos=w.ctx - 1,
+                                   qi_scale=g["qi_scale"], kic_scale=g["kic_scale"], qk_dtype="fp4")
+    res["hybrid_1m_fp4.indexer_topk_us"] = timeit(ind)
+    kernels(ind, ("indexer_score", "indexer_topk"), "hybrid_1m_fp4")
+    res["hybrid_1m_fp4.indexer_score_GBs"] = w.B * w.Nc * (w.dI // 2 + w.dI // 32) / \
+        res["hybrid_1m_fp4.indexer_score_us"] / 1e3
+    del x, g
+
+    # HCA compression of a 1M-token sequence at m'=128
+    T = 1 << 20
+    k = inputs.to_dtype(inputs.normal(80, "k", (1, T, 128)), "bf16").to(dev)
+    v = inputs.to_dtype(inputs.normal(80, "v", (1, T, 128)), "bf16").to(dev)
+    gt = inputs.normal(80, "g", (128,)).to(dev)
+    res["hca_compress_1m.us"] = timeit(lambda: ops.compress(k, v, None, gt, 128))
+    res["hca_compress_1m.GBs"] = (2 * T * 256 + 2 * 8192 * 256) / res["hca_compress_1m.us"] / 1e3
+    print(json.dumps({"suite": {k: round(v, 2) for k, v in res.items()}}), flush=True)
+
+
 def main():
     args = parse()
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary)
+        return
+    if args.suite:
+        suite()
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the multi-GPU "

@@ -189,15 +189,12 @@ csa_status_t hca_attend(const void *q, const void *kc, const void *vc, int m_pri
  *   validation; each problem has its own workspace, sized by its own query
  *   (csa_sparse_attend_workspace / hca_attend_workspace), and the two must not
  *   overlap; out and hout must be different buffers.
- *   When both problems are split decode (Tq = 1) with the same dtype, head
- *   dim and query-head tile shape, one kernel runs the workgroups of both,
- *   with the key lists cut into 256-key (CSA) and 384-key (HCA) splits
- *   (longer than the separate calls' 128 and 256), and one kernel merges the
- *   split partials of both: results then equal those of the separate calls up
- *   to the rounding of the split merge, and, like theirs, do not depend on
- *   the batch size.  Otherwise the two calls run one after the other on
- *   `stream`, with bit-identical results.  An error in either part launches
- *   nothing; the error text names the part.
+ *   Results are bit-identical to the two separate calls.  When both problems
+ *   are split decode (Tq = 1) with the same dtype, head dim and query-head
+ *   tile shape, one kernel runs the workgroups of both (each with the split
+ *   it has in its own call) and one kernel merges the split partials of both;
+ *   otherwise the two calls run one after the other on `stream`.  An error in
+ *   either part launches nothing; the error text names the part.
  */
 csa_status_t csa_hybrid_attend(
     const void *q, const void *kc, const void *vc, const int32_t *idx, int topk,

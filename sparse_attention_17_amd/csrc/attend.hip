@@ -54,8 +54,9 @@ __device__ __forceinline__ int vt_block(int dim, int kb) { return kb ^ ((dim >> 
 // RW row-waves (32 query rows each) x KG key groups (KG=2: each wave of a pair
 // takes one 32-key half of every 64-key tile; the two partial softmax states
 // are merged in LDS at the end).  PF key tiles are in flight ahead of the one
-// being computed (PF=2 for split decode, whose workgroups hold two tiles: all
-// of a workgroup's keys are then requested at once).
+// being computed (PF=2 for split decode: a 128-key CSA split is then requested
+// at once).  Every instance fits 256 VGPRs, two waves per SIMD, so two
+// workgroups share a compute unit and one's loads overlap the other's math.
 // The body takes its workgroup's coordinates (token tile bx, split by,
 // sequence bz) and the dynamic LDS block from the kernel that runs it.
 template <typename T, int D, int RW, int KG, bool SPARSE, int PF>
@@ -489,18 +490,18 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
 }
 
 template <typename T, int D, int RW, int KG, bool SPARSE, int PF>
-__global__ __launch_bounds__(RW * KG * 64) __attribute__((amdgpu_waves_per_eu(PF == 1 ? 2 : 1))) void attend_kernel(AttendArgs a, AttnGeom gm) {
+__global__ __launch_bounds__(RW * KG * 64) __attribute__((amdgpu_waves_per_eu(2))) void attend_kernel(AttendArgs a, AttnGeom gm) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   attend_body<T, D, RW, KG, SPARSE, PF>(a, gm, blockIdx.x, blockIdx.y, blockIdx.z, smem_raw);
 }
 
 // The HCA and CSA attention of one layer pair in a single split-decode launch:
 // a 1-D grid whose first nb0 workgroups run the HCA problem a0 and the rest the
-// CSA problem a1 (each decomposed as its own (tile, split, sequence) grid).  The
-// HCA workgroups, which hold more keys each, are dispatched first; the CSA ones
-// fill the compute units the HCA grid leaves free.
+// CSA problem a1 (each decomposed as its own (tile, split, sequence) grid, the
+// same as in its own launch).  Two workgroups fit a compute unit, so the two
+// grids of a decode batch run side by side instead of one after the other.
 template <typename T, int D, int RW, int KG>
-__global__ __launch_bounds__(RW * KG * 64) __attribute__((amdgpu_waves_per_eu(1))) void attend_pair_kernel(
+__global__ __launch_bounds__(RW * KG * 64) __attribute__((amdgpu_waves_per_eu(2))) void attend_pair_kernel(
     AttendArgs a0, AttnGeom g0, AttendArgs a1, AttnGeom g1, int nb0) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   int bid = blockIdx.x;
@@ -596,11 +597,6 @@ static int keys_per_split(bool sparse, int Tq) {
   return sparse ? 128 : 256;
 }
 
-// keys per split in a paired decode launch (gathered CSA rows take longer per
-// tile than the contiguous HCA blocks, so CSA splits are shorter)
-static constexpr int PAIR_KPS_CSA = 4 * KT;
-static constexpr int PAIR_KPS_HCA = 6 * KT;
-
 static int tokens_per_tile(bool sparse, int H, int Tq) {
   if (sparse) return 1;
   return std::max(1, std::min(128 / H, Tq));
@@ -686,10 +682,10 @@ static hipError_t launch2(const AttendArgs& a, const AttnGeom& gm, hipStream_t s
   return a.sparse ? launch3<T, D, true>(a, gm, st) : launch3<T, D, false>(a, gm, st);
 }
 
-static AttnGeom make_geom(const AttendArgs& a, int kps_override = 0) {
+static AttnGeom make_geom(const AttendArgs& a) {
   AttnGeom gm;
   gm.TT = tokens_per_tile(a.sparse, a.H, a.Tq);
-  const int kps = kps_override > 0 ? kps_override : keys_per_split(a.sparse, a.Tq);
+  const int kps = keys_per_split(a.sparse, a.Tq);
   const long nk = nkeys_upper(a.sparse, a.topk, a.window, a.Nc_cap, a.m_prime, a.max_pos);
   gm.nsplit = (int)std::max(1L, (nk + kps - 1) / kps);
   gm.kps = gm.nsplit > 1 ? kps : INT_MAX / 2;
@@ -719,10 +715,7 @@ static hipError_t launch_pair4(const AttendArgs& h, const AttnGeom& gh, const At
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // a problem left with one split wrote its output directly
-  const long cbh = gh.nsplit > 1 ? (long)((partial_rows(h) + 3) / 4) : 0;
-  const long cbc = gc.nsplit > 1 ? (long)((partial_rows(c) + 3) / 4) : 0;
-  if (cbh + cbc == 0) return hipSuccess;
+  const long cbh = (long)((partial_rows(h) + 3) / 4), cbc = (long)((partial_rows(c) + 3) / 4);
   ProfScope ps("attend_combine", st);
   hipLaunchKernelGGL((combine_pair_kernel<T, D>), dim3((unsigned)(cbh + cbc)), dim3(256), 0, st,
                      h, gh.nsplit, c, gc.nsplit, (int)cbh);
@@ -741,7 +734,7 @@ static hipError_t launch_pair2(const AttendArgs& h, const AttnGeom& gh, const At
 hipError_t launch_attend_pair(const AttendArgs& csa_a, const AttendArgs& hca_a, hipStream_t st) {
   if (csa_a.B == 0 || csa_a.Tq == 0) return launch_attend(hca_a, st);
   if (hca_a.B == 0 || hca_a.Tq == 0) return launch_attend(csa_a, st);
-  AttnGeom gc = make_geom(csa_a), gh = make_geom(hca_a);
+  const AttnGeom gc = make_geom(csa_a), gh = make_geom(hca_a);
   int rwc, kgc, rwh, kgh;
   wave_shape(gc.TT * csa_a.H, &rwc, &kgc);
   wave_shape(gh.TT * hca_a.H, &rwh, &kgh);
@@ -753,13 +746,6 @@ hipError_t launch_attend_pair(const AttendArgs& csa_a, const AttendArgs& hca_a, 
     const hipError_t e = launch_attend(csa_a, st);
     return e != hipSuccess ? e : launch_attend(hca_a, st);
   }
-  // Longer splits than in the separate calls: the decode kernel holds one
-  // workgroup per compute unit, so fewer splits let the CSA and HCA
-  // workgroups of a decode batch run side by side instead of in two rounds.
-  // The split length depends on nothing but the problem kind, so results stay
-  // independent of the batch.
-  gc = make_geom(csa_a, PAIR_KPS_CSA);
-  gh = make_geom(hca_a, PAIR_KPS_HCA);
   if (csa_a.f32)
     return csa_a.d == 64 ? launch_pair2<float, 64>(hca_a, gh, csa_a, gc, rwc, st)
                          : launch_pair2<float, 128>(hca_a, gh, csa_a, gc, rwc, st);
