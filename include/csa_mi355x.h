@@ -93,6 +93,23 @@ csa_status_t csa_compress(const void *k, const void *v, const void *ki,
                           void *kc, void *vc, void *kic, void *stream);
 
 /*
+ * csa_compress_window — csa_compress with overlapping windows (CSA).
+ * hyper.ai "Method": the HCA paragraph states that HCA compresses without
+ * overlap, setting it apart from CSA, whose windows the page leaves open.
+ * Entry j pools the `width` tokens ending where block j ends:
+ *   rows t = (j+1)m - width + i, i = 0..width-1 (rows t < 0 are absent),
+ *   a_i = k_t . g + pos_bias[i],  p = softmax over the window's rows,
+ *   Kc_j = sum p_i k_t,  Vc_j = sum p_i v_t,  KIc_j = sum p_i kI_t.
+ * m <= width <= 2m; width = m is csa_compress.  pos_bias has `width` entries
+ * (window positions, oldest first) or is NULL.  Entry j is complete once
+ * (j+1)m tokens exist, as without overlap; other arguments as csa_compress.
+ */
+csa_status_t csa_compress_window(const void *k, const void *v, const void *ki,
+                                 const float *gate, const float *pos_bias,
+                                 int B, int T, int d, int dI, int m, int width, int Nc_cap,
+                                 csa_dtype_t dt, void *kc, void *vc, void *kic, void *stream);
+
+/*
  * csa_indexer_topk — lightning-indexer scores and top-k selection.
  * hyper.ai "Method", CSA paragraph (a lightning indexer selects the top-k
  * compressed entries); aiboss88 "Technical Principles", CSA bullet (index

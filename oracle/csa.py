@@ -48,6 +48,41 @@ def compress(x_k, x_v, x_ki, g, m, pos_bias=None):
     return kc, vc, kic
 
 
+def compress_window(x_k, x_v, x_ki, g, m, width, pos_bias=None):
+    """Softmax-gated pooling over overlapping windows.
+
+    Reading: the HCA paragraph of the hyper.ai summary singles HCA out as
+    compressing without overlap, so CSA's windows may overlap; the page gives
+    no width.  Entry j pools the `width` tokens that end where block j ends,
+    t = (j+1)m - width + i for i = 0..width-1, skipping t < 0, with the gate
+    a_i = k_t . g + b_i (b indexed by window position) and the same softmax
+    pooling as `compress`.  width = m is `compress`; entry j still needs
+    (j+1)m tokens.
+
+    x_k, x_v: [T, d]; x_ki: [T, dI] or None; pos_bias: [width] or None.
+    """
+    x_k = np.asarray(x_k, dtype=np.float64)
+    x_v = np.asarray(x_v, dtype=np.float64)
+    gv = np.asarray(g, dtype=np.float64)
+    T, d = x_k.shape
+    nc = T // m
+    bias = np.zeros(width) if pos_bias is None else np.asarray(pos_bias, dtype=np.float64)
+    kc = np.zeros((nc, d))
+    vc = np.zeros((nc, d))
+    kic = None if x_ki is None else np.zeros((nc, np.asarray(x_ki).shape[1]))
+    for j in range(nc):
+        start = (j + 1) * m - width
+        rows = [start + i for i in range(width) if start + i >= 0]
+        a = np.array([x_k[t] @ gv + bias[t - start] for t in rows])
+        p = np.exp(a - a.max())
+        p /= p.sum()
+        kc[j] = p @ x_k[rows]
+        vc[j] = p @ x_v[rows]
+        if kic is not None:
+            kic[j] = p @ np.asarray(x_ki, dtype=np.float64)[rows]
+    return kc, vc, kic
+
+
 def n_eligible(t, m):
     """Entries visible to a query at absolute position t: completed blocks
     only, i.e. block j is visible once its last token jm+m-1 <= t."""

@@ -23,6 +23,8 @@ EXPORTS = {
     "csa_abi_version": (_I, []),
     "csa_last_error": (C.c_char_p, []),
     "csa_compress": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P]),
+    "csa_compress_window": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P,
+                                 _P]),
     "csa_indexer_topk_workspace": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
     "csa_indexer_topk": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I,
                               _P, _P, _P, _SZ, _P]),

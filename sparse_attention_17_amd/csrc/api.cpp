@@ -71,11 +71,14 @@ int csa_abi_version(void) { return CSA_ABI_VERSION; }
 
 const char* csa_last_error(void) { return g_err.c_str(); }
 
-csa_status_t csa_compress(const void* k, const void* v, const void* ki, const float* gate,
-                          const float* pos_bias, int B, int T, int d, int dI, int m, int Nc_cap,
-                          csa_dtype_t dt, void* kc, void* vc, void* kic, void* stream) {
+csa_status_t csa_compress_window(const void* k, const void* v, const void* ki, const float* gate,
+                                 const float* pos_bias, int B, int T, int d, int dI, int m,
+                                 int width, int Nc_cap, csa_dtype_t dt, void* kc, void* vc,
+                                 void* kic, void* stream) {
   REQUIRE(B >= 0 && T >= 0, CSA_INVALID_ARGUMENT, "B and T must be >= 0 (got %d, %d)", B, T);
   REQUIRE(m >= 1 && m <= 4096, CSA_INVALID_ARGUMENT, "m must be in [1, 4096] (got %d)", m);
+  REQUIRE(width >= m && width <= 2 * m, CSA_INVALID_ARGUMENT,
+          "width must be in [m, 2m] (got %d for m=%d)", width, m);
   REQUIRE(Nc_cap >= 0 && T / m <= Nc_cap, CSA_INVALID_ARGUMENT,
           "Nc_cap (%d) must hold T/m = %d entries", Nc_cap, T / m);
   REQUIRE(attn_dtype_ok(dt), CSA_UNSUPPORTED, "csa_compress: dtype must be CSA_F32 or CSA_BF16");
@@ -95,8 +98,15 @@ csa_status_t csa_compress(const void* k, const void* v, const void* ki, const fl
     REQUIRE_PTR(kic, "kic");
   }
   if (pos_bias) REQUIRE(aligned(pos_bias, 4), CSA_INVALID_ARGUMENT, "pos_bias must be 4-byte aligned");
-  csa::CompressArgs a{k, v, ki, gate, pos_bias, B, T, d, dI, m, Nc_cap, dt == CSA_F32, kc, vc, kic};
+  csa::CompressArgs a{k, v, ki, gate, pos_bias, B, T, d, dI, m, width, Nc_cap, dt == CSA_F32, kc, vc, kic};
   return device_status(csa::launch_compress(a, (hipStream_t)stream), "csa_compress launch");
+}
+
+csa_status_t csa_compress(const void* k, const void* v, const void* ki, const float* gate,
+                          const float* pos_bias, int B, int T, int d, int dI, int m, int Nc_cap,
+                          csa_dtype_t dt, void* kc, void* vc, void* kic, void* stream) {
+  return csa_compress_window(k, v, ki, gate, pos_bias, B, T, d, dI, m, m, Nc_cap, dt, kc, vc, kic,
+                             stream);
 }
 
 size_t csa_indexer_topk_workspace(int B, int Tq, int Nc_cap, int HI, int dI, int topk,

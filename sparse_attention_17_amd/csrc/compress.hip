@@ -2,9 +2,13 @@
 // the indexer keys into one entry (CSA with m, HCA with m').
 // Method: DeepSeek-V4 summary (hyper.ai), "Method", CSA paragraph — m tokens
 // become one entry through learnable compression weights and positional
-// biases; HCA paragraph — m' tokens, no overlap.  Form implemented:
-//   a_i = k_i . g + b_(i mod m),  p = softmax over the block,
-//   Kc = sum p_i k_i,  Vc = sum p_i v_i,  KIc = sum p_i kI_i.
+// biases; HCA paragraph — m' tokens with no overlap between entries, which
+// the page states for HCA only.  Form implemented, for entry j and a window of `width`
+// tokens ending where block j ends (width = m: the block itself; width > m:
+// windows of consecutive entries overlap by width - m tokens):
+//   rows t = (j+1)m - width + i, i = 0..width-1, t >= 0 (earlier ones absent)
+//   a_i = k_t . g + b_i,  p = softmax over the window's rows,
+//   Kc = sum p_i k_t,  Vc = sum p_i v_t,  KIc = sum p_i kI_t.
 //
 // Mapping: one wavefront per block.  A row of d elements is read by G lanes
 // with 16-byte loads (G = d*sizeof(T)/16), so a wave covers R = 64/G rows per
@@ -20,7 +24,7 @@ template <typename T, int D, int DI>
 __global__ __launch_bounds__(256) void compress_kernel(
     const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ ki,
     const float* __restrict__ gate, const float* __restrict__ pos_bias,
-    int T_len, int m, int Nc, int Nc_cap,
+    int T_len, int m, int width, int Nc, int Nc_cap,
     T* __restrict__ kc, T* __restrict__ vc, T* __restrict__ kic) {
   constexpr int VEC = 16 / sizeof(T);          // elements per lane per K/V row
   constexpr int G = D / VEC;                   // lanes per row
@@ -46,16 +50,19 @@ __global__ __launch_bounds__(256) void compress_kernel(
 #pragma unroll
   for (int e = 0; e < KIV; ++e) ai[e] = 0.f;
 
-  const size_t row0 = (size_t)b * T_len + (size_t)j * m;
+  // window rows t = t0 + i; rows before the sequence start are absent
+  const long long t0 = (long long)(j + 1) * m - width;
+  const int i_lo = t0 < 0 ? (int)-t0 : 0;
+  const size_t seq0 = (size_t)b * T_len;
   const bool has_ki = (ki != nullptr);
 
-  for (int i0 = 0; i0 < m; i0 += R * U) {
+  for (int i0 = i_lo; i0 < width; i0 += R * U) {
     T rk[U][VEC], rv[U][VEC], ri[U][KIV];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i = i0 + u * R + slot;
-      if (i < m) {
-        const size_t r = row0 + i;
+      if (i < width) {
+        const size_t r = seq0 + (size_t)(t0 + i);
 #pragma unroll
         for (int e = 0; e < VEC; e += 16 / sizeof(T)) {
           *reinterpret_cast<u32x4*>(&rk[u][e]) =
@@ -78,7 +85,7 @@ __global__ __launch_bounds__(256) void compress_kernel(
       for (int e = 0; e < VEC; ++e) a = fmaf(to_f32(rk[u][e]), g[e], a);
 #pragma unroll
       for (int o = 1; o < G; o <<= 1) a += __shfl_xor(a, o, 64);
-      if (i < m) {
+      if (i < width) {
         if (pos_bias) a += pos_bias[i];
         const float Mn = fmaxf(M, a);
         const float c = __expf(M - Mn);
@@ -143,7 +150,7 @@ static hipError_t launch_t(const CompressArgs& a, hipStream_t st) {
   ProfScope ps("compress", st);
   hipLaunchKernelGGL((compress_kernel<T, D, DI>), grid, dim3(256), 0, st,
                      (const T*)a.k, (const T*)a.v, (const T*)a.ki, a.gate, a.pos_bias,
-                     a.T, a.m, Nc, a.Nc_cap, (T*)a.kc, (T*)a.vc, (T*)a.kic);
+                     a.T, a.m, a.width, Nc, a.Nc_cap, (T*)a.kc, (T*)a.vc, (T*)a.kic);
   return hipGetLastError();
 }
 

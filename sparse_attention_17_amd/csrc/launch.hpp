@@ -24,7 +24,7 @@ class ProfScope {
 struct CompressArgs {
   const void *k, *v, *ki;
   const float *gate, *pos_bias;
-  int B, T, d, dI, m, Nc_cap;
+  int B, T, d, dI, m, width, Nc_cap;   // width: tokens pooled per entry (m: no overlap)
   bool f32;
   void *kc, *vc, *kic;
 };

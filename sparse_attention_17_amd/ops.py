@@ -48,10 +48,12 @@ def _ws(nbytes: int, dev):
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=dev)
 
 
-def compress(k, v, ki, gate, m, pos_bias=None, Nc_cap=None):
+def compress(k, v, ki, gate, m, pos_bias=None, Nc_cap=None, width=None):
     """Softmax-gated block pooling.  k, v [B,T,d]; ki [B,T,dI] or None;
-    gate [d] fp32; pos_bias [m] fp32 or None.  Returns kc, vc [B,Nc_cap,d],
-    kic [B,Nc_cap,dI] (None without ki); rows >= T//m are left unwritten."""
+    gate [d] fp32; pos_bias [width] fp32 or None; width (m..2m, default m)
+    tokens pooled per entry, ending where the entry's block ends.  Returns kc,
+    vc [B,Nc_cap,d], kic [B,Nc_cap,dI] (None without ki); rows >= T//m are
+    left unwritten."""
     dev = _dev_check(k, v, ki, gate, pos_bias)
     B, T, d = k.shape
     dI = ki.shape[-1] if ki is not None else 0
@@ -59,8 +61,9 @@ def compress(k, v, ki, gate, m, pos_bias=None, Nc_cap=None):
     kc = torch.empty(B, cap, d, dtype=k.dtype, device=dev)
     vc = torch.empty_like(kc)
     kic = torch.empty(B, cap, dI, dtype=k.dtype, device=dev) if ki is not None else None
-    L.check(L.load().csa_compress(_p(k), _p(v), _p(ki), _p(gate), _p(pos_bias), B, T, d, dI, m,
-                                  cap, _attn_dt(k), _p(kc), _p(vc), _p(kic), _stream(dev)))
+    L.check(L.load().csa_compress_window(_p(k), _p(v), _p(ki), _p(gate), _p(pos_bias), B, T, d,
+                                         dI, m, m if width is None else width, cap, _attn_dt(k),
+                                         _p(kc), _p(vc), _p(kic), _stream(dev)))
     return kc, vc, kic
 
 

@@ -64,6 +64,16 @@ def test_compress_validation(lib):
     assert lib.csa_last_error() == b""
 
 
+def test_compress_window_validation(lib):
+    a = dict(k=FAKE, v=FAKE, ki=None, gate=FAKE, pos_bias=None, B=1, T=64, d=128, dI=64, m=4,
+             width=8, Nc_cap=16, dt=L.BF16, kc=FAKE, vc=FAKE, kic=None, stream=None)
+    call = lambda **kw: lib.csa_compress_window(*{**a, **kw}.values())
+    assert call(width=3) == L.INVALID_ARGUMENT          # below m
+    assert call(width=9) == L.INVALID_ARGUMENT          # above 2m
+    assert b"width" in lib.csa_last_error()
+    assert call(B=0) == L.OK
+
+
 def _indexer(lib, **kw):
     a = dict(qi=FAKE, qi_scale=None, w=FAKE, kic=FAKE, kic_scale=None, pos0=FAKE, max_pos=1023,
              B=1, Tq=1, Nc_cap=256, HI=4, dI=64, m=4, topk=32, qk=L.BF16, idx=FAKE, score=None,

@@ -1,5 +1,6 @@
 """GPU parity of csa_compress against the fp64 oracle: fp32 within 1e-5
-max-abs, bf16 within one bf16 ulp of the exact pooled value."""
+max-abs, bf16 within one bf16 ulp of the exact pooled value; overlapping
+windows (csa_compress_window) within the fp32 / bf16 output tolerances."""
 import numpy as np
 import pytest
 import torch
@@ -89,3 +90,24 @@ def test_hca_1m_compress_sample():
         assert bf16_ulp_ok(kc[0, j], rk[0], 1.0, pool_slack(f64(k[0, sl]), 128)[0])[0] == 0
         assert bf16_ulp_ok(vc[0, j], rv[0], 1.0, pool_slack(f64(v[0, sl]), 128)[0])[0] == 0
     del w
+
+
+@pytest.mark.parametrize("dtype,T,m,width,B", [("f32", 1024, 4, 8, 1), ("f32", 1030, 4, 5, 2),
+                                               ("bf16", 32768, 4, 8, 1), ("bf16", 4099, 5, 10, 2),
+                                               ("bf16", 2048, 128, 256, 1)])
+def test_overlapping_windows(dtype, T, m, width, B):
+    # each entry pools the `width` tokens ending at its block's end (csa_compress_window)
+    base = configs.TINY if dtype == "f32" else configs.CSA_PREFILL_32K
+    w = base.with_(ctx=T, Tq=T, m=m, B=B)
+    x = inputs.make_inputs(w)
+    pb = inputs.normal(w.wid, "pos_bias", (width,), False)
+    g = {k: v.to(dev()) for k, v in x.items()}
+    kc, vc, kic = ops.compress(g["k"], g["v"], g["ki"], g["g"], m, pos_bias=pb.to(dev()), width=width)
+    torch.cuda.synchronize()
+    assert kc.shape[1] == T // m
+    for b in range(B):
+        rk, rv, rki = oracle.csa.compress_window(f64(x["k"][b]), f64(x["v"][b]), f64(x["ki"][b]),
+                                                 f64(x["g"]), m, width, f64(pb))
+        assert_close(kc[b], rk, dtype, f"kc[{b}]")
+        assert_close(vc[b], rv, dtype, f"vc[{b}]")
+        assert_close(kic[b], rki, dtype, f"kic[{b}]")

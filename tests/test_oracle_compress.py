@@ -1,5 +1,7 @@
 """Pins for oracle.csa.compress: closed forms of softmax-gated pooling and a
-pure-Python brute force on tiny blocks."""
+pure-Python brute force on tiny blocks; for compress_window: width m is block
+compression, a zero gate gives the mean of the window's present rows, and a
+dominant bias selects the row at that window position."""
 import math
 
 import numpy as np
@@ -90,3 +92,39 @@ def test_eligibility_counts_completed_blocks():
     assert csa.n_eligible(3, 4) == 1
     assert csa.n_eligible(7, 4) == 2
     assert csa.n_eligible(131071, 4) == 32768
+
+
+# ---- overlapping windows ----
+def test_window_of_m_is_block_compression():
+    rng = np.random.default_rng(40)
+    T, d, dI, m = 37, 6, 4, 4
+    k, v, ki = rng.standard_normal((T, d)), rng.standard_normal((T, d)), rng.standard_normal((T, dI))
+    g, b = rng.standard_normal(d), rng.standard_normal(m)
+    got = csa.compress_window(k, v, ki, g, m, m, b)
+    ref = csa.compress(k, v, ki, g, m, b)
+    for x, y in zip(got, ref):
+        np.testing.assert_allclose(x, y, rtol=1e-12, atol=1e-13)
+
+
+def test_window_without_gate_is_the_mean_of_present_rows():
+    # zero gate and biases: every present row of the window has weight 1/count
+    rng = np.random.default_rng(41)
+    T, d, m, width = 20, 5, 4, 7
+    k, v = rng.standard_normal((T, d)), rng.standard_normal((T, d))
+    kc, vc, _ = csa.compress_window(k, v, None, np.zeros(d), m, width)
+    np.testing.assert_allclose(kc[0], k[0:4].mean(axis=0), rtol=1e-13)    # rows -3..3: 0..3 present
+    np.testing.assert_allclose(vc[1], v[1:8].mean(axis=0), rtol=1e-13)    # rows 1..7
+    np.testing.assert_allclose(vc[4], v[13:20].mean(axis=0), rtol=1e-13)  # rows 13..19
+
+
+def test_window_bias_indexes_window_positions():
+    # a dominant bias on window position p selects row (j+1)m - width + p
+    rng = np.random.default_rng(42)
+    T, d, m, width = 24, 3, 4, 8
+    k, v = rng.standard_normal((T, d)), rng.standard_normal((T, d))
+    for p in (0, 3, 7):
+        b = np.zeros(width)
+        b[p] = 200.0
+        kc, vc, _ = csa.compress_window(k, v, None, rng.standard_normal(d) * 0.1, m, width, b)
+        for j in range(1, T // m):
+            np.testing.assert_allclose(vc[j], v[(j + 1) * m - width + p], rtol=1e-9, atol=1e-12)
