@@ -249,7 +249,7 @@ def suite():
         for name in names:
             c, t = C.c_int(0), C.c_double(0)
             if lib.csa_profile_query(name.encode(), C.byref(c), C.byref(t)) == 0:
-                res[f"{key}.{name}_us"] = t.value / c.value * 1e3
+                res[f"{key}.kernel.{name}_us"] = t.value / c.value * 1e3
         lib.csa_profile_reset()
 
     # CSA prefill, 32K tokens (compress -> fused indexer/top-k -> sparse attention)
@@ -295,8 +295,14 @@ def suite():
     res[f"{key}.indexer_topk_us"] = timeit(ind)
     res[f"{key}.sparse_attend_us"] = timeit(att)
     kernels(lambda: (ind(), att()), ("indexer_score", "indexer_topk", "attend_csa", "attend_combine"), key)
-    res[f"{key}.indexer_score_GBs"] = w.B * w.Nc * w.dI * 2 / res[f"{key}.indexer_score_us"] / 1e3
-    del x, g, idx
+    res[f"{key}.indexer_score_GBs"] = w.B * w.Nc * w.dI * 2 / res[f"{key}.kernel.indexer_score_us"] / 1e3
+    # the same attention over FP8 caches with the BF16 RoPE half (328 instead of 512 bytes per entry)
+    from synth import quant
+    c8 = tuple(t.to(dev) for t in quant.quant_kv8(x["kc"], x["vc"]))
+    att8 = lambda: ops.sparse_attend_kv8(g["q"], c8, idx, pos0, w.ctx - 1, w.window, kw=g["kw"],
+                                         vw=g["vw"], raw_pos0=rp0, sink=g["sink"])
+    res[f"{key}.sparse_attend_kv8_us"] = timeit(att8)
+    del x, g, idx, c8
 
     # HCA at 1M context: decode batch 16 and a 4096-query prefill chunk
     for w in (configs.HCA_1M_DECODE, configs.HCA_1M_PREFILL):
@@ -309,6 +315,12 @@ def suite():
         res[f"{key}.hca_us"] = timeit(fn, n=20 if w.Tq == 1 else 5)
         if w.Tq == 1:
             res[f"{key}.GBs"] = w.B * (w.Nc_hca * w.d * 2 * 2 + 2 * w.H * w.d * 2) / res[f"{key}.hca_us"] / 1e3
+            from synth import quant
+            c8 = tuple(t.to(dev) for t in quant.quant_kv8(x["kc_hca"], x["vc_hca"]))
+            fn8 = lambda: ops.hca_attend_kv8(g["q_hca"], c8, w.m_hca, pos0, w.ctx - 1, sink=g["sink_hca"])
+            res[f"{key}.hca_kv8_us"] = timeit(fn8)
+            res[f"{key}.kv8_GBs"] = w.B * (w.Nc_hca * 328 + 2 * w.H * w.d * 2) / res[f"{key}.hca_kv8_us"] / 1e3
+            del c8
         else:
             res[f"{key}.TFLOPs"] = 1.097e12 / res[f"{key}.hca_us"] / 1e6
         del x, g
@@ -323,7 +335,7 @@ def suite():
     res["hybrid_1m_fp4.indexer_topk_us"] = timeit(ind)
     kernels(ind, ("indexer_score", "indexer_topk"), "hybrid_1m_fp4")
     res["hybrid_1m_fp4.indexer_score_GBs"] = w.B * w.Nc * (w.dI // 2 + w.dI // 32) / \
-        res["hybrid_1m_fp4.indexer_score_us"] / 1e3
+        res["hybrid_1m_fp4.kernel.indexer_score_us"] / 1e3
     del x, g
 
     # HCA compression of a 1M-token sequence at m'=128

@@ -197,6 +197,41 @@ csa_status_t hca_attend(const void *q, const void *kc, const void *vc, int m_pri
                         void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * csa_sparse_attend_kv8 / hca_attend_kv8 — the same attention over caches
+ * stored in mixed precision.  hyper.ai "Method", efficiency paragraph: the
+ * KV cache keeps its RoPE dimensions in BF16 and the other dimensions in
+ * FP8.  Layout read here (the page fixes neither the split nor the scales):
+ *   k8     [B, Nc_cap, d/2]  uint8  E4M3 codes of key dims 0 .. d/2-1
+ *   krope  [B, Nc_cap, d/2]  bf16   key dims d/2 .. d-1 (the RoPE part)
+ *   kscale [B, Nc_cap]       fp32   one scale per key row (codes * scale)
+ *   v8     [B, Nc_cap, d]    uint8  E4M3 codes of all value dims (values
+ *                                   carry no position encoding)
+ *   vscale [B, Nc_cap]       fp32   one scale per value row
+ * Codes are widened exactly, multiplied by the row scale in fp32 and rounded
+ * to bf16 while the tile is staged in LDS (exact when scales are powers of
+ * two); the attention then runs as on bf16 caches.  q, out, kw, vw are bf16;
+ * d = 128.  Other arguments, workspace sizes and errors as csa_sparse_attend
+ * and hca_attend.
+ */
+csa_status_t csa_sparse_attend_kv8(const void *q, const void *k8, const void *krope,
+                                   const float *kscale, const void *v8, const float *vscale,
+                                   const int32_t *idx, int topk,
+                                   const void *kw, const void *vw, const int32_t *raw_pos0, int R,
+                                   const int32_t *pos0, int max_pos, int window,
+                                   const float *sink, float softmax_scale,
+                                   int B, int Tq, int H, int d, int Nc_cap,
+                                   void *out, float *lse_out,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+csa_status_t hca_attend_kv8(const void *q, const void *k8, const void *krope, const float *kscale,
+                            const void *v8, const float *vscale, int m_prime, int Nc_cap,
+                            const void *kw, const void *vw, const int32_t *raw_pos0, int R,
+                            int window, const int32_t *pos0, int max_pos,
+                            const float *sink, float softmax_scale,
+                            int B, int Tq, int H, int d,
+                            void *out, float *lse_out,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * csa_hybrid_attend — the CSA attention and the HCA attention of one hybrid
  * layer pair (hyper.ai "Method": a CSA layer and an HCA layer side by side,
  * each with its sliding-window branch) in one call.

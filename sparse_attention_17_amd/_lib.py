@@ -34,6 +34,10 @@ EXPORTS = {
     "hca_attend_workspace": (_SZ, [_I, _I, _I, _I, _I, _I, _I]),
     "hca_attend": (_I, [_P, _P, _P, _I, _I, _P, _P, _P, _I, _I, _P, _I, _P, C.c_float,
                         _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
+    "csa_sparse_attend_kv8": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _I, _P, _I, _I, _P,
+                                   C.c_float, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
+    "hca_attend_kv8": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _P, _P, _P, _I, _I, _P, _I, _P,
+                            C.c_float, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
     "csa_hybrid_attend": (_I, [_P, _P, _P, _P, _I, _P, _P, _P, _I, _P, _I, _I, _P, C.c_float,
                                _I, _I, _I, _I, _I, _I, _P, _P, _P, _SZ,
                                _P, _P, _P, _I, _I, _P, _P, _P, _I, _I, _P, _I, _P, C.c_float,

@@ -296,6 +296,57 @@ csa_status_t hca_attend(const void* q, const void* kc, const void* vc, int m_pri
   return device_status(csa::launch_attend(a, (hipStream_t)stream), "hca_attend launch");
 }
 
+// FP8 cache planes (validated after the shared checks, which see k8/v8 as kc/vc)
+static csa_status_t add_kv8(csa::AttendArgs* a, int d, csa_dtype_t dt, const void* k8,
+                            const void* krope, const float* kscale, const void* v8,
+                            const float* vscale) {
+  REQUIRE(dt == CSA_BF16, CSA_UNSUPPORTED, "FP8 caches need bf16 queries and window rows");
+  REQUIRE(d == 128, CSA_UNSUPPORTED, "FP8 caches are built for d=128 (got %d)", d);
+  REQUIRE_PTR(krope, "krope");
+  REQUIRE_PTR4(kscale, "kscale");
+  REQUIRE_PTR4(vscale, "vscale");
+  a->kv8 = true;
+  a->k8 = k8; a->krope = krope; a->v8 = v8; a->kscale = kscale; a->vscale = vscale;
+  a->kc = nullptr; a->vc = nullptr;
+  return ok();
+}
+
+csa_status_t csa_sparse_attend_kv8(const void* q, const void* k8, const void* krope,
+                                   const float* kscale, const void* v8, const float* vscale,
+                                   const int32_t* idx, int topk, const void* kw, const void* vw,
+                                   const int32_t* raw_pos0, int R, const int32_t* pos0,
+                                   int max_pos, int window, const float* sink, float softmax_scale,
+                                   int B, int Tq, int H, int d, int Nc_cap, void* out,
+                                   float* lse_out, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  csa::AttendArgs a;
+  bool empty;
+  csa_status_t st = build_sparse(q, k8, v8, idx, topk, kw, vw, raw_pos0, R, pos0, max_pos, window,
+                                 sink, softmax_scale, B, Tq, H, d, Nc_cap, CSA_BF16, out, lse_out,
+                                 workspace, workspace_bytes, &a, &empty);
+  if (st != CSA_OK || empty) return st;
+  st = add_kv8(&a, d, CSA_BF16, k8, krope, kscale, v8, vscale);
+  if (st != CSA_OK) return st;
+  return device_status(csa::launch_attend(a, (hipStream_t)stream), "csa_sparse_attend_kv8 launch");
+}
+
+csa_status_t hca_attend_kv8(const void* q, const void* k8, const void* krope, const float* kscale,
+                            const void* v8, const float* vscale, int m_prime, int Nc_cap,
+                            const void* kw, const void* vw, const int32_t* raw_pos0, int R,
+                            int window, const int32_t* pos0, int max_pos, const float* sink,
+                            float softmax_scale, int B, int Tq, int H, int d, void* out,
+                            float* lse_out, void* workspace, size_t workspace_bytes, void* stream) {
+  csa::AttendArgs a;
+  bool empty;
+  csa_status_t st = build_hca(q, k8, v8, m_prime, Nc_cap, kw, vw, raw_pos0, R, window, pos0, max_pos,
+                              sink, softmax_scale, B, Tq, H, d, CSA_BF16, out, lse_out, workspace,
+                              workspace_bytes, &a, &empty);
+  if (st != CSA_OK || empty) return st;
+  st = add_kv8(&a, d, CSA_BF16, k8, krope, kscale, v8, vscale);
+  if (st != CSA_OK) return st;
+  return device_status(csa::launch_attend(a, (hipStream_t)stream), "hca_attend_kv8 launch");
+}
+
 csa_status_t csa_hybrid_attend(
     const void* q, const void* kc, const void* vc, const int32_t* idx, int topk, const void* kw,
     const void* vw, const int32_t* raw_pos0, int R, const int32_t* pos0, int max_pos, int window,

@@ -59,9 +59,10 @@ __device__ __forceinline__ int vt_block(int dim, int kb) { return kb ^ ((dim >> 
 // workgroups share a compute unit and one's loads overlap the other's math.
 // The body takes its workgroup's coordinates (token tile bx, split by,
 // sequence bz) and the dynamic LDS block from the kernel that runs it.
-template <typename T, int D, int RW, int KG, bool SPARSE, int PF>
+template <typename T, int D, int RW, int KG, bool SPARSE, int PF, bool KV8 = false>
 __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom& gm, int bx, int by,
                                             int bz, unsigned char* smem_raw) {
+  static_assert(!KV8 || sizeof(T) == 2, "FP8 caches go with bf16 queries");
   constexpr int NW = RW * KG;
   constexpr int NT = NW * 64;
   constexpr int NSUB = 2 / KG;                 // 32-key sub-tiles per wave per tile
@@ -203,10 +204,44 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
   const __amdgpu_buffer_rsrc_t rvc = rsrc(vcb, (uint32_t)a.Nc_cap * ROWB);
   const __amdgpu_buffer_rsrc_t rkw = rsrc(kwb, kwb ? (uint32_t)a.R * ROWB : 0u);
   const __amdgpu_buffer_rsrc_t rvw = rsrc(vwb, vwb ? (uint32_t)a.R * ROWB : 0u);
-  auto comp_off = [&](int s) -> uint32_t {
-    if (s < kbeg || s >= kend || s >= ncomp) return OOB;
+  // compressed entry held by key slot s, or -1
+  auto ent = [&](int s) -> int {
+    if (s < kbeg || s >= kend || s >= ncomp) return -1;
     const int e = SPARSE ? sel[s - sel_base] : s;
-    return (e >= 0 && e < a.Nc_cap) ? (uint32_t)e * ROWB : OOB;
+    return (e >= 0 && e < a.Nc_cap) ? e : -1;
+  };
+  auto comp_off = [&](int s) -> uint32_t {
+    const int e = ent(s);
+    return e >= 0 ? (uint32_t)e * ROWB : OOB;
+  };
+  // FP8 cache planes of this sequence
+  constexpr int DN = D / 2;                                  // E4M3 dims of a K row (the rest is bf16)
+  const size_t cb = (size_t)b * a.Nc_cap;
+  const __amdgpu_buffer_rsrc_t rk8 = rsrc(KV8 ? (const uint8_t*)a.k8 + cb * DN : nullptr, KV8 ? (uint32_t)a.Nc_cap * DN : 0u);
+  const __amdgpu_buffer_rsrc_t rkr = rsrc(KV8 ? (const uint16_t*)a.krope + cb * (D - DN) : nullptr,
+                                          KV8 ? (uint32_t)a.Nc_cap * (D - DN) * 2 : 0u);
+  const __amdgpu_buffer_rsrc_t rv8 = rsrc(KV8 ? (const uint8_t*)a.v8 + cb * D : nullptr, KV8 ? (uint32_t)a.Nc_cap * D : 0u);
+  const __amdgpu_buffer_rsrc_t rks = rsrc(KV8 ? a.kscale + cb : nullptr, KV8 ? (uint32_t)a.Nc_cap * 4 : 0u);
+  const __amdgpu_buffer_rsrc_t rvs = rsrc(KV8 ? a.vscale + cb : nullptr, KV8 ? (uint32_t)a.Nc_cap * 4 : 0u);
+  // 8 codes (x, y) and their row scale (z) of an FP8 row chunk, or zeros
+  auto ld8 = [](const __amdgpu_buffer_rsrc_t& rc, const __amdgpu_buffer_rsrc_t& rs, int e, uint32_t off) -> u32x4 {
+    const auto c = __builtin_amdgcn_raw_buffer_load_b64(rc, e >= 0 ? off : OOB, 0, 0);
+    const uint32_t sc = __builtin_amdgcn_raw_buffer_load_b32(rs, e >= 0 ? (uint32_t)e * 4 : OOB, 0, 0);
+    return u32x4{c[0], c[1], sc, 0u};
+  };
+  // 8 E4M3 codes times the row scale, as 8 bf16 (codes widen exactly; the
+  // product is rounded to nearest even)
+  auto dequant8 = [](const u32x4& r) -> u32x4 {
+    const float sc = __uint_as_float(r[2]);
+    u32x4 o;
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r[w], 1.0f, false));
+      const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r[w], 1.0f, true));
+      o[2 * w] = pack_bf16x2(bf16_bits_to_f32(lo & 0xFFFFu) * sc, bf16_bits_to_f32(lo >> 16) * sc);
+      o[2 * w + 1] = pack_bf16x2(bf16_bits_to_f32(hi & 0xFFFFu) * sc, bf16_bits_to_f32(hi >> 16) * sc);
+    }
+    return o;
   };
   auto win_off = [&](int s) -> uint32_t {
     if (s < kbeg || s >= kend || s < ncomp) return OOB;
@@ -245,7 +280,17 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
           vreg[i][u] = fetch(false, c < VTOT ? s0 + (c / KCH) * 4 + u : INT_MAX / 2, c % KCH);
       }
     };
-    if (s0 + KT <= ncomp || nwin == 0) {
+    if constexpr (KV8) {
+      // FP8 rows: a K chunk below DN dims is 8 codes + scale, above it 8 bf16
+      // RoPE values; a V chunk is 8 codes + scale.  Window rows are bf16.
+      load_all([&](bool k, int s, int ch) {
+        const int e = ent(s);
+        u32x4 r = ld(k ? rkw : rvw, win_off(s), ch);
+        if (k && ch >= DN / VEC) return r | ld(rkr, e >= 0 ? (uint32_t)e * (D - DN) * 2 : OOB, ch - DN / VEC);
+        if (k) return r | ld8(rk8, rks, e, (uint32_t)e * DN + ch * 8);
+        return r | ld8(rv8, rvs, e, (uint32_t)e * D + ch * 8);
+      });
+    } else if (s0 + KT <= ncomp || nwin == 0) {
       load_all([&](bool k, int s, int ch) { return ld(k ? rkc : rvc, comp_off(s), ch); });
     } else if (s0 >= ncomp) {
       load_all([&](bool k, int s, int ch) { return ld(k ? rkw : rvw, win_off(s), ch); });
@@ -255,18 +300,29 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
       });
     }
   };
-  auto stage_store = [&](const auto& kreg, const auto& vreg) {
+  auto stage_store = [&](const auto& kreg, const auto& vreg, int s0) {
 #pragma unroll
     for (int i = 0; i < KLD; ++i) {
       const int c = tid + i * NT;
-      if (c < KT * KCH) *reinterpret_cast<u32x4*>(Ks + (c / KCH) * KS + (c % KCH) * VEC) = kreg[i];
+      if (c >= KT * KCH) continue;
+      u32x4 r = kreg[i];
+      if constexpr (KV8)
+        if (c % KCH < DN / VEC && ent(s0 + c / KCH) >= 0) r = dequant8(r);
+      *reinterpret_cast<u32x4*>(Ks + (c / KCH) * KS + (c % KCH) * VEC) = r;
     }
 #pragma unroll
     for (int i = 0; i < VTK; ++i) {
       const int c = tid + i * NT;
       if (c >= VTOT) continue;
       const int kg = c / KCH, ch = c % KCH;
-      const T* rows = reinterpret_cast<const T*>(vreg[i]);      // [4][VEC]
+      u32x4 vr[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        vr[u] = vreg[i][u];
+        if constexpr (KV8)
+          if (ent(s0 + kg * 4 + u) >= 0) vr[u] = dequant8(vr[u]);
+      }
+      const T* rows = reinterpret_cast<const T*>(vr);           // [4][VEC]
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
         T four[4] = {rows[e], rows[VEC + e], rows[2 * VEC + e], rows[3 * VEC + e]};
@@ -397,13 +453,13 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
   };
   if constexpr (PF == 2) {
     for (int s0 = kbeg; s0 < kend; s0 += 2 * KT) {
-      stage_store(kregA, vregA);
+      stage_store(kregA, vregA, s0);
       __syncthreads();
       if (s0 + 2 * KT < kend) stage_load(kregA, vregA, s0 + 2 * KT);
       tile(s0);
       __syncthreads();
       if (s0 + KT >= kend) break;
-      stage_store(kregB, vregB);
+      stage_store(kregB, vregB, s0 + KT);
       __syncthreads();
       if (s0 + 3 * KT < kend) stage_load(kregB, vregB, s0 + 3 * KT);
       tile(s0 + KT);
@@ -411,7 +467,7 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
     }
   } else {
     for (int s0 = kbeg; s0 < kend; s0 += KT) {
-      stage_store(kregA, vregA);
+      stage_store(kregA, vregA, s0);
       __syncthreads();
       if (s0 + KT < kend) stage_load(kregA, vregA, s0 + KT);
       tile(s0);
@@ -489,10 +545,10 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
   if (a.lse && half == 0) a.lse[grow] = lse;
 }
 
-template <typename T, int D, int RW, int KG, bool SPARSE, int PF>
-__global__ __launch_bounds__(RW * KG * 64) __attribute__((amdgpu_waves_per_eu(2))) void attend_kernel(AttendArgs a, AttnGeom gm) {
+template <typename T, int D, int RW, int KG, bool SPARSE, int PF, bool KV8>
+__global__ __launch_bounds__(RW * KG * 64) __attribute__((amdgpu_waves_per_eu(KV8 && !(RW == 2 && KG == 2) ? 1 : 2))) void attend_kernel(AttendArgs a, AttnGeom gm) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  attend_body<T, D, RW, KG, SPARSE, PF>(a, gm, blockIdx.x, blockIdx.y, blockIdx.z, smem_raw);
+  attend_body<T, D, RW, KG, SPARSE, PF, KV8>(a, gm, blockIdx.x, blockIdx.y, blockIdx.z, smem_raw);
 }
 
 // The HCA and CSA attention of one layer pair in a single split-decode launch:
@@ -634,10 +690,10 @@ static hipError_t set_lds(K kfn, size_t lds) {
 
 static size_t partial_rows(const AttendArgs& a) { return (size_t)a.B * a.Tq * a.H; }
 
-template <typename T, int D, int RW, int KG, bool SPARSE, int PF>
+template <typename T, int D, int RW, int KG, bool SPARSE, int PF, bool KV8>
 static hipError_t launch5(const AttendArgs& a, const AttnGeom& gm, hipStream_t st) {
   const size_t lds = attend_lds<T, D, SPARSE>(a, RW, KG);
-  auto kfn = attend_kernel<T, D, RW, KG, SPARSE, PF>;
+  auto kfn = attend_kernel<T, D, RW, KG, SPARSE, PF, KV8>;
   hipError_t e = set_lds(kfn, lds);
   if (e != hipSuccess) return e;
   dim3 grid((a.Tq + gm.TT - 1) / gm.TT, gm.nsplit, a.B);
@@ -653,9 +709,10 @@ static hipError_t launch5(const AttendArgs& a, const AttnGeom& gm, hipStream_t s
   return hipGetLastError();
 }
 
-template <typename T, int D, int RW, int KG, bool SPARSE>
+template <typename T, int D, int RW, int KG, bool SPARSE, bool KV8>
 static hipError_t launch4(const AttendArgs& a, const AttnGeom& gm, hipStream_t st) {
-  return gm.nsplit > 1 ? launch5<T, D, RW, KG, SPARSE, 2>(a, gm, st) : launch5<T, D, RW, KG, SPARSE, 1>(a, gm, st);
+  return gm.nsplit > 1 ? launch5<T, D, RW, KG, SPARSE, 2, KV8>(a, gm, st)
+                       : launch5<T, D, RW, KG, SPARSE, 1, KV8>(a, gm, st);
 }
 
 // Row-waves cover the tile's (token, head) rows; tiles of at most 64 rows get
@@ -667,19 +724,19 @@ static void wave_shape(int rows, int* RW, int* KG) {
   else { *RW = 4; *KG = 1; }
 }
 
-template <typename T, int D, bool SPARSE>
+template <typename T, int D, bool SPARSE, bool KV8>
 static hipError_t launch3(const AttendArgs& a, const AttnGeom& gm, hipStream_t st) {
   int RW, KG;
   wave_shape(gm.TT * a.H, &RW, &KG);
-  if (RW == 1) return launch4<T, D, 1, 2, SPARSE>(a, gm, st);
-  if (RW == 2) return launch4<T, D, 2, 2, SPARSE>(a, gm, st);
-  if (RW == 3) return launch4<T, D, 3, 1, SPARSE>(a, gm, st);
-  return launch4<T, D, 4, 1, SPARSE>(a, gm, st);
+  if (RW == 1) return launch4<T, D, 1, 2, SPARSE, KV8>(a, gm, st);
+  if (RW == 2) return launch4<T, D, 2, 2, SPARSE, KV8>(a, gm, st);
+  if (RW == 3) return launch4<T, D, 3, 1, SPARSE, KV8>(a, gm, st);
+  return launch4<T, D, 4, 1, SPARSE, KV8>(a, gm, st);
 }
 
-template <typename T, int D>
+template <typename T, int D, bool KV8 = false>
 static hipError_t launch2(const AttendArgs& a, const AttnGeom& gm, hipStream_t st) {
-  return a.sparse ? launch3<T, D, true>(a, gm, st) : launch3<T, D, false>(a, gm, st);
+  return a.sparse ? launch3<T, D, true, KV8>(a, gm, st) : launch3<T, D, false, KV8>(a, gm, st);
 }
 
 static AttnGeom make_geom(const AttendArgs& a) {
@@ -696,6 +753,7 @@ static AttnGeom make_geom(const AttendArgs& a) {
 hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
   if (a.B == 0 || a.Tq == 0) return hipSuccess;
   const AttnGeom gm = make_geom(a);
+  if (a.kv8) return a.d == 128 && !a.f32 ? launch2<bf16, 128, true>(a, gm, st) : hipErrorInvalidValue;
   if (a.f32) return a.d == 64 ? launch2<float, 64>(a, gm, st) : launch2<float, 128>(a, gm, st);
   return a.d == 64 ? launch2<bf16, 64>(a, gm, st) : launch2<bf16, 128>(a, gm, st);
 }
@@ -741,7 +799,7 @@ hipError_t launch_attend_pair(const AttendArgs& csa_a, const AttendArgs& hca_a, 
   // one launch needs the same kernel shape for both (split decode, same
   // element type, head dim and wave layout); otherwise they run one after the other
   const bool fuse = gc.nsplit > 1 && gh.nsplit > 1 && csa_a.f32 == hca_a.f32 && csa_a.d == hca_a.d &&
-                    rwc == rwh && kgc == kgh;
+                    rwc == rwh && kgc == kgh && !csa_a.kv8 && !hca_a.kv8;
   if (!fuse) {
     const hipError_t e = launch_attend(csa_a, st);
     return e != hipSuccess ? e : launch_attend(hca_a, st);

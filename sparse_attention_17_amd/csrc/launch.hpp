@@ -65,6 +65,12 @@ struct AttendArgs {
   void* out;
   float* lse;
   void* ws;
+  // FP8 cache storage (kv8): K rows hold d/2 E4M3 codes (dims 0..d/2-1, one
+  // fp32 scale per row) and d/2 bf16 values (dims d/2..d-1, the RoPE part); V
+  // rows hold d codes with one fp32 scale per row.  kc/vc are unused then.
+  bool kv8;
+  const void *k8, *krope, *v8;
+  const float *kscale, *vscale;
 };
 size_t attend_workspace(bool sparse, int B, int Tq, int H, int d, int topk, int window,
                         int Nc_cap, int m_prime, int max_pos);

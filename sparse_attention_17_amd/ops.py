@@ -196,3 +196,47 @@ def grouped_out_proj(o, w):
     L.check(lib.csa_grouped_out_proj(_p(o), _p(w), T, H, d, G, dg, _attn_dt(o), _p(y), _stream(dev)))
     return y
 
+
+def sparse_attend_kv8(q, cache, idx, pos0, max_pos, window, kw=None, vw=None, raw_pos0=None,
+                      sink=None, scale=None, return_lse=False):
+    """CSA core attention over FP8/BF16-RoPE caches.  cache = (k8 [B,N,d/2] uint8,
+    krope [B,N,d/2] bf16, kscale [B,N] f32, v8 [B,N,d] uint8, vscale [B,N] f32);
+    other arguments as sparse_attend (q, kw, vw bf16)."""
+    k8, krope, ks, v8, vs = cache
+    dev = _dev_check(q, k8, krope, ks, v8, vs, idx, pos0, kw, vw, raw_pos0, sink)
+    B, Tq, H, d = q.shape
+    topk = idx.shape[-1]
+    R = kw.shape[1] if kw is not None else 0
+    scale = d ** -0.5 if scale is None else scale
+    lib = L.load()
+    nws = lib.csa_sparse_attend_workspace(B, Tq, H, d, topk, window)
+    ws = _ws(nws, dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(B, Tq, H, dtype=torch.float32, device=dev) if return_lse else None
+    L.check(lib.csa_sparse_attend_kv8(_p(q), _p(k8), _p(krope), _p(ks), _p(v8), _p(vs), _p(idx),
+                                      topk, _p(kw), _p(vw), _p(raw_pos0), R, _p(pos0),
+                                      int(max_pos), window, _p(sink), float(scale), B, Tq, H, d,
+                                      k8.shape[1], _p(out), _p(lse), _p(ws), nws, _stream(dev)))
+    return (out, lse) if return_lse else out
+
+
+def hca_attend_kv8(q, cache, m_prime, pos0, max_pos, sink=None, scale=None, window=0, kw=None,
+                   vw=None, raw_pos0=None, return_lse=False):
+    """HCA dense attention over FP8/BF16-RoPE caches (cache as sparse_attend_kv8)."""
+    k8, krope, ks, v8, vs = cache
+    dev = _dev_check(q, k8, krope, ks, v8, vs, pos0, kw, vw, raw_pos0, sink)
+    B, Tq, H, d = q.shape
+    Nc_cap = k8.shape[1]
+    R = kw.shape[1] if kw is not None else 0
+    scale = d ** -0.5 if scale is None else scale
+    lib = L.load()
+    nws = lib.hca_attend_workspace(B, Tq, H, d, Nc_cap, m_prime, window)
+    ws = _ws(nws, dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(B, Tq, H, dtype=torch.float32, device=dev) if return_lse else None
+    L.check(lib.hca_attend_kv8(_p(q), _p(k8), _p(krope), _p(ks), _p(v8), _p(vs), m_prime, Nc_cap,
+                               _p(kw), _p(vw), _p(raw_pos0), R, window, _p(pos0), int(max_pos),
+                               _p(sink), float(scale), B, Tq, H, d, _p(out), _p(lse), _p(ws), nws,
+                               _stream(dev)))
+    return (out, lse) if return_lse else out
+

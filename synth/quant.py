@@ -69,3 +69,26 @@ def quant_fp4_blocks(x: torch.Tensor, block: int = 32):
         code = code.reshape(-1, n)
         oc[r0:r0 + step] = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
     return torch.from_numpy(out_codes), torch.from_numpy(out_scale)
+
+
+def quant_kv8(kc: torch.Tensor, vc: torch.Tensor):
+    """Mixed-precision cache rows (BF16 RoPE dims, FP8 the rest).
+
+    kc, vc: [..., d] values.  Key dims 0 .. d/2-1 become E4M3 codes with one
+    power-of-two scale per row, dims d/2 .. d-1 stay bf16; value rows become
+    E4M3 codes with one power-of-two scale per row.  Power-of-two scales
+    (2^ceil(log2(amax/448))) make code * scale exactly representable in bf16.
+    Returns (k8, krope, kscale, v8, vscale)."""
+    def rows(x):
+        x = x.float()
+        amax = x.abs().amax(dim=-1)
+        e = torch.ceil(torch.log2(torch.where(amax > 0, amax / FP8_MAX, torch.ones_like(amax))))
+        scale = torch.exp2(e).float()
+        y = (x / scale.unsqueeze(-1)).clamp(-FP8_MAX, FP8_MAX)
+        return y.to(torch.float8_e4m3fn).view(torch.uint8).contiguous(), scale.contiguous()
+    d = kc.shape[-1]
+    k8, ks = rows(kc[..., : d // 2])
+    v8, vs = rows(vc)
+    krope = kc[..., d // 2:].to(torch.bfloat16).contiguous()
+    return k8, krope, ks, v8, vs
+
