@@ -230,10 +230,20 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
     return u32x4{c[0], c[1], sc, 0u};
   };
   // 8 E4M3 codes times the row scale, as 8 bf16 (codes widen exactly; the
-  // product is rounded to nearest even)
+  // product is rounded to nearest even).  The hardware conversion applies only
+  // the exponent of its scale operand (measured on gfx950), so it serves the
+  // power-of-two scales directly and other scales take an fp32 multiply.
   auto dequant8 = [](const u32x4& r) -> u32x4 {
     const float sc = __uint_as_float(r[2]);
     u32x4 o;
+    if ((r[2] & 0x007FFFFFu) == 0u) {
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        o[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r[w], sc, false));
+        o[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r[w], sc, true));
+      }
+      return o;
+    }
 #pragma unroll
     for (int w = 0; w < 2; ++w) {
       const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r[w], 1.0f, false));
@@ -259,6 +269,11 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
   constexpr int VTK = (VTOT + NT - 1) / NT;
   u32x4 kregA[KLD], vregA[VTK][4];
   u32x4 kregB[PF == 2 ? KLD : 1], vregB[PF == 2 ? VTK : 1][4];
+  // K staging task c -> (row, 16-byte chunk): row-major for bf16 caches; for
+  // FP8 caches chunk-major, so that a wave's 64 lanes share one chunk (and
+  // with it the chunk's kind: codes or RoPE values)
+  auto krow = [](int c) { return KV8 ? c % KT : c / KCH; };
+  auto kch = [](int c) { return KV8 ? c / KT : c % KCH; };
   auto ld = [](const __amdgpu_buffer_rsrc_t& r, uint32_t off, uint32_t ch) -> u32x4 {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off == OOB ? OOB : off + ch * 16, 0, 0));
   };
@@ -270,7 +285,7 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
 #pragma unroll
       for (int i = 0; i < KLD; ++i) {
         const int c = tid + i * NT;
-        kreg[i] = fetch(true, c < KT * KCH ? s0 + c / KCH : INT_MAX / 2, c % KCH);
+        kreg[i] = fetch(true, c < KT * KCH ? s0 + krow(c) : INT_MAX / 2, kch(c));
       }
 #pragma unroll
       for (int i = 0; i < VTK; ++i) {
@@ -282,14 +297,20 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
     };
     if constexpr (KV8) {
       // FP8 rows: a K chunk below DN dims is 8 codes + scale, above it 8 bf16
-      // RoPE values; a V chunk is 8 codes + scale.  Window rows are bf16.
-      load_all([&](bool k, int s, int ch) {
+      // RoPE values (the chunk kind is uniform over a wave); a V chunk is 8
+      // codes + scale.  Window rows are bf16.
+      auto comp8 = [&](bool k, int s, int ch) -> u32x4 {
         const int e = ent(s);
-        u32x4 r = ld(k ? rkw : rvw, win_off(s), ch);
-        if (k && ch >= DN / VEC) return r | ld(rkr, e >= 0 ? (uint32_t)e * (D - DN) * 2 : OOB, ch - DN / VEC);
-        if (k) return r | ld8(rk8, rks, e, (uint32_t)e * DN + ch * 8);
-        return r | ld8(rv8, rvs, e, (uint32_t)e * D + ch * 8);
-      });
+        if (k && ch >= DN / VEC) return ld(rkr, e >= 0 ? (uint32_t)e * (D - DN) * 2 : OOB, ch - DN / VEC);
+        if (k) return ld8(rk8, rks, e, (uint32_t)e * DN + ch * 8);
+        return ld8(rv8, rvs, e, (uint32_t)e * D + ch * 8);
+      };
+      if (s0 + KT <= ncomp || nwin == 0)
+        load_all(comp8);
+      else if (s0 >= ncomp)
+        load_all([&](bool k, int s, int ch) { return ld(k ? rkw : rvw, win_off(s), ch); });
+      else
+        load_all([&](bool k, int s, int ch) { return comp8(k, s, ch) | ld(k ? rkw : rvw, win_off(s), ch); });
     } else if (s0 + KT <= ncomp || nwin == 0) {
       load_all([&](bool k, int s, int ch) { return ld(k ? rkc : rvc, comp_off(s), ch); });
     } else if (s0 >= ncomp) {
@@ -307,8 +328,8 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
       if (c >= KT * KCH) continue;
       u32x4 r = kreg[i];
       if constexpr (KV8)
-        if (c % KCH < DN / VEC && ent(s0 + c / KCH) >= 0) r = dequant8(r);
-      *reinterpret_cast<u32x4*>(Ks + (c / KCH) * KS + (c % KCH) * VEC) = r;
+        if (kch(c) < DN / VEC && ent(s0 + krow(c)) >= 0) r = dequant8(r);
+      *reinterpret_cast<u32x4*>(Ks + krow(c) * KS + kch(c) * VEC) = r;
     }
 #pragma unroll
     for (int i = 0; i < VTK; ++i) {
