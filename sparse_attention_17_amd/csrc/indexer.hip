@@ -915,12 +915,17 @@ __device__ __forceinline__ void pick_body(PickSmem& sm, const PickRow& R) {
     return;
   }
 
-  // ---- 4. output in slot order (= ascending entry order): thread tid owns
-  // the contiguous slots [32 tid, 32 tid + 32): keys > tau, and the first
-  // `need` keys == tau over the whole row ----
+  // ---- 4. output in slot order (= ascending entry order): the bitmap words
+  // are split into Q parts of L slots, thread tid owning part tid % Q of word
+  // tid / Q (so the threads hold the slots in order): keys > tau, and the
+  // first `need` keys == tau over the whole row ----
   constexpr int NWORDS = PER * PICK_NT / 32;
-  const uint32_t wgt = tid < NWORDS ? sm.bm_gt[tid] : 0u;
-  const uint32_t weq = tid < NWORDS ? sm.bm_eq[tid] : 0u;
+  constexpr int Q = PICK_NT / NWORDS >= 4 ? 4 : PICK_NT / NWORDS >= 2 ? 2 : 1;
+  constexpr int L = 32 / Q;
+  constexpr uint32_t LMASK = L == 32 ? 0xFFFFFFFFu : (1u << L) - 1u;
+  const int word = tid / Q, wpart = tid % Q;
+  const uint32_t wgt = word < NWORDS ? (sm.bm_gt[word] >> (wpart * L)) & LMASK : 0u;
+  const uint32_t weq = word < NWORDS ? (sm.bm_eq[word] >> (wpart * L)) & LMASK : 0u;
   const uint64_t pk = ((uint64_t)__popc(wgt) << 32) | (uint32_t)__popc(weq);
   uint64_t inc = pk;
 #pragma unroll
@@ -940,8 +945,9 @@ __device__ __forceinline__ void pick_body(PickSmem& sm, const PickRow& R) {
     const int bit = __ffs(m) - 1;
     if (e_seen++ < need) take |= 1u << bit;
   }
+  const int s0 = word * 32 + wpart * L;
   for (; take; take &= take - 1) {
-    const int s = tid * 32 + __ffs(take) - 1;
+    const int s = s0 + __ffs(take) - 1;
     if (pos < (uint32_t)k) {
       R.idx[pos] = (int32_t)(s < PICK_STASH ? sm.sel[s] : R.cand[s].y);
       if (R.sco) R.sco[pos] = __uint_as_float(R.cand[s].x);
