@@ -40,19 +40,12 @@
 namespace csa {
 
 static constexpr int SCORE_WG_ENTRIES = 256;   // prefill tile kernel: 4 waves x 4 tiles x 16
-static constexpr int ROW_CHUNK = 2048;         // long-row select: entries per split workgroup
-#ifndef CSA_SCORE_CHUNK
-#define CSA_SCORE_CHUNK 2048
-#endif
-static constexpr int SCORE_CHUNK = CSA_SCORE_CHUNK;   // decode score kernels: entries per chunk
-#ifndef CSA_SCORE_CPW
-#define CSA_SCORE_CPW 1
-#endif
-static constexpr int SCORE_CPW = CSA_SCORE_CPW;       // chunks per score_row_kernel workgroup
-#ifndef CSA_SCORE_DEPTH
-#define CSA_SCORE_DEPTH 3
-#endif
-static constexpr int SCORE_DEPTH = CSA_SCORE_DEPTH;   // entry groups in flight per wave
+// decode score kernels: entries per chunk (one chunk per workgroup; 1024
+// gives two rounds of resident workgroups on a 1M-entry batch, so one round's
+// chunk cuts overlap the other's loads)
+static constexpr int SCORE_CHUNK = 1024;
+static constexpr int SCORE_CPW = 1;            // chunks per score_row_kernel workgroup
+static constexpr int SCORE_DEPTH = 3;          // entry groups in flight per wave
 static constexpr int H1_BITS = 12;             // first radix digit (key bits 20..31)
 static constexpr int H1_BINS = 1 << H1_BITS;
 static constexpr int TOPK_NT = 512;
