@@ -189,3 +189,22 @@ def test_f32_decode_pair():
         ro, rl = oracle.hca.hca_attend(f64(x["q_hca"][b, -1:]), kh64[b], vh64[b], w.m_hca,
                                        [w.ctx - 1], f64(x["sink_hca"]), w.scale)
         assert_close(got[2][b], ro, "f32", f"hca[{b}]", got[3][b], rl)
+
+
+def test_decode_pair_hca_with_window():
+    # the HCA problem with its own sliding window over raw rows
+    w = configs.HYBRID_1M_FP8.with_(ctx=4 * 65536, B=2)
+    x = inputs.make_inputs(w)
+    csa, hca = _setup(w, x)
+    hca.update(window=64, kw=csa["kw"], vw=csa["vw"], raw_pos0=csa["raw_pos0"])
+    ref = _separate(csa, hca)
+    got = []
+    assert _pair_launches(lambda: got.extend(_fused(csa, hca))) == 1
+    assert _same(ref, got)
+    for b in range(w.B):
+        ro, rl = oracle.hca.hca_attend(f64(x["q_hca"][b]), f64(x["kc_hca"][b]), f64(x["vc_hca"][b]),
+                                       w.m_hca, [w.ctx - 1], f64(x["sink_hca"]), w.scale,
+                                       kraw=f64(x["kw"][b]), vraw=f64(x["vw"][b]),
+                                       raw_pos0=w.ctx - w.window, window=64)
+        assert_close(got[2][b], ro, w.dtype, f"hca+window[{b}]", got[3][b], rl)
+

@@ -125,3 +125,28 @@ def test_hca_decode_kv8_general_scales():
         ro, rl = oracle.hca.hca_attend(f64(x["q_hca"][b]), kd[b], vd[b], w.m_hca, [w.ctx - 1],
                                        f64(x["sink_hca"]), w.scale)
         assert_close(out[b], ro, "bf16", f"kv8 general scales [{b}]", lse[b], rl)
+
+
+@pytest.mark.parametrize("H,Tq", [(16, 1), (48, 40), (64, 70), (128, 1)])
+def test_hca_kv8_other_tile_shapes(H, Tq):
+    # query tiles of 16, 96, 128 and 128 rows: the other wave layouts of the kernel
+    w = configs.HCA_1M_DECODE.with_(B=2, H=H, Tq=Tq, ctx=128 * 700 + 5)
+    x = inputs.make_inputs(w)
+    cache = quant.quant_kv8(x["kc_hca"], x["vc_hca"])
+    kd, vd = _dequant(*cache)
+    g = {k: v.to(dev()) for k, v in x.items()}
+    c = tuple(t.to(dev()) for t in cache)
+    pos0 = torch.full((w.B,), w.ctx - Tq, dtype=torch.int32, device=dev())
+    out, lse = ops.hca_attend_kv8(g["q_hca"], c, w.m_hca, pos0, w.ctx - 1, sink=g["sink_hca"],
+                                  return_lse=True)
+    kb = torch.from_numpy(kd).to(torch.bfloat16).to(dev())
+    vb = torch.from_numpy(vd).to(torch.bfloat16).to(dev())
+    ref_o, ref_l = ops.hca_attend(g["q_hca"], kb, vb, w.m_hca, pos0, w.ctx - 1, sink=g["sink_hca"],
+                                  return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(out), _bits(ref_o)) and torch.equal(lse, ref_l)
+    pos = np.arange(w.ctx - Tq, w.ctx)
+    for b in range(w.B):
+        ro, rl = oracle.hca.hca_attend(f64(x["q_hca"][b]), kd[b], vd[b], w.m_hca, pos,
+                                       f64(x["sink_hca"]), w.scale)
+        assert_close(out[b], ro, "bf16", f"kv8 hca H={H} Tq={Tq} [{b}]", lse[b], rl)
