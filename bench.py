@@ -18,6 +18,7 @@ bytes over its event-timed average launch duration against 8 TB/s;
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import multiprocessing as mp
 import os
@@ -199,22 +200,25 @@ def _oracle_one(b):
     return b, o1, o2
 
 
-def cpu_baseline(x, w, workers, min_s=10.0):
-    """The oracle's decode step over all sequences, repeated until at least
-    `min_s` seconds have passed; returns (seconds per step, steps, outputs)."""
+def cpu_pool(x, w, workers):
+    """Worker processes for the oracle baseline, forked before anything touches
+    the GPU (the inputs reach them through the fork)."""
     global _CPU_DATA
     _CPU_DATA = (x, w)
-    ctx = mp.get_context("fork")
+    return mp.get_context("fork").Pool(workers)
+
+
+def cpu_baseline(pool, w, min_s=10.0):
+    """The oracle's decode step over all sequences, repeated until at least
+    `min_s` seconds have passed; returns (seconds per step, steps, outputs)."""
     steps = 0
     t0 = time.perf_counter()
-    with ctx.Pool(workers) as pool:
-        while True:
-            res = pool.map(_oracle_one, range(w.B))
-            steps += 1
-            if time.perf_counter() - t0 >= min_s:
-                break
+    while True:
+        res = pool.map(_oracle_one, range(w.B))
+        steps += 1
+        if time.perf_counter() - t0 >= min_s:
+            break
     dt = (time.perf_counter() - t0) / steps
-    _CPU_DATA = None
     outs = {b: (o1, o2) for b, o1, o2 in res}
     return dt, steps, outs
 
@@ -379,18 +383,14 @@ def main():
 
     cpu = None
     ref = None
+    pool = None
     if not args.no_cpu:
         try:
             ncores = len(os.sched_getaffinity(0))
         except AttributeError:
             ncores = os.cpu_count() or 1
         workers = args.cpu_workers or max(1, min(w.B, ncores, 16))
-        dt, nsteps, ref = cpu_baseline(x, w, workers)
-        cpu = {"value": round(w.B / dt, 3), "unit": "query-tokens/s", "cores": workers,
-               "kind": "oracle",
-               "sample": f"{nsteps} full decode steps of {args.workload} (all {w.B} sequences: "
-                         f"fp64 indexer over {w.Nc} entries, top-{w.topk}, CSA + HCA attention), "
-                         f"{dt:.2f} s wall per step on {workers} processes x 1 BLAS thread"}
+        pool = cpu_pool(x, w, workers)
 
     from sparse_attention_17_amd import _lib as L
     from sparse_attention_17_amd import ops
@@ -449,8 +449,10 @@ def main():
     else:
         runners = [((lambda g=g: step(g)), None) for g in sets]
 
-    # timed region
+    # timed region (no garbage collection inside it)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    gc.collect()
+    gc.disable()
     torch.cuda.synchronize()
     e0.record()
     h0 = time.perf_counter()
@@ -459,6 +461,7 @@ def main():
     host_us = (time.perf_counter() - h0) / args.steps * 1e6
     e1.record()
     torch.cuda.synchronize()
+    gc.enable()
     ms = e0.elapsed_time(e1) / args.steps
 
     # per-kernel launch durations from library-recorded hipEvents (eager steps)
@@ -486,6 +489,17 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom,
             "bytes_per_launch": alg[dom], "us_per_launch": round(kern[dom], 2)}
     step_bytes = sum(v for k, v in alg.items() if k != "attend_pair")   # pair = csa + hca
+
+    # the oracle on the host cores, after the GPU measurement
+    if pool is not None:
+        dt, nsteps, ref = cpu_baseline(pool, w)
+        pool.close()
+        pool.join()
+        cpu = {"value": round(w.B / dt, 3), "unit": "query-tokens/s", "cores": workers,
+               "kind": "oracle",
+               "sample": f"{nsteps} full decode steps of {args.workload} (all {w.B} sequences: "
+                         f"fp64 indexer over {w.Nc} entries, top-{w.topk}, CSA + HCA attention), "
+                         f"{dt:.2f} s wall per step on {workers} processes x 1 BLAS thread"}
 
     # parity of the GPU step against the oracle outputs (when the baseline ran)
     parity = None
