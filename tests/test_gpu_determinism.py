@@ -43,8 +43,32 @@ def _same(a, b):
 def test_decode_repeats_are_bitwise_identical():
     x = inputs.make_inputs(W)
     ref = _decode_step(x, W)
-    for _ in range(5):
+    for _ in range(20):
         assert _same(ref, _decode_step(x, W))
+
+
+def test_decode_batch64_invariance():
+    # the 128K decode batch of 64: sequences 0, 37 and 63 alone give the bits
+    # they get inside the batch (indexer, top-k and sparse attention)
+    w = configs.CSA_DECODE_128K
+    x = inputs.make_inputs(w)
+
+    def run(xx, B):
+        g = {k: v.to(dev()) for k, v in xx.items()}
+        pos0 = torch.full((B,), w.ctx - 1, dtype=torch.int32, device=dev())
+        rp0 = torch.full((B,), w.ctx - w.window, dtype=torch.int32, device=dev())
+        idx = ops.indexer_topk(g["qi"], g["w"], g["kic"], pos0, w.m, w.topk, max_pos=w.ctx - 1)
+        o, l = ops.sparse_attend(g["q"], g["kc"], g["vc"], idx, pos0, w.ctx - 1, w.window,
+                                 kw=g["kw"], vw=g["vw"], raw_pos0=rp0, sink=g["sink"],
+                                 return_lse=True)
+        torch.cuda.synchronize()
+        return [t.cpu() for t in (idx, o, l)]
+
+    full = run(x, w.B)
+    for b in (0, 37, 63):
+        xb = {k: (v[b:b + 1].contiguous() if v.dim() >= 2 and v.shape[0] == w.B else v)
+              for k, v in x.items()}
+        assert _same([t[b:b + 1] for t in full], run(xb, 1)), f"sequence {b} differs at batch 1"
 
 
 def test_decode_batch_invariance():
