@@ -207,6 +207,8 @@ csa_status_t hca_attend(const void *q, const void *kc, const void *vc, int m_pri
  *   v8     [B, Nc_cap, d]    uint8  E4M3 codes of all value dims (values
  *                                   carry no position encoding)
  *   vscale [B, Nc_cap]       fp32   one scale per value row
+ * v8 = vscale = NULL selects the shared-entry variant: each value row is its
+ * key row (codes for dims < d/2, the bf16 RoPE half above).
  * Codes are widened exactly, multiplied by the row scale in fp32 and rounded
  * to bf16 while the tile is staged in LDS (exact when scales are powers of
  * two); the attention then runs as on bf16 caches.  q, out, kw, vw are bf16;

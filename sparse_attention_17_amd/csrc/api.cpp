@@ -304,7 +304,10 @@ static csa_status_t add_kv8(csa::AttendArgs* a, int d, csa_dtype_t dt, const voi
   REQUIRE(d == 128, CSA_UNSUPPORTED, "FP8 caches are built for d=128 (got %d)", d);
   REQUIRE_PTR(krope, "krope");
   REQUIRE_PTR4(kscale, "kscale");
-  REQUIRE_PTR4(vscale, "vscale");
+  REQUIRE((v8 == nullptr) == (vscale == nullptr), CSA_INVALID_ARGUMENT,
+          "v8 and vscale must both be given, or both be NULL (values = key rows)");
+  if (vscale) REQUIRE_PTR4(vscale, "vscale");
+  if (v8) REQUIRE_PTR(v8, "v8");
   a->kv8 = true;
   a->k8 = k8; a->krope = krope; a->v8 = v8; a->kscale = kscale; a->vscale = vscale;
   a->kc = nullptr; a->vc = nullptr;
@@ -321,7 +324,7 @@ csa_status_t csa_sparse_attend_kv8(const void* q, const void* k8, const void* kr
                                    void* stream) {
   csa::AttendArgs a;
   bool empty;
-  csa_status_t st = build_sparse(q, k8, v8, idx, topk, kw, vw, raw_pos0, R, pos0, max_pos, window,
+  csa_status_t st = build_sparse(q, k8, v8 ? v8 : k8, idx, topk, kw, vw, raw_pos0, R, pos0, max_pos, window,
                                  sink, softmax_scale, B, Tq, H, d, Nc_cap, CSA_BF16, out, lse_out,
                                  workspace, workspace_bytes, &a, &empty);
   if (st != CSA_OK || empty) return st;
@@ -338,7 +341,7 @@ csa_status_t hca_attend_kv8(const void* q, const void* k8, const void* krope, co
                             float* lse_out, void* workspace, size_t workspace_bytes, void* stream) {
   csa::AttendArgs a;
   bool empty;
-  csa_status_t st = build_hca(q, k8, v8, m_prime, Nc_cap, kw, vw, raw_pos0, R, window, pos0, max_pos,
+  csa_status_t st = build_hca(q, k8, v8 ? v8 : k8, m_prime, Nc_cap, kw, vw, raw_pos0, R, window, pos0, max_pos,
                               sink, softmax_scale, B, Tq, H, d, CSA_BF16, out, lse_out, workspace,
                               workspace_bytes, &a, &empty);
   if (st != CSA_OK || empty) return st;

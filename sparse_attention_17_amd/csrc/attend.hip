@@ -220,9 +220,12 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
   const __amdgpu_buffer_rsrc_t rk8 = rsrc(KV8 ? (const uint8_t*)a.k8 + cb * DN : nullptr, KV8 ? (uint32_t)a.Nc_cap * DN : 0u);
   const __amdgpu_buffer_rsrc_t rkr = rsrc(KV8 ? (const uint16_t*)a.krope + cb * (D - DN) : nullptr,
                                           KV8 ? (uint32_t)a.Nc_cap * (D - DN) * 2 : 0u);
-  const __amdgpu_buffer_rsrc_t rv8 = rsrc(KV8 ? (const uint8_t*)a.v8 + cb * D : nullptr, KV8 ? (uint32_t)a.Nc_cap * D : 0u);
+  const bool vshared = KV8 && a.v8 == nullptr;                // values = key rows (shared entry)
+  const __amdgpu_buffer_rsrc_t rv8 = rsrc(KV8 && !vshared ? (const uint8_t*)a.v8 + cb * D : nullptr,
+                                          KV8 && !vshared ? (uint32_t)a.Nc_cap * D : 0u);
   const __amdgpu_buffer_rsrc_t rks = rsrc(KV8 ? a.kscale + cb : nullptr, KV8 ? (uint32_t)a.Nc_cap * 4 : 0u);
-  const __amdgpu_buffer_rsrc_t rvs = rsrc(KV8 ? a.vscale + cb : nullptr, KV8 ? (uint32_t)a.Nc_cap * 4 : 0u);
+  const __amdgpu_buffer_rsrc_t rvs = rsrc(KV8 && !vshared ? a.vscale + cb : nullptr,
+                                          KV8 && !vshared ? (uint32_t)a.Nc_cap * 4 : 0u);
   // 8 codes (x, y) and their row scale (z) of an FP8 row chunk, or zeros
   auto ld8 = [](const __amdgpu_buffer_rsrc_t& rc, const __amdgpu_buffer_rsrc_t& rs, int e, uint32_t off) -> u32x4 {
     const auto c = __builtin_amdgcn_raw_buffer_load_b64(rc, e >= 0 ? off : OOB, 0, 0);
@@ -299,10 +302,11 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
       // FP8 rows: a K chunk below DN dims is 8 codes + scale, above it 8 bf16
       // RoPE values (the chunk kind is uniform over a wave); a V chunk is 8
       // codes + scale.  Window rows are bf16.
+      // (values shared with keys: the value row is the key row)
       auto comp8 = [&](bool k, int s, int ch) -> u32x4 {
         const int e = ent(s);
-        if (k && ch >= DN / VEC) return ld(rkr, e >= 0 ? (uint32_t)e * (D - DN) * 2 : OOB, ch - DN / VEC);
-        if (k) return ld8(rk8, rks, e, (uint32_t)e * DN + ch * 8);
+        if ((k || vshared) && ch >= DN / VEC) return ld(rkr, e >= 0 ? (uint32_t)e * (D - DN) * 2 : OOB, ch - DN / VEC);
+        if (k || vshared) return ld8(rk8, rks, e, (uint32_t)e * DN + ch * 8);
         return ld8(rv8, rvs, e, (uint32_t)e * D + ch * 8);
       };
       if (s0 + KT <= ncomp || nwin == 0)
@@ -341,7 +345,7 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
       for (int u = 0; u < 4; ++u) {
         vr[u] = vreg[i][u];
         if constexpr (KV8)
-          if (ent(s0 + kg * 4 + u) >= 0) vr[u] = dequant8(vr[u]);
+          if ((!vshared || ch < DN / VEC) && ent(s0 + kg * 4 + u) >= 0) vr[u] = dequant8(vr[u]);
       }
       const T* rows = reinterpret_cast<const T*>(vr);           // [4][VEC]
 #pragma unroll

@@ -200,6 +200,18 @@ def test_grouped_out_proj_validation(lib):
     assert _proj(lib, T=0) == L.OK
 
 
+def test_kv8_validation(lib):
+    a = dict(q=FAKE, k8=FAKE, krope=FAKE, kscale=FAKE, v8=FAKE, vscale=FAKE, m_prime=128,
+             Nc_cap=8192, kw=None, vw=None, raw_pos0=None, R=0, window=0, pos0=FAKE,
+             max_pos=(1 << 20) - 1, sink=None, scale=C.c_float(0.1), B=16, Tq=1, H=64, d=128,
+             out=FAKE, lse=None, ws=FAKE, ws_bytes=1 << 26, stream=None)
+    call = lambda **kw: lib.hca_attend_kv8(*{**a, **kw}.values())
+    assert call(d=64) == L.UNSUPPORTED                       # built for d = 128
+    assert call(vscale=None) == L.INVALID_ARGUMENT           # v8 without its scales
+    assert call(krope=None) == L.INVALID_ARGUMENT
+    assert call(B=0) == L.OK
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(L, "_lib", None)
     monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "nope.so"))

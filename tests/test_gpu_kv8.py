@@ -150,3 +150,45 @@ def test_hca_kv8_other_tile_shapes(H, Tq):
         ro, rl = oracle.hca.hca_attend(f64(x["q_hca"][b]), kd[b], vd[b], w.m_hca, pos,
                                        f64(x["sink_hca"]), w.scale)
         assert_close(out[b], ro, "bf16", f"kv8 hca H={H} Tq={Tq} [{b}]", lse[b], rl)
+
+
+@pytest.mark.parametrize("kind", ["csa", "hca"])
+def test_kv8_shared_entry(kind):
+    # values are the key rows themselves (v8 = vscale = NULL)
+    if kind == "csa":
+        w = configs.CSA_DECODE_128K.with_(ctx=4 * 6000, B=2, topk=1024)
+        x = inputs.make_inputs(w, peaky=True)
+        kc = x["kc"]
+    else:
+        w = configs.HCA_1M_DECODE.with_(B=2, ctx=128 * 3000 + 77)
+        x = inputs.make_inputs(w, peaky=True)
+        kc = x["kc_hca"]
+    k8, krope, ks, _, _ = quant.quant_kv8(kc, kc)
+    kd = np.concatenate([formats.dequant_fp8_rows(k8.numpy(), ks.numpy()), f64(krope)], axis=-1)
+    g = {k: v.to(dev()) for k, v in x.items()}
+    c = (k8.to(dev()), krope.to(dev()), ks.to(dev()), None, None)
+    kb = torch.from_numpy(kd).to(torch.bfloat16).to(dev())
+    pos0 = torch.full((w.B,), w.ctx - 1, dtype=torch.int32, device=dev())
+    if kind == "csa":
+        rp0 = torch.full((w.B,), w.ctx - w.window, dtype=torch.int32, device=dev())
+        idx = ops.indexer_topk(g["qi"], g["w"], g["kic"], pos0, w.m, w.topk, max_pos=w.ctx - 1)
+        out, lse = ops.sparse_attend_kv8(g["q"], c, idx, pos0, w.ctx - 1, w.window, kw=g["kw"],
+                                         vw=g["vw"], raw_pos0=rp0, sink=g["sink"], return_lse=True)
+        ref_o, ref_l = ops.sparse_attend(g["q"], kb, kb, idx, pos0, w.ctx - 1, w.window, kw=g["kw"],
+                                         vw=g["vw"], raw_pos0=rp0, sink=g["sink"], return_lse=True)
+    else:
+        out, lse = ops.hca_attend_kv8(g["q_hca"], c, w.m_hca, pos0, w.ctx - 1, sink=g["sink_hca"],
+                                      return_lse=True)
+        ref_o, ref_l = ops.hca_attend(g["q_hca"], kb, kb, w.m_hca, pos0, w.ctx - 1,
+                                      sink=g["sink_hca"], return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(out), _bits(ref_o)) and torch.equal(lse, ref_l)
+    for b in range(w.B):
+        if kind == "csa":
+            ro, rl = oracle.csa.sparse_attend(f64(x["q"][b]), kd[b], kd[b], idx.cpu().numpy()[b],
+                                              f64(x["kw"][b]), f64(x["vw"][b]), w.ctx - w.window,
+                                              [w.ctx - 1], w.window, f64(x["sink"]), w.scale)
+        else:
+            ro, rl = oracle.hca.hca_attend(f64(x["q_hca"][b]), kd[b], kd[b], w.m_hca, [w.ctx - 1],
+                                           f64(x["sink_hca"]), w.scale)
+        assert_close(out[b], ro, "bf16", f"kv8 shared {kind}[{b}]", lse[b], rl)
