@@ -161,7 +161,9 @@ csa_status_t csa_indexer_topk(const void *qi, const void *qi_scale, const float 
  *   raw_pos0  [B] int32 device (NULL when window == 0)
  *   pos0      [B] int32 device: query positions as for csa_indexer_topk
  *   window    W >= 0: the query at t also attends raw positions
- *             max(0, t-W+1) .. t (its own token included)
+ *             max(0, t-W+1) .. t (its own token included); window
+ *             positions the raw buffer does not hold are left out, so
+ *             queries at Tq positions need R >= W + Tq - 1 rows
  *   sink      [H] fp32 sink logits, or NULL for no sink
  *   lse_out   [B, Tq, H] fp32 natural-log denominators (incl. sink), or NULL
  *   softmax_scale  sigma > 0 (finite); logits are sigma * q.k

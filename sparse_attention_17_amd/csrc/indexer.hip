@@ -763,6 +763,17 @@ struct PickSmem {
 };
 static_assert(sizeof(TopkSmem<PICK_NT>) <= sizeof(PickSmem), "fallback select aliases PickSmem");
 
+// Sum of the per-wave totals w[0 .. wave-1] (wave = this thread's wave):
+// lane i < PICK_NW reads w[i] once and a masked wave sum replaces a serial
+// walk over the totals.
+__device__ __forceinline__ uint32_t waves_below(const uint32_t* w, int wave) {
+  const int lane = threadIdx.x & 63;
+  uint32_t v = lane < wave ? w[lane] : 0u;                   // wave < PICK_NW <= 64
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) v += (uint32_t)__shfl_xor((int)v, o, 64);
+  return v;
+}
+
 struct PickRow {
   int row, n, k, nch, cap, lg, nslot;
   const uint2* meta;
@@ -861,7 +872,7 @@ __device__ __forceinline__ void pick_body(PickSmem& sm, const PickRow& R) {
       if (lane == 63) sm.wv[0][wave] = incl;
       __syncthreads();
       uint32_t before = incl - local;
-      for (int w = 0; w < wave; ++w) before += sm.wv[0][w];
+      before += waves_below(sm.wv[0], wave);
       if (before < need && before + local >= need) {
         uint32_t cum = before;
         for (int i = 0; i < pb; ++i) {
@@ -930,7 +941,8 @@ __device__ __forceinline__ void pick_body(PickSmem& sm, const PickRow& R) {
   if (lane == 63) { sm.wv[1][wave] = (uint32_t)(inc >> 32); sm.wv[2][wave] = (uint32_t)inc; }
   __syncthreads();
   uint32_t gt_before = (uint32_t)((inc - pk) >> 32), eq_before = (uint32_t)(inc - pk);
-  for (int w = 0; w < wave; ++w) { gt_before += sm.wv[1][w]; eq_before += sm.wv[2][w]; }
+  gt_before += waves_below(sm.wv[1], wave);
+  eq_before += waves_below(sm.wv[2], wave);
   uint32_t pos = gt_before + min(eq_before, need);
   uint32_t e_seen = eq_before;
   uint32_t take = wgt;

@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import oracle
-from helpers import check_topk_row, dev, f64
+from helpers import assert_close, check_topk_row, dev, f64
 from oracle import formats
 from sparse_attention_17_amd import ops
 from synth import configs, inputs, quant
@@ -281,3 +281,34 @@ def test_prefill_boundary_ties_take_lowest_indices():
         ne = (t + 1) // w.m
         sc = oracle.csa.indexer_scores(qi[t:t + 1], w64[t:t + 1], k64[:ne])[0]
         assert check_topk_row(idx[0, t], sc, ne, w.topk, band_rel=0.0), t
+
+
+@pytest.mark.parametrize("qk", ["bf16", "fp8"])
+def test_multi_token_decode_long_rows(qk):
+    # three query tokens per sequence (the last three positions), long rows:
+    # each token sees its own eligible prefix; then the sparse attention
+    w = configs.CSA_DECODE_128K.with_(ctx=4 * 40000 + 2, B=2, Tq=3, topk=1024, qk_dtype=qk)
+    x = inputs.make_inputs(w)
+    g = {k: v.to(dev()) for k, v in x.items()}
+    pos0 = torch.full((w.B,), w.ctx - 3, dtype=torch.int32, device=dev())
+    idx = ops.indexer_topk(g["qi"], g["w"], g["kic"], pos0, w.m, w.topk, max_pos=w.ctx - 1,
+                           qi_scale=g.get("qi_scale"), kic_scale=g.get("kic_scale"), qk_dtype=qk)
+    # the raw buffer holds the last `window` tokens: a window two shorter fits
+    # every one of the three queries
+    win = w.window - 2
+    rp0 = torch.full((w.B,), w.ctx - w.window, dtype=torch.int32, device=dev())
+    out, lse = ops.sparse_attend(g["q"], g["kc"], g["vc"], idx, pos0, w.ctx - 1, win,
+                                 kw=g["kw"], vw=g["vw"], raw_pos0=rp0, sink=g["sink"],
+                                 return_lse=True)
+    torch.cuda.synchronize()
+    idx = idx.cpu().numpy()
+    qi, kic = _dequant(x, "qi", qk), _dequant(x, "kic", qk)
+    positions = list(range(w.ctx - 3, w.ctx))
+    exact = 0
+    for b in range(w.B):
+        exact += _check_rows(idx[b], qi[b], f64(x["w"][b]), kic[b], positions, w.m, w.topk)[0]
+        ro, rl = oracle.csa.sparse_attend(f64(x["q"][b]), f64(x["kc"][b]), f64(x["vc"][b]), idx[b],
+                                          f64(x["kw"][b]), f64(x["vw"][b]), w.ctx - w.window,
+                                          positions, win, f64(x["sink"]), w.scale)
+        assert_close(out[b], ro, "bf16", f"attend[{b}]", lse[b], rl)
+    assert exact >= 3 * w.B - 1
