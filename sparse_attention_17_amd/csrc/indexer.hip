@@ -759,7 +759,7 @@ struct PickSmem {
   uint32_t bm_eq[PICK_WORDS];
   uint32_t sel[PICK_STASH];                    // entry index of selected slots
   uint32_t wv[4][PICK_NW];                     // per-wave partials
-  uint32_t res[2];
+  uint32_t res[3];                             // bin, count above it, count in it
 };
 static_assert(sizeof(TopkSmem<PICK_NT>) <= sizeof(PickSmem), "fallback select aliases PickSmem");
 
@@ -877,7 +877,10 @@ __device__ __forceinline__ void pick_body(PickSmem& sm, const PickRow& R) {
         uint32_t cum = before;
         for (int i = 0; i < pb; ++i) {
           const uint32_t h = hist[hb - 1 - i];
-          if (cum + h >= need) { sm.res[0] = (uint32_t)(hb - 1 - i); sm.res[1] = cum; break; }
+          if (cum + h >= need) {
+            sm.res[0] = (uint32_t)(hb - 1 - i); sm.res[1] = cum; sm.res[2] = h;
+            break;
+          }
           cum += h;
         }
       }
@@ -886,6 +889,12 @@ __device__ __forceinline__ void pick_body(PickSmem& sm, const PickRow& R) {
       pmask |= (uint32_t)(nb - 1) << sh;
       need -= sm.res[1];
       buf ^= 1;
+      // Every key in the bin is taken: tau = the bin's floor (bits below sh
+      // zero) then selects the same set (the keys above it plus the whole bin)
+      // and the later passes are skipped.  Only for sh <= 12, where the floor
+      // and the k-th key compare alike against the chunk cuts (multiples of
+      // 2^12) in the safety check below.
+      if (sm.res[2] == need && sh <= 12) break;
     }
     tau = prefix;
   }
