@@ -8,6 +8,11 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    # CSA_TEST_LIB runs the tests against another build of the library (the
+    # host-sanitised one built by tests/test_abi_asan.py)
+    if os.environ.get("CSA_TEST_LIB"):
+        from sparse_attention_17_amd import _lib
+        _lib.LIB_PATH = os.environ["CSA_TEST_LIB"]
 
 
 import pytest  # noqa: E402
