@@ -283,7 +283,7 @@ def test_prefill_boundary_ties_take_lowest_indices():
         assert check_topk_row(idx[0, t], sc, ne, w.topk, band_rel=0.0), t
 
 
-@pytest.mark.parametrize("qk", ["bf16", "fp8"])
+@pytest.mark.parametrize("qk", ["bf16", "fp8", "fp4"])
 def test_multi_token_decode_long_rows(qk):
     # three query tokens per sequence (the last three positions), long rows:
     # each token sees its own eligible prefix; then the sparse attention
