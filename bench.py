@@ -6,14 +6,20 @@ Default workload: one decode step of a hybrid CSA + HCA layer pair at a
        and queries (per-row fp32 scales, 4 heads x 64), top-2048, sliding
        window 128, sink, 64 query heads sharing one KV head, d=128;
   HCA: 8,192 entries (m'=128), dense over completed blocks, sink.
-A step = csa_indexer_topk -> csa_sparse_attend -> hca_attend on inputs already
-resident in HBM.  Inputs are seeded synthetic tensors; several copies rotate
-so consecutive steps do not hit the 256 MB last-level cache.
+A step = one csa_hybrid_decode_step call (indexer scores + top-k, the HCA
+attention launched so that it overlaps the top-k pick, the CSA attention, one
+merge of both problems' split partials) on inputs already resident in HBM.
+Inputs are seeded synthetic tensors; several copies (>= 4, each > 1 GB)
+rotate so consecutive steps do not hit the 256 MB last-level cache.
 
 Prints one JSON line.  `value` is query tokens per second for the step
-(batch / step time); `roofline` reports the dominant kernel's algorithmic
-bytes over its event-timed average launch duration against 8 TB/s;
-`cpu_baseline` times the fp64 oracle on the same inputs on host cores.
+(batch / mean step time over the timed region; p50/p90 of the per-step event
+times beside it); `roofline` reports the dominant kernel's algorithmic bytes
+over its event-timed average launch duration against 8 TB/s; `cpu_baseline`
+times the fp64 oracle on the same inputs on host cores; `parity_vs_oracle`
+checks one step against the oracle; `other_workloads` holds the 128K CSA
+decode step, HCA at 1M context (decode and prefill chunk) and the 32K CSA
+prefill chain.
 """
 from __future__ import annotations
 
@@ -42,14 +48,20 @@ def parse():
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="hybrid_1m_fp8")
-    p.add_argument("--rotate", type=int, default=3, help="input copies cycled through")
+    p.add_argument("--rotate", type=int, default=4, help="input copies cycled through")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     # Measured on MI355X: the eager step (one stream, host enqueue ~40 us/step,
     # below the GPU time) runs ~7 us faster than the same step replayed as a
     # captured HIP graph.
     p.add_argument("--graph", type=int, default=0, help="replay the step as a HIP graph")
-    p.add_argument("--pair", type=int, default=1,
-                   help="run CSA and HCA attention through csa_hybrid_attend (one launch)")
+    p.add_argument("--mode", choices=("step", "calls"), default="step",
+                   help="step: the whole step in one csa_hybrid_decode_step call; calls: "
+                        "csa_indexer_topk then csa_hybrid_attend")
+    p.add_argument("--in-order", type=int, default=0,
+                   help="step mode: launch every kernel in order (no HCA / top-k overlap)")
+    p.add_argument("--extra", type=int, default=1,
+                   help="also time the 128K decode step, HCA 1M decode / prefill and the 32K "
+                        "prefill (extra keys of the JSON line)")
     p.add_argument("--cpu-workers", type=int, default=0)
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run three 256 MiB device copies (known traffic for counter scaling)")
@@ -192,12 +204,12 @@ def _oracle_one(b):
         ne = (t + 1) // w.m
         sc = oracle.csa.indexer_scores(qi, f(x["w"][b]), kic[:ne])[0]
         idx = oracle.csa.topk(sc, ne, w.topk)[None, :]
-        o1, _ = oracle.csa.sparse_attend(f(x["q"][b]), f(x["kc"][b]), f(x["vc"][b]), idx,
-                                         f(x["kw"][b]), f(x["vw"][b]), w.ctx - w.window, [t],
-                                         w.window, f(x["sink"]), w.scale)
-        o2, _ = oracle.hca.hca_attend(f(x["q_hca"][b]), f(x["kc_hca"][b]), f(x["vc_hca"][b]),
-                                      w.m_hca, [t], f(x["sink_hca"]), w.scale)
-    return b, o1, o2
+        o1, l1 = oracle.csa.sparse_attend(f(x["q"][b]), f(x["kc"][b]), f(x["vc"][b]), idx,
+                                          f(x["kw"][b]), f(x["vw"][b]), w.ctx - w.window, [t],
+                                          w.window, f(x["sink"]), w.scale)
+        o2, l2 = oracle.hca.hca_attend(f(x["q_hca"][b]), f(x["kc_hca"][b]), f(x["vc_hca"][b]),
+                                       w.m_hca, [t], f(x["sink_hca"]), w.scale)
+    return b, (o1, l1, o2, l2, sc)
 
 
 def cpu_pool(x, w, workers):
@@ -219,7 +231,7 @@ def cpu_baseline(pool, w, min_s=10.0):
         if time.perf_counter() - t0 >= min_s:
             break
     dt = (time.perf_counter() - t0) / steps
-    outs = {b: (o1, o2) for b, o1, o2 in res}
+    outs = dict(res)
     return dt, steps, outs
 
 
@@ -359,6 +371,149 @@ def suite():
     print(json.dumps({"suite": {k: round(v, 2) for k, v in res.items()}}), flush=True)
 
 
+def _pct(v, q):
+    return float(np.percentile(np.asarray(v), q))
+
+
+def _timed(fn, n, warm=3):
+    """Event-timed calls of fn on the current stream: (mean ms, p50 ms, p90 ms)."""
+    import torch
+    for _ in range(warm):
+        fn(0)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    ev[0].record()
+    for i in range(n):
+        fn(i)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
+    return ev[0].elapsed_time(ev[n]) / n, _pct(per, 50), _pct(per, 90)
+
+
+def extra_workloads():
+    """The other workloads' timings, reported beside the headline: the 128K CSA
+    decode step (batch 64), HCA at 1M context (decode batch 16 and a
+    4096-query prefill chunk) and the 32K CSA prefill chain."""
+    import torch
+    from synth import configs, inputs
+    from sparse_attention_17_amd import ops
+    dev = torch.device("cuda:0")
+    res = {}
+
+    # CSA decode step at 128K context: indexer + top-1024 + sparse attention
+    w = configs.CSA_DECODE_128K
+    x = inputs.make_inputs(w)
+    sets = [{k: v.to(dev) for k, v in x.items()}]
+    sets.append({k: v.clone() for k, v in sets[0].items()})
+    del x
+    pos0 = torch.full((w.B,), w.ctx - 1, dtype=torch.int32, device=dev)
+    rp0 = torch.full((w.B,), w.ctx - w.window, dtype=torch.int32, device=dev)
+
+    def csa_step(i):
+        g = sets[i % 2]
+        idx = ops.indexer_topk(g["qi"], g["w"], g["kic"], pos0, w.m, w.topk, max_pos=w.ctx - 1)
+        ops.sparse_attend(g["q"], g["kc"], g["vc"], idx, pos0, w.ctx - 1, w.window, kw=g["kw"],
+                          vw=g["vw"], raw_pos0=rp0, sink=g["sink"])
+    ms, p50, p90 = _timed(csa_step, 30)
+    alg = w.B * (w.Nc * w.dI * 2 + w.HI * w.dI * 2 + w.HI * 4 + w.topk * 4 +
+                 (w.topk + w.window) * 2 * w.d * 2 + 2 * w.H * w.d * 2)
+    res["csa_decode_128k"] = {"ms_per_step": round(ms, 4), "p50_ms": round(p50, 4),
+                              "p90_ms": round(p90, 4), "query_tokens_per_s": round(w.B / (ms * 1e-3), 1),
+                              "algorithmic_bytes": alg,
+                              "hbm_frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del sets
+
+    # HCA at 1M context: decode batch 16 (8 rotating copies: 512 MiB) and the prefill chunk
+    w = configs.HCA_1M_DECODE
+    x = inputs.make_inputs(w)
+    sets = [{k: v.to(dev) for k, v in x.items()}]
+    sets += [{k: v.clone() for k, v in sets[0].items()} for _ in range(7)]
+    pos0 = torch.full((w.B,), w.ctx - 1, dtype=torch.int32, device=dev)
+    fn = lambda i: ops.hca_attend(sets[i % 8]["q_hca"], sets[i % 8]["kc_hca"], sets[i % 8]["vc_hca"],  # noqa: E731
+                                  w.m_hca, pos0, w.ctx - 1, sink=sets[i % 8]["sink_hca"])
+    ms, p50, p90 = _timed(fn, 40)
+    alg = w.B * (w.Nc_hca * 2 * w.d * 2 + 2 * w.H * w.d * 2)
+    res["hca_1m_decode"] = {"ms_per_call": round(ms, 4), "p50_ms": round(p50, 4), "p90_ms": round(p90, 4),
+                            "query_tokens_per_s": round(w.B / (ms * 1e-3), 1), "algorithmic_bytes": alg,
+                            "hbm_frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del sets, x
+    w = configs.HCA_1M_PREFILL
+    x = inputs.make_inputs(w)
+    g = {k: v.to(dev) for k, v in x.items()}
+    pos0 = torch.full((w.B,), w.ctx - w.Tq, dtype=torch.int32, device=dev)
+    fn = lambda i: ops.hca_attend(g["q_hca"], g["kc_hca"], g["vc_hca"], w.m_hca, pos0, w.ctx - 1,  # noqa: E731
+                                  sink=g["sink_hca"])
+    ms, p50, p90 = _timed(fn, 8, warm=2)
+    flop = 4.0 * w.d * w.H * 33486880
+    res["hca_1m_prefill4k"] = {"ms_per_call": round(ms, 4), "p50_ms": round(p50, 4),
+                               "query_tokens_per_s": round(w.Tq / (ms * 1e-3), 1),
+                               "tflops": round(flop / (ms * 1e-3) / 1e12, 1),
+                               "mfma_frac": round(flop / (ms * 1e-3) / 2.5e15, 4)}
+    del g, x
+
+    # CSA prefill, 32K tokens: compress -> indexer/top-512 -> sparse attention
+    w = configs.CSA_PREFILL_32K
+    x = inputs.make_inputs(w)
+    g = {k: v.to(dev) for k, v in x.items()}
+    del x
+    pos0 = torch.zeros(1, dtype=torch.int32, device=dev)
+    kc, vc, kic = ops.compress(g["k"], g["v"], g["ki"], g["g"], w.m)
+    idx = ops.indexer_topk(g["qi"], g["w"], kic, pos0, w.m, w.topk, max_pos=w.ctx - 1)
+    ms_c, _, _ = _timed(lambda i: ops.compress(g["k"], g["v"], g["ki"], g["g"], w.m), 10)
+    ms_i, p50_i, _ = _timed(lambda i: ops.indexer_topk(g["qi"], g["w"], kic, pos0, w.m, w.topk,
+                                                       max_pos=w.ctx - 1), 10, warm=2)
+    ms_a, p50_a, _ = _timed(lambda i: ops.sparse_attend(g["q"], kc, vc, idx, pos0, w.ctx - 1, w.window,
+                                                        kw=g["k"], vw=g["v"], raw_pos0=pos0,
+                                                        sink=g["sink"]), 5, warm=1)
+    f_idx = 2.0 * w.HI * w.dI * 134209536
+    f_att = 4.0 * w.d * w.H * 20438592
+    res["csa_prefill_32k"] = {
+        "compress_ms": round(ms_c, 4), "indexer_topk_ms": round(ms_i, 4), "indexer_p50_ms": round(p50_i, 4),
+        "indexer_tflops": round(f_idx / (ms_i * 1e-3) / 1e12, 1),
+        "indexer_mfma_frac": round(f_idx / (ms_i * 1e-3) / 2.5e15, 4),
+        "attend_ms": round(ms_a, 4), "attend_tflops": round(f_att / (ms_a * 1e-3) / 1e12, 1),
+        "attend_mfma_frac": round(f_att / (ms_a * 1e-3) / 2.5e15, 4),
+        "chain_query_tokens_per_s": round(w.Tq / ((ms_c + ms_i + ms_a) * 1e-3), 1)}
+    del g, kc, vc, kic, idx
+    torch.cuda.empty_cache()
+    return res
+
+
+def _parity(w, x, ref, st, idx_gpu):
+    """GPU step outputs of input set 0 against the oracle's: index sets under
+    the near-tie band (1e-6 of the row's largest score around the k-th score),
+    max-abs 2e-2, relative Frobenius 1e-2 and lse 1e-3 (bf16)."""
+    res = {"csa_max_abs": 0.0, "hca_max_abs": 0.0, "csa_rel": 0.0, "hca_rel": 0.0,
+           "csa_lse": 0.0, "hca_lse": 0.0, "idx_rows_exact": 0, "idx_band_ok": True}
+    out = [t.double().cpu().numpy() for t in (st.out, st.lse, st.hout, st.hlse)]
+    idx = idx_gpu.cpu().numpy()
+    n_e = w.ctx // w.m
+    for b in range(w.B):
+        o1, l1, o2, l2, sc = ref[b]
+        for key, got, want, lg, lw in (("csa", out[0][b], o1, out[1][b], l1),
+                                       ("hca", out[2][b], o2, out[3][b], l2)):
+            res[f"{key}_max_abs"] = max(res[f"{key}_max_abs"], float(np.abs(got - want).max()))
+            res[f"{key}_rel"] = max(res[f"{key}_rel"],
+                                    float(np.linalg.norm(got - want) / np.linalg.norm(want)))
+            res[f"{key}_lse"] = max(res[f"{key}_lse"], float(np.abs(lg - lw).max()))
+        sel = idx[b, 0]
+        tau = np.partition(sc, n_e - w.topk)[n_e - w.topk]
+        band = 1e-6 * sc.max()
+        inside = np.zeros(n_e, dtype=bool)
+        inside[sel[sel >= 0]] = True
+        ok = (np.all(np.diff(sel) > 0) and inside.sum() == w.topk and
+              np.all(inside[sc > tau + band]) and not np.any(inside & (sc < tau - band)))
+        res["idx_band_ok"] = bool(res["idx_band_ok"] and ok)
+        order = np.lexsort((np.arange(n_e), -sc))
+        res["idx_rows_exact"] += int(np.array_equal(np.sort(order[:w.topk]), sel))
+    res["tol"] = {"max_abs": 2e-2, "rel": 1e-2, "lse": 1e-3}
+    res["ok"] = bool(res["idx_band_ok"] and max(res["csa_max_abs"], res["hca_max_abs"]) <= 2e-2 and
+                     max(res["csa_rel"], res["hca_rel"]) <= 1e-2 and
+                     max(res["csa_lse"], res["hca_lse"]) <= 1e-3)
+    return res
+
+
 def main():
     args = parse()
     if args.pmc_summary:
@@ -412,66 +567,78 @@ def main():
     rp0 = torch.full((w.B,), w.ctx - w.window, dtype=torch.int32, device=dev)
     qk = w.qk_dtype
 
-    def step(g):
-        idx = ops.indexer_topk(g["qi"], g["w"], g["kic"], pos0, w.m, w.topk, max_pos=w.ctx - 1,
-                               qi_scale=g.get("qi_scale"), kic_scale=g.get("kic_scale"),
-                               qk_dtype=qk)
-        csa = dict(q=g["q"], kc=g["kc"], vc=g["vc"], idx=idx, pos0=pos0, max_pos=w.ctx - 1,
-                   window=w.window, kw=g["kw"], vw=g["vw"], raw_pos0=rp0, sink=g["sink"])
-        hca = dict(q=g["q_hca"], kc=g["kc_hca"], vc=g["vc_hca"], m_prime=w.m_hca, pos0=pos0,
-                   max_pos=w.ctx - 1, sink=g["sink_hca"])
-        if args.pair:
-            # both attention problems in one launch (plus one split merge)
-            return ops.hybrid_attend(csa, hca)
-        return ops.sparse_attend(**csa), ops.hca_attend(**hca)
+    def step_args(g):
+        idx = dict(qi=g["qi"], w=g["w"], kic=g["kic"], m=w.m, topk=w.topk, qi_scale=g.get("qi_scale"),
+                   kic_scale=g.get("kic_scale"), qk_dtype=qk)
+        csa = dict(q=g["q"], kc=g["kc"], vc=g["vc"], window=w.window, kw=g["kw"], vw=g["vw"],
+                   raw_pos0=rp0, sink=g["sink"])
+        hca = dict(q=g["q_hca"], kc=g["kc_hca"], vc=g["vc_hca"], m_prime=w.m_hca, sink=g["sink_hca"])
+        return idx, csa, hca
 
-    # warm-up, then optional graph capture of one step per input copy
+    steps_obj = [ops.DecodeStep(*step_args(g), pos0, w.ctx - 1, return_lse=True,
+                                in_order=bool(args.in_order)) for g in sets]
+
+    def step_calls(g):
+        i, c, h = step_args(g)
+        idx = ops.indexer_topk(i["qi"], i["w"], i["kic"], pos0, w.m, w.topk, max_pos=w.ctx - 1,
+                               qi_scale=i["qi_scale"], kic_scale=i["kic_scale"], qk_dtype=qk)
+        return ops.hybrid_attend(dict(c, idx=idx, pos0=pos0, max_pos=w.ctx - 1),
+                                 dict(h, pos0=pos0, max_pos=w.ctx - 1))
+
+    if args.mode == "step":
+        runners = [s.run for s in steps_obj]
+    else:
+        runners = [(lambda g=g: step_calls(g)) for g in sets]
+
     for i in range(args.warmup):
-        step(sets[i % len(sets)])
+        runners[i % len(runners)]()
     torch.cuda.synchronize()
-    runners = []
     if args.graph:
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
-            for g in sets:
-                step(g)
+            for r in runners:
+                r()
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
-        for g in sets:
+        graphs = []
+        for r in runners:
             gr = torch.cuda.CUDAGraph()
             with torch.cuda.graph(gr):
-                outs = step(g)
-            runners.append((gr.replay, outs))
-        for r, _ in runners:
-            r()
+                r()
+            graphs.append(gr)
+        for gr in graphs:
+            gr.replay()
         torch.cuda.synchronize()
-    else:
-        runners = [((lambda g=g: step(g)), None) for g in sets]
+        runners = [gr.replay for gr in graphs]
 
-    # timed region (no garbage collection inside it)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # timed region: an event before every step and after the last (no garbage
+    # collection inside it); ms_per_step is the whole region over the steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     gc.collect()
     gc.disable()
     torch.cuda.synchronize()
-    e0.record()
     h0 = time.perf_counter()
+    ev[0].record()
     for i in range(args.steps):
-        runners[i % len(runners)][0]()
+        runners[i % len(runners)]()
+        ev[i + 1].record()
     host_us = (time.perf_counter() - h0) / args.steps * 1e6
-    e1.record()
     torch.cuda.synchronize()
     gc.enable()
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = ev[0].elapsed_time(ev[args.steps]) / args.steps
+    per_step = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
 
-    # per-kernel launch durations from library-recorded hipEvents (eager steps)
+    # per-kernel launch durations from library-recorded hipEvents (launches in order)
     lib.csa_profile_reset()
     lib.csa_profile_enable(1)
     nprof = 30
+    prof_steps = [ops.DecodeStep(*step_args(g), pos0, w.ctx - 1, in_order=True) for g in sets]
     for i in range(nprof):
-        step(sets[i % len(sets)])
+        prof_steps[i % len(prof_steps)].run()
     torch.cuda.synchronize()
     lib.csa_profile_enable(0)
+    del prof_steps
     import ctypes as C
     kern = {}
     for name in ("indexer_score", "indexer_topk", "attend_csa",
@@ -490,6 +657,8 @@ def main():
             "bytes_per_launch": alg[dom], "us_per_launch": round(kern[dom], 2)}
     step_bytes = sum(v for k, v in alg.items() if k != "attend_pair")   # pair = csa + hca
 
+    extra = extra_workloads() if args.extra else None
+
     # the oracle on the host cores, after the GPU measurement
     if pool is not None:
         dt, nsteps, ref = cpu_baseline(pool, w)
@@ -501,27 +670,24 @@ def main():
                          f"fp64 indexer over {w.Nc} entries, top-{w.topk}, CSA + HCA attention), "
                          f"{dt:.2f} s wall per step on {workers} processes x 1 BLAS thread"}
 
-    # parity of the GPU step against the oracle outputs (when the baseline ran)
     parity = None
     if ref is not None:
-        o1, o2 = runners[0][1] if args.graph else step(sets[0])
+        st = steps_obj[0].run()
         torch.cuda.synchronize()
-        e1m = max(float(np.abs(o1[b].double().cpu().numpy() - ref[b][0]).max()) for b in range(w.B))
-        e2m = max(float(np.abs(o2[b].double().cpu().numpy() - ref[b][1]).max()) for b in range(w.B))
-        parity = {"csa_max_abs": e1m, "hca_max_abs": e2m, "tol": 2e-2,
-                  "ok": bool(e1m <= 2e-2 and e2m <= 2e-2)}
+        parity = _parity(w, x, ref, st, st.idx)
 
     line = {
         "metric": METRIC, "value": round(w.B / (ms * 1e-3), 1), "unit": "query-tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "p50_ms": round(_pct(per_step, 50), 5), "p90_ms": round(_pct(per_step, 90), 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{args.workload}_decode", "batch": w.B, "context": w.ctx,
                    "csa_m": w.m, "csa_entries": w.Nc, "topk": w.topk, "window": w.window,
                    "indexer": f"{w.qk_dtype} {w.HI}x{w.dI}", "hca_m": w.m_hca,
                    "hca_entries": w.Nc_hca, "heads": w.H, "head_dim": w.d,
-                   "graph": bool(args.graph), "attention_pair_launch": bool(args.pair),
-                   "rotating_copies": args.rotate},
+                   "mode": args.mode, "overlap_hca_with_topk": args.mode == "step" and not args.in_order,
+                   "graph": bool(args.graph), "rotating_copies": args.rotate},
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels_us": {k: round(v, 2) for k, v in kern.items()},
@@ -529,6 +695,7 @@ def main():
         "step_hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "host_enqueue_us_per_step": round(host_us, 1),
         "parity_vs_oracle": parity,
+        "other_workloads": extra,
         "input_gen_s": round(t_gen, 1),
     }
     print(json.dumps(line), flush=True)

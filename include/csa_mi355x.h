@@ -265,6 +265,77 @@ csa_status_t csa_hybrid_attend(
     void *hworkspace, size_t hworkspace_bytes, void *stream);
 
 /*
+ * csa_hybrid_decode_step — one decode step of a hybrid CSA + HCA layer pair
+ * in a single call: the CSA lightning indexer and its top-k selection, the
+ * CSA core attention over the selected entries plus the window and sink, and
+ * the HCA dense attention (hyper.ai "Method": CSA compresses, scores with a
+ * lightning indexer, keeps the top-k and attends with a sliding-window branch;
+ * HCA attends densely over its heavily compressed entries; aiboss88 "Technical
+ * Principles", CSA bullet: sliding window plus attention sink).  Each of the B
+ * sequences has one query token at position pos0[b].
+ *
+ * The step is described by the struct below; every field has the meaning,
+ * layout and validation of the same argument of csa_indexer_topk (the first
+ * block), csa_sparse_attend (the second) and hca_attend (the third, fields
+ * prefixed h), with Tq = 1 and B, pos0, max_pos, H, d, dt shared by both
+ * layers.  idx_out receives the CSA index lists; lse_out / hlse_out may be
+ * NULL.  The workspace holds the three calls' workspaces (size from
+ * csa_hybrid_decode_step_workspace).
+ *
+ * Results are bitwise those of csa_indexer_topk, csa_sparse_attend and
+ * hca_attend called one after the other.  The work is enqueued as the
+ * indexer's kernels, the HCA attention, the CSA attention and one merge of
+ * both problems' split partials; unless flags has CSA_STEP_IN_ORDER, the HCA
+ * attention is launched so that it may run beside the top-k select queued
+ * before it (it reads nothing the indexer writes).  An invalid field launches
+ * nothing; the error text names the part.
+ */
+#define CSA_STEP_IN_ORDER 1u
+
+typedef struct csa_decode_step {
+  /* sequences (both layers) */
+  int B;
+  const int32_t *pos0;        /* [B] device: position of each sequence's query */
+  int max_pos;                /* host upper bound of pos0[b] */
+  int H, d;                   /* query heads (one KV head), head dim */
+  csa_dtype_t dt;             /* attention dtype (CSA_F32 / CSA_BF16) */
+  /* CSA lightning indexer + top-k */
+  const void *qi, *qi_scale;  /* [B, 1, HI, dI] (FP4 [.., dI/2]); scales as csa_indexer_topk */
+  const float *w;             /* [B, 1, HI] */
+  const void *kic, *kic_scale;
+  int HI, dI, m, topk;
+  csa_dtype_t qk_dt;
+  int32_t *idx_out;           /* [B, 1, topk] */
+  /* CSA core attention */
+  const void *q;              /* [B, 1, H, d] */
+  const void *kc, *vc;        /* [B, Nc_cap, d] */
+  int Nc_cap;                 /* rows per sequence of kc, vc and kic */
+  const void *kw, *vw;        /* [B, R, d] raw window rows, or NULL when window == 0 */
+  const int32_t *raw_pos0;
+  int R, window;
+  const float *sink;          /* [H] or NULL */
+  float softmax_scale;
+  void *out;                  /* [B, 1, H, d] */
+  float *lse_out;             /* [B, 1, H] or NULL */
+  /* HCA dense attention */
+  const void *hq;             /* [B, 1, H, d] */
+  const void *hkc, *hvc;      /* [B, hNc_cap, d] */
+  int m_prime, hNc_cap;
+  const void *hkw, *hvw;      /* [B, hR, d], or NULL when hwindow == 0 */
+  const int32_t *hraw_pos0;
+  int hR, hwindow;
+  const float *hsink;
+  float hsoftmax_scale;
+  void *hout;                 /* [B, 1, H, d] */
+  float *hlse_out;
+  unsigned flags;             /* CSA_STEP_IN_ORDER: launch every kernel in order */
+} csa_decode_step_t;
+
+size_t csa_hybrid_decode_step_workspace(const csa_decode_step_t *step);
+csa_status_t csa_hybrid_decode_step(const csa_decode_step_t *step, void *workspace,
+                                    size_t workspace_bytes, void *stream);
+
+/*
  * csa_grouped_out_proj — grouped output projection after the core attention.
  * hyper.ai "Method", CSA paragraph (the core attention is followed by a
  * grouped output projection that keeps its cost down).  Form implemented:
@@ -299,6 +370,15 @@ csa_status_t csa_grouped_out_proj(const void *o, const void *w, int T, int H, in
 void csa_profile_enable(int on);
 void csa_profile_reset(void);
 int csa_profile_query(const char *kernel, int *count, double *total_ms);
+
+/* Event counters of the current device, for measurement tools: the number of
+ * query rows whose top-k selection took the exact fallback path since the
+ * last reset ("indexer_prefill_fallback": prefill rows whose candidate set
+ * could not settle the top-k; "indexer_decode_fallback": long decode rows whose
+ * chunk candidates could not).  Writes the count to *value and, if reset is
+ * non-zero, zeroes the counter.  Synchronous (waits for the device); returns 0,
+ * 1 for an unknown name or a NULL value, -1 on a HIP error. */
+int csa_profile_counter(const char *name, unsigned long long *value, int reset);
 
 #ifdef __cplusplus
 }

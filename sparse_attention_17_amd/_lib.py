@@ -19,6 +19,25 @@ _P = C.c_void_p
 _I = C.c_int
 _SZ = C.c_size_t
 
+
+class DecodeStepDesc(C.Structure):
+    """Mirror of csa_decode_step_t (include/csa_mi355x.h), field for field."""
+    _fields_ = [
+        ("B", _I), ("pos0", _P), ("max_pos", _I), ("H", _I), ("d", _I), ("dt", _I),
+        ("qi", _P), ("qi_scale", _P), ("w", _P), ("kic", _P), ("kic_scale", _P),
+        ("HI", _I), ("dI", _I), ("m", _I), ("topk", _I), ("qk_dt", _I), ("idx_out", _P),
+        ("q", _P), ("kc", _P), ("vc", _P), ("Nc_cap", _I), ("kw", _P), ("vw", _P),
+        ("raw_pos0", _P), ("R", _I), ("window", _I), ("sink", _P), ("softmax_scale", C.c_float),
+        ("out", _P), ("lse_out", _P),
+        ("hq", _P), ("hkc", _P), ("hvc", _P), ("m_prime", _I), ("hNc_cap", _I), ("hkw", _P),
+        ("hvw", _P), ("hraw_pos0", _P), ("hR", _I), ("hwindow", _I), ("hsink", _P),
+        ("hsoftmax_scale", C.c_float), ("hout", _P), ("hlse_out", _P),
+        ("flags", C.c_uint),
+    ]
+
+
+STEP_IN_ORDER = 1    # csa_decode_step_t.flags: launch every kernel in order
+
 EXPORTS = {
     "csa_abi_version": (_I, []),
     "csa_last_error": (C.c_char_p, []),
@@ -42,11 +61,16 @@ EXPORTS = {
                                _I, _I, _I, _I, _I, _I, _P, _P, _P, _SZ,
                                _P, _P, _P, _I, _I, _P, _P, _P, _I, _I, _P, _I, _P, C.c_float,
                                _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
+    "csa_hybrid_decode_step_workspace": (_SZ, [C.POINTER(DecodeStepDesc)]),
+    "csa_hybrid_decode_step": (_I, [C.POINTER(DecodeStepDesc), _P, _SZ, _P]),
     "csa_grouped_out_proj": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
     "csa_profile_enable": (None, [_I]),
     "csa_profile_reset": (None, []),
     "csa_profile_query": (_I, [C.c_char_p, C.POINTER(C.c_int), C.POINTER(C.c_double)]),
+    "csa_profile_counter": (_I, [C.c_char_p, C.POINTER(C.c_ulonglong), _I]),
 }
+
+
 
 _lib = None
 

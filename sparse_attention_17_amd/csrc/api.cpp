@@ -115,11 +115,14 @@ size_t csa_indexer_topk_workspace(int B, int Tq, int Nc_cap, int HI, int dI, int
   return csa::indexer_workspace(B, Tq, Nc_cap, HI, dI, topk, (int)qk_dt);
 }
 
-csa_status_t csa_indexer_topk(const void* qi, const void* qi_scale, const float* w,
-                              const void* kic, const void* kic_scale, const int32_t* pos0,
-                              int max_pos, int B, int Tq, int Nc_cap, int HI, int dI, int m,
-                              int topk, csa_dtype_t qk_dt, int32_t* idx_out, float* score_out,
-                              void* workspace, size_t workspace_bytes, void* stream) {
+// Validation and argument packing shared by csa_indexer_topk and the decode step.
+static csa_status_t build_indexer(const void* qi, const void* qi_scale, const float* w,
+                                  const void* kic, const void* kic_scale, const int32_t* pos0,
+                                  int max_pos, int B, int Tq, int Nc_cap, int HI, int dI, int m,
+                                  int topk, csa_dtype_t qk_dt, int32_t* idx_out, float* score_out,
+                                  void* workspace, size_t workspace_bytes, csa::IndexerArgs* a,
+                                  bool* empty) {
+  *empty = true;
   REQUIRE(B >= 0 && Tq >= 0, CSA_INVALID_ARGUMENT, "B and Tq must be >= 0");
   REQUIRE(Nc_cap >= 1, CSA_INVALID_ARGUMENT, "Nc_cap must be >= 1");
   REQUIRE(Nc_cap <= (1 << 23), CSA_UNSUPPORTED, "Nc_cap (%d) above 2^23 entries is not supported", Nc_cap);
@@ -152,8 +155,23 @@ csa_status_t csa_indexer_topk(const void* qi, const void* qi_scale, const float*
   REQUIRE(workspace_bytes >= need, CSA_WORKSPACE_TOO_SMALL,
           "workspace holds %zu bytes, %zu needed", workspace_bytes, need);
   if (need) REQUIRE_PTR(workspace, "workspace");
-  csa::IndexerArgs a{qi, qi_scale, w, kic, kic_scale, pos0, max_pos, B, Tq, Nc_cap, HI, dI, m,
-                     topk, (csa::QkType)qk_dt, idx_out, score_out, workspace};
+  *a = csa::IndexerArgs{qi, qi_scale, w, kic, kic_scale, pos0, max_pos, B, Tq, Nc_cap, HI, dI, m,
+                        topk, (csa::QkType)qk_dt, idx_out, score_out, workspace};
+  *empty = false;
+  return ok();
+}
+
+csa_status_t csa_indexer_topk(const void* qi, const void* qi_scale, const float* w,
+                              const void* kic, const void* kic_scale, const int32_t* pos0,
+                              int max_pos, int B, int Tq, int Nc_cap, int HI, int dI, int m,
+                              int topk, csa_dtype_t qk_dt, int32_t* idx_out, float* score_out,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  csa::IndexerArgs a;
+  bool empty;
+  const csa_status_t st = build_indexer(qi, qi_scale, w, kic, kic_scale, pos0, max_pos, B, Tq, Nc_cap,
+                                        HI, dI, m, topk, qk_dt, idx_out, score_out, workspace,
+                                        workspace_bytes, &a, &empty);
+  if (st != CSA_OK || empty) return st;
   return device_status(csa::launch_indexer_topk(a, (hipStream_t)stream), "csa_indexer_topk launch");
 }
 
@@ -383,6 +401,66 @@ csa_status_t csa_hybrid_attend(
   else if (!ec) e = csa::launch_attend(ac, (hipStream_t)stream);
   else if (!eh) e = csa::launch_attend(ah, (hipStream_t)stream);
   return device_status(e, "csa_hybrid_attend launch");
+}
+
+// Workspace carve-up of the decode step: indexer | CSA attention | HCA attention.
+struct StepWs {
+  size_t idx, csa, hca, total;
+};
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+static StepWs step_ws(const csa_decode_step_t* s) {
+  StepWs w{};
+  if (s->B <= 0) return w;
+  const size_t ni = csa_indexer_topk_workspace(s->B, 1, s->Nc_cap, s->HI, s->dI, s->topk, s->qk_dt);
+  const size_t nc = s->topk >= 1 ? csa::attend_workspace(true, s->B, 1, s->H, s->d, s->topk, s->window,
+                                                         s->Nc_cap, 1, s->max_pos) : 0;
+  const size_t nh = s->m_prime >= 1 ? csa::attend_workspace(false, s->B, 1, s->H, s->d, 0, s->hwindow,
+                                                            s->hNc_cap, s->m_prime, s->max_pos) : 0;
+  w.idx = 0;
+  w.csa = align256(ni);
+  w.hca = align256(w.csa + nc);
+  w.total = w.hca + nh;
+  return w;
+}
+
+size_t csa_hybrid_decode_step_workspace(const csa_decode_step_t* step) {
+  if (step == nullptr || step->B <= 0 || step->H <= 0 || step->Nc_cap <= 0) return 0;
+  return step_ws(step).total;
+}
+
+csa_status_t csa_hybrid_decode_step(const csa_decode_step_t* s, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  REQUIRE(s != nullptr, CSA_INVALID_ARGUMENT, "step must not be NULL");
+  REQUIRE(s->B >= 0, CSA_INVALID_ARGUMENT, "B must be >= 0");
+  if (s->B == 0) return ok();
+  REQUIRE(s->H >= 1 && s->Nc_cap >= 1 && s->m_prime >= 1 && s->topk >= 1, CSA_INVALID_ARGUMENT,
+          "H, Nc_cap, m_prime and topk must be >= 1");
+  REQUIRE(((uintptr_t)workspace % 256) == 0, CSA_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  const StepWs wl = step_ws(s);
+  REQUIRE(workspace_bytes >= wl.total, CSA_WORKSPACE_TOO_SMALL,
+          "workspace holds %zu bytes, %zu needed", workspace_bytes, wl.total);
+  if (wl.total) REQUIRE_PTR(workspace, "workspace");
+  char* ws = reinterpret_cast<char*>(workspace);
+  csa::IndexerArgs ai;
+  csa::AttendArgs ac, ah;
+  bool ei, ec, eh;
+  csa_status_t st = build_indexer(s->qi, s->qi_scale, s->w, s->kic, s->kic_scale, s->pos0, s->max_pos,
+                                  s->B, 1, s->Nc_cap, s->HI, s->dI, s->m, s->topk, s->qk_dt, s->idx_out,
+                                  nullptr, ws ? ws + wl.idx : nullptr, wl.csa - wl.idx, &ai, &ei);
+  if (st != CSA_OK) return fail(st, "indexer part: %s", g_err.c_str());
+  st = build_sparse(s->q, s->kc, s->vc, s->idx_out, s->topk, s->kw, s->vw, s->raw_pos0, s->R, s->pos0,
+                    s->max_pos, s->window, s->sink, s->softmax_scale, s->B, 1, s->H, s->d, s->Nc_cap,
+                    s->dt, s->out, s->lse_out, ws ? ws + wl.csa : nullptr, wl.hca - wl.csa, &ac, &ec);
+  if (st != CSA_OK) return fail(st, "CSA part: %s", g_err.c_str());
+  st = build_hca(s->hq, s->hkc, s->hvc, s->m_prime, s->hNc_cap, s->hkw, s->hvw, s->hraw_pos0, s->hR,
+                 s->hwindow, s->pos0, s->max_pos, s->hsink, s->hsoftmax_scale, s->B, 1, s->H, s->d, s->dt,
+                 s->hout, s->hlse_out, ws ? ws + wl.hca : nullptr, wl.total - wl.hca, &ah, &eh);
+  if (st != CSA_OK) return fail(st, "HCA part: %s", g_err.c_str());
+  REQUIRE(s->out != s->hout, CSA_INVALID_ARGUMENT, "the CSA and HCA outputs are the same buffer");
+  hipError_t e = csa::launch_indexer_topk(ai, (hipStream_t)stream);
+  if (e == hipSuccess)
+    e = csa::launch_attend_overlapped(ac, ah, (s->flags & CSA_STEP_IN_ORDER) == 0, (hipStream_t)stream);
+  return device_status(e, "csa_hybrid_decode_step launch");
 }
 
 csa_status_t csa_grouped_out_proj(const void* o, const void* w, int T, int H, int d, int G, int dg,

@@ -1,693 +1,25 @@
-// Core attention for CSA (selected compressed entries + sliding window + sink)
-// and HCA (every completed m'-block + optional window + sink).
-// Method: DeepSeek-V4 summary (hyper.ai), "Method": CSA core attention is MQA
-// over the top-k compressed entries with shared keys and values; HCA attends
-// densely over its heavily compressed entries; both add a sliding-window
-// branch.  aiboss88 "Technical Principles", CSA bullet: sliding window plus an
-// attention sink.  Form implemented (one softmax over all three parts):
-//   o = sum_j e^(l_j - M) v_j / (e^(s_h - M) + sum_j e^(l_j - M)),
-//   l_j = scale * q.k_j,  lse = M + ln(denominator).
-//
-// Mapping (MI355X, wave64, MFMA 32x32x16 bf16 / 32x32x2 fp32):
-//   * a workgroup owns a tile of query rows = (token, head) pairs: all H
-//     heads of one token for CSA (each token has its own key set), several
-//     tokens x H heads for HCA (all share the block prefix);
-//   * keys are staged KT=64 at a time in LDS: K row-major, V transposed;
-//   * each wave computes S^T = K Q^T for its 32 query rows, so every lane owns
-//     one query column: the online-softmax statistics stay in-lane (one
-//     cross-half shuffle), the probabilities already sit in the B-operand
-//     layout of O^T = V^T P^T, and the O^T accumulator rescale is per lane;
-//   * decode (one query token) splits the key list over workgroups and a
-//     combine kernel merges the partial (o, max, sum) in fixed split order,
-//     so results do not depend on the batch size.
-#include "common.hpp"
-#include "launch.hpp"
-
-#include <climits>
+// Host dispatch of the core attention (CSA: selected compressed entries +
+// sliding window + sink; HCA: every completed m'-block + optional window +
+// sink).  The kernels are templates in attend_impl.hpp, instantiated per
+// variant in the attend_v_*.hip translation units.
+#include "attend_impl.hpp"
 
 namespace csa {
 
-static constexpr int KT = 64;
-static constexpr float LOG2E = 1.4426950408889634f;
-static constexpr float LN2 = 0.6931471805599453f;
-
-struct AttnGeom {
-  int TT;          // tokens per tile
-  int nsplit;      // key splits
-  int kps;         // keys per split (multiple of KT)
-  float scale_log2;
-};
-
-__host__ __device__ __forceinline__ int hca_ne(int pos, int mp, int cap) {
-  return max(0, min((pos + 1) / mp, cap));
-}
-
-template <typename T>
-__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Position of the 4-key block kb (0..15) in row `dim` of the transposed V
-// tile: blocks are XOR-swizzled by the row's 8-dim group so that the staging
-// stores (one 4-key block for each of 8 consecutive dims per lane, lanes 8
-// dims apart) spread over the LDS banks; the MFMA operand reads apply the same map.
-__device__ __forceinline__ int vt_block(int dim, int kb) { return kb ^ ((dim >> 3) & 15); }
-
-// RW row-waves (32 query rows each) x KG key groups (KG=2: each wave of a pair
-// takes one 32-key half of every 64-key tile; the two partial softmax states
-// are merged in LDS at the end).  PF key tiles are in flight ahead of the one
-// being computed (PF=2 for split decode: a 128-key CSA split is then requested
-// at once).  Every instance fits 256 VGPRs, two waves per SIMD, so two
-// workgroups share a compute unit and one's loads overlap the other's math.
-// The body takes its workgroup's coordinates (token tile bx, split by,
-// sequence bz) and the dynamic LDS block from the kernel that runs it.
-template <typename T, int D, int RW, int KG, bool SPARSE, int PF, bool KV8 = false>
-__device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom& gm, int bx, int by,
-                                            int bz, unsigned char* smem_raw) {
-  static_assert(!KV8 || sizeof(T) == 2, "FP8 caches go with bf16 queries");
-  constexpr int NW = RW * KG;
-  constexpr int NT = NW * 64;
-  constexpr int NSUB = 2 / KG;                 // 32-key sub-tiles per wave per tile
-  constexpr int VEC = 16 / sizeof(T);          // elements per 16-byte chunk
-  constexpr int KPAD = VEC;                    // Ks row padding (16 bytes)
-  constexpr int VPAD = 4;                      // Vt row padding (elements)
-  constexpr int KS = D + KPAD;                 // Ks row stride (elements)
-  constexpr int VS = KT + VPAD;                // Vt row stride (elements)
-  constexpr int DSTEP = D / 16;                // k-steps of S^T
-  constexpr int DVT = D / 32;                  // 32-wide dv tiles of O^T
-
-  T* Ks = reinterpret_cast<T*>(smem_raw);
-  T* Vt = Ks + KT * KS;
-  int* sel = reinterpret_cast<int*>(Vt + D * VS);
-  __shared__ uint32_t scan_sm[NW];
-  __shared__ int s_nsel;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int rw = wave % RW, kg = wave / RW;
-  const int half = lane >> 5, col = lane & 31;
-  const int b = bz, split = by;
-  const int t0 = bx * gm.TT;
-  const int tl = min(t0 + gm.TT, a.Tq) - 1;
-  const int p0 = a.pos0[b];
-  const int pos_first = p0 + t0, pos_last = p0 + tl;
-  const int rp0 = a.raw_pos0 ? a.raw_pos0[b] : 0;
-
-  // Buffer resources: a load outside a buffer's range returns zeros, so absent
-  // keys, padding rows and masked slots are fetched without branches (which
-  // also keeps every load of a tile in flight together).
-  constexpr uint32_t OOB = 0x80000000u;                      // offset past every range
-  constexpr uint32_t ROWB = D * sizeof(T);
-  auto rsrc = [](const void* p, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
-  };
-
-  // ---- this wave's query fragments: loaded once into registers, issued
-  // before anything else ----
-  Frag<T> qfr[DSTEP];
-  {
-    const __amdgpu_buffer_rsrc_t rq =
-        rsrc(reinterpret_cast<const T*>(a.q) + (size_t)b * a.Tq * a.H * D, (uint32_t)a.Tq * a.H * ROWB);
-    const int r = rw * 32 + col;
-    const int ttr = r / a.H, hr = r % a.H, tqr = t0 + ttr;
-    const bool ok = ttr < gm.TT && tqr < a.Tq;
-    const uint32_t base = (uint32_t)(tqr * a.H + hr) * ROWB + 8 * half * sizeof(T);
-#pragma unroll
-    for (int s = 0; s < DSTEP; ++s) {
-      const uint32_t off = base + 16 * s * sizeof(T);
-      if constexpr (sizeof(T) == 2) {
-        qfr[s].v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, ok ? off : OOB, 0, 0));
-      } else {
-        const f32x4 lo = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, ok ? off : OOB, 0, 0));
-        const f32x4 hi = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, ok ? off + 16 : OOB, 0, 0));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { qfr[s].v[i] = lo[i]; qfr[s].v[4 + i] = hi[i]; }
-      }
-    }
-  }
-
-  // ---- the tile's key list: [compressed part][window part] ----
-  const int kbeg = split * gm.kps;
-  int ncomp, sel_base = 0;
-  if constexpr (SPARSE) {
-    const int32_t* ir = a.idx + ((size_t)b * a.Tq + t0) * a.topk;
-    const __amdgpu_buffer_rsrc_t ri = rsrc(ir, (uint32_t)a.topk * 4);
-    if (gm.nsplit > 1) {
-      // split decode: this workgroup's own slots of the index row; slots whose
-      // entry is invalid are masked out later
-      ncomp = a.topk;
-      sel_base = kbeg;
-      const int ns = max(0, min(gm.kps, a.topk - kbeg));
-      for (int i = tid; i < ns; i += NT)
-        sel[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(ri, (uint32_t)(kbeg + i) * 4, 0, 0);
-      __syncthreads();
-    } else {
-      // one workgroup per token: compact the valid entries into LDS; each
-      // thread owns a contiguous run of the index row, loaded in one round
-      constexpr int RUN = (4096 + NT - 1) / NT;      // topk <= 4096
-      const int i0 = tid * RUN;
-      int ev[RUN];
-      uint32_t cnt = 0;
-#pragma unroll
-      for (int q = 0; q < RUN; ++q) {
-        const int i = i0 + q;
-        const int v = (int)__builtin_amdgcn_raw_buffer_load_b32(ri, i < a.topk ? (uint32_t)i * 4 : OOB, 0, 0);
-        ev[q] = i < a.topk ? v : -1;
-      }
-#pragma unroll
-      for (int q = 0; q < RUN; ++q) cnt += (ev[q] >= 0 && ev[q] < a.Nc_cap) ? 1u : 0u;
-      uint32_t base;
-      uint32_t pos = block_excl_scan<NT>(cnt, scan_sm, &base);
-#pragma unroll
-      for (int q = 0; q < RUN; ++q)
-        if (ev[q] >= 0 && ev[q] < a.Nc_cap) sel[pos++] = ev[q];
-      if (tid == 0) s_nsel = (int)base;
-      __syncthreads();
-      ncomp = s_nsel;
-    }
-  } else {
-    ncomp = hca_ne(pos_last, a.m_prime, a.Nc_cap);
-  }
-  const int wlo = a.window > 0 ? max(0, pos_first - a.window + 1) : 0;
-  const int nwin = a.window > 0 ? pos_last - wlo + 1 : 0;
-  const int nkeys = ncomp + nwin;
-  const int kend = min(nkeys, kbeg + gm.kps);
-
-  // ---- this lane's query row ----
-  const int qr = rw * 32 + col;
-  const int tt = qr / a.H, hq = qr % a.H;
-  const int tq = t0 + tt;
-  const bool qvalid = (tt < gm.TT) && (tq < a.Tq);
-  const int qpos = p0 + tq;
-  const int q_ne = SPARSE ? ncomp : hca_ne(qpos, a.m_prime, a.Nc_cap);
-  const int q_wlo = max(0, qpos - a.window + 1);
-
-  f32x16 o[DVT];
-#pragma unroll
-  for (int i = 0; i < DVT; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[i][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-
-  const T* kcb = reinterpret_cast<const T*>(a.kc) + (size_t)b * a.Nc_cap * D;
-  const T* vcb = reinterpret_cast<const T*>(a.vc) + (size_t)b * a.Nc_cap * D;
-  const T* kwb = a.kw ? reinterpret_cast<const T*>(a.kw) + (size_t)b * a.R * D : nullptr;
-  const T* vwb = a.vw ? reinterpret_cast<const T*>(a.vw) + (size_t)b * a.R * D : nullptr;
-  // Facts that let whole tiles skip per-element masking (wave-uniform):
-  // every window row is present in the raw buffer, and the smallest number of
-  // compressed entries visible to any valid row of this wave.
-  const bool win_ok = nwin == 0 || (kwb != nullptr && wlo - rp0 >= 0 && wlo + nwin - 1 - rp0 < a.R);
-  int wave_min_ne = qvalid ? q_ne : INT_MAX;
-#pragma unroll
-  for (int o2 = 32; o2 > 0; o2 >>= 1) wave_min_ne = min(wave_min_ne, __shfl_xor(wave_min_ne, o2, 64));
-
-  // byte offset of key slot s's row in the compressed / window buffers (OOB =
-  // not there)
-  const __amdgpu_buffer_rsrc_t rkc = rsrc(kcb, (uint32_t)a.Nc_cap * ROWB);
-  const __amdgpu_buffer_rsrc_t rvc = rsrc(vcb, (uint32_t)a.Nc_cap * ROWB);
-  const __amdgpu_buffer_rsrc_t rkw = rsrc(kwb, kwb ? (uint32_t)a.R * ROWB : 0u);
-  const __amdgpu_buffer_rsrc_t rvw = rsrc(vwb, vwb ? (uint32_t)a.R * ROWB : 0u);
-  // compressed entry held by key slot s, or -1
-  auto ent = [&](int s) -> int {
-    if (s < kbeg || s >= kend || s >= ncomp) return -1;
-    const int e = SPARSE ? sel[s - sel_base] : s;
-    return (e >= 0 && e < a.Nc_cap) ? e : -1;
-  };
-  auto comp_off = [&](int s) -> uint32_t {
-    const int e = ent(s);
-    return e >= 0 ? (uint32_t)e * ROWB : OOB;
-  };
-  // FP8 cache planes of this sequence
-  constexpr int DN = D / 2;                                  // E4M3 dims of a K row (the rest is bf16)
-  const size_t cb = (size_t)b * a.Nc_cap;
-  const __amdgpu_buffer_rsrc_t rk8 = rsrc(KV8 ? (const uint8_t*)a.k8 + cb * DN : nullptr, KV8 ? (uint32_t)a.Nc_cap * DN : 0u);
-  const __amdgpu_buffer_rsrc_t rkr = rsrc(KV8 ? (const uint16_t*)a.krope + cb * (D - DN) : nullptr,
-                                          KV8 ? (uint32_t)a.Nc_cap * (D - DN) * 2 : 0u);
-  const bool vshared = KV8 && a.v8 == nullptr;                // values = key rows (shared entry)
-  const __amdgpu_buffer_rsrc_t rv8 = rsrc(KV8 && !vshared ? (const uint8_t*)a.v8 + cb * D : nullptr,
-                                          KV8 && !vshared ? (uint32_t)a.Nc_cap * D : 0u);
-  const __amdgpu_buffer_rsrc_t rks = rsrc(KV8 ? a.kscale + cb : nullptr, KV8 ? (uint32_t)a.Nc_cap * 4 : 0u);
-  const __amdgpu_buffer_rsrc_t rvs = rsrc(KV8 && !vshared ? a.vscale + cb : nullptr,
-                                          KV8 && !vshared ? (uint32_t)a.Nc_cap * 4 : 0u);
-  // 8 codes (x, y) and their row scale (z) of an FP8 row chunk, or zeros
-  auto ld8 = [](const __amdgpu_buffer_rsrc_t& rc, const __amdgpu_buffer_rsrc_t& rs, int e, uint32_t off) -> u32x4 {
-    const auto c = __builtin_amdgcn_raw_buffer_load_b64(rc, e >= 0 ? off : OOB, 0, 0);
-    const uint32_t sc = __builtin_amdgcn_raw_buffer_load_b32(rs, e >= 0 ? (uint32_t)e * 4 : OOB, 0, 0);
-    return u32x4{c[0], c[1], sc, 0u};
-  };
-  // 8 E4M3 codes times the row scale, as 8 bf16 (codes widen exactly; the
-  // product is rounded to nearest even).  The hardware conversion applies only
-  // the exponent of its scale operand (measured on gfx950), so it serves the
-  // power-of-two scales directly and other scales take an fp32 multiply.
-  auto dequant8 = [](const u32x4& r) -> u32x4 {
-    const float sc = __uint_as_float(r[2]);
-    u32x4 o;
-    if ((r[2] & 0x007FFFFFu) == 0u) {
-#pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        o[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r[w], sc, false));
-        o[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r[w], sc, true));
-      }
-      return o;
-    }
-#pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r[w], 1.0f, false));
-      const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r[w], 1.0f, true));
-      o[2 * w] = pack_bf16x2(bf16_bits_to_f32(lo & 0xFFFFu) * sc, bf16_bits_to_f32(lo >> 16) * sc);
-      o[2 * w + 1] = pack_bf16x2(bf16_bits_to_f32(hi & 0xFFFFu) * sc, bf16_bits_to_f32(hi >> 16) * sc);
-    }
-    return o;
-  };
-  auto win_off = [&](int s) -> uint32_t {
-    if (s < kbeg || s >= kend || s < ncomp) return OOB;
-    const int r = wlo + (s - ncomp) - rp0;
-    return (r >= 0 && r < a.R) ? (uint32_t)r * ROWB : OOB;
-  };
-
-  // ---- staging: all global loads of a tile are issued into registers first
-  // (so they are in flight together), then written to LDS: K row-major, V
-  // transposed.  Tiles that hold only compressed or only window keys read one
-  // buffer; the tile that straddles both ORs the two (one of them is zero).
-  constexpr int KCH = D / VEC;                               // 16-byte chunks per row
-  constexpr int KLD = (KT * KCH + NT - 1) / NT;              // K chunks per thread
-  constexpr int VTOT = (KT / 4) * KCH;                       // V tasks: 4 keys x 16 bytes
-  constexpr int VTK = (VTOT + NT - 1) / NT;
-  u32x4 kregA[KLD], vregA[VTK][4];
-  u32x4 kregB[PF == 2 ? KLD : 1], vregB[PF == 2 ? VTK : 1][4];
-  // K staging task c -> (row, 16-byte chunk): row-major for bf16 caches; for
-  // FP8 caches chunk-major, so that a wave's 64 lanes share one chunk (and
-  // with it the chunk's kind: codes or RoPE values)
-  auto krow = [](int c) { return KV8 ? c % KT : c / KCH; };
-  auto kch = [](int c) { return KV8 ? c / KT : c % KCH; };
-  auto ld = [](const __amdgpu_buffer_rsrc_t& r, uint32_t off, uint32_t ch) -> u32x4 {
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off == OOB ? OOB : off + ch * 16, 0, 0));
-  };
-  auto stage_load = [&](auto& kreg, auto& vreg, int s0) {
-    // per-tile source: compressed keys only, window keys only, or both (the
-    // one tile that straddles the boundary); each branch issues its loads back
-    // to back
-    auto load_all = [&](auto&& fetch) {
-#pragma unroll
-      for (int i = 0; i < KLD; ++i) {
-        const int c = tid + i * NT;
-        kreg[i] = fetch(true, c < KT * KCH ? s0 + krow(c) : INT_MAX / 2, kch(c));
-      }
-#pragma unroll
-      for (int i = 0; i < VTK; ++i) {
-        const int c = tid + i * NT;
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          vreg[i][u] = fetch(false, c < VTOT ? s0 + (c / KCH) * 4 + u : INT_MAX / 2, c % KCH);
-      }
-    };
-    if constexpr (KV8) {
-      // FP8 rows: a K chunk below DN dims is 8 codes + scale, above it 8 bf16
-      // RoPE values (the chunk kind is uniform over a wave); a V chunk is 8
-      // codes + scale.  Window rows are bf16.
-      // (values shared with keys: the value row is the key row)
-      auto comp8 = [&](bool k, int s, int ch) -> u32x4 {
-        const int e = ent(s);
-        if ((k || vshared) && ch >= DN / VEC) return ld(rkr, e >= 0 ? (uint32_t)e * (D - DN) * 2 : OOB, ch - DN / VEC);
-        if (k || vshared) return ld8(rk8, rks, e, (uint32_t)e * DN + ch * 8);
-        return ld8(rv8, rvs, e, (uint32_t)e * D + ch * 8);
-      };
-      if (s0 + KT <= ncomp || nwin == 0)
-        load_all(comp8);
-      else if (s0 >= ncomp)
-        load_all([&](bool k, int s, int ch) { return ld(k ? rkw : rvw, win_off(s), ch); });
-      else
-        load_all([&](bool k, int s, int ch) { return comp8(k, s, ch) | ld(k ? rkw : rvw, win_off(s), ch); });
-    } else if (s0 + KT <= ncomp || nwin == 0) {
-      load_all([&](bool k, int s, int ch) { return ld(k ? rkc : rvc, comp_off(s), ch); });
-    } else if (s0 >= ncomp) {
-      load_all([&](bool k, int s, int ch) { return ld(k ? rkw : rvw, win_off(s), ch); });
-    } else {
-      load_all([&](bool k, int s, int ch) {
-        return ld(k ? rkc : rvc, comp_off(s), ch) | ld(k ? rkw : rvw, win_off(s), ch);
-      });
-    }
-  };
-  auto stage_store = [&](const auto& kreg, const auto& vreg, int s0) {
-#pragma unroll
-    for (int i = 0; i < KLD; ++i) {
-      const int c = tid + i * NT;
-      if (c >= KT * KCH) continue;
-      u32x4 r = kreg[i];
-      if constexpr (KV8)
-        if (kch(c) < DN / VEC && ent(s0 + krow(c)) >= 0) r = dequant8(r);
-      *reinterpret_cast<u32x4*>(Ks + krow(c) * KS + kch(c) * VEC) = r;
-    }
-#pragma unroll
-    for (int i = 0; i < VTK; ++i) {
-      const int c = tid + i * NT;
-      if (c >= VTOT) continue;
-      const int kg = c / KCH, ch = c % KCH;
-      u32x4 vr[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        vr[u] = vreg[i][u];
-        if constexpr (KV8)
-          if ((!vshared || ch < DN / VEC) && ent(s0 + kg * 4 + u) >= 0) vr[u] = dequant8(vr[u]);
-      }
-      const T* rows = reinterpret_cast<const T*>(vr);           // [4][VEC]
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        T four[4] = {rows[e], rows[VEC + e], rows[2 * VEC + e], rows[3 * VEC + e]};
-        T* dst = Vt + (ch * VEC + e) * VS + vt_block(ch * VEC + e, kg) * 4;
-        if constexpr (sizeof(T) == 2) *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<uint2*>(four);
-        else *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<u32x4*>(four);
-      }
-    }
-  };
-
-  if (kbeg < kend) stage_load(kregA, vregA, kbeg);
-  if constexpr (PF == 2) {
-    if (kbeg + KT < kend) stage_load(kregB, vregB, kbeg + KT);
-  }
-
-  auto tile = [&](int s0) {
-    // ---- S^T = K Q^T for this wave's 32-key sub-tiles ----
-    f32x16 st[NSUB];
-#pragma unroll
-    for (int si = 0; si < NSUB; ++si)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st[si][r] = 0.f;
-#pragma unroll
-    for (int s = 0; s < DSTEP; ++s) {
-#pragma unroll
-      for (int si = 0; si < NSUB; ++si) {
-        const int sub = KG == 2 ? kg : si;
-        Frag<T> kf;
-        frag_load(kf, Ks + (sub * 32 + col) * KS + 16 * s + 8 * half);
-        mma32(st[si], kf, qfr[s]);
-      }
-    }
-    // ---- mask (only tiles that reach a boundary), online softmax ----
-    const int t_end = s0 + KT;
-    bool comp_ok = true;                       // every compressed slot of the tile holds an entry
-    if constexpr (SPARSE) {
-      if (sel_base > 0 || gm.nsplit > 1) {
-        const int sl = s0 + lane;
-        const int e = sl < min(t_end, ncomp) ? sel[sl - sel_base] : 0;
-        comp_ok = __all(e >= 0 && e < a.Nc_cap);
-      }
-    }
-    const bool full = t_end <= kend &&
-                      (SPARSE ? comp_ok && (t_end <= ncomp || win_ok) : (t_end <= ncomp && t_end <= wave_min_ne));
-    float mt = -INFINITY;
-#pragma unroll
-    for (int si = 0; si < NSUB; ++si) {
-      const int sub = KG == 2 ? kg : si;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = st[si][r];                   // raw q.k; the scale is applied in the exponent
-        if (!full) {
-          const int s = s0 + sub * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          bool ok = qvalid && s < kend;
-          if (ok && s >= ncomp) {
-            const int p = wlo + (s - ncomp);
-            ok = (p - rp0 >= 0) && (p - rp0 < a.R) && (kwb != nullptr);   // row present
-            if (!SPARSE) ok = ok && p >= q_wlo && p <= qpos;
-          } else if (ok) {
-            if constexpr (SPARSE) {
-              const int e = sel[s - sel_base];
-              ok = e >= 0 && e < a.Nc_cap;
-            } else {
-              ok = s < q_ne;
-            }
-          }
-          x = ok ? x : -INFINITY;
-        }
-        st[si][r] = x;
-        mt = fmaxf(mt, x);
-      }
-    }
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * gm.scale_log2;   // scale > 0 keeps the order
-    // The reference max only moves when a lane's tile max exceeds it by more
-    // than 8 (log2 units): P stays <= 2^8 and most tiles skip the O rescale.
-    if (__any(mt > m_run + 8.f)) {
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = (m_new == -INFINITY) ? 1.f : fexp2<T>(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < DVT; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[i][r] *= alpha;
-      m_run = m_new;
-    }
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-    float psum = 0.f;
-    Frag<T> pf[NSUB][2];
-#pragma unroll
-    for (int si = 0; si < NSUB; ++si) {
-      float pv[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        pv[r] = fexp2<T>(fmaf(st[si][r], gm.scale_log2, -m_use));
-        psum += pv[r];
-      }
-      frag_from_f32(pf[si][0], pv);
-      frag_from_f32(pf[si][1], pv + 8);
-    }
-    l_run += psum;
-
-    // ---- O^T += V^T P^T ----
-#pragma unroll
-    for (int i = 0; i < DVT; ++i) {
-      const T* vrow = Vt + (i * 32 + col) * VS;
-#pragma unroll
-      for (int si = 0; si < NSUB; ++si) {
-        const int sub = KG == 2 ? kg : si;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int kb = sub * 32 + 16 * ks + 4 * half;    // first of keys kb..kb+3, kb+8..kb+11
-          Frag<T> vf;
-          if constexpr (sizeof(T) == 2) {
-            const uint2 lo = *reinterpret_cast<const uint2*>(vrow + vt_block(i * 32 + col, kb / 4) * 4);
-            const uint2 hi = *reinterpret_cast<const uint2*>(vrow + vt_block(i * 32 + col, kb / 4 + 2) * 4);
-            vf.v = u32x4{lo.x, lo.y, hi.x, hi.y};
-          } else {
-            const f32x4 lo = *reinterpret_cast<const f32x4*>(vrow + vt_block(i * 32 + col, kb / 4) * 4);
-            const f32x4 hi = *reinterpret_cast<const f32x4*>(vrow + vt_block(i * 32 + col, kb / 4 + 2) * 4);
-            float* fv = reinterpret_cast<float*>(&vf);
-            fv[0] = lo[0]; fv[1] = lo[1]; fv[2] = lo[2]; fv[3] = lo[3];
-            fv[4] = hi[0]; fv[5] = hi[1]; fv[6] = hi[2]; fv[7] = hi[3];
-          }
-          mma32(o[i], vf, pf[si][ks]);
-        }
-      }
-    }
-  };
-  if constexpr (PF == 2) {
-    for (int s0 = kbeg; s0 < kend; s0 += 2 * KT) {
-      stage_store(kregA, vregA, s0);
-      __syncthreads();
-      if (s0 + 2 * KT < kend) stage_load(kregA, vregA, s0 + 2 * KT);
-      tile(s0);
-      __syncthreads();
-      if (s0 + KT >= kend) break;
-      stage_store(kregB, vregB, s0 + KT);
-      __syncthreads();
-      if (s0 + 3 * KT < kend) stage_load(kregB, vregB, s0 + 3 * KT);
-      tile(s0 + KT);
-      __syncthreads();
-    }
-  } else {
-    for (int s0 = kbeg; s0 < kend; s0 += KT) {
-      stage_store(kregA, vregA, s0);
-      __syncthreads();
-      if (s0 + KT < kend) stage_load(kregA, vregA, s0 + KT);
-      tile(s0);
-      __syncthreads();
-    }
-  }
-
-  // ---- merge the two key groups (their staging area is free now) ----
-  if constexpr (KG == 2) {
-    float* mb = reinterpret_cast<float*>(smem_raw) + (size_t)(rw * 64 + lane) * (DVT * 16 + 2);
-    if (kg == 1) {
-#pragma unroll
-      for (int i = 0; i < DVT; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mb[i * 16 + r] = o[i][r];
-      mb[DVT * 16] = m_run;
-      mb[DVT * 16 + 1] = l_run;
-    }
-    __syncthreads();
-    if (kg == 1) return;
-    const float m1 = mb[DVT * 16], l1 = mb[DVT * 16 + 1];
-    const float M = fmaxf(m_run, m1);
-    const float Mu = (M == -INFINITY) ? 0.f : M;
-    const float c0 = fexp2<T>(m_run - Mu), c1 = fexp2<T>(m1 - Mu);
-#pragma unroll
-    for (int i = 0; i < DVT; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[i][r] = o[i][r] * c0 + mb[i * 16 + r] * c1;
-    l_run = l_run * c0 + l1 * c1;
-    m_run = M;
-  }
-
-  // ---- epilogue ----
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  if (!qvalid) return;
-  const size_t grow = ((size_t)b * a.Tq + tq) * a.H + hq;
-  if (gm.nsplit > 1) {
-    const size_t rows_total = (size_t)a.B * a.Tq * a.H;
-    float* po = reinterpret_cast<float*>(a.ws) + ((size_t)split * rows_total + grow) * D;
-    float* pm = reinterpret_cast<float*>(a.ws) + (size_t)gm.nsplit * rows_total * D;
-    float* pl = pm + (size_t)gm.nsplit * rows_total;
-#pragma unroll
-    for (int i = 0; i < DVT; ++i)
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<f32x4*>(po + i * 32 + 8 * g + 4 * half) =
-            f32x4{o[i][4 * g], o[i][4 * g + 1], o[i][4 * g + 2], o[i][4 * g + 3]};
-    if (half == 0) {
-      pm[(size_t)split * rows_total + grow] = m_run;
-      pl[(size_t)split * rows_total + grow] = l_tot;
-    }
-    return;
-  }
-  const float s2 = a.sink ? a.sink[hq] * LOG2E : -INFINITY;
-  const float M = fmaxf(m_run, s2);
-  float fac = 0.f, lse = -INFINITY;
-  if (M != -INFINITY) {
-    const float cm = fexp2<T>(m_run - M);             // m_run = -inf -> 0
-    const float Z = l_tot * cm + fexp2<T>(s2 - M);
-    fac = cm / Z;
-    lse = (M + __log2f(Z)) * LN2;
-  }
-  T* orow = reinterpret_cast<T*>(a.out) + grow * D;
-#pragma unroll
-  for (int i = 0; i < DVT; ++i)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      T v4[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) v4[u] = from_f32<T>(o[i][4 * g + u] * fac);
-      T* dst = orow + i * 32 + 8 * g + 4 * half;
-      if constexpr (sizeof(T) == 2) *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<uint2*>(v4);
-      else *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<u32x4*>(v4);
-    }
-  if (a.lse && half == 0) a.lse[grow] = lse;
-}
-
-template <typename T, int D, int RW, int KG, bool SPARSE, int PF, bool KV8>
-__global__ __launch_bounds__(RW * KG * 64) __attribute__((amdgpu_waves_per_eu(KV8 && !(RW == 2 && KG == 2) ? 1 : 2))) void attend_kernel(AttendArgs a, AttnGeom gm) {
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  attend_body<T, D, RW, KG, SPARSE, PF, KV8>(a, gm, blockIdx.x, blockIdx.y, blockIdx.z, smem_raw);
-}
-
-// The HCA and CSA attention of one layer pair in a single split-decode launch:
-// a 1-D grid whose first nb0 workgroups run the HCA problem a0 and the rest the
-// CSA problem a1 (each decomposed as its own (tile, split, sequence) grid, the
-// same as in its own launch).  Two workgroups fit a compute unit, so the two
-// grids of a decode batch run side by side instead of one after the other.
-template <typename T, int D, int RW, int KG>
-__global__ __launch_bounds__(RW * KG * 64) __attribute__((amdgpu_waves_per_eu(2))) void attend_pair_kernel(
-    AttendArgs a0, AttnGeom g0, AttendArgs a1, AttnGeom g1, int nb0) {
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  int bid = blockIdx.x;
-  if (bid < nb0) {
-    const int gx = (a0.Tq + g0.TT - 1) / g0.TT;
-    attend_body<T, D, RW, KG, false, 2>(a0, g0, bid % gx, (bid / gx) % g0.nsplit, bid / (gx * g0.nsplit), smem_raw);
-  } else {
-    bid -= nb0;
-    const int gx = (a1.Tq + g1.TT - 1) / g1.TT;
-    attend_body<T, D, RW, KG, true, 2>(a1, g1, bid % gx, (bid / gx) % g1.nsplit, bid / (gx * g1.nsplit), smem_raw);
-  }
-}
-
-// Merge split partials in fixed split order (one wave per query row).  The
-// partials of CB splits are requested together; a running maximum rescales
-// the sums between batches, so the result depends only on the split list.
-template <typename T, int D>
-__device__ __forceinline__ void combine_row(const AttendArgs& a, int nsplit, size_t row) {
-  constexpr int PER = D / 64;
-  constexpr int CB = 32;
-  const int lane = threadIdx.x & 63;
-  const size_t rows_total = (size_t)a.B * a.Tq * a.H;
-  if (row >= rows_total) return;
-  const float* po = reinterpret_cast<const float*>(a.ws);
-  const float* pm = po + (size_t)nsplit * rows_total * D;
-  const float* pl = pm + (size_t)nsplit * rows_total;
-  const int h = (int)(row % a.H);
-  const float s2 = a.sink ? a.sink[h] * LOG2E : -INFINITY;
-  float M = s2, Z = 0.f;
-  float acc[PER];
-#pragma unroll
-  for (int u = 0; u < PER; ++u) acc[u] = 0.f;
-  for (int s0 = 0; s0 < nsplit; s0 += CB) {
-    // every load is unconditional (split indices past the end repeat the last
-    // split, whose weight is then zero), so all of them are in flight together
-    float v[CB][PER];
-    const int sl = min(s0 + (lane & (CB - 1)), nsplit - 1);
-    const bool lv_ok = lane < CB && s0 + lane < nsplit;
-    const float mraw = pm[(size_t)sl * rows_total + row];
-    const float lraw = pl[(size_t)sl * rows_total + row];
-#pragma unroll
-    for (int j = 0; j < CB; ++j) {
-      const float* src = po + ((size_t)min(s0 + j, nsplit - 1) * rows_total + row) * D + lane * PER;
-#pragma unroll
-      for (int u = 0; u < PER; ++u) v[j][u] = src[u];
-    }
-    const float mv = lv_ok ? mraw : -INFINITY;
-    const float lv = lv_ok ? lraw : 0.f;
-    const float M_new = fmaxf(M, wave_max(mv));
-    if (M_new == -INFINITY) continue;
-    const float r = __builtin_amdgcn_exp2f(M - M_new);      // M = -inf -> 0
-    Z *= r;
-#pragma unroll
-    for (int u = 0; u < PER; ++u) acc[u] *= r;
-    const float cl = __builtin_amdgcn_exp2f(mv - M_new);     // this lane's split weight
-    Z += wave_sum(lv * cl);
-#pragma unroll
-    for (int j = 0; j < CB; ++j) {
-      const float c = __shfl(cl, j, 64);
-#pragma unroll
-      for (int u = 0; u < PER; ++u) acc[u] = fmaf(v[j][u], c, acc[u]);
-    }
-    M = M_new;
-  }
-  float lse = -INFINITY, inv = 0.f;
-  if (M != -INFINITY) {
-    Z += __builtin_amdgcn_exp2f(s2 - M);
-    lse = (M + __log2f(Z)) * LN2;
-    inv = 1.f / Z;
-  }
-  T* orow = reinterpret_cast<T*>(a.out) + row * D;
-#pragma unroll
-  for (int u = 0; u < PER; ++u) orow[lane * PER + u] = from_f32<T>(acc[u] * inv);
-  if (a.lse && lane == 0) a.lse[row] = lse;
-}
-
-template <typename T, int D>
-__global__ __launch_bounds__(256) void combine_kernel(AttendArgs a, int nsplit) {
-  combine_row<T, D>(a, nsplit, (size_t)blockIdx.x * 4 + (threadIdx.x >> 6));
-}
-
-// Both problems of a pair launch: workgroups below nb0 merge a0's rows.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void combine_pair_kernel(AttendArgs a0, int ns0, AttendArgs a1, int ns1,
-                                                           int nb0) {
-  if ((int)blockIdx.x < nb0) combine_row<T, D>(a0, ns0, (size_t)blockIdx.x * 4 + (threadIdx.x >> 6));
-  else combine_row<T, D>(a1, ns1, (size_t)(blockIdx.x - nb0) * 4 + (threadIdx.x >> 6));
-}
-
-// ---------------------------------- host -----------------------------------
-static int keys_per_split(bool sparse, int Tq) {
-  if (Tq != 1) return INT_MAX / 2;
-  return sparse ? 128 : 256;
-}
-
-static int tokens_per_tile(bool sparse, int H, int Tq) {
-  if (sparse) return 1;
-  return std::max(1, std::min(128 / H, Tq));
-}
-
-static int nkeys_upper(bool sparse, int topk, int window, int Nc_cap, int m_prime, int max_pos) {
-  const int w = window > 0 ? std::min(window, max_pos + 1) : 0;
-  if (sparse) return topk + w;
-  return hca_ne(max_pos, m_prime, Nc_cap) + w;
-}
+// instantiated in the attend_v_*.hip translation units
+extern template hipError_t attend_variant<float, 64, false>(const AttendArgs&, const AttnGeom&, const AttendLaunch&, hipStream_t);
+extern template hipError_t attend_variant<float, 128, false>(const AttendArgs&, const AttnGeom&, const AttendLaunch&, hipStream_t);
+extern template hipError_t attend_variant<bf16, 64, false>(const AttendArgs&, const AttnGeom&, const AttendLaunch&, hipStream_t);
+extern template hipError_t attend_variant<bf16, 128, false>(const AttendArgs&, const AttnGeom&, const AttendLaunch&, hipStream_t);
+extern template hipError_t attend_variant<bf16, 128, true>(const AttendArgs&, const AttnGeom&, const AttendLaunch&, hipStream_t);
+extern template hipError_t pair_variant<float, 64>(const AttendArgs&, const AttnGeom&, const AttendArgs&, const AttnGeom&, int, hipStream_t);
+extern template hipError_t combine_pair_variant<float, 64>(const AttendArgs&, const AttnGeom&, const AttendArgs&, const AttnGeom&, hipStream_t);
+extern template hipError_t pair_variant<float, 128>(const AttendArgs&, const AttnGeom&, const AttendArgs&, const AttnGeom&, int, hipStream_t);
+extern template hipError_t combine_pair_variant<float, 128>(const AttendArgs&, const AttnGeom&, const AttendArgs&, const AttnGeom&, hipStream_t);
+extern template hipError_t pair_variant<bf16, 64>(const AttendArgs&, const AttnGeom&, const AttendArgs&, const AttnGeom&, int, hipStream_t);
+extern template hipError_t combine_pair_variant<bf16, 64>(const AttendArgs&, const AttnGeom&, const AttendArgs&, const AttnGeom&, hipStream_t);
+extern template hipError_t pair_variant<bf16, 128>(const AttendArgs&, const AttnGeom&, const AttendArgs&, const AttnGeom&, int, hipStream_t);
+extern template hipError_t combine_pair_variant<bf16, 128>(const AttendArgs&, const AttnGeom&, const AttendArgs&, const AttnGeom&, hipStream_t);
 
 size_t attend_workspace(bool sparse, int B, int Tq, int H, int d, int topk, int window,
                         int Nc_cap, int m_prime, int max_pos) {
@@ -698,120 +30,25 @@ size_t attend_workspace(bool sparse, int B, int Tq, int H, int d, int topk, int 
   return (size_t)ns * B * Tq * H * (d + 2) * sizeof(float);
 }
 
-template <typename T, int D, bool SPARSE>
-static size_t attend_lds(const AttendArgs& a, int RW, int KG) {
-  constexpr int KS = D + 16 / sizeof(T);
-  constexpr int VS = KT + 4;
-  size_t lds = (size_t)(KT * KS + D * VS) * sizeof(T) + (SPARSE ? (size_t)a.topk * 4 : 0);
-  if (KG == 2) lds = std::max(lds, (size_t)RW * 64 * ((D / 32) * 16 + 2) * sizeof(float));
-  return lds;
-}
-
-template <typename K>
-static hipError_t set_lds(K kfn, size_t lds) {
-  if (lds <= 65536) return hipSuccess;
-  return hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-}
-
-static size_t partial_rows(const AttendArgs& a) { return (size_t)a.B * a.Tq * a.H; }
-
-template <typename T, int D, int RW, int KG, bool SPARSE, int PF, bool KV8>
-static hipError_t launch5(const AttendArgs& a, const AttnGeom& gm, hipStream_t st) {
-  const size_t lds = attend_lds<T, D, SPARSE>(a, RW, KG);
-  auto kfn = attend_kernel<T, D, RW, KG, SPARSE, PF, KV8>;
-  hipError_t e = set_lds(kfn, lds);
-  if (e != hipSuccess) return e;
-  dim3 grid((a.Tq + gm.TT - 1) / gm.TT, gm.nsplit, a.B);
-  {
-    ProfScope ps(SPARSE ? "attend_csa" : "attend_hca", st);
-    hipLaunchKernelGGL(kfn, grid, dim3(RW * KG * 64), lds, st, a, gm);
-  }
-  e = hipGetLastError();
-  if (e != hipSuccess || gm.nsplit <= 1) return e;
-  ProfScope ps("attend_combine", st);
-  hipLaunchKernelGGL((combine_kernel<T, D>), dim3((unsigned)((partial_rows(a) + 3) / 4)), dim3(256), 0, st,
-                     a, gm.nsplit);
-  return hipGetLastError();
-}
-
-template <typename T, int D, int RW, int KG, bool SPARSE, bool KV8>
-static hipError_t launch4(const AttendArgs& a, const AttnGeom& gm, hipStream_t st) {
-  return gm.nsplit > 1 ? launch5<T, D, RW, KG, SPARSE, 2, KV8>(a, gm, st)
-                       : launch5<T, D, RW, KG, SPARSE, 1, KV8>(a, gm, st);
-}
-
-// Row-waves cover the tile's (token, head) rows; tiles of at most 64 rows get
-// a second key group so that four waves share every staged tile.
-static void wave_shape(int rows, int* RW, int* KG) {
-  if (rows <= 32) { *RW = 1; *KG = 2; }
-  else if (rows <= 64) { *RW = 2; *KG = 2; }
-  else if (rows <= 96) { *RW = 3; *KG = 1; }
-  else { *RW = 4; *KG = 1; }
-}
-
-template <typename T, int D, bool SPARSE, bool KV8>
-static hipError_t launch3(const AttendArgs& a, const AttnGeom& gm, hipStream_t st) {
-  int RW, KG;
-  wave_shape(gm.TT * a.H, &RW, &KG);
-  if (RW == 1) return launch4<T, D, 1, 2, SPARSE, KV8>(a, gm, st);
-  if (RW == 2) return launch4<T, D, 2, 2, SPARSE, KV8>(a, gm, st);
-  if (RW == 3) return launch4<T, D, 3, 1, SPARSE, KV8>(a, gm, st);
-  return launch4<T, D, 4, 1, SPARSE, KV8>(a, gm, st);
-}
-
-template <typename T, int D, bool KV8 = false>
-static hipError_t launch2(const AttendArgs& a, const AttnGeom& gm, hipStream_t st) {
-  return a.sparse ? launch3<T, D, true, KV8>(a, gm, st) : launch3<T, D, false, KV8>(a, gm, st);
-}
-
-static AttnGeom make_geom(const AttendArgs& a) {
-  AttnGeom gm;
-  gm.TT = tokens_per_tile(a.sparse, a.H, a.Tq);
-  const int kps = keys_per_split(a.sparse, a.Tq);
-  const long nk = nkeys_upper(a.sparse, a.topk, a.window, a.Nc_cap, a.m_prime, a.max_pos);
-  gm.nsplit = (int)std::max(1L, (nk + kps - 1) / kps);
-  gm.kps = gm.nsplit > 1 ? kps : INT_MAX / 2;
-  gm.scale_log2 = a.scale * LOG2E;
-  return gm;
+static hipError_t dispatch(const AttendArgs& a, const AttnGeom& gm, const AttendLaunch& how, hipStream_t st) {
+  if (a.kv8) return a.d == 128 && !a.f32 ? attend_variant<bf16, 128, true>(a, gm, how, st) : hipErrorInvalidValue;
+  if (a.f32) return a.d == 64 ? attend_variant<float, 64, false>(a, gm, how, st)
+                              : attend_variant<float, 128, false>(a, gm, how, st);
+  return a.d == 64 ? attend_variant<bf16, 64, false>(a, gm, how, st)
+                   : attend_variant<bf16, 128, false>(a, gm, how, st);
 }
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
   if (a.B == 0 || a.Tq == 0) return hipSuccess;
-  const AttnGeom gm = make_geom(a);
-  if (a.kv8) return a.d == 128 && !a.f32 ? launch2<bf16, 128, true>(a, gm, st) : hipErrorInvalidValue;
-  if (a.f32) return a.d == 64 ? launch2<float, 64>(a, gm, st) : launch2<float, 128>(a, gm, st);
-  return a.d == 64 ? launch2<bf16, 64>(a, gm, st) : launch2<bf16, 128>(a, gm, st);
+  return dispatch(a, make_geom(a), AttendLaunch{}, st);
 }
 
-template <typename T, int D, int RW, int KG>
-static hipError_t launch_pair4(const AttendArgs& h, const AttnGeom& gh, const AttendArgs& c,
+static hipError_t combine_pair(const AttendArgs& h, const AttnGeom& gh, const AttendArgs& c,
                                const AttnGeom& gc, hipStream_t st) {
-  const size_t lds = std::max(attend_lds<T, D, false>(h, RW, KG), attend_lds<T, D, true>(c, RW, KG));
-  auto kfn = attend_pair_kernel<T, D, RW, KG>;
-  hipError_t e = set_lds(kfn, lds);
-  if (e != hipSuccess) return e;
-  const long nbh = (long)((h.Tq + gh.TT - 1) / gh.TT) * gh.nsplit * h.B;
-  const long nbc = (long)((c.Tq + gc.TT - 1) / gc.TT) * gc.nsplit * c.B;
-  {
-    ProfScope ps("attend_pair", st);
-    hipLaunchKernelGGL(kfn, dim3((unsigned)(nbh + nbc)), dim3(RW * KG * 64), lds, st, h, gh, c, gc, (int)nbh);
-  }
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const long cbh = (long)((partial_rows(h) + 3) / 4), cbc = (long)((partial_rows(c) + 3) / 4);
-  ProfScope ps("attend_combine", st);
-  hipLaunchKernelGGL((combine_pair_kernel<T, D>), dim3((unsigned)(cbh + cbc)), dim3(256), 0, st,
-                     h, gh.nsplit, c, gc.nsplit, (int)cbh);
-  return hipGetLastError();
-}
-
-template <typename T, int D>
-static hipError_t launch_pair2(const AttendArgs& h, const AttnGeom& gh, const AttendArgs& c,
-                               const AttnGeom& gc, int RW, hipStream_t st) {
-  if (RW == 1) return launch_pair4<T, D, 1, 2>(h, gh, c, gc, st);
-  if (RW == 2) return launch_pair4<T, D, 2, 2>(h, gh, c, gc, st);
-  if (RW == 3) return launch_pair4<T, D, 3, 1>(h, gh, c, gc, st);
-  return launch_pair4<T, D, 4, 1>(h, gh, c, gc, st);
+  if (c.f32) return c.d == 64 ? combine_pair_variant<float, 64>(h, gh, c, gc, st)
+                              : combine_pair_variant<float, 128>(h, gh, c, gc, st);
+  return c.d == 64 ? combine_pair_variant<bf16, 64>(h, gh, c, gc, st)
+                   : combine_pair_variant<bf16, 128>(h, gh, c, gc, st);
 }
 
 hipError_t launch_attend_pair(const AttendArgs& csa_a, const AttendArgs& hca_a, hipStream_t st) {
@@ -830,10 +67,26 @@ hipError_t launch_attend_pair(const AttendArgs& csa_a, const AttendArgs& hca_a, 
     return e != hipSuccess ? e : launch_attend(hca_a, st);
   }
   if (csa_a.f32)
-    return csa_a.d == 64 ? launch_pair2<float, 64>(hca_a, gh, csa_a, gc, rwc, st)
-                         : launch_pair2<float, 128>(hca_a, gh, csa_a, gc, rwc, st);
-  return csa_a.d == 64 ? launch_pair2<bf16, 64>(hca_a, gh, csa_a, gc, rwc, st)
-                       : launch_pair2<bf16, 128>(hca_a, gh, csa_a, gc, rwc, st);
+    return csa_a.d == 64 ? pair_variant<float, 64>(hca_a, gh, csa_a, gc, rwc, st)
+                         : pair_variant<float, 128>(hca_a, gh, csa_a, gc, rwc, st);
+  return csa_a.d == 64 ? pair_variant<bf16, 64>(hca_a, gh, csa_a, gc, rwc, st)
+                       : pair_variant<bf16, 128>(hca_a, gh, csa_a, gc, rwc, st);
+}
+
+hipError_t launch_attend_overlapped(const AttendArgs& csa_a, const AttendArgs& hca_a, bool hca_any_order,
+                                    hipStream_t st) {
+  const AttnGeom gc = make_geom(csa_a), gh = make_geom(hca_a);
+  const bool merge_together = gc.nsplit > 1 && gh.nsplit > 1 && csa_a.f32 == hca_a.f32 && csa_a.d == hca_a.d;
+  AttendLaunch hl, cl;
+  hl.any_order = hca_any_order;
+  hl.combine = cl.combine = !merge_together;
+  // the HCA problem needs nothing from the work queued ahead of it; with any
+  // order it runs beside that work (the indexer's top-k pick) instead of after it
+  hipError_t e = dispatch(hca_a, gh, hl, st);
+  if (e != hipSuccess) return e;
+  e = dispatch(csa_a, gc, cl, st);
+  if (e != hipSuccess || !merge_together) return e;
+  return combine_pair(hca_a, gh, csa_a, gc, st);
 }
 
 }  // namespace csa

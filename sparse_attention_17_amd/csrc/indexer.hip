@@ -39,6 +39,14 @@
 
 namespace csa {
 
+// Event counters for measurement tools (csa_profile_counter): rows whose
+// top-k took the exact fallback select.  Incremented by one lane per event.
+__device__ unsigned long long g_counters[CNT_COUNT];
+
+__device__ __forceinline__ void count_event(int which) {
+  atomicAdd(&g_counters[which], 1ull);
+}
+
 static constexpr int SCORE_WG_ENTRIES = 256;   // prefill tile kernel: 4 waves x 4 tiles x 16
 // decode score kernels: entries per chunk (one chunk per workgroup; 1024
 // gives two rounds of resident workgroups on a 1M-entry batch, so one round's
@@ -924,6 +932,7 @@ __device__ __forceinline__ void pick_body(PickSmem& sm, const PickRow& R) {
     }
   }
   if (__syncthreads_or(unsafe)) {
+    if (tid == 0) count_event(CNT_DECODE_FALLBACK);
     select_row<PICK_NT>(*reinterpret_cast<TopkSmem<PICK_NT>*>(&sm.hist[0][0]), R.src, R.n, k, R.idx, R.sco);
     return;
   }
@@ -995,6 +1004,7 @@ __global__ __launch_bounds__(PICK_NT) void long_pick_kernel(IndexerArgs a) {
   R.nslot = R.nch << R.lg;                                   // <= L.nch * SCORE_CHUNK
   const int per = (R.nslot + PICK_NT - 1) / PICK_NT;
   if (per > PICK_MAXPER || R.nch > PICK_MAXCH) {
+    if (threadIdx.x == 0) count_event(CNT_DECODE_FALLBACK);
     select_row<PICK_NT>(*reinterpret_cast<TopkSmem<PICK_NT>*>(&sm.hist[0][0]), R.src, R.n, R.k, R.idx, R.sco);
     return;
   }
@@ -1240,7 +1250,10 @@ __global__ __launch_bounds__(FNT) void fused_prefill_kernel(IndexerArgs a) {
     const uint32_t ncand = sm.ncand[tt];
     uint32_t rem = (uint32_t)k - sm.above[tt];
     if (ncand > (uint32_t)FCAP || rem > ncand) {
-      if (lane == 0) sm.fb[tt] = 1u;
+      if (lane == 0) {
+        sm.fb[tt] = 1u;
+        count_event(CNT_PREFILL_FALLBACK);
+      }
       continue;
     }
     const uint32_t(*cand)[2] = sm.u.cand[tt];
@@ -1329,14 +1342,10 @@ static bool use_fused_prefill(const IndexerArgs& a) {
 
 template <int QK, int DI, int HI>
 static hipError_t launch_fused(const IndexerArgs& a, hipStream_t st) {
-  static bool attr_set = false;
   const size_t lds = sizeof(FusedSmem);
   auto kfn = fused_prefill_kernel<QK, DI, HI>;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  hipError_t e = ensure_lds_limit((const void*)kfn, lds);
+  if (e != hipSuccess) return e;
   ProfScope ps("indexer_fused", st);
   hipLaunchKernelGGL(kfn, dim3((a.Tq + FQ - 1) / FQ, a.B), dim3(FNT), lds, st, a);
   return hipGetLastError();
@@ -1352,6 +1361,16 @@ static hipError_t launch_fused_hi(const IndexerArgs& a, hipStream_t st) {
 template <int QK>
 static hipError_t launch_fused_di(const IndexerArgs& a, hipStream_t st) {
   return a.dI == 32 ? launch_fused_hi<QK, 32>(a, st) : launch_fused_hi<QK, 64>(a, st);
+}
+
+hipError_t counter_read(int which, unsigned long long* value, bool reset) {
+  unsigned long long v[CNT_COUNT];
+  hipError_t e = hipMemcpyFromSymbol(v, HIP_SYMBOL(g_counters), sizeof(v), 0, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return e;
+  *value = v[which];
+  if (!reset) return hipSuccess;
+  v[which] = 0;
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_counters), v, sizeof(v), 0, hipMemcpyHostToDevice);
 }
 
 // --------------------------------- launch ----------------------------------

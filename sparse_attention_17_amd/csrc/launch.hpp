@@ -21,6 +21,14 @@ class ProfScope {
   long idx_;
 };
 
+// Raises a kernel's dynamic LDS limit to `lds` bytes (needed above 64 KiB)
+// once per (device, kernel); thread-safe.
+hipError_t ensure_lds_limit(const void* kfn, size_t lds);
+
+// Device event counters (measurement only), read by csa_profile_counter.
+enum CounterId { CNT_PREFILL_FALLBACK = 0, CNT_DECODE_FALLBACK = 1, CNT_COUNT = 2 };
+hipError_t counter_read(int which, unsigned long long* value, bool reset);
+
 struct CompressArgs {
   const void *k, *v, *ki;
   const float *gate, *pos_bias;
@@ -78,6 +86,12 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st);
 // Both attention problems of a hybrid layer pair (csa_a sparse, hca_a dense),
 // in one launch (plus one merge launch) when their split-decode kernels share a shape.
 hipError_t launch_attend_pair(const AttendArgs& csa_a, const AttendArgs& hca_a, hipStream_t st);
+// The two problems of a decode step after the indexer: the HCA attention
+// (launched in any order when hca_any_order: it overlaps the top-k pick queued
+// before it), then the CSA attention, then one merge of both problems' split
+// partials.  Results are those of the separate calls.
+hipError_t launch_attend_overlapped(const AttendArgs& csa_a, const AttendArgs& hca_a, bool hca_any_order,
+                                    hipStream_t st);
 
 struct ProjArgs {
   const void *o, *w;

@@ -7,6 +7,8 @@
 #include <atomic>
 #include <cstring>
 #include <mutex>
+#include <set>
+#include <utility>
 #include <string>
 #include <vector>
 
@@ -36,7 +38,23 @@ hipEvent_t take_event() {
   return e;
 }
 
+std::mutex g_lds_mu;
+std::set<std::pair<int, const void*>> g_lds_done;
+
 }  // namespace
+
+hipError_t ensure_lds_limit(const void* kfn, size_t lds) {
+  if (lds <= 65536) return hipSuccess;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_lds_mu);
+  const auto key = std::make_pair(dev, kfn);
+  if (g_lds_done.count(key)) return hipSuccess;
+  e = hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e == hipSuccess) g_lds_done.insert(key);
+  return e;
+}
 
 ProfScope::ProfScope(const char* name, hipStream_t st) : st_(st), idx_(-1) {
   if (!g_on.load(std::memory_order_relaxed)) return;
@@ -84,6 +102,15 @@ int csa_profile_query(const char* kernel, int* count, double* total_ms) {
   if (count) *count = n;
   if (total_ms) *total_ms = ms;
   return n > 0 ? 0 : 1;
+}
+
+int csa_profile_counter(const char* name, unsigned long long* value, int reset) {
+  int which = -1;
+  if (name == nullptr) return 1;
+  if (std::strcmp(name, "indexer_prefill_fallback") == 0) which = csa::CNT_PREFILL_FALLBACK;
+  else if (std::strcmp(name, "indexer_decode_fallback") == 0) which = csa::CNT_DECODE_FALLBACK;
+  if (which < 0 || value == nullptr) return 1;
+  return csa::counter_read(which, value, reset != 0) == hipSuccess ? 0 : -1;
 }
 
 }  // extern "C"

@@ -217,3 +217,49 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(ImportError):
         L.load()
+
+
+def test_decode_step_struct_layout(tmp_path):
+    # the ctypes mirror must match csa_decode_step_t field for field: compile a
+    # C program against the header that prints every field's offset
+    from sparse_attention_17_amd._lib import DecodeStepDesc
+    names = [f[0] for f in DecodeStepDesc._fields_]
+    prog = tmp_path / "layout.c"
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "csa_mi355x.h"', 'int main(void) {',
+             '  printf("size %zu\\n", sizeof(csa_decode_step_t));']
+    lines += [f'  printf("{n} %zu\\n", offsetof(csa_decode_step_t, {n}));' for n in names]
+    lines += ['  return 0;', '}']
+    prog.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.dirname(HEADER), str(prog), "-o", str(exe)],
+                   check=True)
+    got = dict(ln.split() for ln in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                   check=True).stdout.splitlines())
+    assert int(got["size"]) == C.sizeof(DecodeStepDesc)
+    for n in names:
+        assert int(got[n]) == getattr(DecodeStepDesc, n).offset, n
+
+
+def test_decode_step_validation(lib):
+    from sparse_attention_17_amd._lib import DecodeStepDesc
+    s = DecodeStepDesc()
+    s.B, s.pos0, s.max_pos, s.H, s.d, s.dt = 2, FAKE, 1023, 8, 128, L.BF16
+    s.qi, s.w, s.kic, s.HI, s.dI, s.m, s.topk, s.qk_dt, s.idx_out = FAKE, FAKE, FAKE, 4, 64, 4, 32, L.BF16, FAKE
+    s.q, s.kc, s.vc, s.Nc_cap, s.window, s.softmax_scale, s.out = FAKE, FAKE, FAKE, 256, 0, 0.1, FAKE
+    s.hq, s.hkc, s.hvc, s.m_prime, s.hNc_cap, s.hsoftmax_scale, s.hout = FAKE, FAKE, FAKE, 128, 8, 0.1, FAKE + 256
+    need = lib.csa_hybrid_decode_step_workspace(C.byref(s))
+    assert need > 0
+    assert lib.csa_hybrid_decode_step(C.byref(s), FAKE, need - 1, None) == L.WORKSPACE_TOO_SMALL
+    s.HI = 3
+    assert lib.csa_hybrid_decode_step(C.byref(s), FAKE, need, None) == L.UNSUPPORTED
+    assert b"indexer part" in lib.csa_last_error()
+    s.HI, s.softmax_scale = 4, -1.0
+    assert lib.csa_hybrid_decode_step(C.byref(s), FAKE, need, None) == L.INVALID_ARGUMENT
+    assert b"CSA part" in lib.csa_last_error()
+    s.softmax_scale, s.hkc = 0.1, None
+    assert lib.csa_hybrid_decode_step(C.byref(s), FAKE, need, None) == L.INVALID_ARGUMENT
+    assert b"HCA part" in lib.csa_last_error()
+    s.hkc, s.hout = FAKE, s.out
+    assert lib.csa_hybrid_decode_step(C.byref(s), FAKE, need, None) == L.INVALID_ARGUMENT
+    assert b"same buffer" in lib.csa_last_error()
+    assert lib.csa_hybrid_decode_step(None, FAKE, need, None) == L.INVALID_ARGUMENT

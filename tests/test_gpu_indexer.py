@@ -187,7 +187,7 @@ def test_long_rows_boundary_ties_take_lowest_indices():
 
 
 def test_fp32_and_bf16_long_rows():
-    for qk in ("bf16",):
+    for qk in ("f32", "bf16"):
         w = configs.CSA_DECODE_128K.with_(B=3, ctx=4 * 20000, qk_dtype=qk, topk=777)
         x, idx = _decode(w)
         assert _check_decode(w, x, idx) >= w.B - 1
