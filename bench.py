@@ -6,9 +6,9 @@ Default workload: one decode step of a hybrid CSA + HCA layer pair at a
        and queries (per-row fp32 scales, 4 heads x 64), top-2048, sliding
        window 128, sink, 64 query heads sharing one KV head, d=128;
   HCA: 8,192 entries (m'=128), dense over completed blocks, sink.
-A step = one csa_hybrid_decode_step call (indexer scores + top-k, the HCA
-attention launched so that it overlaps the top-k pick, the CSA attention, one
-merge of both problems' split partials) on inputs already resident in HBM.
+A step = one csa_hybrid_decode_step call (indexer scores + top-k select, the
+CSA and HCA attention in one launch, one merge of both problems' split
+partials) on inputs already resident in HBM.
 Inputs are seeded synthetic tensors; several copies (>= 4, each > 1 GB)
 rotate so consecutive steps do not hit the 256 MB last-level cache.
 
@@ -57,8 +57,6 @@ def parse():
     p.add_argument("--mode", choices=("step", "calls"), default="step",
                    help="step: the whole step in one csa_hybrid_decode_step call; calls: "
                         "csa_indexer_topk then csa_hybrid_attend")
-    p.add_argument("--in-order", type=int, default=0,
-                   help="step mode: launch every kernel in order (no HCA / top-k overlap)")
     p.add_argument("--extra", type=int, default=1,
                    help="also time the 128K decode step, HCA 1M decode / prefill and the 32K "
                         "prefill (extra keys of the JSON line)")
@@ -575,8 +573,7 @@ def main():
         hca = dict(q=g["q_hca"], kc=g["kc_hca"], vc=g["vc_hca"], m_prime=w.m_hca, sink=g["sink_hca"])
         return idx, csa, hca
 
-    steps_obj = [ops.DecodeStep(*step_args(g), pos0, w.ctx - 1, return_lse=True,
-                                in_order=bool(args.in_order)) for g in sets]
+    steps_obj = [ops.DecodeStep(*step_args(g), pos0, w.ctx - 1, return_lse=True) for g in sets]
 
     def step_calls(g):
         i, c, h = step_args(g)
@@ -629,11 +626,11 @@ def main():
     ms = ev[0].elapsed_time(ev[args.steps]) / args.steps
     per_step = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
 
-    # per-kernel launch durations from library-recorded hipEvents (launches in order)
+    # per-kernel launch durations from library-recorded hipEvents
     lib.csa_profile_reset()
     lib.csa_profile_enable(1)
     nprof = 30
-    prof_steps = [ops.DecodeStep(*step_args(g), pos0, w.ctx - 1, in_order=True) for g in sets]
+    prof_steps = [ops.DecodeStep(*step_args(g), pos0, w.ctx - 1) for g in sets]
     for i in range(nprof):
         prof_steps[i % len(prof_steps)].run()
     torch.cuda.synchronize()
@@ -686,7 +683,7 @@ def main():
                    "csa_m": w.m, "csa_entries": w.Nc, "topk": w.topk, "window": w.window,
                    "indexer": f"{w.qk_dtype} {w.HI}x{w.dI}", "hca_m": w.m_hca,
                    "hca_entries": w.Nc_hca, "heads": w.H, "head_dim": w.d,
-                   "mode": args.mode, "overlap_hca_with_topk": args.mode == "step" and not args.in_order,
+                   "mode": args.mode,
                    "graph": bool(args.graph), "rotating_copies": args.rotate},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -211,9 +211,12 @@ csa_status_t hca_attend(const void *q, const void *kc, const void *vc, int m_pri
  *   vscale [B, Nc_cap]       fp32   one scale per value row
  * v8 = vscale = NULL selects the shared-entry variant: each value row is its
  * key row (codes for dims < d/2, the bf16 RoPE half above).
- * Codes are widened exactly, multiplied by the row scale in fp32 and rounded
- * to bf16 while the tile is staged in LDS (exact when scales are powers of
- * two); the attention then runs as on bf16 caches.  q, out, kw, vw are bf16;
+ * Codes are widened exactly to bf16 while the tile is staged in LDS (every
+ * E4M3 value is a bf16 value); the key row scale multiplies the fp32 partial
+ * logits of the code dims, and the value row scale the fp32 probabilities
+ * before they are rounded to bf16 for the product with the values (as on
+ * bf16 caches).  With power-of-two scales the results are bitwise those of
+ * the bf16 kernels on caches holding code x scale.  q, out, kw, vw are bf16;
  * d = 128.  Other arguments, workspace sizes and errors as csa_sparse_attend
  * and hca_attend.
  */
@@ -283,14 +286,12 @@ csa_status_t csa_hybrid_attend(
  * csa_hybrid_decode_step_workspace).
  *
  * Results are bitwise those of csa_indexer_topk, csa_sparse_attend and
- * hca_attend called one after the other.  The work is enqueued as the
- * indexer's kernels, the HCA attention, the CSA attention and one merge of
- * both problems' split partials; unless flags has CSA_STEP_IN_ORDER, the HCA
- * attention is launched so that it may run beside the top-k select queued
- * before it (it reads nothing the indexer writes).  An invalid field launches
- * nothing; the error text names the part.
+ * hca_attend called one after the other.  The work is enqueued on `stream` as
+ * the indexer's kernels, then the CSA and HCA attention as in
+ * csa_hybrid_attend (one launch for both problems and one merge of their
+ * split partials).  An invalid field launches nothing; the error text names
+ * the part.
  */
-#define CSA_STEP_IN_ORDER 1u
 
 typedef struct csa_decode_step {
   /* sequences (both layers) */
@@ -328,7 +329,7 @@ typedef struct csa_decode_step {
   float hsoftmax_scale;
   void *hout;                 /* [B, 1, H, d] */
   float *hlse_out;
-  unsigned flags;             /* CSA_STEP_IN_ORDER: launch every kernel in order */
+  unsigned flags;             /* reserved: must be 0 */
 } csa_decode_step_t;
 
 size_t csa_hybrid_decode_step_workspace(const csa_decode_step_t *step);

@@ -36,8 +36,6 @@ class DecodeStepDesc(C.Structure):
     ]
 
 
-STEP_IN_ORDER = 1    # csa_decode_step_t.flags: launch every kernel in order
-
 EXPORTS = {
     "csa_abi_version": (_I, []),
     "csa_last_error": (C.c_char_p, []),

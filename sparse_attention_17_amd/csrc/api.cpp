@@ -432,6 +432,7 @@ csa_status_t csa_hybrid_decode_step(const csa_decode_step_t* s, void* workspace,
                                     void* stream) {
   REQUIRE(s != nullptr, CSA_INVALID_ARGUMENT, "step must not be NULL");
   REQUIRE(s->B >= 0, CSA_INVALID_ARGUMENT, "B must be >= 0");
+  REQUIRE(s->flags == 0, CSA_INVALID_ARGUMENT, "flags must be 0 (no flags are defined)");
   if (s->B == 0) return ok();
   REQUIRE(s->H >= 1 && s->Nc_cap >= 1 && s->m_prime >= 1 && s->topk >= 1, CSA_INVALID_ARGUMENT,
           "H, Nc_cap, m_prime and topk must be >= 1");
@@ -458,8 +459,7 @@ csa_status_t csa_hybrid_decode_step(const csa_decode_step_t* s, void* workspace,
   if (st != CSA_OK) return fail(st, "HCA part: %s", g_err.c_str());
   REQUIRE(s->out != s->hout, CSA_INVALID_ARGUMENT, "the CSA and HCA outputs are the same buffer");
   hipError_t e = csa::launch_indexer_topk(ai, (hipStream_t)stream);
-  if (e == hipSuccess)
-    e = csa::launch_attend_overlapped(ac, ah, (s->flags & CSA_STEP_IN_ORDER) == 0, (hipStream_t)stream);
+  if (e == hipSuccess) e = csa::launch_attend_pair(ac, ah, (hipStream_t)stream);
   return device_status(e, "csa_hybrid_decode_step launch");
 }
 

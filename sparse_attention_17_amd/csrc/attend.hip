@@ -73,20 +73,4 @@ hipError_t launch_attend_pair(const AttendArgs& csa_a, const AttendArgs& hca_a, 
                        : pair_variant<bf16, 128>(hca_a, gh, csa_a, gc, rwc, st);
 }
 
-hipError_t launch_attend_overlapped(const AttendArgs& csa_a, const AttendArgs& hca_a, bool hca_any_order,
-                                    hipStream_t st) {
-  const AttnGeom gc = make_geom(csa_a), gh = make_geom(hca_a);
-  const bool merge_together = gc.nsplit > 1 && gh.nsplit > 1 && csa_a.f32 == hca_a.f32 && csa_a.d == hca_a.d;
-  AttendLaunch hl, cl;
-  hl.any_order = hca_any_order;
-  hl.combine = cl.combine = !merge_together;
-  // the HCA problem needs nothing from the work queued ahead of it; with any
-  // order it runs beside that work (the indexer's top-k pick) instead of after it
-  hipError_t e = dispatch(hca_a, gh, hl, st);
-  if (e != hipSuccess) return e;
-  e = dispatch(csa_a, gc, cl, st);
-  if (e != hipSuccess || !merge_together) return e;
-  return combine_pair(hca_a, gh, csa_a, gc, st);
-}
-
 }  // namespace csa

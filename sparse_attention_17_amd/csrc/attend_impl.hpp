@@ -24,8 +24,6 @@
 #include "common.hpp"
 #include "launch.hpp"
 
-#include <hip/hip_ext.h>
-
 #include <algorithm>
 #include <climits>
 
@@ -63,10 +61,11 @@ __device__ __forceinline__ int vt_block(int dim, int kb) { return kb ^ ((dim >> 
 // workgroups share a compute unit and one's loads overlap the other's math.
 // The body takes its workgroup's coordinates (token tile bx, split by,
 // sequence bz) and the dynamic LDS block from the kernel that runs it.
-template <typename T, int D, int RW, int KG, bool SPARSE, int PF, bool KV8 = false>
+template <typename T, int D, int RW, int KG, bool SPARSE, int PF, bool KV8 = false, bool VSH = false>
 __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom& gm, int bx, int by,
                                             int bz, unsigned char* smem_raw) {
   static_assert(!KV8 || sizeof(T) == 2, "FP8 caches go with bf16 queries");
+  static_assert(KV8 || !VSH, "a shared value entry is an FP8-cache layout");
   constexpr int NW = RW * KG;
   constexpr int NT = NW * 64;
   constexpr int NSUB = 2 / KG;                 // 32-key sub-tiles per wave per tile
@@ -80,7 +79,11 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
 
   T* Ks = reinterpret_cast<T*>(smem_raw);
   T* Vt = Ks + KT * KS;
-  int* sel = reinterpret_cast<int*>(Vt + D * VS);
+  // FP8 caches: the row scales of the tile's keys (1 for window rows), applied
+  // to the logits of the code half and to the probabilities, in fp32
+  float* kscl = reinterpret_cast<float*>(Vt + D * VS);
+  float* vscl = kscl + KT;
+  int* sel = KV8 ? reinterpret_cast<int*>(vscl + KT) : reinterpret_cast<int*>(Vt + D * VS);
   __shared__ uint32_t scan_sm[NW];
   __shared__ int s_nsel;
 
@@ -224,39 +227,25 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
   const __amdgpu_buffer_rsrc_t rk8 = rsrc(KV8 ? (const uint8_t*)a.k8 + cb * DN : nullptr, KV8 ? (uint32_t)a.Nc_cap * DN : 0u);
   const __amdgpu_buffer_rsrc_t rkr = rsrc(KV8 ? (const uint16_t*)a.krope + cb * (D - DN) : nullptr,
                                           KV8 ? (uint32_t)a.Nc_cap * (D - DN) * 2 : 0u);
-  const bool vshared = KV8 && a.v8 == nullptr;                // values = key rows (shared entry)
+  constexpr bool vshared = VSH;                              // values = key rows (shared entry)
   const __amdgpu_buffer_rsrc_t rv8 = rsrc(KV8 && !vshared ? (const uint8_t*)a.v8 + cb * D : nullptr,
                                           KV8 && !vshared ? (uint32_t)a.Nc_cap * D : 0u);
   const __amdgpu_buffer_rsrc_t rks = rsrc(KV8 ? a.kscale + cb : nullptr, KV8 ? (uint32_t)a.Nc_cap * 4 : 0u);
   const __amdgpu_buffer_rsrc_t rvs = rsrc(KV8 && !vshared ? a.vscale + cb : nullptr,
                                           KV8 && !vshared ? (uint32_t)a.Nc_cap * 4 : 0u);
-  // 8 codes (x, y) and their row scale (z) of an FP8 row chunk, or zeros
-  auto ld8 = [](const __amdgpu_buffer_rsrc_t& rc, const __amdgpu_buffer_rsrc_t& rs, int e, uint32_t off) -> u32x4 {
+  // 8 codes of an FP8 row chunk (x, y), or zeros
+  auto ld8 = [](const __amdgpu_buffer_rsrc_t& rc, int e, uint32_t off) -> u32x4 {
     const auto c = __builtin_amdgcn_raw_buffer_load_b64(rc, e >= 0 ? off : OOB, 0, 0);
-    const uint32_t sc = __builtin_amdgcn_raw_buffer_load_b32(rs, e >= 0 ? (uint32_t)e * 4 : OOB, 0, 0);
-    return u32x4{c[0], c[1], sc, 0u};
+    return u32x4{c[0], c[1], 0u, 0u};
   };
-  // 8 E4M3 codes times the row scale, as 8 bf16 (codes widen exactly; the
-  // product is rounded to nearest even).  The hardware conversion applies only
-  // the exponent of its scale operand (measured on gfx950), so it serves the
-  // power-of-two scales directly and other scales take an fp32 multiply.
-  auto dequant8 = [](const u32x4& r) -> u32x4 {
-    const float sc = __uint_as_float(r[2]);
+  // 8 E4M3 codes as 8 bf16 values: every E4M3 value is a bf16 value, so the
+  // widening is exact; the row scale is applied later in fp32
+  auto widen8 = [](const u32x4& r) -> u32x4 {
     u32x4 o;
-    if ((r[2] & 0x007FFFFFu) == 0u) {
-#pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        o[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r[w], sc, false));
-        o[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r[w], sc, true));
-      }
-      return o;
-    }
 #pragma unroll
     for (int w = 0; w < 2; ++w) {
-      const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r[w], 1.0f, false));
-      const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r[w], 1.0f, true));
-      o[2 * w] = pack_bf16x2(bf16_bits_to_f32(lo & 0xFFFFu) * sc, bf16_bits_to_f32(lo >> 16) * sc);
-      o[2 * w + 1] = pack_bf16x2(bf16_bits_to_f32(hi & 0xFFFFu) * sc, bf16_bits_to_f32(hi >> 16) * sc);
+      o[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r[w], 1.0f, false));
+      o[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(r[w], 1.0f, true));
     }
     return o;
   };
@@ -276,6 +265,7 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
   constexpr int VTK = (VTOT + NT - 1) / NT;
   u32x4 kregA[KLD], vregA[VTK][4];
   u32x4 kregB[PF == 2 ? KLD : 1], vregB[PF == 2 ? VTK : 1][4];
+  float sclA = 1.f, sclB = 1.f;                              // FP8 caches: one row scale per thread
   // K staging task c -> (row, 16-byte chunk): row-major for bf16 caches; for
   // FP8 caches chunk-major, so that a wave's 64 lanes share one chunk (and
   // with it the chunk's kind: codes or RoPE values)
@@ -284,7 +274,7 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
   auto ld = [](const __amdgpu_buffer_rsrc_t& r, uint32_t off, uint32_t ch) -> u32x4 {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off == OOB ? OOB : off + ch * 16, 0, 0));
   };
-  auto stage_load = [&](auto& kreg, auto& vreg, int s0) {
+  auto stage_load = [&](auto& kreg, auto& vreg, float& scl, int s0) {
     // per-tile source: compressed keys only, window keys only, or both (the
     // one tile that straddles the boundary); each branch issues its loads back
     // to back
@@ -303,15 +293,21 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
       }
     };
     if constexpr (KV8) {
-      // FP8 rows: a K chunk below DN dims is 8 codes + scale, above it 8 bf16
-      // RoPE values (the chunk kind is uniform over a wave); a V chunk is 8
-      // codes + scale.  Window rows are bf16.
-      // (values shared with keys: the value row is the key row)
+      // FP8 rows: a K chunk below DN dims is 8 codes, above it 8 bf16 RoPE
+      // values (the chunk kind is uniform over a wave); a V chunk is 8 codes.
+      // Window rows are bf16.  (Values shared with keys: the value row is the
+      // key row.)  Threads 0..KT-1 load the key row scale of slot s0 + tid,
+      // threads KT..2KT-1 the value row scale (absent rows read 0).
+      if (tid < 2 * KT) {
+        const int e = ent(s0 + tid % KT);
+        const bool vs = tid >= KT && !vshared;
+        scl = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(vs ? rvs : rks, e >= 0 ? (uint32_t)e * 4 : OOB, 0, 0));
+      }
       auto comp8 = [&](bool k, int s, int ch) -> u32x4 {
         const int e = ent(s);
         if ((k || vshared) && ch >= DN / VEC) return ld(rkr, e >= 0 ? (uint32_t)e * (D - DN) * 2 : OOB, ch - DN / VEC);
-        if (k || vshared) return ld8(rk8, rks, e, (uint32_t)e * DN + ch * 8);
-        return ld8(rv8, rvs, e, (uint32_t)e * D + ch * 8);
+        if (k || vshared) return ld8(rk8, e, (uint32_t)e * DN + ch * 8);
+        return ld8(rv8, e, (uint32_t)e * D + ch * 8);
       };
       if (s0 + KT <= ncomp || nwin == 0)
         load_all(comp8);
@@ -329,14 +325,18 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
       });
     }
   };
-  auto stage_store = [&](const auto& kreg, const auto& vreg, int s0) {
+  auto stage_store = [&](const auto& kreg, const auto& vreg, float scl, int s0) {
+    if constexpr (KV8) {
+      // row scales of the tile's keys; 1 for window rows (bf16, unscaled)
+      if (tid < 2 * KT) (tid < KT ? kscl : vscl)[tid % KT] = ent(s0 + tid % KT) >= 0 ? scl : 1.f;
+    }
 #pragma unroll
     for (int i = 0; i < KLD; ++i) {
       const int c = tid + i * NT;
       if (c >= KT * KCH) continue;
       u32x4 r = kreg[i];
       if constexpr (KV8)
-        if (kch(c) < DN / VEC && ent(s0 + krow(c)) >= 0) r = dequant8(r);
+        if (kch(c) < DN / VEC && ent(s0 + krow(c)) >= 0) r = widen8(r);
       *reinterpret_cast<u32x4*>(Ks + krow(c) * KS + kch(c) * VEC) = r;
     }
 #pragma unroll
@@ -349,7 +349,7 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
       for (int u = 0; u < 4; ++u) {
         vr[u] = vreg[i][u];
         if constexpr (KV8)
-          if ((!vshared || ch < DN / VEC) && ent(s0 + kg * 4 + u) >= 0) vr[u] = dequant8(vr[u]);
+          if ((!vshared || ch < DN / VEC) && ent(s0 + kg * 4 + u) >= 0) vr[u] = widen8(vr[u]);
       }
       const T* rows = reinterpret_cast<const T*>(vr);           // [4][VEC]
 #pragma unroll
@@ -362,13 +362,26 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
     }
   };
 
-  if (kbeg < kend) stage_load(kregA, vregA, kbeg);
+  if (kbeg < kend) stage_load(kregA, vregA, sclA, kbeg);
   if constexpr (PF == 2) {
-    if (kbeg + KT < kend) stage_load(kregB, vregB, kbeg + KT);
+    if (kbeg + KT < kend) stage_load(kregB, vregB, sclB, kbeg + KT);
   }
+  // the row scales of a lane's 16 keys in sub-tile `sub` (S^T rows
+  // 8 (r >> 2) + 4 half + (r & 3)), from the staged scale array
+  auto lane_scales = [&](const float* scl_arr, int sub, float (&out)[16]) {
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(scl_arr + sub * 32 + 8 * g4 + 4 * half);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) out[4 * g4 + u] = v[u];
+    }
+  };
 
   auto tile = [&](int s0) {
     // ---- S^T = K Q^T for this wave's 32-key sub-tiles ----
+    // (FP8 caches: the dims below DN hold unscaled codes; their partial dot
+    // products are accumulated first and multiplied by the key row scale in
+    // fp32 before the RoPE dims are added)
     f32x16 st[NSUB];
 #pragma unroll
     for (int si = 0; si < NSUB; ++si)
@@ -376,6 +389,17 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
       for (int r = 0; r < 16; ++r) st[si][r] = 0.f;
 #pragma unroll
     for (int s = 0; s < DSTEP; ++s) {
+      if constexpr (KV8) {
+        if (16 * s == DN) {
+#pragma unroll
+          for (int si = 0; si < NSUB; ++si) {
+            float ks[16];
+            lane_scales(kscl, KG == 2 ? kg : si, ks);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) st[si][r] *= ks[r];
+          }
+        }
+      }
 #pragma unroll
       for (int si = 0; si < NSUB; ++si) {
         const int sub = KG == 2 ? kg : si;
@@ -439,7 +463,10 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
     }
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
     float psum = 0.f;
-    Frag<T> pf[NSUB][2];
+    // P for the value dims; FP8 caches: P times the value row scale for the
+    // code dims (pf), and, when values are the key rows, plain P for their
+    // bf16 RoPE dims (pr)
+    Frag<T> pf[NSUB][2], pr[VSH ? NSUB : 1][2];
 #pragma unroll
     for (int si = 0; si < NSUB; ++si) {
       float pv[16];
@@ -448,8 +475,21 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
         pv[r] = fexp2<T>(fmaf(st[si][r], gm.scale_log2, -m_use));
         psum += pv[r];
       }
-      frag_from_f32(pf[si][0], pv);
-      frag_from_f32(pf[si][1], pv + 8);
+      if constexpr (KV8) {
+        float vs[16], pw[16];
+        lane_scales(VSH ? kscl : vscl, KG == 2 ? kg : si, vs);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pw[r] = pv[r] * vs[r];
+        frag_from_f32(pf[si][0], pw);
+        frag_from_f32(pf[si][1], pw + 8);
+        if constexpr (VSH) {
+          frag_from_f32(pr[si][0], pv);
+          frag_from_f32(pr[si][1], pv + 8);
+        }
+      } else {
+        frag_from_f32(pf[si][0], pv);
+        frag_from_f32(pf[si][1], pv + 8);
+      }
     }
     l_run += psum;
 
@@ -475,30 +515,31 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
             fv[0] = lo[0]; fv[1] = lo[1]; fv[2] = lo[2]; fv[3] = lo[3];
             fv[4] = hi[0]; fv[5] = hi[1]; fv[6] = hi[2]; fv[7] = hi[3];
           }
-          mma32(o[i], vf, pf[si][ks]);
+          if constexpr (VSH) mma32(o[i], vf, 32 * i >= DN ? pr[si][ks] : pf[si][ks]);
+          else mma32(o[i], vf, pf[si][ks]);
         }
       }
     }
   };
   if constexpr (PF == 2) {
     for (int s0 = kbeg; s0 < kend; s0 += 2 * KT) {
-      stage_store(kregA, vregA, s0);
+      stage_store(kregA, vregA, sclA, s0);
       __syncthreads();
-      if (s0 + 2 * KT < kend) stage_load(kregA, vregA, s0 + 2 * KT);
+      if (s0 + 2 * KT < kend) stage_load(kregA, vregA, sclA, s0 + 2 * KT);
       tile(s0);
       __syncthreads();
       if (s0 + KT >= kend) break;
-      stage_store(kregB, vregB, s0 + KT);
+      stage_store(kregB, vregB, sclB, s0 + KT);
       __syncthreads();
-      if (s0 + 3 * KT < kend) stage_load(kregB, vregB, s0 + 3 * KT);
+      if (s0 + 3 * KT < kend) stage_load(kregB, vregB, sclB, s0 + 3 * KT);
       tile(s0 + KT);
       __syncthreads();
     }
   } else {
     for (int s0 = kbeg; s0 < kend; s0 += KT) {
-      stage_store(kregA, vregA, s0);
+      stage_store(kregA, vregA, sclA, s0);
       __syncthreads();
-      if (s0 + KT < kend) stage_load(kregA, vregA, s0 + KT);
+      if (s0 + KT < kend) stage_load(kregA, vregA, sclA, s0 + KT);
       tile(s0);
       __syncthreads();
     }
@@ -574,10 +615,10 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
   if (a.lse && half == 0) a.lse[grow] = lse;
 }
 
-template <typename T, int D, int RW, int KG, bool SPARSE, int PF, bool KV8>
+template <typename T, int D, int RW, int KG, bool SPARSE, int PF, bool KV8, bool VSH>
 __global__ __launch_bounds__(RW * KG * 64) __attribute__((amdgpu_waves_per_eu(KV8 && !(RW == 2 && KG == 2) ? 1 : 2))) void attend_kernel(AttendArgs a, AttnGeom gm) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  attend_body<T, D, RW, KG, SPARSE, PF, KV8>(a, gm, blockIdx.x, blockIdx.y, blockIdx.z, smem_raw);
+  attend_body<T, D, RW, KG, SPARSE, PF, KV8, VSH>(a, gm, blockIdx.x, blockIdx.y, blockIdx.z, smem_raw);
 }
 
 // The HCA and CSA attention of one layer pair in a single split-decode launch:
@@ -717,19 +758,17 @@ static inline void wave_shape(int rows, int* RW, int* KG) {
 
 static inline size_t partial_rows(const AttendArgs& a) { return (size_t)a.B * a.Tq * a.H; }
 
-// How a split attention is launched: with or without its split merge, and
-// whether the launch may start before the work queued ahead of it has
-// finished (hipExtAnyOrderLaunch: the caller guarantees it depends on none of it).
+// How a split attention is launched: with or without its split merge.
 struct AttendLaunch {
   bool combine = true;
-  bool any_order = false;
 };
 
 template <typename T, int D, bool SPARSE>
 static size_t attend_lds(const AttendArgs& a, int RW, int KG) {
   constexpr int KS = D + 16 / sizeof(T);
   constexpr int VS = KT + 4;
-  size_t lds = (size_t)(KT * KS + D * VS) * sizeof(T) + (SPARSE ? (size_t)a.topk * 4 : 0);
+  size_t lds = (size_t)(KT * KS + D * VS) * sizeof(T) + (SPARSE ? (size_t)a.topk * 4 : 0) +
+               (a.kv8 ? 2 * KT * sizeof(float) : 0);
   if (KG == 2) lds = std::max(lds, (size_t)RW * 64 * ((D / 32) * 16 + 2) * sizeof(float));
   return lds;
 }
@@ -739,20 +778,16 @@ static hipError_t set_lds(K kfn, size_t lds) {
   return ensure_lds_limit((const void*)kfn, lds);
 }
 
-template <typename T, int D, int RW, int KG, bool SPARSE, int PF, bool KV8>
+template <typename T, int D, int RW, int KG, bool SPARSE, int PF, bool KV8, bool VSH>
 static hipError_t launch5(const AttendArgs& a, const AttnGeom& gm, const AttendLaunch& how, hipStream_t st) {
   const size_t lds = attend_lds<T, D, SPARSE>(a, RW, KG);
-  auto kfn = attend_kernel<T, D, RW, KG, SPARSE, PF, KV8>;
+  auto kfn = attend_kernel<T, D, RW, KG, SPARSE, PF, KV8, VSH>;
   hipError_t e = set_lds(kfn, lds);
   if (e != hipSuccess) return e;
   dim3 grid((a.Tq + gm.TT - 1) / gm.TT, gm.nsplit, a.B);
   {
     ProfScope ps(SPARSE ? "attend_csa" : "attend_hca", st);
-    if (how.any_order)
-      hipExtLaunchKernelGGL(kfn, grid, dim3(RW * KG * 64), (uint32_t)lds, st, nullptr, nullptr,
-                            hipExtAnyOrderLaunch, a, gm);
-    else
-      hipLaunchKernelGGL(kfn, grid, dim3(RW * KG * 64), lds, st, a, gm);
+    hipLaunchKernelGGL(kfn, grid, dim3(RW * KG * 64), lds, st, a, gm);
   }
   e = hipGetLastError();
   if (e != hipSuccess || gm.nsplit <= 1 || !how.combine) return e;
@@ -764,8 +799,13 @@ static hipError_t launch5(const AttendArgs& a, const AttnGeom& gm, const AttendL
 
 template <typename T, int D, int RW, int KG, bool SPARSE, bool KV8>
 static hipError_t launch4(const AttendArgs& a, const AttnGeom& gm, const AttendLaunch& how, hipStream_t st) {
-  return gm.nsplit > 1 ? launch5<T, D, RW, KG, SPARSE, 2, KV8>(a, gm, how, st)
-                       : launch5<T, D, RW, KG, SPARSE, 1, KV8>(a, gm, how, st);
+  if constexpr (KV8) {
+    if (a.v8 == nullptr)                     // values are the key rows
+      return gm.nsplit > 1 ? launch5<T, D, RW, KG, SPARSE, 2, true, true>(a, gm, how, st)
+                           : launch5<T, D, RW, KG, SPARSE, 1, true, true>(a, gm, how, st);
+  }
+  return gm.nsplit > 1 ? launch5<T, D, RW, KG, SPARSE, 2, KV8, false>(a, gm, how, st)
+                       : launch5<T, D, RW, KG, SPARSE, 1, KV8, false>(a, gm, how, st);
 }
 
 template <typename T, int D, bool SPARSE, bool KV8>

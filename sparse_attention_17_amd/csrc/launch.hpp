@@ -86,12 +86,6 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st);
 // Both attention problems of a hybrid layer pair (csa_a sparse, hca_a dense),
 // in one launch (plus one merge launch) when their split-decode kernels share a shape.
 hipError_t launch_attend_pair(const AttendArgs& csa_a, const AttendArgs& hca_a, hipStream_t st);
-// The two problems of a decode step after the indexer: the HCA attention
-// (launched in any order when hca_any_order: it overlaps the top-k pick queued
-// before it), then the CSA attention, then one merge of both problems' split
-// partials.  Results are those of the separate calls.
-hipError_t launch_attend_overlapped(const AttendArgs& csa_a, const AttendArgs& hca_a, bool hca_any_order,
-                                    hipStream_t st);
 
 struct ProjArgs {
   const void *o, *w;

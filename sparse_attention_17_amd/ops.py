@@ -381,7 +381,7 @@ class DecodeStep:
     max_pos are shared.  Outputs: self.idx, self.out, self.hout (+ self.lse,
     self.hlse with return_lse)."""
 
-    def __init__(self, idx, csa, hca, pos0, max_pos, return_lse=False, in_order=False):
+    def __init__(self, idx, csa, hca, pos0, max_pos, return_lse=False):
         i = dict(qi_scale=None, kic_scale=None, qk_dtype=None)
         i.update(idx)
         c = dict(kw=None, vw=None, raw_pos0=None, sink=None, scale=None)
@@ -430,7 +430,7 @@ class DecodeStep:
         s.hwindow, s.hsink = h["window"], _p(h["sink"])
         s.hsoftmax_scale = d ** -0.5 if h["scale"] is None else h["scale"]
         s.hout, s.hlse_out = _p(self.hout), _p(self.hlse)
-        s.flags = L.STEP_IN_ORDER if in_order else 0
+        s.flags = 0
         self._desc = s
         self._lib = L.load()
         self._nws = self._lib.csa_hybrid_decode_step_workspace(s)

@@ -1,8 +1,9 @@
 """GPU parity of the attention over mixed-precision caches (FP8 E4M3 codes
-with a power-of-two scale per row, BF16 RoPE half of the key): against the
-fp64 oracle on the dequantized caches, and bitwise against the bf16 kernels
-run on bf16 caches holding the same dequantized values (the codes times a
-power-of-two scale are bf16 values, so the staged tiles are identical)."""
+with a scale per row, BF16 RoPE half of the key): against the fp64 oracle on
+the dequantized caches (power-of-two and general scales), and, for
+power-of-two scales, bitwise against the bf16 kernels run on bf16 caches
+holding the same dequantized values (scaling the fp32 partial sums by a power
+of two is exact, so both kernels compute the same numbers)."""
 import numpy as np
 import pytest
 import torch
@@ -102,29 +103,47 @@ def test_csa_prefill_kv8_with_window():
     assert_close(out[0, ts], ro, "bf16", "kv8 prefill", lse[0, ts], rl)
 
 
-def test_hca_decode_kv8_general_scales():
-    # scales that are not powers of two (amax / 448): the dequantized values
-    # are rounded to bf16 in the staging, one more rounding of every key and
-    # value element than on bf16 caches.  With the workload's own q scale the
-    # outputs stay within the bf16 tolerance; the "peaky" inputs (q x 4d) turn
-    # that rounding into lse errors of ~1e-2, which is why they are not used.
-    w = configs.HCA_1M_DECODE.with_(B=2, ctx=128 * 1500)
-    x = inputs.make_inputs(w)
-    k8, ks = quant.quant_fp8_rows(x["kc_hca"][..., :64].float())
-    v8, vs = quant.quant_fp8_rows(x["vc_hca"].float())
-    krope = x["kc_hca"][..., 64:].contiguous()
+@pytest.mark.parametrize("kind", ["csa", "hca"])
+def test_decode_kv8_general_scales(kind):
+    # row scales that are not powers of two (amax / 448): the codes are widened
+    # exactly and the scales multiply the fp32 logits of the code half and the
+    # probabilities, so even the sharp ("peaky": q x 4d) softmax stays within
+    # the bf16 output and lse tolerances against the oracle on code x scale
+    if kind == "csa":
+        w = configs.CSA_DECODE_128K.with_(ctx=4 * 6000, B=2, topk=1024)
+        x = inputs.make_inputs(w, peaky=True)
+        kc, vc = x["kc"], x["vc"]
+    else:
+        w = configs.HCA_1M_DECODE.with_(B=2, ctx=128 * 1500)
+        x = inputs.make_inputs(w, peaky=True)
+        kc, vc = x["kc_hca"], x["vc_hca"]
+    k8, ks = quant.quant_fp8_rows(kc[..., :64].float())
+    v8, vs = quant.quant_fp8_rows(vc.float())
+    krope = kc[..., 64:].contiguous()
     assert not torch.all(torch.frexp(ks)[0] == 0.5)          # some scale is not a power of two
     kd, vd = _dequant(k8, krope, ks, v8, vs)
     g = {k: v.to(dev()) for k, v in x.items()}
     c = tuple(t.to(dev()) for t in (k8, krope, ks, v8, vs))
     pos0 = torch.full((w.B,), w.ctx - 1, dtype=torch.int32, device=dev())
-    out, lse = ops.hca_attend_kv8(g["q_hca"], c, w.m_hca, pos0, w.ctx - 1, sink=g["sink_hca"],
-                                  return_lse=True)
+    if kind == "csa":
+        rp0 = torch.full((w.B,), w.ctx - w.window, dtype=torch.int32, device=dev())
+        idx = ops.indexer_topk(g["qi"], g["w"], g["kic"], pos0, w.m, w.topk, max_pos=w.ctx - 1)
+        out, lse = ops.sparse_attend_kv8(g["q"], c, idx, pos0, w.ctx - 1, w.window, kw=g["kw"],
+                                         vw=g["vw"], raw_pos0=rp0, sink=g["sink"], return_lse=True)
+        idx_np = idx.cpu().numpy()
+    else:
+        out, lse = ops.hca_attend_kv8(g["q_hca"], c, w.m_hca, pos0, w.ctx - 1, sink=g["sink_hca"],
+                                      return_lse=True)
     torch.cuda.synchronize()
     for b in range(w.B):
-        ro, rl = oracle.hca.hca_attend(f64(x["q_hca"][b]), kd[b], vd[b], w.m_hca, [w.ctx - 1],
-                                       f64(x["sink_hca"]), w.scale)
-        assert_close(out[b], ro, "bf16", f"kv8 general scales [{b}]", lse[b], rl)
+        if kind == "csa":
+            ro, rl = oracle.csa.sparse_attend(f64(x["q"][b]), kd[b], vd[b], idx_np[b], f64(x["kw"][b]),
+                                              f64(x["vw"][b]), w.ctx - w.window, [w.ctx - 1],
+                                              w.window, f64(x["sink"]), w.scale)
+        else:
+            ro, rl = oracle.hca.hca_attend(f64(x["q_hca"][b]), kd[b], vd[b], w.m_hca, [w.ctx - 1],
+                                           f64(x["sink_hca"]), w.scale)
+        assert_close(out[b], ro, "bf16", f"kv8 {kind} general scales [{b}]", lse[b], rl)
 
 
 @pytest.mark.parametrize("H,Tq", [(16, 1), (48, 40), (64, 70), (128, 1)])

@@ -1,8 +1,7 @@
 """csa_hybrid_decode_step: the whole decode step of a hybrid CSA + HCA layer
 pair in one library call must give bitwise the results of csa_indexer_topk,
-csa_sparse_attend and hca_attend called one after the other, with the HCA
-attention overlapping the top-k pick or launched in order; and those results
-match the oracle (hyper.ai "Method", CSA and HCA paragraphs)."""
+csa_sparse_attend and hca_attend called one after the other, and those
+results match the oracle (hyper.ai "Method", CSA and HCA paragraphs)."""
 import numpy as np
 import pytest
 import torch
@@ -51,14 +50,13 @@ def test_step_equals_separate_calls(name, qk, B, ctx):
     g = {k: v.to(dev()) for k, v in x.items()}
     pos0, idx, csa, hca = _args(w, g)
     ref = _separate(w, pos0, idx, csa, hca)
-    for in_order in (False, True):
-        st = ops.DecodeStep(idx, csa, hca, pos0, w.ctx - 1, return_lse=True, in_order=in_order)
-        for _ in range(3):             # repeated runs of one step object
-            st.run()
-        torch.cuda.synchronize()
-        got = (st.idx, st.out, st.lse, st.hout, st.hlse)
-        for a, b, nm in zip(got, ref, ("idx", "out", "lse", "hout", "hlse")):
-            assert torch.equal(_bits(a), _bits(b)), f"{name} in_order={in_order}: {nm} differs"
+    st = ops.DecodeStep(idx, csa, hca, pos0, w.ctx - 1, return_lse=True)
+    for _ in range(3):                 # repeated runs of one step object
+        st.run()
+    torch.cuda.synchronize()
+    got = (st.idx, st.out, st.lse, st.hout, st.hlse)
+    for a, b, nm in zip(got, ref, ("idx", "out", "lse", "hout", "hlse")):
+        assert torch.equal(_bits(a), _bits(b)), f"{name}: {nm} differs"
 
 
 def test_step_matches_oracle():
