@@ -337,6 +337,21 @@ csa_status_t csa_hybrid_decode_step(const csa_decode_step_t *step, void *workspa
                                     size_t workspace_bytes, void *stream);
 
 /*
+ * csa_hybrid_decode_step_static — csa_hybrid_decode_step without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, serving loops that forbid allocation).  The scratch is a
+ * static array of CSA_STEP_SCRATCH_BYTES in device memory, one per device,
+ * held until the process ends; the call allocates nothing.  Every call on a
+ * device shares that device's array, so calls that overlap on one device
+ * (several host threads or streams) race and must be serialised by the
+ * caller.  A step whose csa_hybrid_decode_step_workspace exceeds the array
+ * returns CSA_WORKSPACE_TOO_SMALL and launches nothing.  Results, arguments
+ * and other errors as csa_hybrid_decode_step.
+ */
+#define CSA_STEP_SCRATCH_BYTES (64u << 20)
+csa_status_t csa_hybrid_decode_step_static(const csa_decode_step_t *step, void *stream);
+
+/*
  * csa_grouped_out_proj — grouped output projection after the core attention.
  * hyper.ai "Method", CSA paragraph (the core attention is followed by a
  * grouped output projection that keeps its cost down).  Form implemented:

@@ -61,6 +61,7 @@ EXPORTS = {
                                _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
     "csa_hybrid_decode_step_workspace": (_SZ, [C.POINTER(DecodeStepDesc)]),
     "csa_hybrid_decode_step": (_I, [C.POINTER(DecodeStepDesc), _P, _SZ, _P]),
+    "csa_hybrid_decode_step_static": (_I, [C.POINTER(DecodeStepDesc), _P]),
     "csa_grouped_out_proj": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
     "csa_profile_enable": (None, [_I]),
     "csa_profile_reset": (None, []),

@@ -65,6 +65,18 @@ constexpr long long kMaxElems = (long long)1 << 40;
 
 }  // namespace
 
+namespace csa {
+csa_status_t set_error(csa_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+}  // namespace csa
+
 extern "C" {
 
 int csa_abi_version(void) { return CSA_ABI_VERSION; }

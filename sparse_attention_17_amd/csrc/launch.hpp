@@ -2,6 +2,8 @@
 // Arguments arrive here already validated.
 #pragma once
 #include <hip/hip_runtime.h>
+
+#include "csa_mi355x.h"
 #include <stddef.h>
 #include <stdint.h>
 
@@ -20,6 +22,9 @@ class ProfScope {
   hipStream_t st_;
   long idx_;
 };
+
+// Sets the calling thread's error text (csa_last_error) and returns st.
+csa_status_t set_error(csa_status_t st, const char* fmt, ...);
 
 // Raises a kernel's dynamic LDS limit to `lds` bytes (needed above 64 KiB)
 // once per (device, kernel); thread-safe.

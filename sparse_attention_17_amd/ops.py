@@ -445,3 +445,11 @@ class DecodeStep:
         st = _stream(self._dev) if stream is None else stream
         L.check(self._lib.csa_hybrid_decode_step(self._desc, self._wsp, self._nws, st))
         return self
+
+    def run_static(self, stream=None):
+        """The same step through csa_hybrid_decode_step_static: its scratch is
+        the library's static per-device array (no workspace of this object is
+        used; calls that overlap on one device race)."""
+        st = _stream(self._dev) if stream is None else stream
+        L.check(self._lib.csa_hybrid_decode_step_static(self._desc, st))
+        return self

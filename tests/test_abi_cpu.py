@@ -271,3 +271,17 @@ def test_decode_step_flags_reserved(lib):
     s.B, s.H, s.Nc_cap, s.m_prime, s.topk, s.flags = 1, 8, 64, 8, 4, 1
     assert lib.csa_hybrid_decode_step(C.byref(s), None, 0, None) == L.INVALID_ARGUMENT
     assert b"flags" in lib.csa_last_error()
+
+
+def test_static_step_validation(lib):
+    # rejected before any device work: no step, or a step whose scratch needs
+    # more than the static array holds
+    from sparse_attention_17_amd._lib import DecodeStepDesc
+    assert lib.csa_hybrid_decode_step_static(None, None) == L.INVALID_ARGUMENT
+    s = DecodeStepDesc()
+    s.B, s.pos0, s.max_pos, s.H, s.d, s.dt = 64, FAKE, (1 << 23) * 4 - 1, 64, 128, L.BF16
+    s.HI, s.dI, s.m, s.topk, s.qk_dt, s.Nc_cap = 4, 64, 4, 2048, L.FP8_E4M3, 1 << 23
+    s.m_prime, s.hNc_cap, s.window = 128, 1 << 18, 128
+    assert lib.csa_hybrid_decode_step_workspace(C.byref(s)) > 64 << 20
+    assert lib.csa_hybrid_decode_step_static(C.byref(s), None) == L.WORKSPACE_TOO_SMALL
+    assert b"static array" in lib.csa_last_error()
