@@ -202,8 +202,7 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
   // compressed entries visible to any valid row of this wave.
   const bool win_ok = nwin == 0 || (kwb != nullptr && wlo - rp0 >= 0 && wlo + nwin - 1 - rp0 < a.R);
   int wave_min_ne = qvalid ? q_ne : INT_MAX;
-#pragma unroll
-  for (int o2 = 32; o2 > 0; o2 >>= 1) wave_min_ne = min(wave_min_ne, __shfl_xor(wave_min_ne, o2, 64));
+  wave_min_ne = (int)wave_min_u32((uint32_t)wave_min_ne);                 // q_ne >= 0
 
   // byte offset of key slot s's row in the compressed / window buffers (OOB =
   // not there)
@@ -618,7 +617,9 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
 template <typename T, int D, int RW, int KG, bool SPARSE, int PF, bool KV8, bool VSH>
 __global__ __launch_bounds__(RW * KG * 64) __attribute__((amdgpu_waves_per_eu(KV8 && !(RW == 2 && KG == 2) ? 1 : 2))) void attend_kernel(AttendArgs a, AttnGeom gm) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  attend_body<T, D, RW, KG, SPARSE, PF, KV8, VSH>(a, gm, blockIdx.x, blockIdx.y, blockIdx.z, smem_raw);
+  const int gx = (a.Tq + gm.TT - 1) / gm.TT;
+  const RowJ rj = xcd_rows(blockIdx.x, a.B, gx * gm.nsplit);
+  attend_body<T, D, RW, KG, SPARSE, PF, KV8, VSH>(a, gm, rj.j % gx, rj.j / gx, rj.row, smem_raw);
 }
 
 // The HCA and CSA attention of one layer pair in a single split-decode launch:
@@ -633,11 +634,13 @@ __global__ __launch_bounds__(RW * KG * 64) __attribute__((amdgpu_waves_per_eu(2)
   int bid = blockIdx.x;
   if (bid < nb0) {
     const int gx = (a0.Tq + g0.TT - 1) / g0.TT;
-    attend_body<T, D, RW, KG, false, 2>(a0, g0, bid % gx, (bid / gx) % g0.nsplit, bid / (gx * g0.nsplit), smem_raw);
+    const RowJ rj = xcd_rows(bid, a0.B, gx * g0.nsplit);
+    attend_body<T, D, RW, KG, false, 2>(a0, g0, rj.j % gx, rj.j / gx, rj.row, smem_raw);
   } else {
     bid -= nb0;
     const int gx = (a1.Tq + g1.TT - 1) / g1.TT;
-    attend_body<T, D, RW, KG, true, 2>(a1, g1, bid % gx, (bid / gx) % g1.nsplit, bid / (gx * g1.nsplit), smem_raw);
+    const RowJ rj = xcd_rows(bid, a1.B, gx * g1.nsplit);
+    attend_body<T, D, RW, KG, true, 2>(a1, g1, rj.j % gx, rj.j / gx, rj.row, smem_raw);
   }
 }
 
@@ -686,7 +689,7 @@ __device__ __forceinline__ void combine_row(const AttendArgs& a, int nsplit, siz
     Z += wave_sum(lv * cl);
 #pragma unroll
     for (int j = 0; j < CB; ++j) {
-      const float c = __shfl(cl, j, 64);
+      const float c = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(cl), j));
 #pragma unroll
       for (int u = 0; u < PER; ++u) acc[u] = fmaf(v[j][u], c, acc[u]);
     }
@@ -704,17 +707,29 @@ __device__ __forceinline__ void combine_row(const AttendArgs& a, int nsplit, siz
   if (a.lse && lane == 0) a.lse[row] = lse;
 }
 
+// The query row merged by wave `wave` of merge workgroup `bid` (4 rows per
+// workgroup): the rows of one sequence on that sequence's XCD (xcd_rows),
+// where its split workgroups wrote their partials.
+__device__ __forceinline__ size_t combine_row_of(const AttendArgs& a, int bid, int wave) {
+  const int per = a.Tq * a.H;
+  if ((per & 3) == 0) {
+    const RowJ rj = xcd_rows(bid, a.B, per >> 2);
+    return (size_t)rj.row * per + (size_t)rj.j * 4 + wave;
+  }
+  return (size_t)bid * 4 + wave;
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void combine_kernel(AttendArgs a, int nsplit) {
-  combine_row<T, D>(a, nsplit, (size_t)blockIdx.x * 4 + (threadIdx.x >> 6));
+  combine_row<T, D>(a, nsplit, combine_row_of(a, blockIdx.x, threadIdx.x >> 6));
 }
 
 // Both problems of a pair launch: workgroups below nb0 merge a0's rows.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void combine_pair_kernel(AttendArgs a0, int ns0, AttendArgs a1, int ns1,
                                                            int nb0) {
-  if ((int)blockIdx.x < nb0) combine_row<T, D>(a0, ns0, (size_t)blockIdx.x * 4 + (threadIdx.x >> 6));
-  else combine_row<T, D>(a1, ns1, (size_t)(blockIdx.x - nb0) * 4 + (threadIdx.x >> 6));
+  if ((int)blockIdx.x < nb0) combine_row<T, D>(a0, ns0, combine_row_of(a0, blockIdx.x, threadIdx.x >> 6));
+  else combine_row<T, D>(a1, ns1, combine_row_of(a1, blockIdx.x - nb0, threadIdx.x >> 6));
 }
 
 // ------------------------- host launch templates ---------------------------
@@ -784,7 +799,7 @@ static hipError_t launch5(const AttendArgs& a, const AttnGeom& gm, const AttendL
   auto kfn = attend_kernel<T, D, RW, KG, SPARSE, PF, KV8, VSH>;
   hipError_t e = set_lds(kfn, lds);
   if (e != hipSuccess) return e;
-  dim3 grid((a.Tq + gm.TT - 1) / gm.TT, gm.nsplit, a.B);
+  dim3 grid((unsigned)((a.Tq + gm.TT - 1) / gm.TT * gm.nsplit * a.B));
   {
     ProfScope ps(SPARSE ? "attend_csa" : "attend_hca", st);
     hipLaunchKernelGGL(kfn, grid, dim3(RW * KG * 64), lds, st, a, gm);

@@ -38,6 +38,22 @@ template <> __device__ __forceinline__ bf16 from_f32<bf16>(float f) { bf16 r; r.
 // element types share one fragment layout and one reduction order per lane.
 // ---------------------------------------------------------------------------
 template <typename T> struct Frag;
+
+// Workgroups of a 1-D launch are dealt to the chip's 8 XCDs round-robin
+// (workgroup i to XCD i mod 8), each XCD with its own L2.  xcd_rows maps
+// workgroup `bid` of a launch of rows x per_row workgroups to (row, j) so
+// that, when rows is a multiple of 8, every workgroup of one row runs on the
+// XCD of that row (row mod 8): what one kernel writes for a row then stays in
+// the L2 that the next kernel's workgroups for the row read.  Other row counts
+// keep row-major order.
+struct RowJ { int row, j; };
+__device__ __forceinline__ RowJ xcd_rows(int bid, int rows, int per_row) {
+  if ((rows & 7) == 0) {
+    const int q = bid >> 3, nb8 = rows >> 3;
+    return RowJ{(bid & 7) + 8 * (q % nb8), q / nb8};
+  }
+  return RowJ{bid / per_row, bid % per_row};
+}
 template <> struct Frag<bf16> { u32x4 v; };          // 8 packed bf16
 template <> struct Frag<float> { float v[8]; };
 
@@ -87,25 +103,55 @@ __device__ __forceinline__ void mma16(f32x4& c, const Frag<float>& a, const Frag
 // ---------------------------------------------------------------------------
 // Reductions / scans.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+// Wave-wide scans and reductions move lanes with DPP (VALU operand
+// modifiers, no LDS round trip).  GFX9 controls: row_shr:n (0x110 + n) inside
+// each 16-lane row, row_bcast:15 (0x142: lane 15 of a row to the next row)
+// and row_bcast:31 (0x143: lane 31 to rows 2 and 3).  Lanes with no source,
+// and rows outside ROW_MASK, receive `id`.  Callers run them with every lane
+// of the wave active.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_move(uint32_t id, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, CTRL, ROW_MASK, 0xf, false);
+}
+// Inclusive scan of the associative `op` (identity `id`) over the 64 lanes:
+// shifts by 1, 2, 4, 8 inside the rows, then the row totals carried up.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_scan(uint32_t v, uint32_t id, Op op) {
+  v = op(v, dpp_move<0x111, 0xf>(id, v));
+  v = op(v, dpp_move<0x112, 0xf>(id, v));
+  v = op(v, dpp_move<0x114, 0xf>(id, v));
+  v = op(v, dpp_move<0x118, 0xf>(id, v));
+  v = op(v, dpp_move<0x142, 0xa>(id, v));
+  v = op(v, dpp_move<0x143, 0xc>(id, v));
   return v;
 }
+// Reduction of `op` over the wave: the scan's last lane, read as a scalar.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t v, uint32_t id, Op op) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_scan(v, id, op), 63);
+}
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  return wave_reduce(v, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  return wave_reduce(v, 0xFFFFFFFFu, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  return wave_reduce(v, 0u, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+__device__ __forceinline__ float wave_max(float v) {
+  return __uint_as_float(wave_reduce(__float_as_uint(v), 0xFF800000u, [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+  }));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  return __uint_as_float(wave_reduce(__float_as_uint(v), 0u, [](uint32_t a, uint32_t b) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+  }));
 }
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t t = __shfl_up(v, o, 64);
-    if (lane >= o) v += t;
-  }
-  return v;
+  return wave_scan(v, 0u, [](uint32_t a, uint32_t b) { return a + b; });
 }
 // Exclusive prefix sum over a block of NT threads; `smem` holds NT/64 words.
 // Returns the exclusive prefix; *total receives the block sum.

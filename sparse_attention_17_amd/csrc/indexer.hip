@@ -258,8 +258,8 @@ __device__ __forceinline__ void wave_top_bin(int per, uint32_t need, Cnt cnt, ui
   }
   const uint64_t m = __ballot(mine);
   const int src = m ? __ffsll((unsigned long long)m) - 1 : 0;
-  bin = __shfl(bb, src, 64);
-  above = __shfl(ab, src, 64);
+  bin = (uint32_t)__builtin_amdgcn_readlane((int)bb, src);
+  above = (uint32_t)__builtin_amdgcn_readlane((int)ab, src);
 }
 
 // End of a decode score workgroup (256 threads): keep the chunk's entries at
@@ -422,41 +422,15 @@ __global__ __launch_bounds__(256) void score_row_kernel(IndexerArgs a) {
   __shared__ uint32_t cut_ws[516];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int row = blockIdx.y;
+  const RowJ rj = xcd_rows(blockIdx.x, a.B * a.Tq, gridDim.x / (a.B * a.Tq));
+  const int row = rj.row;
   const int b = row / a.Tq, t = row % a.Tq;
   const int n = row_len(a, b, t);
-  const int chunk0 = blockIdx.x * SCORE_CPW;
+  const int chunk0 = rj.j * SCORE_CPW;
   if (chunk0 * SCORE_CHUNK >= n) return;
   LongWs L = long_ws(a.ws, a.B * a.Tq, a.Nc_cap);
 
-  // A operands: for tile u the query's HI head rows sit at rows u*HI .. u*HI+HI-1
   const int r = lane & 15, g = lane >> 4;
-  const int hq = r % HI, uq = r / HI;
-  const size_t qrow = ((size_t)b * a.Tq + t) * HI + hq;
-  const char* qptr = reinterpret_cast<const char*>(a.qi) + qrow * qk_row_bytes<QK>(DI);
-  const uint8_t* qsc = nullptr;
-  if constexpr (QK == QK_FP4) qsc = reinterpret_cast<const uint8_t*>(a.qi_scale) + qrow * (DI / 32);
-  F qv[KC];
-#pragma unroll
-  for (int c = 0; c < KC; ++c) load_qk_frag<QK>(qv[c], qptr, qsc, 8 * (g * KC + c));
-  F qa[TPC][KC];
-#pragma unroll
-  for (int u = 0; u < TPC; ++u)
-#pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      if (u == uq) qa[u][c] = qv[c];
-      else frag_zero(qa[u][c]);
-    }
-  // weights of the head rows this lane receives: rows 4g+i -> head (4g+i) % HI
-  float wr[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const size_t wi = ((size_t)b * a.Tq + t) * HI + ((4 * g + i) % HI);
-    float wv = a.w[wi];
-    if constexpr (QK == QK_FP8) wv *= reinterpret_cast<const float*>(a.qi_scale)[wi];
-    wr[i] = wv;
-  }
-
   const size_t rb = qk_row_bytes<QK>(DI);
   const char* kbase = reinterpret_cast<const char*>(a.kic) + (size_t)b * a.Nc_cap * rb;
   const uint8_t* sbase = nullptr;
@@ -483,6 +457,49 @@ __global__ __launch_bounds__(256) void score_row_kernel(IndexerArgs a) {
       else ks[s] = 1.f;
     }
   };
+
+  // DEPTH groups in flight per wave; a chunk's groups are fully unrolled and
+  // branch-free (loads clamp to the chunk, stores are masked).  The first
+  // chunk's groups are requested before the query and the head weights, so
+  // the two latencies overlap.  A workgroup scores SCORE_CPW consecutive
+  // chunks and requests the next chunk's first groups before cutting the
+  // current one, so the cut overlaps those loads.
+  constexpr int STRIDE = 4 * EPC;
+  constexpr int NG = (SCORE_CHUNK + STRIDE - 1) / STRIDE;
+  constexpr int DEPTH = NG < SCORE_DEPTH ? NG : SCORE_DEPTH;
+  R kb[DEPTH][TPC][KC];
+  float ks[DEPTH][SPL];
+  {
+    const int c0 = chunk0 * SCORE_CHUNK, c1 = min(n, c0 + SCORE_CHUNK);
+#pragma unroll
+    for (int j = 0; j < DEPTH; ++j) load_group(c0 + wave * EPC + j * STRIDE, c1, kb[j], ks[j]);
+  }
+  // A operands: for tile u the query's HI head rows sit at rows u*HI .. u*HI+HI-1
+  const int hq = r % HI, uq = r / HI;
+  const size_t qrow = ((size_t)b * a.Tq + t) * HI + hq;
+  const char* qptr = reinterpret_cast<const char*>(a.qi) + qrow * qk_row_bytes<QK>(DI);
+  const uint8_t* qsc = nullptr;
+  if constexpr (QK == QK_FP4) qsc = reinterpret_cast<const uint8_t*>(a.qi_scale) + qrow * (DI / 32);
+  F qv[KC];
+#pragma unroll
+  for (int c = 0; c < KC; ++c) load_qk_frag<QK>(qv[c], qptr, qsc, 8 * (g * KC + c));
+  F qa[TPC][KC];
+#pragma unroll
+  for (int u = 0; u < TPC; ++u)
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      if (u == uq) qa[u][c] = qv[c];
+      else frag_zero(qa[u][c]);
+    }
+  // weights of the head rows this lane receives: rows 4g+i -> head (4g+i) % HI
+  float wr[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const size_t wi = ((size_t)b * a.Tq + t) * HI + ((4 * g + i) % HI);
+    float wv = a.w[wi];
+    if constexpr (QK == QK_FP8) wv *= reinterpret_cast<const float*>(a.qi_scale)[wi];
+    wr[i] = wv;
+  }
 
   // process one group of the chunk [c0, c1): MFMAs, ReLU + head weights, store,
   // chunk key copy and histogram
@@ -512,20 +529,6 @@ __global__ __launch_bounds__(256) void score_row_kernel(IndexerArgs a) {
     }
   };
 
-  // DEPTH groups in flight per wave; a chunk's groups are fully unrolled and
-  // branch-free (loads clamp to the chunk, stores are masked).  A workgroup
-  // scores SCORE_CPW consecutive chunks and requests the next chunk's first
-  // groups before cutting the current one, so the cut overlaps those loads.
-  constexpr int STRIDE = 4 * EPC;
-  constexpr int NG = (SCORE_CHUNK + STRIDE - 1) / STRIDE;
-  constexpr int DEPTH = NG < SCORE_DEPTH ? NG : SCORE_DEPTH;
-  R kb[DEPTH][TPC][KC];
-  float ks[DEPTH][SPL];
-  {
-    const int c0 = chunk0 * SCORE_CHUNK, c1 = min(n, c0 + SCORE_CHUNK);
-#pragma unroll
-    for (int j = 0; j < DEPTH; ++j) load_group(c0 + wave * EPC + j * STRIDE, c1, kb[j], ks[j]);
-  }
 #pragma unroll 1
   for (int ci = 0; ci < SCORE_CPW; ++ci) {
     const int chunk = chunk0 + ci;
@@ -572,10 +575,11 @@ __global__ __launch_bounds__(256) void score_row_fp4_kernel(IndexerArgs a) {
   __shared__ uint32_t sk[SCORE_CHUNK];
   __shared__ uint32_t cut_ws[516];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int row = blockIdx.y;
+  const RowJ rj = xcd_rows(blockIdx.x, a.B * a.Tq, gridDim.x / (a.B * a.Tq));
+  const int row = rj.row, chunk = rj.j;
   const int b = row / a.Tq, t = row % a.Tq;
   const int n = row_len(a, b, t);
-  const int c0 = blockIdx.x * SCORE_CHUNK;
+  const int c0 = chunk * SCORE_CHUNK;
   if (c0 >= n) return;
   const int c1 = min(n, c0 + SCORE_CHUNK);
   LongWs L = long_ws(a.ws, a.B * a.Tq, a.Nc_cap);
@@ -653,7 +657,7 @@ __global__ __launch_bounds__(256) void score_row_fp4_kernel(IndexerArgs a) {
     }
   }
   __syncthreads();
-  if (n > a.topk) chunk_cut(a, L, row, blockIdx.x, n, c0, c1 - c0, sk, hist, cut_ws);
+  if (n > a.topk) chunk_cut(a, L, row, chunk, n, c0, c1 - c0, sk, hist, cut_ws);
 }
 
 // --------------------------- shared select helpers --------------------------
@@ -776,10 +780,7 @@ static_assert(sizeof(TopkSmem<PICK_NT>) <= sizeof(PickSmem), "fallback select al
 // walk over the totals.
 __device__ __forceinline__ uint32_t waves_below(const uint32_t* w, int wave) {
   const int lane = threadIdx.x & 63;
-  uint32_t v = lane < wave ? w[lane] : 0u;                   // wave < PICK_NW <= 64
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) v += (uint32_t)__shfl_xor((int)v, o, 64);
-  return v;
+  return wave_sum_u32(lane < wave ? w[lane] : 0u);           // wave < PICK_NW <= 64
 }
 
 struct PickRow {
@@ -828,13 +829,10 @@ __device__ __forceinline__ void pick_body(PickSmem& sm, const PickRow& R) {
     kmin = ok ? min(kmin, kv[q].x) : kmin;
     kmax = ok ? max(kmax, kv[q].x) : kmax;
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
-    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
-    part += (uint32_t)__shfl_xor((int)part, o, 64);
-    bad |= __shfl_xor(bad, o, 64);
-  }
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
+  part = wave_sum_u32(part);
+  bad = wave_max_u32((uint32_t)bad) != 0u;
   if (lane == 0) { sm.wv[0][wave] = part; sm.wv[1][wave] = kmin; sm.wv[2][wave] = kmax; sm.wv[3][wave] = bad; }
   __syncthreads();
   uint32_t total = 0;
@@ -948,17 +946,11 @@ __device__ __forceinline__ void pick_body(PickSmem& sm, const PickRow& R) {
   const int word = tid / Q, wpart = tid % Q;
   const uint32_t wgt = word < NWORDS ? (sm.bm_gt[word] >> (wpart * L)) & LMASK : 0u;
   const uint32_t weq = word < NWORDS ? (sm.bm_eq[word] >> (wpart * L)) & LMASK : 0u;
-  const uint64_t pk = ((uint64_t)__popc(wgt) << 32) | (uint32_t)__popc(weq);
-  uint64_t inc = pk;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint64_t y = ((uint64_t)(uint32_t)__shfl_up((int)(uint32_t)(inc >> 32), o, 64) << 32) |
-                       (uint32_t)__shfl_up((int)(uint32_t)inc, o, 64);
-    if (lane >= o) inc += y;
-  }
-  if (lane == 63) { sm.wv[1][wave] = (uint32_t)(inc >> 32); sm.wv[2][wave] = (uint32_t)inc; }
+  const uint32_t pgt = (uint32_t)__popc(wgt), peq = (uint32_t)__popc(weq);
+  const uint32_t inc_gt = wave_incl_scan(pgt), inc_eq = wave_incl_scan(peq);
+  if (lane == 63) { sm.wv[1][wave] = inc_gt; sm.wv[2][wave] = inc_eq; }
   __syncthreads();
-  uint32_t gt_before = (uint32_t)((inc - pk) >> 32), eq_before = (uint32_t)(inc - pk);
+  uint32_t gt_before = inc_gt - pgt, eq_before = inc_eq - peq;
   gt_before += waves_below(sm.wv[1], wave);
   eq_before += waves_below(sm.wv[2], wave);
   uint32_t pos = gt_before + min(eq_before, need);
@@ -1084,8 +1076,8 @@ __device__ __forceinline__ void wave_find_bin(int nb, uint32_t need, Cnt cnt, ui
   }
   const uint64_t m = __ballot(mine);
   const int src = m ? __ffsll((unsigned long long)m) - 1 : 0;
-  bin = __shfl(bb, src, 64);
-  above = __shfl(ab, src, 64);
+  bin = (uint32_t)__builtin_amdgcn_readlane((int)bb, src);
+  above = (uint32_t)__builtin_amdgcn_readlane((int)ab, src);
 }
 
 template <int QK, int DI, int HI>
@@ -1315,7 +1307,7 @@ __global__ __launch_bounds__(FNT) void fused_prefill_kernel(IndexerArgs a) {
         ++pos;
       }
     }
-    const uint32_t tot = __shfl(pos, 63, 64);
+    const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)pos, 63);
     for (uint32_t i = tot + lane; i < (uint32_t)k; i += 64) idx[i] = -1;
     wave_sync();
   }
@@ -1388,9 +1380,9 @@ static void launch_scores(const IndexerArgs& a, hipStream_t st, bool long_path) 
     const int nch = (ne_ub + SCORE_CHUNK - 1) / SCORE_CHUNK;
     ProfScope ps("indexer_score", st);
     if constexpr (QK == QK_FP4 && HI == 4)
-      hipLaunchKernelGGL((score_row_fp4_kernel<DI>), dim3(nch, a.B * a.Tq), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((score_row_fp4_kernel<DI>), dim3(nch * a.B * a.Tq), dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((score_row_kernel<QK, DI, HI>), dim3((nch + SCORE_CPW - 1) / SCORE_CPW, a.B * a.Tq),
+      hipLaunchKernelGGL((score_row_kernel<QK, DI, HI>), dim3((nch + SCORE_CPW - 1) / SCORE_CPW * a.B * a.Tq),
                          dim3(256), 0, st, a);
   } else {
     const int TT = 16 / HI;
