@@ -480,17 +480,31 @@ __global__ __launch_bounds__(256) void score_row_kernel(IndexerArgs a) {
   const char* qptr = reinterpret_cast<const char*>(a.qi) + qrow * qk_row_bytes<QK>(DI);
   const uint8_t* qsc = nullptr;
   if constexpr (QK == QK_FP4) qsc = reinterpret_cast<const uint8_t*>(a.qi_scale) + qrow * (DI / 32);
-  F qv[KC];
-#pragma unroll
-  for (int c = 0; c < KC; ++c) load_qk_frag<QK>(qv[c], qptr, qsc, 8 * (g * KC + c));
-  F qa[TPC][KC];
-#pragma unroll
-  for (int u = 0; u < TPC; ++u)
+  // FP8: the codes themselves are the operands of the FP8 MFMA (E4M3 x E4M3
+  // products are exact in its fp32 accumulation, as in the bf16 MFMA on the
+  // exactly widened codes); the row scales multiply the weights and scores.
+  constexpr bool NATIVE8 = QK == QK_FP8;
+  F qa[NATIVE8 ? 1 : TPC][KC];
+  uint64_t qa8[NATIVE8 ? TPC : 1][KC];
+  if constexpr (NATIVE8) {
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
-      if (u == uq) qa[u][c] = qv[c];
-      else frag_zero(qa[u][c]);
+      const uint64_t qc = *reinterpret_cast<const uint64_t*>(qptr + 8 * (g * KC + c));
+#pragma unroll
+      for (int u = 0; u < TPC; ++u) qa8[u][c] = u == uq ? qc : 0ull;
     }
+  } else {
+    F qv[KC];
+#pragma unroll
+    for (int c = 0; c < KC; ++c) load_qk_frag<QK>(qv[c], qptr, qsc, 8 * (g * KC + c));
+#pragma unroll
+    for (int u = 0; u < TPC; ++u)
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        if (u == uq) qa[u][c] = qv[c];
+        else frag_zero(qa[u][c]);
+      }
+  }
   // weights of the head rows this lane receives: rows 4g+i -> head (4g+i) % HI
   float wr[4];
 #pragma unroll
@@ -508,7 +522,13 @@ __global__ __launch_bounds__(256) void score_row_kernel(IndexerArgs a) {
 #pragma unroll
     for (int u = 0; u < TPC; ++u)
 #pragma unroll
-      for (int c = 0; c < KC; ++c) mma16(acc, qa[u][c], widen<QK>(cur[u][c]));
+      for (int c = 0; c < KC; ++c) {
+        if constexpr (NATIVE8)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)qa8[u][c], __builtin_bit_cast(long, cur[u][c].c),
+                                                          acc, 0, 0, 0);
+        else
+          mma16(acc, qa[u][c], widen<QK>(cur[u][c]));
+      }
 #pragma unroll
     for (int s = 0; s < SPL; ++s) {
       const int u = (4 * g) / HI + s;
