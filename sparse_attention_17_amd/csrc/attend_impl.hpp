@@ -574,16 +574,23 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
   if (!qvalid) return;
   const size_t grow = ((size_t)b * a.Tq + tq) * a.H + hq;
   if (gm.nsplit > 1) {
+    // split partial: o (unnormalised, in the element type: bf16 problems keep
+    // bf16 partials, which halves the partials' HBM round trip), max, sum
     const size_t rows_total = (size_t)a.B * a.Tq * a.H;
-    float* po = reinterpret_cast<float*>(a.ws) + ((size_t)split * rows_total + grow) * D;
+    T* po = reinterpret_cast<T*>(a.ws) + ((size_t)split * rows_total + grow) * D;
     float* pm = reinterpret_cast<float*>(a.ws) + (size_t)gm.nsplit * rows_total * D;
     float* pl = pm + (size_t)gm.nsplit * rows_total;
 #pragma unroll
     for (int i = 0; i < DVT; ++i)
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<f32x4*>(po + i * 32 + 8 * g + 4 * half) =
-            f32x4{o[i][4 * g], o[i][4 * g + 1], o[i][4 * g + 2], o[i][4 * g + 3]};
+      for (int g = 0; g < 4; ++g) {
+        if constexpr (sizeof(T) == 2)
+          *reinterpret_cast<uint2*>(po + i * 32 + 8 * g + 4 * half) =
+              uint2{pack_bf16x2(o[i][4 * g], o[i][4 * g + 1]), pack_bf16x2(o[i][4 * g + 2], o[i][4 * g + 3])};
+        else
+          *reinterpret_cast<f32x4*>(po + i * 32 + 8 * g + 4 * half) =
+              f32x4{o[i][4 * g], o[i][4 * g + 1], o[i][4 * g + 2], o[i][4 * g + 3]};
+      }
     if (half == 0) {
       pm[(size_t)split * rows_total + grow] = m_run;
       pl[(size_t)split * rows_total + grow] = l_tot;
@@ -654,8 +661,8 @@ __device__ __forceinline__ void combine_row(const AttendArgs& a, int nsplit, siz
   const int lane = threadIdx.x & 63;
   const size_t rows_total = (size_t)a.B * a.Tq * a.H;
   if (row >= rows_total) return;
-  const float* po = reinterpret_cast<const float*>(a.ws);
-  const float* pm = po + (size_t)nsplit * rows_total * D;
+  const T* po = reinterpret_cast<const T*>(a.ws);               // partials in the element type
+  const float* pm = reinterpret_cast<const float*>(a.ws) + (size_t)nsplit * rows_total * D;
   const float* pl = pm + (size_t)nsplit * rows_total;
   const int h = (int)(row % a.H);
   const float s2 = a.sink ? a.sink[h] * LOG2E : -INFINITY;
@@ -673,9 +680,9 @@ __device__ __forceinline__ void combine_row(const AttendArgs& a, int nsplit, siz
     const float lraw = pl[(size_t)sl * rows_total + row];
 #pragma unroll
     for (int j = 0; j < CB; ++j) {
-      const float* src = po + ((size_t)min(s0 + j, nsplit - 1) * rows_total + row) * D + lane * PER;
+      const T* src = po + ((size_t)min(s0 + j, nsplit - 1) * rows_total + row) * D + lane * PER;
 #pragma unroll
-      for (int u = 0; u < PER; ++u) v[j][u] = src[u];
+      for (int u = 0; u < PER; ++u) v[j][u] = to_f32(src[u]);
     }
     const float mv = lv_ok ? mraw : -INFINITY;
     const float lv = lv_ok ? lraw : 0.f;
