@@ -65,6 +65,9 @@ def parse():
                    help="first run three 256 MiB device copies (known traffic for counter scaling)")
     p.add_argument("--suite", action="store_true",
                    help="time every op at the other workloads' sizes (one JSON object) and exit")
+    p.add_argument("--prefill", action="store_true",
+                   help="run only the prefill kernels (32K CSA indexer/top-512 and sparse attention, "
+                        "HCA 4096-query chunk at 1M context), three calls each, for counter runs")
     p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                         "`bench.py --copy-calibration --graph 0` into profiles/ and exit")
@@ -369,6 +372,41 @@ def suite():
     print(json.dumps({"suite": {k: round(v, 2) for k, v in res.items()}}), flush=True)
 
 
+def prefill_only(calls=3):
+    """The prefill kernels alone (for rocprofv3 counter runs): the 32K CSA
+    prefill's fused indexer/top-512 and sparse attention, and the HCA
+    4096-query chunk at 1M context, `calls` event-timed calls each."""
+    import torch
+    from synth import configs, inputs
+    from sparse_attention_17_amd import ops
+    dev = torch.device("cuda:0")
+    res = {}
+    w = configs.CSA_PREFILL_32K
+    x = inputs.make_inputs(w)
+    g = {k: v.to(dev) for k, v in x.items()}
+    del x
+    pos0 = torch.zeros(1, dtype=torch.int32, device=dev)
+    kc, vc, kic = ops.compress(g["k"], g["v"], g["ki"], g["g"], w.m)
+    idx = ops.indexer_topk(g["qi"], g["w"], kic, pos0, w.m, w.topk, max_pos=w.ctx - 1)
+    ms, _, _ = _timed(lambda i: ops.indexer_topk(g["qi"], g["w"], kic, pos0, w.m, w.topk,
+                                                 max_pos=w.ctx - 1), calls, warm=0)
+    res["csa_prefill_32k.indexer_topk_ms"] = round(ms, 4)
+    ms, _, _ = _timed(lambda i: ops.sparse_attend(g["q"], kc, vc, idx, pos0, w.ctx - 1, w.window,
+                                                  kw=g["k"], vw=g["v"], raw_pos0=pos0, sink=g["sink"]),
+                      calls, warm=0)
+    res["csa_prefill_32k.sparse_attend_ms"] = round(ms, 4)
+    del g, kc, vc, kic, idx
+    w = configs.HCA_1M_PREFILL
+    x = inputs.make_inputs(w)
+    g = {k: v.to(dev) for k, v in x.items()}
+    del x
+    pos0 = torch.full((w.B,), w.ctx - w.Tq, dtype=torch.int32, device=dev)
+    ms, _, _ = _timed(lambda i: ops.hca_attend(g["q_hca"], g["kc_hca"], g["vc_hca"], w.m_hca, pos0,
+                                               w.ctx - 1, sink=g["sink_hca"]), calls, warm=0)
+    res["hca_1m_prefill4k.hca_ms"] = round(ms, 4)
+    print(json.dumps({"prefill": res}), flush=True)
+
+
 def _pct(v, q):
     return float(np.percentile(np.asarray(v), q))
 
@@ -519,6 +557,9 @@ def main():
         return
     if args.suite:
         suite()
+        return
+    if args.prefill:
+        prefill_only()
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the multi-GPU "
