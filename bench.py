@@ -68,6 +68,9 @@ def parse():
     p.add_argument("--prefill", action="store_true",
                    help="run only the prefill kernels (32K CSA indexer/top-512 and sparse attention, "
                         "HCA 4096-query chunk at 1M context), three calls each, for counter runs")
+    p.add_argument("--topk-clustered", action="store_true",
+                   help="time the decode indexer + top-k of the 1M FP8 batch on i.i.d. rows and on "
+                        "rows whose top-k clusters in the last 5 %% of the entries, then exit")
     p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                         "`bench.py --copy-calibration --graph 0` into profiles/ and exit")
@@ -180,6 +183,8 @@ def algorithmic_bytes(w):
         "attend_csa": B * (nk_csa * 2 * d * 2 + 2 * H * d * 2),
         "attend_hca": B * (w.Nc_hca * 2 * d * 2 + 2 * H * d * 2),
         "attend_pair": B * ((nk_csa + w.Nc_hca) * 2 * d * 2 + 4 * H * d * 2),
+        # the fused step tail: top-k picks, both attention problems and their merges
+        "decode_tail": B * (w.topk * 4 + (nk_csa + w.Nc_hca) * 2 * d * 2 + 4 * H * d * 2),
     }
 
 
@@ -407,6 +412,37 @@ def prefill_only(calls=3):
     print(json.dumps({"prefill": res}), flush=True)
 
 
+def topk_clustered(calls=20):
+    """Decode indexer + top-2048 of the 1M-context FP8 batch (B=8): i.i.d. rows
+    against rows whose last 5 % of keys are three times larger (their top-k
+    entries cluster there, beyond what the per-chunk candidate cut keeps), with
+    the number of rows that took the second pick round or the exact select."""
+    import torch
+    from synth import configs, inputs
+    from sparse_attention_17_amd import ops
+    dev = torch.device("cuda:0")
+    w = configs.HYBRID_1M_FP8
+    x = inputs.make_inputs(w)
+    res = {}
+    for name in ("iid", "clustered"):
+        if name == "clustered":
+            x["kic_scale"][:, w.Nc - w.Nc // 20:] *= 3.0
+        g = {k: v.to(dev) for k, v in x.items()}
+        pos0 = torch.full((w.B,), w.ctx - 1, dtype=torch.int32, device=dev)
+        fn = lambda i: ops.indexer_topk(g["qi"], g["w"], g["kic"], pos0, w.m, w.topk,  # noqa: E731
+                                        max_pos=w.ctx - 1, qi_scale=g["qi_scale"],
+                                        kic_scale=g["kic_scale"], qk_dtype="fp8")
+        ops.profile_counter("indexer_decode_second_round", reset=True)
+        ops.profile_counter("indexer_decode_fallback", reset=True)
+        ms, p50, p90 = _timed(fn, calls)
+        res[name] = {"ms_per_call": round(ms, 4), "p50_ms": round(p50, 4), "p90_ms": round(p90, 4),
+                     "second_round_rows": ops.profile_counter("indexer_decode_second_round", reset=True),
+                     "exact_select_rows": ops.profile_counter("indexer_decode_fallback", reset=True),
+                     "rows": w.B * (calls + 3)}
+        del g
+    print(json.dumps({"topk_clustered": res}), flush=True)
+
+
 def _pct(v, q):
     return float(np.percentile(np.asarray(v), q))
 
@@ -561,6 +597,9 @@ def main():
     if args.prefill:
         prefill_only()
         return
+    if args.topk_clustered:
+        topk_clustered()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the multi-GPU "
               "sharding of this path is a design, not an implementation.", file=sys.stderr)
@@ -680,7 +719,7 @@ def main():
     import ctypes as C
     kern = {}
     for name in ("indexer_score", "indexer_topk", "attend_csa",
-                 "attend_hca", "attend_pair", "attend_combine"):
+                 "attend_hca", "attend_pair", "attend_combine", "decode_tail"):
         n, t = C.c_int(0), C.c_double(0)
         if lib.csa_profile_query(name.encode(), C.byref(n), C.byref(t)) == 0:
             kern[name] = t.value / n.value * 1e3          # us per launch
@@ -693,7 +732,7 @@ def main():
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": dom,
             "bytes_per_launch": alg[dom], "us_per_launch": round(kern[dom], 2)}
-    step_bytes = sum(v for k, v in alg.items() if k != "attend_pair")   # pair = csa + hca
+    step_bytes = sum(alg[k] for k in ("indexer_score", "indexer_topk", "attend_csa", "attend_hca"))
 
     extra = extra_workloads() if args.extra else None
 

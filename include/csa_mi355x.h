@@ -282,16 +282,28 @@ csa_status_t csa_hybrid_attend(
  * block), csa_sparse_attend (the second) and hca_attend (the third, fields
  * prefixed h), with Tq = 1 and B, pos0, max_pos, H, d, dt shared by both
  * layers.  idx_out receives the CSA index lists; lse_out / hlse_out may be
- * NULL.  The workspace holds the three calls' workspaces (size from
- * csa_hybrid_decode_step_workspace).
+ * NULL.  The workspace (size from csa_hybrid_decode_step_workspace) holds the
+ * three calls' workspaces behind a block of control words that must be zero
+ * before the workspace's first use (allocate it zeroed); every call leaves
+ * them zero again, so a workspace is reused as is.  Nothing else may write
+ * the workspace between steps.
  *
  * Results are bitwise those of csa_indexer_topk, csa_sparse_attend and
- * hca_attend called one after the other.  The work is enqueued on `stream` as
- * the indexer's kernels, then the CSA and HCA attention as in
- * csa_hybrid_attend (one launch for both problems and one merge of their
- * split partials).  An invalid field launches nothing; the error text names
- * the part.
+ * hca_attend called one after the other.  The work is enqueued on `stream`
+ * as the indexer's kernels (score kernel, row pick), then the CSA and HCA
+ * attention as in csa_hybrid_attend (one launch for both problems and one
+ * merge of their split partials).  With flags = CSA_STEP_FUSED_TAIL, decode
+ * rows on the chunked indexer path (Nc_cap > 12288) with bf16 attention of
+ * head dim 128, 33-64 query heads and B <= 1580 instead run both attention
+ * problems and both merges in one kernel that orders them through counters
+ * in the control words (same results; measured slower on MI355X, where the
+ * device-scope counter updates serialise).  The waits inside that kernel are
+ * bounded (0.5 s); a wait that runs out (a workspace whose control words were
+ * not zero) is counted by the "step_timeout" event counter and leaves the
+ * step's outputs undefined.  An invalid field launches nothing; the error
+ * text names the part.
  */
+#define CSA_STEP_FUSED_TAIL 1u
 
 typedef struct csa_decode_step {
   /* sequences (both layers) */
@@ -329,7 +341,7 @@ typedef struct csa_decode_step {
   float hsoftmax_scale;
   void *hout;                 /* [B, 1, H, d] */
   float *hlse_out;
-  unsigned flags;             /* reserved: must be 0 */
+  unsigned flags;             /* 0, or CSA_STEP_FUSED_TAIL */
 } csa_decode_step_t;
 
 size_t csa_hybrid_decode_step_workspace(const csa_decode_step_t *step);
@@ -345,7 +357,8 @@ csa_status_t csa_hybrid_decode_step(const csa_decode_step_t *step, void *workspa
  * device shares that device's array, so calls that overlap on one device
  * (several host threads or streams) race and must be serialised by the
  * caller.  A step whose csa_hybrid_decode_step_workspace exceeds the array
- * returns CSA_WORKSPACE_TOO_SMALL and launches nothing.  Results, arguments
+ * returns CSA_WORKSPACE_TOO_SMALL and launches nothing.  The array starts
+ * zeroed and every step leaves its control words zero.  Results, arguments
  * and other errors as csa_hybrid_decode_step.
  */
 #define CSA_STEP_SCRATCH_BYTES (64u << 20)
@@ -380,7 +393,8 @@ csa_status_t csa_grouped_out_proj(const void *o, const void *w, int T, int H, in
  * (decode scores and per-chunk cut), "indexer_topk" (row select),
  * "indexer_fused" (prefill scores and select in one kernel), "attend_csa",
  * "attend_hca", "attend_pair" (both of csa_hybrid_attend in one kernel),
- * "attend_combine", "out_proj".
+ * "attend_combine", "decode_tail" (the fused tail of csa_hybrid_decode_step:
+ * picks, both attention problems and their merges), "out_proj".
  * csa_profile_reset forgets all records (events are kept for reuse).
  */
 void csa_profile_enable(int on);
@@ -391,7 +405,8 @@ int csa_profile_query(const char *kernel, int *count, double *total_ms);
  * query rows whose top-k selection took the exact fallback path since the
  * last reset ("indexer_prefill_fallback": prefill rows whose candidate set
  * could not settle the top-k; "indexer_decode_fallback": long decode rows whose
- * chunk candidates could not).  Writes the count to *value and, if reset is
+ * chunk candidates could not), and "step_timeout": waits of the fused decode
+ * step that ran out of time.  Writes the count to *value and, if reset is
  * non-zero, zeroes the counter.  Synchronous (waits for the device); returns 0,
  * 1 for an unknown name or a NULL value, -1 on a HIP error. */
 int csa_profile_counter(const char *name, unsigned long long *value, int reset);

@@ -14,6 +14,8 @@ LIB_PATH = os.path.join(PKG, "libcsa_mi355x.so")
 OK, INVALID_ARGUMENT, UNSUPPORTED, WORKSPACE_TOO_SMALL, DEVICE_ERROR = range(5)
 # csa_dtype_t
 F32, BF16, FP8_E4M3, FP4_E2M1 = range(4)
+# csa_decode_step_t.flags
+STEP_FUSED_TAIL = 1
 
 _P = C.c_void_p
 _I = C.c_int

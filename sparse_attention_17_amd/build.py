@@ -21,7 +21,7 @@ OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libcsa_mi355x.so")
 SOURCES = ["api.cpp", "profile.cpp", "compress.hip", "indexer.hip", "attend.hip", "attend_v_f32.hip",
            "attend_v_bf16_64.hip", "attend_v_bf16_128.hip", "attend_v_pair_bf16_128.hip",
-           "attend_v_kv8.hip", "proj.hip", "step_static.hip"]
+           "attend_v_kv8.hip", "proj.hip", "step_static.hip", "step_tail.hip"]
 ARCH = "gfx950"
 
 

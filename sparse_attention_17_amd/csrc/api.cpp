@@ -12,6 +12,7 @@
 #include <string>
 
 #include "launch.hpp"
+#include "step_tail.hpp"
 
 namespace {
 
@@ -415,9 +416,10 @@ csa_status_t csa_hybrid_attend(
   return device_status(e, "csa_hybrid_attend launch");
 }
 
-// Workspace carve-up of the decode step: indexer | CSA attention | HCA attention.
+// Workspace carve-up of the decode step: control words of the fused tail |
+// indexer | CSA attention | HCA attention.
 struct StepWs {
-  size_t idx, csa, hca, total;
+  size_t ctl, idx, csa, hca, total;
 };
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 static StepWs step_ws(const csa_decode_step_t* s) {
@@ -428,8 +430,9 @@ static StepWs step_ws(const csa_decode_step_t* s) {
                                                          s->Nc_cap, 1, s->max_pos) : 0;
   const size_t nh = s->m_prime >= 1 ? csa::attend_workspace(false, s->B, 1, s->H, s->d, 0, s->hwindow,
                                                             s->hNc_cap, s->m_prime, s->max_pos) : 0;
-  w.idx = 0;
-  w.csa = align256(ni);
+  w.ctl = 0;
+  w.idx = csa::decode_tail_ctl_bytes();
+  w.csa = align256(w.idx + ni);
   w.hca = align256(w.csa + nc);
   w.total = w.hca + nh;
   return w;
@@ -444,7 +447,8 @@ csa_status_t csa_hybrid_decode_step(const csa_decode_step_t* s, void* workspace,
                                     void* stream) {
   REQUIRE(s != nullptr, CSA_INVALID_ARGUMENT, "step must not be NULL");
   REQUIRE(s->B >= 0, CSA_INVALID_ARGUMENT, "B must be >= 0");
-  REQUIRE(s->flags == 0, CSA_INVALID_ARGUMENT, "flags must be 0 (no flags are defined)");
+  REQUIRE((s->flags & ~(unsigned)CSA_STEP_FUSED_TAIL) == 0, CSA_INVALID_ARGUMENT,
+          "flags holds undefined bits (0x%x)", s->flags);
   if (s->B == 0) return ok();
   REQUIRE(s->H >= 1 && s->Nc_cap >= 1 && s->m_prime >= 1 && s->topk >= 1, CSA_INVALID_ARGUMENT,
           "H, Nc_cap, m_prime and topk must be >= 1");
@@ -470,8 +474,21 @@ csa_status_t csa_hybrid_decode_step(const csa_decode_step_t* s, void* workspace,
                  s->hout, s->hlse_out, ws ? ws + wl.hca : nullptr, wl.total - wl.hca, &ah, &eh);
   if (st != CSA_OK) return fail(st, "HCA part: %s", g_err.c_str());
   REQUIRE(s->out != s->hout, CSA_INVALID_ARGUMENT, "the CSA and HCA outputs are the same buffer");
-  hipError_t e = csa::launch_indexer_topk(ai, (hipStream_t)stream);
-  if (e == hipSuccess) e = csa::launch_attend_pair(ac, ah, (hipStream_t)stream);
+  hipError_t e = hipSuccess;
+  const bool fused = (s->flags & CSA_STEP_FUSED_TAIL) && !ei && !ec && !eh &&
+                     csa::indexer_long_path(ai) && csa::decode_tail_supported(ac, ah);
+  if (fused) {
+    unsigned long long* counters = nullptr;
+    e = csa::counters_device_ptr(&counters);
+    // the row picks as their own 1024-thread launch (a 256-thread pick inside
+    // the tail measured twice as long), then attention and merges in one launch
+    if (e == hipSuccess) e = csa::launch_indexer_topk(ai, (hipStream_t)stream);
+    if (e == hipSuccess)
+      e = csa::launch_decode_tail(ai, ac, ah, ws + wl.ctl, counters, false, (hipStream_t)stream);
+  } else {
+    e = csa::launch_indexer_topk(ai, (hipStream_t)stream);
+    if (e == hipSuccess) e = csa::launch_attend_pair(ac, ah, (hipStream_t)stream);
+  }
   return device_status(e, "csa_hybrid_decode_step launch");
 }
 

@@ -60,11 +60,17 @@ __device__ __forceinline__ int vt_block(int dim, int kb) { return kb ^ ((dim >> 
 // at once).  Every instance fits 256 VGPRs, two waves per SIMD, so two
 // workgroups share a compute unit and one's loads overlap the other's math.
 // The body takes its workgroup's coordinates (token tile bx, split by,
-// sequence bz) and the dynamic LDS block from the kernel that runs it.
-template <typename T, int D, int RW, int KG, bool SPARSE, int PF, bool KV8 = false, bool VSH = false>
+// sequence bz) and the dynamic LDS block from the kernel that runs it.  COH
+// (bit mask): COH_IDX reads the index row, COH_PART writes the split partials
+// with device-scope (sc1) accesses, coherent across the XCDs' L2 caches, for
+// an index producer or a merge running in the same launch.
+static constexpr int COH_IDX = 1, COH_PART = 2;
+template <typename T, int D, int RW, int KG, bool SPARSE, int PF, bool KV8 = false, bool VSH = false,
+          int COH = 0>
 __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom& gm, int bx, int by,
                                             int bz, unsigned char* smem_raw) {
   static_assert(!KV8 || sizeof(T) == 2, "FP8 caches go with bf16 queries");
+  constexpr int IDX_AUX = (COH & COH_IDX) ? 16 : 0;   // buffer-load cache policy: sc1 (device scope)
   static_assert(KV8 || !VSH, "a shared value entry is an FP8-cache layout");
   constexpr int NW = RW * KG;
   constexpr int NT = NW * 64;
@@ -143,7 +149,7 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
       sel_base = kbeg;
       const int ns = max(0, min(gm.kps, a.topk - kbeg));
       for (int i = tid; i < ns; i += NT)
-        sel[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(ri, (uint32_t)(kbeg + i) * 4, 0, 0);
+        sel[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(ri, (uint32_t)(kbeg + i) * 4, 0, IDX_AUX);
       __syncthreads();
     } else {
       // one workgroup per token: compact the valid entries into LDS; each
@@ -155,7 +161,7 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
 #pragma unroll
       for (int q = 0; q < RUN; ++q) {
         const int i = i0 + q;
-        const int v = (int)__builtin_amdgcn_raw_buffer_load_b32(ri, i < a.topk ? (uint32_t)i * 4 : OOB, 0, 0);
+        const int v = (int)__builtin_amdgcn_raw_buffer_load_b32(ri, i < a.topk ? (uint32_t)i * 4 : OOB, 0, IDX_AUX);
         ev[q] = i < a.topk ? v : -1;
       }
 #pragma unroll
@@ -584,16 +590,35 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
     for (int i = 0; i < DVT; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        if constexpr (sizeof(T) == 2)
-          *reinterpret_cast<uint2*>(po + i * 32 + 8 * g + 4 * half) =
+        T* dst = po + i * 32 + 8 * g + 4 * half;
+        if constexpr ((COH & COH_PART) != 0) {
+          if constexpr (sizeof(T) == 2) {
+            const uint64_t v = (uint64_t)pack_bf16x2(o[i][4 * g], o[i][4 * g + 1]) |
+                               ((uint64_t)pack_bf16x2(o[i][4 * g + 2], o[i][4 * g + 3]) << 32);
+            __hip_atomic_store(reinterpret_cast<uint64_t*>(dst), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              __hip_atomic_store(reinterpret_cast<uint32_t*>(dst) + u, __float_as_uint(o[i][4 * g + u]),
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        } else if constexpr (sizeof(T) == 2) {
+          *reinterpret_cast<uint2*>(dst) =
               uint2{pack_bf16x2(o[i][4 * g], o[i][4 * g + 1]), pack_bf16x2(o[i][4 * g + 2], o[i][4 * g + 3])};
-        else
-          *reinterpret_cast<f32x4*>(po + i * 32 + 8 * g + 4 * half) =
-              f32x4{o[i][4 * g], o[i][4 * g + 1], o[i][4 * g + 2], o[i][4 * g + 3]};
+        } else {
+          *reinterpret_cast<f32x4*>(dst) = f32x4{o[i][4 * g], o[i][4 * g + 1], o[i][4 * g + 2], o[i][4 * g + 3]};
+        }
       }
     if (half == 0) {
-      pm[(size_t)split * rows_total + grow] = m_run;
-      pl[(size_t)split * rows_total + grow] = l_tot;
+      if constexpr ((COH & COH_PART) != 0) {
+        __hip_atomic_store(reinterpret_cast<uint32_t*>(pm) + (size_t)split * rows_total + grow,
+                           __float_as_uint(m_run), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(reinterpret_cast<uint32_t*>(pl) + (size_t)split * rows_total + grow,
+                           __float_as_uint(l_tot), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        pm[(size_t)split * rows_total + grow] = m_run;
+        pl[(size_t)split * rows_total + grow] = l_tot;
+      }
     }
     return;
   }
@@ -654,8 +679,12 @@ __global__ __launch_bounds__(RW * KG * 64) __attribute__((amdgpu_waves_per_eu(2)
 // Merge split partials in fixed split order (one wave per query row).  The
 // partials of CB splits are requested together; a running maximum rescales
 // the sums between batches, so the result depends only on the split list.
-template <typename T, int D>
+// COH: the partials are read with device-scope (sc1) loads (written in the
+// same launch, possibly through another XCD's L2).
+template <typename T, int D, bool COH = false>
 __device__ __forceinline__ void combine_row(const AttendArgs& a, int nsplit, size_t row) {
+  static_assert(!COH || (D / 64) * sizeof(T) == 4 || (D / 64) * sizeof(T) == 8,
+                "device-scope partial loads take 4 or 8 bytes per lane");
   constexpr int PER = D / 64;
   constexpr int CB = 32;
   const int lane = threadIdx.x & 63;
@@ -676,13 +705,36 @@ __device__ __forceinline__ void combine_row(const AttendArgs& a, int nsplit, siz
     float v[CB][PER];
     const int sl = min(s0 + (lane & (CB - 1)), nsplit - 1);
     const bool lv_ok = lane < CB && s0 + lane < nsplit;
-    const float mraw = pm[(size_t)sl * rows_total + row];
-    const float lraw = pl[(size_t)sl * rows_total + row];
+    float mraw, lraw;
+    if constexpr (COH) {
+      mraw = __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t*>(pm) + (size_t)sl * rows_total + row,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      lraw = __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t*>(pl) + (size_t)sl * rows_total + row,
+                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    } else {
+      mraw = pm[(size_t)sl * rows_total + row];
+      lraw = pl[(size_t)sl * rows_total + row];
+    }
 #pragma unroll
     for (int j = 0; j < CB; ++j) {
       const T* src = po + ((size_t)min(s0 + j, nsplit - 1) * rows_total + row) * D + lane * PER;
+      if constexpr (COH) {
+        T t[PER];
+        if constexpr (PER * sizeof(T) == 4) {
+          const uint32_t w = __hip_atomic_load(reinterpret_cast<const uint32_t*>(src), __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+          __builtin_memcpy(t, &w, 4);
+        } else {
+          const uint64_t w = __hip_atomic_load(reinterpret_cast<const uint64_t*>(src), __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+          __builtin_memcpy(t, &w, 8);
+        }
 #pragma unroll
-      for (int u = 0; u < PER; ++u) v[j][u] = to_f32(src[u]);
+        for (int u = 0; u < PER; ++u) v[j][u] = to_f32(t[u]);
+      } else {
+#pragma unroll
+        for (int u = 0; u < PER; ++u) v[j][u] = to_f32(src[u]);
+      }
     }
     const float mv = lv_ok ? mraw : -INFINITY;
     const float lv = lv_ok ? lraw : 0.f;

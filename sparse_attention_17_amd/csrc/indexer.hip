@@ -34,8 +34,10 @@
 //     low 20 bits, lowest index among ties) and sorts the k indices.  A row
 //     whose boundary bin overflows the candidate buffer falls back to the
 //     exact single-workgroup select over the stored scores.
-#include "common.hpp"
-#include "launch.hpp"
+#include "pick_impl.hpp"
+
+#include <map>
+#include <mutex>
 
 namespace csa {
 
@@ -48,18 +50,8 @@ __device__ __forceinline__ void count_event(int which) {
 }
 
 static constexpr int SCORE_WG_ENTRIES = 256;   // prefill tile kernel: 4 waves x 4 tiles x 16
-// decode score kernels: entries per chunk (one chunk per workgroup; 1024
-// gives two rounds of resident workgroups on a 1M-entry batch, so one round's
-// chunk cuts overlap the other's loads)
-static constexpr int SCORE_CHUNK = 1024;
 static constexpr int SCORE_CPW = 1;            // chunks per score_row_kernel workgroup
 static constexpr int SCORE_DEPTH = 3;          // entry groups in flight per wave
-static constexpr int H1_BITS = 12;             // first radix digit (key bits 20..31)
-static constexpr int H1_BINS = 1 << H1_BITS;
-static constexpr int TOPK_NT = 512;
-static constexpr int TOPK_LDS_KEYS = 12288;
-
-__host__ __device__ __forceinline__ int nc_pad(int Nc_cap) { return (Nc_cap + 63) & ~63; }
 
 // ---------------- operand loaders: 8 k-values -> one fragment --------------
 template <int QK> struct QkTraits;
@@ -163,104 +155,7 @@ template <int QK> __host__ __device__ __forceinline__ size_t qk_row_bytes(int dI
   else return (size_t)dI / 2;
 }
 
-__device__ __forceinline__ int row_len(const IndexerArgs& a, int b, int t) {
-  return max(0, min((a.pos0[b] + t + 1) / a.m, a.Nc_cap));
-}
-
-// Workspace carve-up for the long-row path (per query row; nch = score chunks):
-//   scores [rows][ldo] f32 | meta [rows][nch][2] u32 (kept count, cut) |
-//   cand [rows][nch * SCORE_CHUNK][2] u32 (key, entry), chunk c's kept entries
-//   at slots c * cap ..  (cap = the row's per-chunk capacity)
-// Every score workgroup owns one chunk's slots, so no atomics are needed.
-struct LongWs {
-  float* scores;
-  uint32_t *meta, *cand;
-  int nch;
-};
-__host__ __device__ __forceinline__ int row_chunks(int Nc_cap) { return (Nc_cap + SCORE_CHUNK - 1) / SCORE_CHUNK; }
-__host__ __device__ __forceinline__ LongWs long_ws(void* ws, int rows, int Nc_cap) {
-  LongWs w;
-  w.nch = row_chunks(Nc_cap);
-  char* p = reinterpret_cast<char*>(ws);
-  w.scores = reinterpret_cast<float*>(p);
-  p += (size_t)rows * nc_pad(Nc_cap) * 4;
-  w.meta = reinterpret_cast<uint32_t*>(p);
-  p += (size_t)rows * ((w.nch * 2 + 3) & ~3) * 4;
-  w.cand = reinterpret_cast<uint32_t*>(p);
-  return w;
-}
-static size_t long_ws_bytes(int rows, int Nc_cap) {
-  const int nch = row_chunks(Nc_cap);
-  return (size_t)rows * ((size_t)nc_pad(Nc_cap) * 4 + (size_t)((nch * 2 + 3) & ~3) * 4 +
-                         (size_t)nch * SCORE_CHUNK * 8);
-}
-// Candidate slots per chunk for the row select: a power of two in
-// [32, SCORE_CHUNK] near four times the chunk's expected share of the top k;
-// the chunk keeps its kc = 3/4 of that (three times its share) largest keys
-// plus whatever shares the kc-th key's 20-bit prefix, up to the slots.
-__host__ __device__ __forceinline__ int chunk_cap_n(int k, int n) {
-  const long long want = (4LL * k * SCORE_CHUNK + n - 1) / n;
-  int cap = 32;
-  while (cap < want && cap < SCORE_CHUNK) cap <<= 1;
-  return cap;
-}
-__host__ __device__ __forceinline__ int chunk_keep(int k, int n) {
-  const int cap = chunk_cap_n(k, n);
-  return cap < SCORE_CHUNK ? cap - cap / 4 : SCORE_CHUNK;
-}
-static constexpr uint32_t CUT_ALL = 0xFFFFFFFFu;   // the chunk kept every entry
 static bool use_long_path(int Tq, int Nc_cap) { return Tq <= 4 && Nc_cap > TOPK_LDS_KEYS; }
-
-// Scanning bins from the top down, find the bin where the running count first
-// reaches `need`; out[0] = bin, out[1] = count strictly above it.
-template <int NT>
-__device__ void find_bin(const uint32_t* hist, int nbins, uint32_t need, uint32_t* scan,
-                         uint32_t* out) {
-  const int per = nbins / NT;
-  const int tid = threadIdx.x;
-  const int hi = nbins - tid * per;
-  uint32_t local = 0;
-  for (int i = 0; i < per; ++i) local += hist[hi - 1 - i];
-  uint32_t tot;
-  const uint32_t excl = block_excl_scan<NT>(local, scan, &tot);
-  if (excl < need && excl + local >= need) {
-    uint32_t cum = excl;
-    for (int i = 0; i < per; ++i) {
-      const uint32_t h = hist[hi - 1 - i];
-      if (cum + h >= need) { out[0] = hi - 1 - i; out[1] = cum; break; }
-      cum += h;
-    }
-  }
-  __syncthreads();
-}
-
-// Top-down search within a wave: given cnt(i) for bins [0, nb) (nb = 64*per),
-// the bin where the running count from the top first reaches `need`, and the
-// count strictly above it (all lanes get the result).
-template <typename Cnt>
-__device__ __forceinline__ void wave_top_bin(int per, uint32_t need, Cnt cnt, uint32_t& bin,
-                                             uint32_t& above) {
-  const int lane = threadIdx.x & 63;
-  const int hi = 64 * per - lane * per;
-  uint32_t local = 0;
-  for (int i = 0; i < per; ++i) local += cnt(hi - 1 - i);
-  const uint32_t incl = wave_incl_scan(local);
-  const uint32_t excl = incl - local;
-  const bool mine = excl < need && incl >= need;
-  uint32_t bb = 0, ab = 0;
-  if (mine) {
-    uint32_t cum = excl;
-    for (int i = 0; i < per; ++i) {
-      const uint32_t h = cnt(hi - 1 - i);
-      if (cum + h >= need) { bb = hi - 1 - i; ab = cum; break; }
-      cum += h;
-    }
-  }
-  const uint64_t m = __ballot(mine);
-  const int src = m ? __ffsll((unsigned long long)m) - 1 : 0;
-  bin = (uint32_t)__builtin_amdgcn_readlane((int)bb, src);
-  above = (uint32_t)__builtin_amdgcn_readlane((int)ab, src);
-}
 
 // End of a decode score workgroup (256 threads): keep the chunk's entries at
 // or above its cut, in index order, in the chunk's candidate slots.  The cut
@@ -480,31 +375,20 @@ __global__ __launch_bounds__(256) void score_row_kernel(IndexerArgs a) {
   const char* qptr = reinterpret_cast<const char*>(a.qi) + qrow * qk_row_bytes<QK>(DI);
   const uint8_t* qsc = nullptr;
   if constexpr (QK == QK_FP4) qsc = reinterpret_cast<const uint8_t*>(a.qi_scale) + qrow * (DI / 32);
-  // FP8: the codes themselves are the operands of the FP8 MFMA (E4M3 x E4M3
-  // products are exact in its fp32 accumulation, as in the bf16 MFMA on the
-  // exactly widened codes); the row scales multiply the weights and scores.
-  constexpr bool NATIVE8 = QK == QK_FP8;
-  F qa[NATIVE8 ? 1 : TPC][KC];
-  uint64_t qa8[NATIVE8 ? TPC : 1][KC];
-  if constexpr (NATIVE8) {
+  // FP8 codes are widened exactly to bf16 and multiplied on the bf16 MFMA,
+  // which accumulates in fp32; the native FP8 MFMA was measured on gfx950 at
+  // ~1e-5 relative error in these sums, outside the 1e-6 near-tie band.
+  F qv[KC];
+#pragma unroll
+  for (int c = 0; c < KC; ++c) load_qk_frag<QK>(qv[c], qptr, qsc, 8 * (g * KC + c));
+  F qa[TPC][KC];
+#pragma unroll
+  for (int u = 0; u < TPC; ++u)
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
-      const uint64_t qc = *reinterpret_cast<const uint64_t*>(qptr + 8 * (g * KC + c));
-#pragma unroll
-      for (int u = 0; u < TPC; ++u) qa8[u][c] = u == uq ? qc : 0ull;
+      if (u == uq) qa[u][c] = qv[c];
+      else frag_zero(qa[u][c]);
     }
-  } else {
-    F qv[KC];
-#pragma unroll
-    for (int c = 0; c < KC; ++c) load_qk_frag<QK>(qv[c], qptr, qsc, 8 * (g * KC + c));
-#pragma unroll
-    for (int u = 0; u < TPC; ++u)
-#pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        if (u == uq) qa[u][c] = qv[c];
-        else frag_zero(qa[u][c]);
-      }
-  }
   // weights of the head rows this lane receives: rows 4g+i -> head (4g+i) % HI
   float wr[4];
 #pragma unroll
@@ -522,13 +406,7 @@ __global__ __launch_bounds__(256) void score_row_kernel(IndexerArgs a) {
 #pragma unroll
     for (int u = 0; u < TPC; ++u)
 #pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        if constexpr (NATIVE8)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8((long)qa8[u][c], __builtin_bit_cast(long, cur[u][c].c),
-                                                          acc, 0, 0, 0);
-        else
-          mma16(acc, qa[u][c], widen<QK>(cur[u][c]));
-      }
+      for (int c = 0; c < KC; ++c) mma16(acc, qa[u][c], widen<QK>(cur[u][c]));
 #pragma unroll
     for (int s = 0; s < SPL; ++s) {
       const int u = (4 * g) / HI + s;
@@ -680,68 +558,6 @@ __global__ __launch_bounds__(256) void score_row_fp4_kernel(IndexerArgs a) {
   if (n > a.topk) chunk_cut(a, L, row, chunk, n, c0, c1 - c0, sk, hist, cut_ws);
 }
 
-// --------------------------- shared select helpers --------------------------
-template <int NT>
-struct TopkSmem {
-  uint32_t hist[2048];
-  uint32_t scan[NT / 64];
-  uint32_t res[2];
-};
-
-// Exact select of one row whose keys are in `row` (LDS or global), n > k.
-template <int NT>
-__device__ void select_row(TopkSmem<NT>& sm, const uint32_t* __restrict__ row, int n, int k,
-                           int32_t* __restrict__ idx_out, float* __restrict__ score_out) {
-  const int tid = threadIdx.x;
-  uint32_t prefix = 0, pmask = 0, need = (uint32_t)k;
-  if (tid == 0) { sm.res[0] = 0; sm.res[1] = 0; }
-#pragma unroll 1
-  for (int p = 0; p < 3; ++p) {
-    const int sh = p == 0 ? 21 : (p == 1 ? 10 : 0);
-    const int nb = p == 2 ? 1024 : 2048;
-    for (int i = tid; i < nb; i += NT) sm.hist[i] = 0;
-    __syncthreads();
-    for (int i = tid; i < n; i += NT) {
-      const uint32_t key = row[i];
-      if ((key & pmask) == prefix) atomicAdd(&sm.hist[(key >> sh) & (nb - 1)], 1u);
-    }
-    __syncthreads();
-    find_bin<NT>(sm.hist, nb, need, sm.scan, sm.res);
-    prefix |= sm.res[0] << sh;
-    pmask |= (uint32_t)(nb - 1) << sh;
-    need -= sm.res[1];
-    __syncthreads();
-  }
-  const uint32_t tau = prefix, need_eq = need;
-  uint32_t base = 0, eq_seen = 0;
-#pragma unroll 1
-  for (int c0 = 0; c0 < n; c0 += NT) {
-    const int i = c0 + tid;
-    const uint32_t key = i < n ? row[i] : 0u;
-    const uint32_t is_gt = (i < n && key > tau) ? 1u : 0u;
-    const uint32_t is_eq = (i < n && key == tau) ? 1u : 0u;
-    uint32_t tot_eq;
-    const uint32_t eq_x = block_excl_scan<NT>(is_eq, sm.scan, &tot_eq);
-    const uint32_t take = is_gt | ((is_eq && eq_seen + eq_x < need_eq) ? 1u : 0u);
-    uint32_t tot_take;
-    const uint32_t pos = block_excl_scan<NT>(take, sm.scan, &tot_take);
-    if (take && base + pos < (uint32_t)k) {
-      idx_out[base + pos] = i;
-      if (score_out) score_out[base + pos] = __uint_as_float(key);
-    }
-    base += tot_take;
-    eq_seen += tot_eq;
-    if (base >= (uint32_t)k) break;
-  }
-}
-
-__device__ __forceinline__ void write_all_eligible(int n, int k, const uint32_t* src,
-                                                   int32_t* idx, float* sco, int nt) {
-  for (int i = threadIdx.x; i < k; i += nt) {
-    idx[i] = i < n ? i : -1;
-    if (sco) sco[i] = i < n ? __uint_as_float(src[i]) : -INFINITY;
-  }
-}
 
 // ------------------------- per-row LDS top-k kernel -------------------------
 __global__ __launch_bounds__(TOPK_NT) void topk_row_kernel(IndexerArgs a) {
@@ -767,292 +583,56 @@ __global__ __launch_bounds__(TOPK_NT) void topk_row_kernel(IndexerArgs a) {
   }
 }
 
+
 // ------------------------------ long-row path ------------------------------
-// One workgroup per query row picks the row's k largest keys among the
-// chunks' candidates.  Candidate slot (chunk c, j) holds the j-th kept entry
-// of chunk c; slots in (c, j) order are in ascending entry order, so the
-// lowest-index rule among equal keys is slot order and the output needs no
-// sort.  The pick is exact when every chunk's dropped entries lie below the
-// selected threshold tau (tau >= cut << 12) and no chunk overflowed its slots;
-// otherwise the row is selected exactly from the stored scores.
-static constexpr int PICK_NT = 1024;
-static constexpr int PICK_NW = PICK_NT / 64;
-static constexpr int PICK_MAXCH = 4096;        // rows up to 8M entries
-static constexpr int PICK_MAXPER = 30;         // candidate slots per thread, largest body
-static constexpr int PICK_WORDS = PICK_MAXPER * PICK_NT / 32;
-static constexpr int PICK_STASH = 16384;       // slots whose selected entry is kept in LDS
-static constexpr int PICK_BINS = 4096;         // 12-bit radix digits
-
-struct PickSmem {
-  uint32_t hist[2][PICK_BINS];                 // alternating digit histograms
-  uint32_t ccnt[PICK_MAXCH];                   // kept count per chunk (clamped to cap)
-  uint32_t ccut[PICK_MAXCH];                   // cut key prefix per chunk
-  uint32_t bm_gt[PICK_WORDS];                  // output bitmaps over slots
-  uint32_t bm_eq[PICK_WORDS];
-  uint32_t sel[PICK_STASH];                    // entry index of selected slots
-  uint32_t wv[4][PICK_NW];                     // per-wave partials
-  uint32_t res[3];                             // bin, count above it, count in it
-};
-static_assert(sizeof(TopkSmem<PICK_NT>) <= sizeof(PickSmem), "fallback select aliases PickSmem");
-
-// Sum of the per-wave totals w[0 .. wave-1] (wave = this thread's wave):
-// lane i < PICK_NW reads w[i] once and a masked wave sum replaces a serial
-// walk over the totals.
-__device__ __forceinline__ uint32_t waves_below(const uint32_t* w, int wave) {
-  const int lane = threadIdx.x & 63;
-  return wave_sum_u32(lane < wave ? w[lane] : 0u);           // wave < PICK_NW <= 64
-}
-
-struct PickRow {
-  int row, n, k, nch, cap, lg, nslot;
-  const uint2* meta;
-  const uint2* cand;
-  const uint32_t* src;
-  int32_t* idx;
-  float* sco;
-};
-
-// Select for one row whose nslot fits PER slots per thread.  Slot s holds
-// (key, entry) of the (s mod cap)-th kept entry of chunk s / cap; thread tid
-// holds slots q * PICK_NT + tid (coalesced loads).  Every loop runs exactly
-// PER times, and the output bitmaps are built from wave ballots.
-template <int PER>
-__device__ __forceinline__ void pick_body(PickSmem& sm, const PickRow& R) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  constexpr uint2 EMPTY = {0u, 0xFFFFFFFFu};
-  const int k = R.k, cap = R.cap, lg = R.lg, nslot = R.nslot, nch = R.nch;
-
-  // ---- 1. candidate slots and chunk records, requested together ----
-  uint2 kv[PER];
-#pragma unroll
-  for (int q = 0; q < PER; ++q) kv[q] = R.cand[min(q * PICK_NT + tid, nslot - 1)];
-  uint32_t part = 0;
-  int bad = 0;
-  for (int c = tid; c < nch; c += PICK_NT) {
-    const uint2 r = R.meta[c];
-    sm.ccnt[c] = min(r.x, (uint32_t)cap);
-    sm.ccut[c] = r.y;
-    bad |= r.x > (uint32_t)cap;
-    part += min(r.x, (uint32_t)cap);
-  }
-  for (int i = tid; i < PICK_BINS; i += PICK_NT) sm.hist[0][i] = 0;
-  __syncthreads();
-
-  // ---- 2. mask empty slots; candidate total, key range, overflow ----
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0;
-#pragma unroll
-  for (int q = 0; q < PER; ++q) {
-    const int s = q * PICK_NT + tid;
-    const bool ok = s < nslot && (s & (cap - 1)) < (int)sm.ccnt[min(s >> lg, PICK_MAXCH - 1)];
-    kv[q].x = ok ? kv[q].x : EMPTY.x;
-    kv[q].y = ok ? kv[q].y : EMPTY.y;
-    kmin = ok ? min(kmin, kv[q].x) : kmin;
-    kmax = ok ? max(kmax, kv[q].x) : kmax;
-  }
-  kmin = wave_min_u32(kmin);
-  kmax = wave_max_u32(kmax);
-  part = wave_sum_u32(part);
-  bad = wave_max_u32((uint32_t)bad) != 0u;
-  if (lane == 0) { sm.wv[0][wave] = part; sm.wv[1][wave] = kmin; sm.wv[2][wave] = kmax; sm.wv[3][wave] = bad; }
-  __syncthreads();
-  uint32_t total = 0;
-  kmin = 0xFFFFFFFFu; kmax = 0; bad = 0;
-#pragma unroll
-  for (int w = 0; w < PICK_NW; ++w) {
-    total += sm.wv[0][w];
-    kmin = min(kmin, sm.wv[1][w]);
-    kmax = max(kmax, sm.wv[2][w]);
-    bad |= sm.wv[3][w];
-  }
-  bad |= total < (uint32_t)k;
-
-  // ---- 3. exact radix select of the k-th largest candidate key ----
-  // The candidates are the tops of their chunks and share leading bits, so
-  // the 12-bit digits start at the highest bit where the smallest and largest
-  // key differ; that spreads them over the bins.
-  uint32_t tau = kmin, need = (uint32_t)k;
-  if (!bad && kmin != kmax) {
-    const int top = 31 - __clz((int)(kmin ^ kmax));
-    uint32_t prefix = top >= 31 ? 0u : (kmin & ~((2u << top) - 1u));
-    uint32_t pmask = top >= 31 ? 0u : ~((2u << top) - 1u);
-    int buf = 0;
-#pragma unroll 1
-    for (int hi = top; hi >= 0; hi -= 12) {
-      const int sh = hi >= 11 ? hi - 11 : 0;
-      const int nb = 1 << (hi - sh + 1);
-      const int nbs = max(nb, PICK_NT);                       // bins scanned
-      uint32_t* hist = sm.hist[buf];
-      for (int i = tid; i < PICK_BINS; i += PICK_NT) sm.hist[buf ^ 1][i] = 0;   // next pass's buffer
-#pragma unroll
-      for (int q = 0; q < PER; ++q) {
-        const uint2 v = kv[q];
-        if (v.y != EMPTY.y && (v.x & pmask) == prefix) atomicAdd(&hist[(v.x >> sh) & (nb - 1)], 1u);
-      }
-      __syncthreads();
-      // top-down scan: thread tid owns bins [nbs - pb*(tid+1), nbs - pb*tid)
-      const int pb = nbs / PICK_NT;
-      const int hb = nbs - pb * tid;
-      uint32_t local = 0;
-      for (int i = 0; i < pb; ++i) local += hist[hb - 1 - i];
-      const uint32_t incl = wave_incl_scan(local);
-      if (lane == 63) sm.wv[0][wave] = incl;
-      __syncthreads();
-      uint32_t before = incl - local;
-      before += waves_below(sm.wv[0], wave);
-      if (before < need && before + local >= need) {
-        uint32_t cum = before;
-        for (int i = 0; i < pb; ++i) {
-          const uint32_t h = hist[hb - 1 - i];
-          if (cum + h >= need) {
-            sm.res[0] = (uint32_t)(hb - 1 - i); sm.res[1] = cum; sm.res[2] = h;
-            break;
-          }
-          cum += h;
-        }
-      }
-      __syncthreads();
-      prefix |= sm.res[0] << sh;
-      pmask |= (uint32_t)(nb - 1) << sh;
-      need -= sm.res[1];
-      buf ^= 1;
-      // Every key in the bin is taken: tau = the bin's floor (bits below sh
-      // zero) then selects the same set (the keys above it plus the whole bin)
-      // and the later passes are skipped.  Only for sh <= 12, where the floor
-      // and the k-th key compare alike against the chunk cuts (multiples of
-      // 2^12) in the safety check below.
-      if (sm.res[2] == need && sh <= 12) break;
-    }
-    tau = prefix;
-  }
-  // the chunks' dropped entries must all lie below tau
-  int unsafe = bad;
-  if (!bad)
-    for (int c = tid; c < nch; c += PICK_NT) {
-      const uint32_t cut = sm.ccut[c];
-      unsafe |= cut != CUT_ALL && tau < (cut << 12);
-    }
-  // slot bitmaps of keys > tau and keys == tau, one ballot per 64 slots (each
-  // word has one writer: no atomics, no clearing); selected entries kept
-#pragma unroll
-  for (int q = 0; q < PER; ++q) {
-    const uint2 v = kv[q];
-    const int s = q * PICK_NT + tid;
-    const bool valid = v.y != EMPTY.y;
-    const bool gt = valid && v.x > tau, eq = valid && v.x == tau;
-    if ((gt || eq) && s < PICK_STASH) sm.sel[s] = v.y;
-    const uint64_t bg = __ballot(gt), be = __ballot(eq);
-    if (lane == 0) {
-      const int w0 = (q * PICK_NT + wave * 64) >> 5;
-      sm.bm_gt[w0] = (uint32_t)bg;
-      sm.bm_gt[w0 + 1] = (uint32_t)(bg >> 32);
-      sm.bm_eq[w0] = (uint32_t)be;
-      sm.bm_eq[w0 + 1] = (uint32_t)(be >> 32);
-    }
-  }
-  if (__syncthreads_or(unsafe)) {
-    if (tid == 0) count_event(CNT_DECODE_FALLBACK);
-    select_row<PICK_NT>(*reinterpret_cast<TopkSmem<PICK_NT>*>(&sm.hist[0][0]), R.src, R.n, k, R.idx, R.sco);
-    return;
-  }
-
-  // ---- 4. output in slot order (= ascending entry order): the bitmap words
-  // are split into Q parts of L slots, thread tid owning part tid % Q of word
-  // tid / Q (so the threads hold the slots in order): keys > tau, and the
-  // first `need` keys == tau over the whole row ----
-  constexpr int NWORDS = PER * PICK_NT / 32;
-  constexpr int Q = PICK_NT / NWORDS >= 4 ? 4 : PICK_NT / NWORDS >= 2 ? 2 : 1;
-  constexpr int L = 32 / Q;
-  constexpr uint32_t LMASK = L == 32 ? 0xFFFFFFFFu : (1u << L) - 1u;
-  const int word = tid / Q, wpart = tid % Q;
-  const uint32_t wgt = word < NWORDS ? (sm.bm_gt[word] >> (wpart * L)) & LMASK : 0u;
-  const uint32_t weq = word < NWORDS ? (sm.bm_eq[word] >> (wpart * L)) & LMASK : 0u;
-  const uint32_t pgt = (uint32_t)__popc(wgt), peq = (uint32_t)__popc(weq);
-  const uint32_t inc_gt = wave_incl_scan(pgt), inc_eq = wave_incl_scan(peq);
-  if (lane == 63) { sm.wv[1][wave] = inc_gt; sm.wv[2][wave] = inc_eq; }
-  __syncthreads();
-  uint32_t gt_before = inc_gt - pgt, eq_before = inc_eq - peq;
-  gt_before += waves_below(sm.wv[1], wave);
-  eq_before += waves_below(sm.wv[2], wave);
-  uint32_t pos = gt_before + min(eq_before, need);
-  uint32_t e_seen = eq_before;
-  uint32_t take = wgt;
-  for (uint32_t m = weq; m; m &= m - 1) {
-    const int bit = __ffs(m) - 1;
-    if (e_seen++ < need) take |= 1u << bit;
-  }
-  const int s0 = word * 32 + wpart * L;
-  for (; take; take &= take - 1) {
-    const int s = s0 + __ffs(take) - 1;
-    if (pos < (uint32_t)k) {
-      R.idx[pos] = (int32_t)(s < PICK_STASH ? sm.sel[s] : R.cand[s].y);
-      if (R.sco) R.sco[pos] = __uint_as_float(R.cand[s].x);
-    }
-    ++pos;
-  }
-}
-
-// One workgroup per row: the row's geometry, then the body specialised for
-// its slots per thread (a uniform branch).
-__global__ __launch_bounds__(PICK_NT) void long_pick_kernel(IndexerArgs a) {
-  __shared__ PickSmem sm;
-  PickRow R;
-  R.row = blockIdx.x;
-  const int b = R.row / a.Tq, t = R.row % a.Tq;
-  R.k = a.topk;
-  const LongWs L = long_ws(a.ws, a.B * a.Tq, a.Nc_cap);
-  R.idx = a.idx_out + (size_t)R.row * R.k;
-  R.sco = a.score_out ? a.score_out + (size_t)R.row * R.k : nullptr;
-  R.src = reinterpret_cast<const uint32_t*>(L.scores) + (size_t)R.row * nc_pad(a.Nc_cap);
-  R.meta = reinterpret_cast<const uint2*>(L.meta) + (size_t)R.row * L.nch;
-  R.cand = reinterpret_cast<const uint2*>(L.cand) + (size_t)R.row * L.nch * SCORE_CHUNK;
-  R.n = row_len(a, b, t);
-  if (R.n <= R.k) {
-    write_all_eligible(R.n, R.k, R.src, R.idx, R.sco, PICK_NT);
-    return;
-  }
-  R.nch = (R.n + SCORE_CHUNK - 1) / SCORE_CHUNK;
-  R.cap = chunk_cap_n(R.k, R.n);
-  R.lg = 31 - __clz(R.cap);                                  // cap is a power of two
-  R.nslot = R.nch << R.lg;                                   // <= L.nch * SCORE_CHUNK
-  const int per = (R.nslot + PICK_NT - 1) / PICK_NT;
-  if (per > PICK_MAXPER || R.nch > PICK_MAXCH) {
-    if (threadIdx.x == 0) count_event(CNT_DECODE_FALLBACK);
-    select_row<PICK_NT>(*reinterpret_cast<TopkSmem<PICK_NT>*>(&sm.hist[0][0]), R.src, R.n, R.k, R.idx, R.sco);
-    return;
-  }
-  if (per <= 8) pick_body<8>(sm, R);
-  else if (per <= 16) pick_body<16>(sm, R);
-  else pick_body<PICK_MAXPER>(sm, R);
+// One 1024-thread workgroup per query row picks the row's k largest keys among
+// the chunks' candidates (pick_row).
+__global__ __launch_bounds__(1024) void long_pick_kernel(IndexerArgs a) {
+  __shared__ PickSmem<1024> sm;
+  pick_row<1024>(sm, a, blockIdx.x, g_counters);
 }
 
 // --------------------------- fused prefill path ----------------------------
 // One workgroup (8 waves) per FQ consecutive query tokens.  Scores never reach
-// HBM: the eligible indexer keys are streamed twice (from L2) and the scores
-// recomputed on MFMA each time.
-//   pass 1: an 11-bit radix histogram of each token's score keys in LDS (bits
-//           30..20 — bit 31 is the sign, always 0 here — as two 16-bit counters
-//           per word); two tokens per wave then find the bin b1 holding the
-//           k-th largest key and the count above it;
-//   pass 2: entries whose digit is above b1 set their bit in the token's LDS
-//           selection bitmap, entries inside b1 append (key, index) to the
-//           token's candidate slots;
-//   resolve: per token, a radix select over the low 20 bits of the candidates
-//           (lowest index among equal keys) marks the remaining winners in the
-//           bitmap, which is then written out as the ascending index list.
-// A token whose boundary bin overflows its candidate slots is rescored into the
-// workspace and selected by the exact block-wide select.
+// HBM; the eligible indexer keys stream from L2 and the scores are computed on
+// MFMA.
+//   sample: the scores of one 128-entry step in every FSAMPLE (a block-strided
+//           quarter of the row) feed an 11-bit radix histogram per token in
+//           LDS (key bits 30..20 — bit 31, the sign, is always 0 here — as two
+//           16-bit counters per word).  From it each token takes a band of
+//           digits [b_lo, b_hi] meant to hold its k-th largest score: b_hi
+//           leaves about (k - 3 sigma) sampled scores above it, b_lo about
+//           (k + 3 sigma) at or above it, sigma the binomial spread of the
+//           sample count above the k-th largest score;
+//   full pass: every score is computed once; a score above the band sets its
+//           bit in the token's LDS selection bitmap, a score inside it appends
+//           (key, index) to the token's candidate slots;
+//   resolve: per token, the band holds the k-th largest score exactly when the
+//           entries above it number at most k and those above it plus inside
+//           it at least k (every dropped entry lies below every kept one); a
+//           radix select over the candidates (the digit in 6 + 5 bits, then
+//           the low 20 bits in 8 + 8 + 4, lowest index among equal keys) marks
+//           the remaining winners in the bitmap, which is written out as the
+//           ascending index list.
+// The 16 lanes that hold one token's scores of 16 consecutive entries publish
+// them together: one atomicOr of their bitmap bits, one slot reservation for
+// their candidates.
+// A token whose band misses (checked exactly) or overflows its candidate slots
+// is rescored into the workspace and selected by the exact block-wide select.
 static constexpr int FQ = 16;                  // query tokens per workgroup
 static constexpr int FNT = 512;                // threads per workgroup
 static constexpr int FNW = FNT / 64;
 static constexpr int FK = 512;                 // largest top-k on this path
-static constexpr int FCAP = 512;               // boundary-bin candidates per token
+static constexpr int FCAP = 1024;              // band candidates per token
 static constexpr int FMAXN = 8192;             // largest eligible row on this path
 static constexpr int FBM = FMAXN / 32;         // bitmap words per token
-// Histogram rows are padded with one word after every 32 (pass 1) or 16
+static constexpr int FSTEP = 16 * FNW;         // entries per step of the scoring loop
+static constexpr int FSAMPLE = 4;              // one step in FSAMPLE is sampled
+// Histogram rows are padded with one word after every 32 (sample) or 16
 // (resolve) so that the per-lane bin ranges of the top-down scan fall in
 // distinct LDS banks.
-static constexpr int HROW = 1024 + 1024 / 32;  // pass-1 row: 2048 bins as 16-bit pairs
-static constexpr int SROW = 1024 + 1024 / 16;  // resolve row: 1024 bins
+static constexpr int HROW = 1024 + 1024 / 32;  // sample row: 2048 bins as 16-bit pairs
+static constexpr int SROW = 256 + 256 / 16;    // resolve row: 256 bins
 __device__ __forceinline__ int hpad(int w) { return w + (w >> 5); }
 __device__ __forceinline__ int spad(int w) { return w + (w >> 4); }
 
@@ -1064,7 +644,7 @@ struct FusedSmem {
   } u;
   uint32_t bm[FQ][FBM];
   uint32_t scr[FNW][SROW];                     // per-wave radix scratch; fallback select
-  uint32_t ncand[FQ], b1[FQ], above[FQ], fb[FQ];
+  uint32_t ncand[FQ], lo_key[FQ], hi_key[FQ], fb[FQ];
 };
 
 __device__ __forceinline__ void wave_sync() {
@@ -1098,6 +678,13 @@ __device__ __forceinline__ void wave_find_bin(int nb, uint32_t need, Cnt cnt, ui
   const int src = m ? __ffsll((unsigned long long)m) - 1 : 0;
   bin = (uint32_t)__builtin_amdgcn_readlane((int)bb, src);
   above = (uint32_t)__builtin_amdgcn_readlane((int)ab, src);
+}
+
+// Sampled entries of a row of n eligible entries: the first 128 of every
+// FSAMPLE * 128 (the steps the sample pass scores).
+__device__ __forceinline__ int sample_count(int n) {
+  const int blk = FSAMPLE * FSTEP;
+  return (n / blk) * FSTEP + min(n % blk, FSTEP);
 }
 
 template <int QK, int DI, int HI>
@@ -1157,17 +744,17 @@ __global__ __launch_bounds__(FNT) void fused_prefill_kernel(IndexerArgs a) {
   }
   for (int i = tid; i < (FQ + 1) * HROW; i += FNT) (&sm.u.hist[0][0])[i] = 0u;
   for (int i = tid; i < FQ * FBM; i += FNT) (&sm.bm[0][0])[i] = 0u;
-  if (tid < FQ) { sm.ncand[tid] = 0; sm.fb[tid] = 0; sm.b1[tid] = 0; sm.above[tid] = 0; }
+  if (tid < FQ) { sm.ncand[tid] = 0; sm.fb[tid] = 0; }
   __syncthreads();
 
   const char* kbase = reinterpret_cast<const char*>(a.kic) + (size_t)b * a.Nc_cap * rb;
   const uint8_t* sbase = QK == QK_FP4 ? reinterpret_cast<const uint8_t*>(a.kic_scale) + (size_t)b * a.Nc_cap * (DI / 32) : nullptr;
   const float* fsc = QK == QK_FP8 ? reinterpret_cast<const float*>(a.kic_scale) + (size_t)b * a.Nc_cap : nullptr;
 
-  // Scores of entries e0 + 16 wave + r (e0 steps by 16 FNW) for every row tile;
-  // f(rt, sp, entry, key, eligible) is called for each.  All MFMAs of an entry
-  // tile issue before the epilogue reads their results.
-  auto pass = [&](auto&& f) {
+  // Scores of entries e0 + 16 wave + r for e0 = first, first + stride, ...
+  // (< ne_max) for every row tile; f(rt, sp, entry, score) is called for
+  // each.  All MFMAs of an entry tile issue before the epilogue reads them.
+  auto pass = [&](int first, int stride, auto&& f) {
     RawFrag<QK> kb[KC];
     float ks = 1.f;
     auto load = [&](int e0) {
@@ -1178,14 +765,14 @@ __global__ __launch_bounds__(FNT) void fused_prefill_kernel(IndexerArgs a) {
                      8 * (g * KC + c));
       if constexpr (QK == QK_FP8) ks = fsc[e];
     };
-    if (ne_max > 0) load(0);
+    if (first < ne_max) load(first);
 #pragma unroll 1
-    for (int e0 = 0; e0 < ne_max; e0 += 16 * FNW) {
+    for (int e0 = first; e0 < ne_max; e0 += stride) {
       RawFrag<QK> cur[KC];
 #pragma unroll
       for (int c = 0; c < KC; ++c) cur[c] = kb[c];
       const float cks = ks;
-      if (e0 + 16 * FNW < ne_max) load(e0 + 16 * FNW);
+      if (e0 + stride < ne_max) load(e0 + stride);
       const int e = e0 + 16 * wave + r;
       f32x4 acc[NRT];
 #pragma unroll
@@ -1206,50 +793,78 @@ __global__ __launch_bounds__(FNT) void fused_prefill_kernel(IndexerArgs a) {
             sc = fmaf(wr[rt][sp * HI + h], x, sc);
           }
           if constexpr (QK == QK_FP8) sc *= cks;
-          f(rt, sp, e, __float_as_uint(sc), e < tne[rt][sp]);
+          f(rt, sp, e, sc);
         }
       }
     }
   };
 
-  // ---- pass 1: per-token histograms of key bits 30..20 ----
-  pass([&](int rt, int sp, int e, uint32_t key, bool ok) {
-    const uint32_t bin = key >> 20;
-    atomicAdd(&sm.u.hist[ok ? tok[rt][sp] : FQ][hpad(bin & 1023u)], 1u << ((bin >> 10) << 4));
+  // ---- sample: per-token histograms of key bits 30..20 over a quarter of the row ----
+  pass(0, FSAMPLE * FSTEP, [&](int rt, int sp, int e, float sc) {
+    const uint32_t bin = __float_as_uint(sc) >> 20;
+    atomicAdd(&sm.u.hist[e < tne[rt][sp] ? tok[rt][sp] : FQ][hpad(bin & 1023u)], 1u << ((bin >> 10) << 4));
   });
   __syncthreads();
+  // ---- each token's band from its sample ----
   for (int j = 0; j < TPW; ++j) {
     const int tt = TPW * wave + j;
-    if (tt >= nt || row_len(a, b, t0 + tt) <= k) continue;
-    const uint32_t* hrow = sm.u.hist[tt];
-    uint32_t bin, ab;
-    wave_find_bin(2048, (uint32_t)k,
-                  [&](int i) { return (hrow[hpad(i & 1023)] >> ((i >> 10) << 4)) & 0xFFFFu; }, bin, ab);
-    if (lane == 0) { sm.b1[tt] = bin; sm.above[tt] = ab; }
+    if (tt >= nt) continue;
+    const int ne = row_len(a, b, t0 + tt);
+    uint32_t lo_key = 0x7F800000u, hi_key = 0x7F800000u;         // n_e <= k: nothing to select
+    if (ne > k) {
+      const uint32_t* hrow = sm.u.hist[tt];
+      auto cnt = [&](int i) { return (hrow[hpad(i & 1023)] >> ((i >> 10) << 4)) & 0xFFFFu; };
+      const int ns = sample_count(ne);
+      const float p = (float)k / (float)ne;
+      const float mean = (float)ns * p;
+      const float dev = ceilf(3.f * sqrtf(mean * (1.f - p))) + 2.f;
+      const int r_hi = (int)floorf(mean - dev), r_lo = (int)ceilf(mean + dev);
+      uint32_t bhi = 2047, blo = 0, ab;
+      if (r_hi >= 1) wave_find_bin(2048, (uint32_t)r_hi + 1u, cnt, bhi, ab);   // <= r_hi sampled above
+      if (r_lo <= ns) wave_find_bin(2048, (uint32_t)r_lo, cnt, blo, ab);      // >= r_lo sampled at or above
+      blo = min(blo, bhi);
+      lo_key = blo << 20;
+      hi_key = min((bhi + 1u) << 20, 0x7F800000u);
+    }
+    if (lane == 0) { sm.lo_key[tt] = lo_key; sm.hi_key[tt] = hi_key; }
   }
   __syncthreads();
-  uint32_t tb1[NRT][SPL];
+  float thr_lo[NRT][SPL], thr_hi[NRT][SPL];
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-    for (int sp = 0; sp < SPL; ++sp) tb1[rt][sp] = tne[rt][sp] > k ? sm.b1[tok[rt][sp]] : 0xFFFFFFFFu;
-  __syncthreads();                                           // histograms become candidate slots
-  // ---- pass 2: bits above b1, candidates inside b1 ----
-  pass([&](int rt, int sp, int e, uint32_t key, bool ok) {
-    const uint32_t d = key >> 20;
-    if (ok && d >= tb1[rt][sp]) {
+    for (int sp = 0; sp < SPL; ++sp) {
       const int tt = tok[rt][sp];
-      if (d > tb1[rt][sp]) {
-        atomicOr(&sm.bm[tt][e >> 5], 1u << (e & 31));
-      } else {
-        const uint32_t slot = atomicAdd(&sm.ncand[tt], 1u);
-        if (slot < (uint32_t)FCAP) { sm.u.cand[tt][slot][0] = key; sm.u.cand[tt][slot][1] = (uint32_t)e; }
-      }
+      const bool live = tt < nt;
+      thr_lo[rt][sp] = __uint_as_float(live ? sm.lo_key[tt] : 0x7F800000u);
+      thr_hi[rt][sp] = __uint_as_float(live ? sm.hi_key[tt] : 0x7F800000u);
+    }
+  __syncthreads();                                           // the histograms become candidate slots
+  // ---- full pass: bits above the band, candidates inside it ----
+  // Lane group g (lanes 16g..16g+15) holds one token's scores of the 16
+  // consecutive entries e - r .. e - r + 15, which share a bitmap half-word.
+  pass(0, FSTEP, [&](int rt, int sp, int e, float sc) {
+    const bool ok = e < tne[rt][sp] && sc >= thr_lo[rt][sp];
+    const bool above = ok && sc >= thr_hi[rt][sp];
+    const bool inband = ok && !above;
+    const uint64_t ma = __ballot(above), mc = __ballot(inband);
+    if ((ma | mc) == 0) return;                              // uniform
+    const int tt = tok[rt][sp];
+    const uint32_t ga = (uint32_t)(ma >> (16 * g)) & 0xFFFFu;
+    const uint32_t gc = (uint32_t)(mc >> (16 * g)) & 0xFFFFu;
+    if (r == 0 && ga) atomicOr(&sm.bm[tt][e >> 5], ga << (e & 31));
+    uint32_t base = 0;
+    if (r == 0 && gc) base = atomicAdd(&sm.ncand[tt], (uint32_t)__popc(gc));
+    base = (uint32_t)__shfl((int)base, 16 * g, 64);
+    if (inband) {
+      const uint32_t slot = base + (uint32_t)__popc(gc & ((1u << r) - 1u));
+      if (slot < (uint32_t)FCAP) { sm.u.cand[tt][slot][0] = __float_as_uint(sc); sm.u.cand[tt][slot][1] = (uint32_t)e; }
     }
   });
   __syncthreads();
-  // ---- resolve the boundary bin, write ascending lists ----
+  // ---- resolve the band, write ascending lists ----
   uint32_t* scr = sm.scr[wave];
+  constexpr int WPL = FBM / 64;                               // bitmap words per lane
   for (int j = 0; j < TPW; ++j) {
     const int tt = TPW * wave + j;
     if (tt >= nt) break;
@@ -1260,8 +875,11 @@ __global__ __launch_bounds__(FNT) void fused_prefill_kernel(IndexerArgs a) {
       continue;
     }
     const uint32_t ncand = sm.ncand[tt];
-    uint32_t rem = (uint32_t)k - sm.above[tt];
-    if (ncand > (uint32_t)FCAP || rem > ncand) {
+    uint32_t nabove = 0;
+#pragma unroll
+    for (int q = 0; q < WPL; ++q) nabove += (uint32_t)__popc(sm.bm[tt][lane * WPL + q]);
+    nabove = wave_sum_u32(nabove);
+    if (nabove > (uint32_t)k || nabove + ncand < (uint32_t)k || ncand > (uint32_t)FCAP) {
       if (lane == 0) {
         sm.fb[tt] = 1u;
         count_event(CNT_PREFILL_FALLBACK);
@@ -1269,44 +887,67 @@ __global__ __launch_bounds__(FNT) void fused_prefill_kernel(IndexerArgs a) {
       continue;
     }
     const uint32_t(*cand)[2] = sm.u.cand[tt];
-    uint32_t prefix = 0, pmask = 0;
-    for (int p = 0; p < 2; ++p) {
-      const int sh = p == 0 ? 10 : 0;
-      for (int i = lane; i < SROW; i += 64) scr[i] = 0u;
-      wave_sync();
-      for (uint32_t i = lane; i < ncand; i += 64) {
-        const uint32_t low = cand[i][0] & 0xFFFFFu;
-        if ((low & pmask) == prefix) atomicAdd(&scr[spad((low >> sh) & 1023u)], 1u);
-      }
-      wave_sync();
-      uint32_t bin, ab;
-      wave_find_bin(1024, rem, [&](int i) { return scr[spad(i)]; }, bin, ab);
-      prefix |= bin << sh;
-      pmask |= 1023u << sh;
-      rem -= ab;
-      wave_sync();
-    }
-    // rem keys equal to the threshold's low bits remain to be taken
-    uint32_t neq = 0;
-    for (uint32_t i = lane; i < ncand; i += 64) neq += (cand[i][0] & 0xFFFFFu) == prefix;
-    neq = (uint32_t)wave_sum((float)neq);
-    for (uint32_t i = lane; i < ncand; i += 64) {
-      const uint32_t low = cand[i][0] & 0xFFFFFu;
-      bool take = low > prefix;
-      if (low == prefix) {
-        if (neq == rem) {
-          take = true;
-        } else {
-          uint32_t rank = 0;
-          for (uint32_t q = 0; q < ncand; ++q)
-            rank += ((cand[q][0] & 0xFFFFFu) == prefix) && (cand[q][1] < cand[i][1]);
-          take = rank < rem;
+    const uint32_t need = (uint32_t)k - nabove;
+    if (need > 0) {
+      // the 11-bit digit of the need-th largest candidate key (6 then 5 bits),
+      // and the candidates above that digit
+      uint32_t rem = need, d1 = 0;
+      for (int p = 0; p < 2; ++p) {
+        const int sh = p == 0 ? 25 : 20, nb = p == 0 ? 64 : 32;
+        for (int i = lane; i < 64; i += 64) scr[i] = 0u;
+        wave_sync();
+        for (uint32_t i = lane; i < ncand; i += 64) {
+          const uint32_t key = cand[i][0];
+          if (p == 0 || (key >> 25) == (d1 >> 5)) atomicAdd(&scr[(key >> sh) & (nb - 1)], 1u);
         }
+        wave_sync();
+        uint32_t bin, ab;
+        wave_find_bin(64, rem, [&](int i) { return scr[i]; }, bin, ab);
+        d1 |= p == 0 ? bin << 5 : bin;
+        rem -= ab;
+        wave_sync();
       }
-      if (take) atomicOr(&sm.bm[tt][cand[i][1] >> 5], 1u << (cand[i][1] & 31));
+      for (uint32_t i = lane; i < ncand; i += 64)
+        if ((cand[i][0] >> 20) > d1) atomicOr(&sm.bm[tt][cand[i][1] >> 5], 1u << (cand[i][1] & 31));
+      uint32_t prefix = 0, pmask = 0;
+      for (int p = 0; p < 3; ++p) {
+        const int sh = p == 0 ? 12 : (p == 1 ? 4 : 0);
+        const uint32_t dm = p == 2 ? 15u : 255u;
+        for (int i = lane; i < SROW; i += 64) scr[i] = 0u;
+        wave_sync();
+        for (uint32_t i = lane; i < ncand; i += 64) {
+          const uint32_t key = cand[i][0], low = key & 0xFFFFFu;
+          if ((key >> 20) == d1 && (low & pmask) == prefix) atomicAdd(&scr[spad((low >> sh) & dm)], 1u);
+        }
+        wave_sync();
+        uint32_t b2, ab2;
+        wave_find_bin(256, rem, [&](int i) { return scr[spad(i)]; }, b2, ab2);
+        prefix |= b2 << sh;
+        pmask |= dm << sh;
+        rem -= ab2;
+        wave_sync();
+      }
+      // rem keys equal to the threshold key (d1, prefix) remain to be taken
+      const uint32_t tkey = (d1 << 20) | prefix;
+      uint32_t neq = 0;
+      for (uint32_t i = lane; i < ncand; i += 64) neq += cand[i][0] == tkey;
+      neq = wave_sum_u32(neq);
+      for (uint32_t i = lane; i < ncand; i += 64) {
+        const uint32_t key = cand[i][0];
+        bool take = (key >> 20) == d1 && key > tkey;
+        if (key == tkey) {
+          if (neq == rem) {
+            take = true;
+          } else {
+            uint32_t rank = 0;
+            for (uint32_t q = 0; q < ncand; ++q) rank += cand[q][0] == tkey && cand[q][1] < cand[i][1];
+            take = rank < rem;
+          }
+        }
+        if (take) atomicOr(&sm.bm[tt][cand[i][1] >> 5], 1u << (cand[i][1] & 31));
+      }
+      wave_sync();
     }
-    wave_sync();
-    constexpr int WPL = FBM / 64;                           // bitmap words per lane
     const int nw = (ne + 31) / 32;
     uint32_t words[WPL];
     uint32_t cnt = 0;
@@ -1332,13 +973,13 @@ __global__ __launch_bounds__(FNT) void fused_prefill_kernel(IndexerArgs a) {
     wave_sync();
   }
   __syncthreads();
-  // ---- exact fallback for tokens whose boundary bin overflowed ----
+  // ---- exact fallback for tokens whose band missed or overflowed ----
   for (int tt = 0; tt < nt; ++tt) {
     if (!sm.fb[tt]) continue;                                // uniform: LDS after a barrier
     const int ne = row_len(a, b, t0 + tt);
     float* srow = reinterpret_cast<float*>(a.ws) + ((size_t)b * a.Tq + t0 + tt) * nc_pad(a.Nc_cap);
-    pass([&](int rt, int sp, int e, uint32_t key, bool ok) {
-      if (ok && tok[rt][sp] == tt) srow[e] = __uint_as_float(key);
+    pass(0, FSTEP, [&](int rt, int sp, int e, float sc) {
+      if (e < tne[rt][sp] && tok[rt][sp] == tt) srow[e] = sc;
     });
     __syncthreads();
     TopkSmem<FNT>& ts = *reinterpret_cast<TopkSmem<FNT>*>(&sm.scr[0][0]);
@@ -1373,6 +1014,24 @@ static hipError_t launch_fused_hi(const IndexerArgs& a, hipStream_t st) {
 template <int QK>
 static hipError_t launch_fused_di(const IndexerArgs& a, hipStream_t st) {
   return a.dI == 32 ? launch_fused_hi<QK, 32>(a, st) : launch_fused_hi<QK, 64>(a, st);
+}
+
+hipError_t counters_device_ptr(unsigned long long** p) {
+  static std::mutex mu;
+  static std::map<int, unsigned long long*> cache;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = cache.find(dev);
+  if (it == cache.end()) {
+    void* q = nullptr;
+    e = hipGetSymbolAddress(&q, HIP_SYMBOL(g_counters));
+    if (e != hipSuccess) return e;
+    it = cache.emplace(dev, reinterpret_cast<unsigned long long*>(q)).first;
+  }
+  *p = it->second;
+  return hipSuccess;
 }
 
 hipError_t counter_read(int which, unsigned long long* value, bool reset) {
@@ -1425,6 +1084,21 @@ static void launch_scores_di(const IndexerArgs& a, hipStream_t st, bool lp) {
   else launch_scores_hi<QK, 64>(a, st, lp);
 }
 
+bool indexer_long_path(const IndexerArgs& a) {
+  return a.B > 0 && a.Tq > 0 && !use_fused_prefill(a) && use_long_path(a.Tq, a.Nc_cap);
+}
+
+hipError_t launch_indexer_scores(const IndexerArgs& a, hipStream_t st) {
+  if (!indexer_long_path(a)) return hipErrorInvalidValue;
+  switch (a.qk) {
+    case QK_F32: launch_scores_di<QK_F32>(a, st, true); break;
+    case QK_BF16: launch_scores_di<QK_BF16>(a, st, true); break;
+    case QK_FP8: launch_scores_di<QK_FP8>(a, st, true); break;
+    case QK_FP4: launch_scores_di<QK_FP4>(a, st, true); break;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t st) {
   if (a.B == 0 || a.Tq == 0) return hipSuccess;
   if (use_fused_prefill(a)) {
@@ -1445,7 +1119,7 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   ProfScope ps("indexer_topk", st);
-  if (lp) hipLaunchKernelGGL(long_pick_kernel, dim3(a.B * a.Tq), dim3(PICK_NT), 0, st, a);
+  if (lp) hipLaunchKernelGGL(long_pick_kernel, dim3(a.B * a.Tq), dim3(1024), 0, st, a);
   else hipLaunchKernelGGL(topk_row_kernel, dim3(a.Tq, a.B), dim3(TOPK_NT), 0, st, a);
   return hipGetLastError();
 }

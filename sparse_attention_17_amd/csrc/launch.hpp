@@ -31,8 +31,12 @@ csa_status_t set_error(csa_status_t st, const char* fmt, ...);
 hipError_t ensure_lds_limit(const void* kfn, size_t lds);
 
 // Device event counters (measurement only), read by csa_profile_counter.
-enum CounterId { CNT_PREFILL_FALLBACK = 0, CNT_DECODE_FALLBACK = 1, CNT_COUNT = 2 };
+enum CounterId { CNT_PREFILL_FALLBACK = 0, CNT_DECODE_FALLBACK = 1, CNT_STEP_TIMEOUT = 2,
+                 CNT_DECODE_SECOND_ROUND = 3, CNT_COUNT = 4 };
 hipError_t counter_read(int which, unsigned long long* value, bool reset);
+// Device address of the counters (this device), for kernels in other
+// translation units.
+hipError_t counters_device_ptr(unsigned long long** p);
 
 struct CompressArgs {
   const void *k, *v, *ki;
@@ -59,6 +63,10 @@ struct IndexerArgs {
 };
 size_t indexer_workspace(int B, int Tq, int Nc_cap, int HI, int dI, int topk, int qk);
 hipError_t launch_indexer_topk(const IndexerArgs& a, hipStream_t st);
+// Decode rows long enough for the chunked path (score kernel + per-row pick):
+// whether `a` takes it, and its score kernel alone (the pick left to the caller).
+bool indexer_long_path(const IndexerArgs& a);
+hipError_t launch_indexer_scores(const IndexerArgs& a, hipStream_t st);
 
 struct AttendArgs {
   bool sparse;                     // CSA (idx list) or HCA (dense over completed blocks)

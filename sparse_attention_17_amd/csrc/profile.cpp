@@ -109,6 +109,8 @@ int csa_profile_counter(const char* name, unsigned long long* value, int reset) 
   if (name == nullptr) return 1;
   if (std::strcmp(name, "indexer_prefill_fallback") == 0) which = csa::CNT_PREFILL_FALLBACK;
   else if (std::strcmp(name, "indexer_decode_fallback") == 0) which = csa::CNT_DECODE_FALLBACK;
+  else if (std::strcmp(name, "step_timeout") == 0) which = csa::CNT_STEP_TIMEOUT;
+  else if (std::strcmp(name, "indexer_decode_second_round") == 0) which = csa::CNT_DECODE_SECOND_ROUND;
   if (which < 0 || value == nullptr) return 1;
   return csa::counter_read(which, value, reset != 0) == hipSuccess ? 0 : -1;
 }

@@ -379,9 +379,11 @@ class DecodeStep:
     optionally kw, vw, raw_pos0, sink, scale), `hca` those of hca_attend (q, kc,
     vc, m_prime, and optionally sink, scale, window, kw, vw, raw_pos0); pos0 and
     max_pos are shared.  Outputs: self.idx, self.out, self.hout (+ self.lse,
-    self.hlse with return_lse)."""
+    self.hlse with return_lse).  fused_tail=True runs both attention problems
+    and their merges in one kernel ordered by device counters (same
+    results)."""
 
-    def __init__(self, idx, csa, hca, pos0, max_pos, return_lse=False):
+    def __init__(self, idx, csa, hca, pos0, max_pos, return_lse=False, fused_tail=False):
         i = dict(qi_scale=None, kic_scale=None, qk_dtype=None)
         i.update(idx)
         c = dict(kw=None, vw=None, raw_pos0=None, sink=None, scale=None)
@@ -430,11 +432,13 @@ class DecodeStep:
         s.hwindow, s.hsink = h["window"], _p(h["sink"])
         s.hsoftmax_scale = d ** -0.5 if h["scale"] is None else h["scale"]
         s.hout, s.hlse_out = _p(self.hout), _p(self.hlse)
-        s.flags = 0
+        s.flags = L.STEP_FUSED_TAIL if fused_tail else 0
         self._desc = s
         self._lib = L.load()
         self._nws = self._lib.csa_hybrid_decode_step_workspace(s)
-        self._ws = _ws(self._nws, dev)
+        # allocated zeroed: the step's control words must start at zero (every
+        # call leaves them zero)
+        self._ws = torch.zeros(max(self._nws, 1), dtype=torch.uint8, device=dev)
         self._wsp = self._ws.data_ptr()
         self._dev = dev
         self._inputs = (i, c, h, pos0)     # keep the tensors alive

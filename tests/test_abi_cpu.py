@@ -265,10 +265,10 @@ def test_decode_step_validation(lib):
     assert lib.csa_hybrid_decode_step(None, FAKE, need, None) == L.INVALID_ARGUMENT
 
 
-def test_decode_step_flags_reserved(lib):
+def test_decode_step_flags_undefined_bits(lib):
     from sparse_attention_17_amd._lib import DecodeStepDesc
     s = DecodeStepDesc()
-    s.B, s.H, s.Nc_cap, s.m_prime, s.topk, s.flags = 1, 8, 64, 8, 4, 1
+    s.B, s.H, s.Nc_cap, s.m_prime, s.topk, s.flags = 1, 8, 64, 8, 4, 2
     assert lib.csa_hybrid_decode_step(C.byref(s), None, 0, None) == L.INVALID_ARGUMENT
     assert b"flags" in lib.csa_last_error()
 

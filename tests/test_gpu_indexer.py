@@ -312,3 +312,29 @@ def test_multi_token_decode_long_rows(qk):
                                           positions, win, f64(x["sink"]), w.scale)
         assert_close(out[b], ro, "bf16", f"attend[{b}]", lse[b], rl)
     assert exact >= 3 * w.B - 1
+
+
+@pytest.mark.parametrize("qk", ["fp8", "fp4", "bf16"])
+def test_decode_score_accuracy(qk):
+    # the decode score kernels' fp32 scores of the selected entries against the
+    # oracle's fp64 scores of the same decoded values: the error must stay far
+    # inside the 1e-6 near-tie band (relative to the row maximum), so that the
+    # index sets are exact outside it
+    w = configs.HYBRID_1M_FP8.with_(ctx=65536 * 4, B=2, qk_dtype=qk, topk=2048)
+    x = inputs.make_inputs(w, peaky=True)
+    g = {k: v.to(dev()) for k, v in x.items()}
+    pos0 = torch.full((w.B,), w.ctx - 1, dtype=torch.int32, device=dev())
+    idx, sc = ops.indexer_topk(g["qi"], g["w"], g["kic"], pos0, w.m, w.topk, max_pos=w.ctx - 1,
+                               qi_scale=g.get("qi_scale"), kic_scale=g.get("kic_scale"),
+                               qk_dtype=qk, return_scores=True)
+    idx, sc = idx.cpu().numpy(), sc.cpu().numpy().astype(np.float64)
+    qi = _dequant(x, "qi", qk)
+    kic = _dequant(x, "kic", qk)
+    worst = 0.0
+    for b in range(w.B):
+        ref = oracle.csa.indexer_scores(qi[b], f64(x["w"][b]), kic[b])[0]
+        sel = idx[b, 0]
+        rel = np.abs(sc[b, 0] - ref[sel]).max() / ref.max()
+        worst = max(worst, rel)
+    print(f"decode {qk} score error: {worst:.2e} of the row maximum")
+    assert worst < 3e-7                     # the band is 1e-6; native FP8 MFMA sums measured ~1e-5

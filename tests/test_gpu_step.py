@@ -59,6 +59,58 @@ def test_step_equals_separate_calls(name, qk, B, ctx):
         assert torch.equal(_bits(a), _bits(b)), f"{name}: {nm} differs"
 
 
+def _ragged_args(w, g, lens):
+    """Step arguments with per-sequence query positions lens[b] - 1 (window rows
+    start at max(0, position - window + 1))."""
+    pos0, idx, csa, hca = _args(w, g)
+    p = torch.tensor([n - 1 for n in lens], dtype=torch.int32, device=dev())
+    pos0.copy_(p)
+    csa["raw_pos0"] = torch.clamp(p - w.window + 1, min=0).to(torch.int32)
+    return pos0, idx, csa, hca
+
+
+@pytest.mark.parametrize("name,qk,B,ctx,short", [
+    ("fp8 1M, 16 rows (two per queue)", "fp8", 16, 1 << 20, True),
+    ("bf16, 3 rows (one queue)", "bf16", 3, 4 * 20000 + 3, True),
+    ("fp4 512K, 8 rows", "fp4", 8, 1 << 19, False)])
+def test_fused_step_equals_separate_launches(name, qk, B, ctx, short):
+    # The step with the fused tail (both attention problems and both merges
+    # in one kernel ordered through control counters) against the separate
+    # kernels, bitwise, over several calls of one step object (the control
+    # words must come back to zero after every call); rows of different
+    # lengths, including one no longer than k and one whose chunk count
+    # differs from the longest row's.
+    w = configs.HYBRID_1M_FP8.with_(qk_dtype=qk, B=B, ctx=ctx)
+    x = inputs.make_inputs(w, peaky=True)
+    g = {k: v.to(dev()) for k, v in x.items()}
+    lens = [ctx - 977 * b for b in range(B)]
+    if short:
+        lens[1] = 4 * (w.topk - 5) + 2                          # n_e < k: every entry selected
+        lens[-1] = 4 * 3000 + 1                                  # fewer chunks than the longest row
+    pos0, idx, csa, hca = _ragged_args(w, g, lens)
+    ops.profile_counter("step_timeout", reset=True)
+    fused = ops.DecodeStep(idx, csa, hca, pos0, w.ctx - 1, return_lse=True, fused_tail=True)
+    sep = ops.DecodeStep(idx, csa, hca, pos0, w.ctx - 1, return_lse=True)
+    sep.run()
+    for _ in range(4):
+        fused.run()
+    torch.cuda.synchronize()
+    for nm in ("idx", "out", "lse", "hout", "hlse"):
+        a, b = getattr(fused, nm), getattr(sep, nm)
+        assert torch.equal(_bits(a), _bits(b)), f"{name}: {nm} differs"
+    assert ops.profile_counter("step_timeout", reset=True) == 0
+    # the static-scratch entry point with the same flag (when the step fits
+    # its array)
+    if fused._nws > 64 << 20:
+        return
+    fused.run_static()
+    fused.run_static()
+    torch.cuda.synchronize()
+    for nm in ("idx", "out", "hout"):
+        assert torch.equal(_bits(getattr(fused, nm)), _bits(getattr(sep, nm))), f"{name}: static {nm}"
+    assert ops.profile_counter("step_timeout", reset=True) == 0
+
+
 def test_step_matches_oracle():
     w = configs.HYBRID_1M_FP8.with_(B=2, ctx=4 * 20000 + 3)
     x = inputs.make_inputs(w, peaky=True)

@@ -30,7 +30,10 @@ def _step(w):
 
 
 def test_static_step_matches_workspace_step_twice():
-    for w in (configs.HYBRID_1M_FP8, configs.HYBRID_1M_FP8.with_(B=3, ctx=4 * 20000 + 1, qk_dtype="bf16")):
+    # B=8, a smaller B=3 step, then B=8 again: the static array's control words
+    # must be zero for every batch size after any earlier call
+    small = configs.HYBRID_1M_FP8.with_(B=3, ctx=4 * 20000 + 1, qk_dtype="bf16")
+    for w in (configs.HYBRID_1M_FP8, small, configs.HYBRID_1M_FP8):
         st, _ = _step(w)
         st.run()
         torch.cuda.synchronize()
