@@ -610,13 +610,16 @@ __global__ __launch_bounds__(1024) void long_pick_kernel(IndexerArgs a) {
 //   resolve: per token, the band holds the k-th largest score exactly when the
 //           entries above it number at most k and those above it plus inside
 //           it at least k (every dropped entry lies below every kept one); a
-//           radix select over the candidates (the digit in 6 + 5 bits, then
-//           the low 20 bits in 8 + 8 + 4, lowest index among equal keys) marks
-//           the remaining winners in the bitmap, which is written out as the
-//           ascending index list.
+//           histogram of the candidates' 11-bit digits (counted while their
+//           per-wave slots are compacted) gives the digit of the k-th largest
+//           key; the candidates of that digit (up to 64) are ranked exactly
+//           (larger key first, then lower index — a radix select over the low
+//           20 bits when more share the digit), which completes the bitmap,
+//           written out as the ascending index list.
 // The 16 lanes that hold one token's scores of 16 consecutive entries publish
-// them together: one atomicOr of their bitmap bits, one slot reservation for
-// their candidates.
+// them together: one atomicOr of their bitmap bits; candidates go to the
+// wave's own slots of the token, counted in registers (no LDS round trip in
+// the scoring loop), and are compacted per token before the resolve.
 // A token whose band misses (checked exactly) or overflows its candidate slots
 // is rescored into the workspace and selected by the exact block-wide select.
 static constexpr int FQ = 16;                  // query tokens per workgroup
@@ -624,6 +627,7 @@ static constexpr int FNT = 512;                // threads per workgroup
 static constexpr int FNW = FNT / 64;
 static constexpr int FK = 512;                 // largest top-k on this path
 static constexpr int FCAP = 1024;              // band candidates per token
+static constexpr int FCAPW = FCAP / FNW;       // ... per (token, wave)
 static constexpr int FMAXN = 8192;             // largest eligible row on this path
 static constexpr int FBM = FMAXN / 32;         // bitmap words per token
 static constexpr int FSTEP = 16 * FNW;         // entries per step of the scoring loop
@@ -640,11 +644,12 @@ struct FusedSmem {
   union {
     uint32_t hist[FQ + 1][HROW];               // bin i: word hpad(i & 1023), half i >> 10;
                                                // row FQ absorbs ineligible entries
-    uint32_t cand[FQ][FCAP][2];                // (key, index)
+    uint32_t cand[FQ][FNW][FCAPW][2];          // (key, index) per (token, wave)
   } u;
   uint32_t bm[FQ][FBM];
   uint32_t scr[FNW][SROW];                     // per-wave radix scratch; fallback select
-  uint32_t ncand[FQ], lo_key[FQ], hi_key[FQ], fb[FQ];
+  uint32_t ncw[FQ][FNW];                       // candidates per (token, wave)
+  uint32_t lo_key[FQ], hi_key[FQ], fb[FQ];
 };
 
 __device__ __forceinline__ void wave_sync() {
@@ -652,8 +657,11 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
-// Wave-level: scanning nb bins from the top down, the bin where the running
-// count first reaches `need` (>= 1, <= total) and the count strictly above it.
+// Wave-level: scanning nb bins (nb / 64 <= 64 per lane) from the top down, the
+// bin where the running count first reaches `need` (>= 1, <= total) and the
+// count strictly above it.  Each lane sums its run of bins; a scan finds the
+// run, whose bins are then read one per lane and scanned again (no serial
+// search).
 template <typename Cnt>
 __device__ __forceinline__ void wave_find_bin(int nb, uint32_t need, Cnt cnt, uint32_t& bin,
                                               uint32_t& above) {
@@ -664,20 +672,16 @@ __device__ __forceinline__ void wave_find_bin(int nb, uint32_t need, Cnt cnt, ui
   for (int i = 0; i < per; ++i) local += cnt(hi - 1 - i);
   const uint32_t incl = wave_incl_scan(local);
   const uint32_t excl = incl - local;
-  const bool mine = excl < need && incl >= need;
-  uint32_t bb = 0, ab = 0;
-  if (mine) {
-    uint32_t cum = excl;
-    for (int i = 0; i < per; ++i) {
-      const uint32_t h = cnt(hi - 1 - i);
-      if (cum + h >= need) { bb = hi - 1 - i; ab = cum; break; }
-      cum += h;
-    }
-  }
-  const uint64_t m = __ballot(mine);
+  const uint64_t m = __ballot(excl < need && incl >= need);
   const int src = m ? __ffsll((unsigned long long)m) - 1 : 0;
-  bin = (uint32_t)__builtin_amdgcn_readlane((int)bb, src);
-  above = (uint32_t)__builtin_amdgcn_readlane((int)ab, src);
+  const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)excl, src);
+  const int shi = nb - src * per;                            // lane src's bins: shi-per .. shi-1
+  const uint32_t h = lane < per ? cnt(shi - 1 - lane) : 0u;
+  const uint32_t hin = wave_incl_scan(h);
+  const uint64_t m2 = __ballot(lane < per && base + hin >= need);
+  const int f = m2 ? __ffsll((unsigned long long)m2) - 1 : 0;
+  bin = (uint32_t)(shi - 1 - f);
+  above = base + (uint32_t)__builtin_amdgcn_readlane((int)(hin - h), f);
 }
 
 // Sampled entries of a row of n eligible entries: the first 128 of every
@@ -744,7 +748,7 @@ __global__ __launch_bounds__(FNT) void fused_prefill_kernel(IndexerArgs a) {
   }
   for (int i = tid; i < (FQ + 1) * HROW; i += FNT) (&sm.u.hist[0][0])[i] = 0u;
   for (int i = tid; i < FQ * FBM; i += FNT) (&sm.bm[0][0])[i] = 0u;
-  if (tid < FQ) { sm.ncand[tid] = 0; sm.fb[tid] = 0; }
+  if (tid < FQ) sm.fb[tid] = 0;
   __syncthreads();
 
   const char* kbase = reinterpret_cast<const char*>(a.kic) + (size_t)b * a.Nc_cap * rb;
@@ -754,10 +758,13 @@ __global__ __launch_bounds__(FNT) void fused_prefill_kernel(IndexerArgs a) {
   // Scores of entries e0 + 16 wave + r for e0 = first, first + stride, ...
   // (< ne_max) for every row tile; f(rt, sp, entry, score) is called for
   // each.  All MFMAs of an entry tile issue before the epilogue reads them.
+  // Two steps of loads are in flight ahead of the one being computed (the
+  // keys come from L2; one step of MFMA + epilogue is shorter than its
+  // latency).
   auto pass = [&](int first, int stride, auto&& f) {
-    RawFrag<QK> kb[KC];
-    float ks = 1.f;
-    auto load = [&](int e0) {
+    RawFrag<QK> kbA[KC], kbB[KC];
+    float ksA = 1.f, ksB = 1.f;
+    auto load = [&](RawFrag<QK> (&kb)[KC], float& ks, int e0) {
       const int e = min(e0 + 16 * wave + r, ne_max - 1);
 #pragma unroll
       for (int c = 0; c < KC; ++c)
@@ -765,14 +772,7 @@ __global__ __launch_bounds__(FNT) void fused_prefill_kernel(IndexerArgs a) {
                      8 * (g * KC + c));
       if constexpr (QK == QK_FP8) ks = fsc[e];
     };
-    if (first < ne_max) load(first);
-#pragma unroll 1
-    for (int e0 = first; e0 < ne_max; e0 += stride) {
-      RawFrag<QK> cur[KC];
-#pragma unroll
-      for (int c = 0; c < KC; ++c) cur[c] = kb[c];
-      const float cks = ks;
-      if (e0 + stride < ne_max) load(e0 + stride);
+    auto step = [&](int e0, const RawFrag<QK> (&cur)[KC], float cks) {
       const int e = e0 + 16 * wave + r;
       f32x4 acc[NRT];
 #pragma unroll
@@ -796,6 +796,23 @@ __global__ __launch_bounds__(FNT) void fused_prefill_kernel(IndexerArgs a) {
           f(rt, sp, e, sc);
         }
       }
+    };
+    if (first < ne_max) load(kbA, ksA, first);
+    if (first + stride < ne_max) load(kbB, ksB, first + stride);
+#pragma unroll 1
+    for (int e0 = first; e0 < ne_max; e0 += 2 * stride) {
+      RawFrag<QK> cur[KC];
+#pragma unroll
+      for (int c = 0; c < KC; ++c) cur[c] = kbA[c];
+      float cks = ksA;
+      if (e0 + 2 * stride < ne_max) load(kbA, ksA, e0 + 2 * stride);
+      step(e0, cur, cks);
+      if (e0 + stride >= ne_max) break;                       // uniform
+#pragma unroll
+      for (int c = 0; c < KC; ++c) cur[c] = kbB[c];
+      cks = ksB;
+      if (e0 + 3 * stride < ne_max) load(kbB, ksB, e0 + 3 * stride);
+      step(e0 + stride, cur, cks);
     }
   };
 
@@ -842,7 +859,14 @@ __global__ __launch_bounds__(FNT) void fused_prefill_kernel(IndexerArgs a) {
   __syncthreads();                                           // the histograms become candidate slots
   // ---- full pass: bits above the band, candidates inside it ----
   // Lane group g (lanes 16g..16g+15) holds one token's scores of the 16
-  // consecutive entries e - r .. e - r + 15, which share a bitmap half-word.
+  // consecutive entries e - r .. e - r + 15, which share a bitmap half-word;
+  // the group's running candidate count of its token (the same in its 16
+  // lanes) places the candidates in this wave's slots of the token.
+  uint32_t cntr[NRT][SPL];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+    for (int sp = 0; sp < SPL; ++sp) cntr[rt][sp] = 0;
   pass(0, FSTEP, [&](int rt, int sp, int e, float sc) {
     const bool ok = e < tne[rt][sp] && sc >= thr_lo[rt][sp];
     const bool above = ok && sc >= thr_hi[rt][sp];
@@ -853,14 +877,18 @@ __global__ __launch_bounds__(FNT) void fused_prefill_kernel(IndexerArgs a) {
     const uint32_t ga = (uint32_t)(ma >> (16 * g)) & 0xFFFFu;
     const uint32_t gc = (uint32_t)(mc >> (16 * g)) & 0xFFFFu;
     if (r == 0 && ga) atomicOr(&sm.bm[tt][e >> 5], ga << (e & 31));
-    uint32_t base = 0;
-    if (r == 0 && gc) base = atomicAdd(&sm.ncand[tt], (uint32_t)__popc(gc));
-    base = (uint32_t)__shfl((int)base, 16 * g, 64);
-    if (inband) {
-      const uint32_t slot = base + (uint32_t)__popc(gc & ((1u << r) - 1u));
-      if (slot < (uint32_t)FCAP) { sm.u.cand[tt][slot][0] = __float_as_uint(sc); sm.u.cand[tt][slot][1] = (uint32_t)e; }
+    const uint32_t slot = cntr[rt][sp] + (uint32_t)__popc(gc & ((1u << r) - 1u));
+    if (inband && slot < (uint32_t)FCAPW) {
+      sm.u.cand[tt][wave][slot][0] = __float_as_uint(sc);
+      sm.u.cand[tt][wave][slot][1] = (uint32_t)e;
     }
+    cntr[rt][sp] += (uint32_t)__popc(gc);
   });
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+    for (int sp = 0; sp < SPL; ++sp)
+      if (r == 0 && tok[rt][sp] < nt) sm.ncw[tok[rt][sp]][wave] = cntr[rt][sp];
   __syncthreads();
   // ---- resolve the band, write ascending lists ----
   uint32_t* scr = sm.scr[wave];
@@ -874,77 +902,132 @@ __global__ __launch_bounds__(FNT) void fused_prefill_kernel(IndexerArgs a) {
       for (int i = lane; i < k; i += 64) idx[i] = i < ne ? i : -1;
       continue;
     }
-    const uint32_t ncand = sm.ncand[tt];
+    const uint32_t cw = lane < FNW ? sm.ncw[tt][lane] : 0u;
+    const uint32_t ncand = wave_sum_u32(min(cw, (uint32_t)FCAPW));
+    const bool ovf = wave_max_u32(cw) > (uint32_t)FCAPW;
     uint32_t nabove = 0;
 #pragma unroll
     for (int q = 0; q < WPL; ++q) nabove += (uint32_t)__popc(sm.bm[tt][lane * WPL + q]);
     nabove = wave_sum_u32(nabove);
-    if (nabove > (uint32_t)k || nabove + ncand < (uint32_t)k || ncand > (uint32_t)FCAP) {
+    if (nabove > (uint32_t)k || nabove + ncand < (uint32_t)k || ovf) {
       if (lane == 0) {
         sm.fb[tt] = 1u;
         count_event(CNT_PREFILL_FALLBACK);
       }
       continue;
     }
-    const uint32_t(*cand)[2] = sm.u.cand[tt];
+    // compact the waves' slots of the token into one list, in place (each
+    // wave's run moves to a lower or equal offset, in wave order); a band of
+    // at most 256 digits is counted by digit on the way
+    uint32_t(*cand)[2] = reinterpret_cast<uint32_t(*)[2]>(&sm.u.cand[tt][0][0][0]);
+    const uint32_t blo = sm.lo_key[tt] >> 20;
+    const bool narrow = (sm.hi_key[tt] >> 20) - blo <= 256u;   // hi_key = (b_hi + 1) << 20, or +inf
+    for (int i = lane; i < SROW; i += 64) scr[i] = 0u;
+    wave_sync();
+    uint32_t at = 0;
+    for (int w = 0; w < FNW; ++w) {
+      const uint32_t n = (uint32_t)__builtin_amdgcn_readlane((int)cw, w);
+      const uint32_t* src = &sm.u.cand[tt][w][0][0];
+      for (uint32_t i = lane; i < n; i += 64) {
+        const uint32_t key = src[2 * i], ent = src[2 * i + 1];
+        if (at != (uint32_t)w * FCAPW) { cand[at + i][0] = key; cand[at + i][1] = ent; }
+        if (narrow) atomicAdd(&scr[spad(min((key >> 20) - blo, 255u))], 1u);
+      }
+      at += n;
+      wave_sync();
+    }
     const uint32_t need = (uint32_t)k - nabove;
     if (need > 0) {
-      // the 11-bit digit of the need-th largest candidate key (6 then 5 bits),
-      // and the candidates above that digit
+      // the 11-bit digit d1 of the need-th largest candidate key, and how many
+      // of digit d1 are still needed
       uint32_t rem = need, d1 = 0;
-      for (int p = 0; p < 2; ++p) {
-        const int sh = p == 0 ? 25 : 20, nb = p == 0 ? 64 : 32;
-        for (int i = lane; i < 64; i += 64) scr[i] = 0u;
-        wave_sync();
+      if (narrow) {
+        uint32_t bin, ab;
+        wave_find_bin(256, need, [&](int i) { return scr[spad(i)]; }, bin, ab);
+        d1 = blo + bin;
+        rem = need - ab;
+      } else {
+        for (int p = 0; p < 2; ++p) {                        // 6 then 5 bits of the digit
+          const int sh = p == 0 ? 25 : 20, nb = p == 0 ? 64 : 32;
+          wave_sync();
+          for (int i = lane; i < 64; i += 64) scr[i] = 0u;
+          wave_sync();
+          for (uint32_t i = lane; i < ncand; i += 64) {
+            const uint32_t key = cand[i][0];
+            if (p == 0 || (key >> 25) == (d1 >> 5)) atomicAdd(&scr[(key >> sh) & (nb - 1)], 1u);
+          }
+          wave_sync();
+          uint32_t bin, ab;
+          wave_find_bin(64, rem, [&](int i) { return scr[i]; }, bin, ab);
+          d1 |= p == 0 ? bin << 5 : bin;
+          rem -= ab;
+        }
+      }
+      wave_sync();
+      // candidates above digit d1 are selected; those of digit d1 (up to 64)
+      // are gathered into scr for an exact rank
+      uint32_t n1 = 0;
+      for (uint32_t i0 = 0; i0 < ncand; i0 += 64) {
+        const uint32_t i = i0 + lane;
+        const uint32_t key = i < ncand ? cand[i][0] : 0u, ent = i < ncand ? cand[i][1] : 0u;
+        const uint32_t d = key >> 20;
+        if (i < ncand && d > d1) atomicOr(&sm.bm[tt][ent >> 5], 1u << (ent & 31));
+        const uint64_t m = __ballot(i < ncand && d == d1);
+        const uint32_t slot = n1 + (uint32_t)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        if (i < ncand && d == d1 && slot < 64u) { scr[2 * slot] = key; scr[2 * slot + 1] = ent; }
+        n1 += (uint32_t)__popcll(m);
+      }
+      wave_sync();
+      if (n1 <= 64u) {
+        // rank of each gathered key among them: larger keys first, then lower index
+        const uint32_t kl = lane < (int)n1 ? scr[2 * lane] : 0u, el = lane < (int)n1 ? scr[2 * lane + 1] : 0u;
+        uint32_t rank = 0;
+        for (uint32_t j = 0; j < n1; ++j) {
+          const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)kl, (int)j);
+          const uint32_t ej = (uint32_t)__builtin_amdgcn_readlane((int)el, (int)j);
+          rank += (kj > kl || (kj == kl && ej < el)) ? 1u : 0u;
+        }
+        if (lane < (int)n1 && rank < rem) atomicOr(&sm.bm[tt][el >> 5], 1u << (el & 31));
+      } else {
+        // a crowded boundary digit: radix select over its low 20 bits
+        uint32_t prefix = 0, pmask = 0;
+        for (int p = 0; p < 3; ++p) {
+          const int sh = p == 0 ? 12 : (p == 1 ? 4 : 0);
+          const uint32_t dm = p == 2 ? 15u : 255u;
+          wave_sync();
+          for (int i = lane; i < SROW; i += 64) scr[i] = 0u;
+          wave_sync();
+          for (uint32_t i = lane; i < ncand; i += 64) {
+            const uint32_t key = cand[i][0], low = key & 0xFFFFFu;
+            if ((key >> 20) == d1 && (low & pmask) == prefix) atomicAdd(&scr[spad((low >> sh) & dm)], 1u);
+          }
+          wave_sync();
+          uint32_t b2, ab2;
+          wave_find_bin(256, rem, [&](int i) { return scr[spad(i)]; }, b2, ab2);
+          prefix |= b2 << sh;
+          pmask |= dm << sh;
+          rem -= ab2;
+        }
+        // rem keys equal to the threshold key (d1, prefix) remain to be taken
+        const uint32_t tkey = (d1 << 20) | prefix;
+        uint32_t neq = 0;
+        for (uint32_t i = lane; i < ncand; i += 64) neq += cand[i][0] == tkey;
+        neq = wave_sum_u32(neq);
         for (uint32_t i = lane; i < ncand; i += 64) {
           const uint32_t key = cand[i][0];
-          if (p == 0 || (key >> 25) == (d1 >> 5)) atomicAdd(&scr[(key >> sh) & (nb - 1)], 1u);
-        }
-        wave_sync();
-        uint32_t bin, ab;
-        wave_find_bin(64, rem, [&](int i) { return scr[i]; }, bin, ab);
-        d1 |= p == 0 ? bin << 5 : bin;
-        rem -= ab;
-        wave_sync();
-      }
-      for (uint32_t i = lane; i < ncand; i += 64)
-        if ((cand[i][0] >> 20) > d1) atomicOr(&sm.bm[tt][cand[i][1] >> 5], 1u << (cand[i][1] & 31));
-      uint32_t prefix = 0, pmask = 0;
-      for (int p = 0; p < 3; ++p) {
-        const int sh = p == 0 ? 12 : (p == 1 ? 4 : 0);
-        const uint32_t dm = p == 2 ? 15u : 255u;
-        for (int i = lane; i < SROW; i += 64) scr[i] = 0u;
-        wave_sync();
-        for (uint32_t i = lane; i < ncand; i += 64) {
-          const uint32_t key = cand[i][0], low = key & 0xFFFFFu;
-          if ((key >> 20) == d1 && (low & pmask) == prefix) atomicAdd(&scr[spad((low >> sh) & dm)], 1u);
-        }
-        wave_sync();
-        uint32_t b2, ab2;
-        wave_find_bin(256, rem, [&](int i) { return scr[spad(i)]; }, b2, ab2);
-        prefix |= b2 << sh;
-        pmask |= dm << sh;
-        rem -= ab2;
-        wave_sync();
-      }
-      // rem keys equal to the threshold key (d1, prefix) remain to be taken
-      const uint32_t tkey = (d1 << 20) | prefix;
-      uint32_t neq = 0;
-      for (uint32_t i = lane; i < ncand; i += 64) neq += cand[i][0] == tkey;
-      neq = wave_sum_u32(neq);
-      for (uint32_t i = lane; i < ncand; i += 64) {
-        const uint32_t key = cand[i][0];
-        bool take = (key >> 20) == d1 && key > tkey;
-        if (key == tkey) {
-          if (neq == rem) {
-            take = true;
-          } else {
-            uint32_t rank = 0;
-            for (uint32_t q = 0; q < ncand; ++q) rank += cand[q][0] == tkey && cand[q][1] < cand[i][1];
-            take = rank < rem;
+          bool take = (key >> 20) == d1 && key > tkey;
+          if (key == tkey) {
+            if (neq == rem) {
+              take = true;
+            } else {
+              uint32_t rank = 0;
+              for (uint32_t q = 0; q < ncand; ++q) rank += cand[q][0] == tkey && cand[q][1] < cand[i][1];
+              take = rank < rem;
+            }
           }
+          if (take) atomicOr(&sm.bm[tt][cand[i][1] >> 5], 1u << (cand[i][1] & 31));
         }
-        if (take) atomicOr(&sm.bm[tt][cand[i][1] >> 5], 1u << (cand[i][1] & 31));
       }
       wave_sync();
     }
