@@ -595,7 +595,8 @@ __global__ __launch_bounds__(1024) void long_pick_kernel(IndexerArgs a) {
 // --------------------------- fused prefill path ----------------------------
 // One workgroup (8 waves) per FQ consecutive query tokens.  Scores never reach
 // HBM; the eligible indexer keys stream from L2 and the scores are computed on
-// MFMA.
+// MFMA.  Workgroups are launched longest rows first (causal rows grow with the
+// token), so the last workgroups to start are the shortest.
 //   sample: the scores of one 128-entry step in every FSAMPLE (a block-strided
 //           quarter of the row) feed an 11-bit radix histogram per token in
 //           LDS (key bits 30..20 — bit 31, the sign, is always 0 here — as two
@@ -603,33 +604,39 @@ __global__ __launch_bounds__(1024) void long_pick_kernel(IndexerArgs a) {
 //           digits [b_lo, b_hi] meant to hold its k-th largest score: b_hi
 //           leaves about (k - 3 sigma) sampled scores above it, b_lo about
 //           (k + 3 sigma) at or above it, sigma the binomial spread of the
-//           sample count above the k-th largest score;
-//   full pass: every score is computed once; a score above the band sets its
-//           bit in the token's LDS selection bitmap, a score inside it appends
-//           (key, index) to the token's candidate slots;
-//   resolve: per token, the band holds the k-th largest score exactly when the
-//           entries above it number at most k and those above it plus inside
-//           it at least k (every dropped entry lies below every kept one); a
-//           histogram of the candidates' 11-bit digits (counted while their
-//           per-wave slots are compacted) gives the digit of the k-th largest
-//           key; the candidates of that digit (up to 64) are ranked exactly
-//           (larger key first, then lower index — a radix select over the low
-//           20 bits when more share the digit), which completes the bitmap,
-//           written out as the ascending index list.
-// The 16 lanes that hold one token's scores of 16 consecutive entries publish
-// them together: one atomicOr of their bitmap bits; candidates go to the
-// wave's own slots of the token, counted in registers (no LDS round trip in
-// the scoring loop), and are compacted per token before the resolve.
-// A token whose band misses (checked exactly) or overflows its candidate slots
-// is rescored into the workspace and selected by the exact block-wide select.
+//           sample count above the k-th largest score; inside each of those
+//           two digits the band edge is placed by linear interpolation of the
+//           digit's key range over its sampled count;
+//   full pass: every score is computed once; the ballot of "above the band"
+//           over a wave holds four tokens' 16-entry bitmap fields and is
+//           stored whole by one lane (one writer per field: no atomics, no
+//           clearing); scores inside the band are appended as (key, entry)
+//           records to the wave's stream of the four tokens, placed by a
+//           wave-uniform counter and the lane's rank in the ballot;
+//   resolve: two waves per stream set (four tokens), each taking its two
+//           tokens one after the other.  The band holds the k-th largest
+//           score exactly when the entries above it number at most k and
+//           those above plus inside it at least k (every dropped entry is
+//           below every kept one; checked).  A
+//           256-bin histogram of the token's records over its band range
+//           gives the bin of the k-th largest key; records above it are
+//           selected, and those of that bin (up to 64) ranked exactly —
+//           larger key first, then lower index; a bin holding more is
+//           histogrammed again over its own range, down to single keys,
+//           whose ties go to the lowest indices.  The bitmap is written out
+//           as the ascending index list.
+// The LDS footprint stays under half a CU's, so two workgroups share a CU and
+// one's band resolve overlaps the other's scoring.
+// A token whose band misses, or whose stream set overflows, is rescored into
+// the workspace and selected by the exact block-wide select.
 static constexpr int FQ = 16;                  // query tokens per workgroup
 static constexpr int FNT = 512;                // threads per workgroup
 static constexpr int FNW = FNT / 64;
 static constexpr int FK = 512;                 // largest top-k on this path
-static constexpr int FCAP = 1024;              // band candidates per token
-static constexpr int FCAPW = FCAP / FNW;       // ... per (token, wave)
 static constexpr int FMAXN = 8192;             // largest eligible row on this path
-static constexpr int FBM = FMAXN / 32;         // bitmap words per token
+static constexpr int FG = FMAXN / 16;          // 16-entry groups per row
+static constexpr int FU = 4;                   // ballot units (row tile, score slot) of 4 tokens
+static constexpr int FCAPS = 216;              // band records per (unit, wave) stream
 static constexpr int FSTEP = 16 * FNW;         // entries per step of the scoring loop
 static constexpr int FSAMPLE = 4;              // one step in FSAMPLE is sampled
 // Histogram rows are padded with one word after every 32 (sample) or 16
@@ -640,37 +647,53 @@ static constexpr int SROW = 256 + 256 / 16;    // resolve row: 256 bins
 __device__ __forceinline__ int hpad(int w) { return w + (w >> 5); }
 __device__ __forceinline__ int spad(int w) { return w + (w >> 4); }
 
+// The sample histograms are dead once the bands are known, so the record
+// streams and the selection bitmaps share their space; the whole stays
+// under half of a CU's LDS, so two workgroups share a CU and one's resolve
+// overlaps the other's scoring.
 struct FusedSmem {
   union {
     uint32_t hist[FQ + 1][HROW];               // bin i: word hpad(i & 1023), half i >> 10;
                                                // row FQ absorbs ineligible entries
-    uint32_t cand[FQ][FNW][FCAPW][2];          // (key, index) per (token, wave)
+    struct {
+      uint32_t cand[FU][FNW][FCAPS][2];        // (key, entry | g << 16) per (unit, wave)
+      uint64_t bm[FG][FU];                     // 16-bit field g: entries 16E.. of token (u, g)
+    } s;
   } u;
-  uint32_t bm[FQ][FBM];
-  uint32_t scr[FNW][SROW];                     // per-wave radix scratch; fallback select
-  uint32_t ncw[FQ][FNW];                       // candidates per (token, wave)
+  uint32_t scr[FNW][SROW];                     // per-wave resolve scratch; fallback select
+  uint32_t ncs[FU][FNW];                       // records per (unit, wave)
   uint32_t lo_key[FQ], hi_key[FQ], fb[FQ];
 };
+static_assert(sizeof(FusedSmem) <= 80 * 1024, "two workgroups per CU");
+
+// Token of lane group g (lanes 16g..16g+15) in ballot unit u: accumulator rows
+// 16 rt + 4g + i hold token (16 rt + 4g + i) / HI, head (16 rt + 4g + i) % HI;
+// unit u = rt * (4 / HI) + sp takes the sp-th token of the lane's four rows.
+template <int HI>
+__device__ __forceinline__ int unit_token(int u, int g) {
+  constexpr int SPL = 4 / HI;
+  return (16 * (u / SPL) + 4 * g) / HI + u % SPL;
+}
 
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
 }
 
-// Wave-level: scanning nb bins (nb / 64 <= 64 per lane) from the top down, the
-// bin where the running count first reaches `need` (>= 1, <= total) and the
-// count strictly above it.  Each lane sums its run of bins; a scan finds the
-// run, whose bins are then read one per lane and scanned again (no serial
-// search).
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Wave-level: with every lane holding the summed count `local` of its run of
+// `per` bins (lane 0 the top run), the bin where the running count from the
+// top first reaches `need` (>= 1, <= total) and the count strictly above it.
+// The run is found by a scan; its bins are then read one per lane (cnt(i) for
+// bin i of nb) and scanned again (no serial search).
 template <typename Cnt>
-__device__ __forceinline__ void wave_find_bin(int nb, uint32_t need, Cnt cnt, uint32_t& bin,
-                                              uint32_t& above) {
+__device__ __forceinline__ void wave_find_bin_runs(int nb, int per, uint32_t incl, uint32_t local,
+                                                   uint32_t need, Cnt cnt, uint32_t& bin,
+                                                   uint32_t& above) {
   const int lane = threadIdx.x & 63;
-  const int per = nb / 64;
-  const int hi = nb - lane * per;
-  uint32_t local = 0;
-  for (int i = 0; i < per; ++i) local += cnt(hi - 1 - i);
-  const uint32_t incl = wave_incl_scan(local);
   const uint32_t excl = incl - local;
   const uint64_t m = __ballot(excl < need && incl >= need);
   const int src = m ? __ffsll((unsigned long long)m) - 1 : 0;
@@ -683,6 +706,16 @@ __device__ __forceinline__ void wave_find_bin(int nb, uint32_t need, Cnt cnt, ui
   bin = (uint32_t)(shi - 1 - f);
   above = base + (uint32_t)__builtin_amdgcn_readlane((int)(hin - h), f);
 }
+template <typename Cnt>
+__device__ __forceinline__ void wave_find_bin(int nb, uint32_t need, Cnt cnt, uint32_t& bin,
+                                              uint32_t& above) {
+  const int lane = threadIdx.x & 63;
+  const int per = nb / 64;
+  const int hi = nb - lane * per;
+  uint32_t local = 0;
+  for (int i = 0; i < per; ++i) local += cnt(hi - 1 - i);
+  wave_find_bin_runs(nb, per, wave_incl_scan(local), local, need, cnt, bin, above);
+}
 
 // Sampled entries of a row of n eligible entries: the first 128 of every
 // FSAMPLE * 128 (the steps the sample pass scores).
@@ -692,62 +725,67 @@ __device__ __forceinline__ int sample_count(int n) {
 }
 
 template <int QK, int DI, int HI>
-__global__ __launch_bounds__(FNT) void fused_prefill_kernel(IndexerArgs a) {
+__global__ __launch_bounds__(FNT, 4) void fused_prefill_kernel(IndexerArgs a) {
   constexpr int KC = DI / 32;
   constexpr int NRT = HI;                      // 16-row tiles of (token, head) rows
   constexpr int SPL = 4 / HI;                  // scores per lane per row tile
-  constexpr int TPW = FQ / FNW;                // tokens resolved per wave
+  constexpr int TPW = FQ / FNW;                // tokens per wave in the band and resolve phases
+  static_assert(NRT * SPL == FU, "four ballot units");
   using F = typename QkTraits<QK>::F;
   extern __shared__ __align__(16) unsigned char fsm_raw[];
   FusedSmem& sm = *reinterpret_cast<FusedSmem*>(fsm_raw);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
-  const int b = blockIdx.y, t0 = blockIdx.x * FQ;
+  const int b = blockIdx.y, t0 = ((int)gridDim.x - 1 - (int)blockIdx.x) * FQ;
   const int nt = min(FQ, a.Tq - t0);
   const int k = a.topk;
   const int ne_max = row_len(a, b, t0 + nt - 1);
+  const int ne_min = row_len(a, b, t0);                      // rows grow with the token
   const size_t rb = qk_row_bytes<QK>(DI);
 
-  // A operands: row 16 rt + r of the tiles is token (16 rt + r) / HI, head (16 rt + r) % HI
+  // Scoring operands (loaded again for the rare exact fallback rather than
+  // held in registers through the resolve).  A operands: row 16 rt + r of
+  // the tiles is token (16 rt + r) / HI, head (16 rt + r) % HI; the
+  // accumulator rows of lane group g in tile rt are 16 rt + 4g + i.
   F qa[NRT][KC];
-#pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) {
-    const int tt = (16 * rt + r) / HI, h = (16 * rt + r) % HI;
-    const size_t qrow = ((size_t)b * a.Tq + t0 + tt) * HI + h;
-    const char* qptr = reinterpret_cast<const char*>(a.qi) + qrow * rb;
-    const uint8_t* qsc = QK == QK_FP4 ? reinterpret_cast<const uint8_t*>(a.qi_scale) + qrow * (DI / 32) : nullptr;
-#pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      if (tt < nt) load_qk_frag<QK>(qa[rt][c], qptr, qsc, 8 * (g * KC + c));
-      else frag_zero(qa[rt][c]);
-    }
-  }
-  // accumulator rows of lane group g in tile rt: 16 rt + 4g + i -> token (16 rt + 4g + i) / HI
   float wr[NRT][4];
-  int tok[NRT][SPL], tne[NRT][SPL];
+  int tok[FU], tne[FU];
+  auto load_operands = [&]() {
 #pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) {
+    for (int rt = 0; rt < NRT; ++rt) {
+      const int tt = (16 * rt + r) / HI, h = (16 * rt + r) % HI;
+      const size_t qrow = ((size_t)b * a.Tq + t0 + tt) * HI + h;
+      const char* qptr = reinterpret_cast<const char*>(a.qi) + qrow * rb;
+      const uint8_t* qsc = QK == QK_FP4 ? reinterpret_cast<const uint8_t*>(a.qi_scale) + qrow * (DI / 32) : nullptr;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rr = 16 * rt + 4 * g + i;
-      const int tt = rr / HI, h = rr % HI;
-      float wv = 0.f;
-      if (tt < nt) {
-        const size_t wi = ((size_t)b * a.Tq + t0 + tt) * HI + h;
-        wv = a.w[wi];
-        if constexpr (QK == QK_FP8) wv *= reinterpret_cast<const float*>(a.qi_scale)[wi];
+      for (int c = 0; c < KC; ++c) {
+        if (tt < nt) load_qk_frag<QK>(qa[rt][c], qptr, qsc, 8 * (g * KC + c));
+        else frag_zero(qa[rt][c]);
       }
-      wr[rt][i] = wv;
     }
 #pragma unroll
-    for (int sp = 0; sp < SPL; ++sp) {
-      const int tt = (16 * rt + 4 * g) / HI + sp;
-      tok[rt][sp] = tt;
-      tne[rt][sp] = tt < nt ? row_len(a, b, t0 + tt) : 0;
+    for (int rt = 0; rt < NRT; ++rt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rr = 16 * rt + 4 * g + i;
+        const int tt = rr / HI, h = rr % HI;
+        float wv = 0.f;
+        if (tt < nt) {
+          const size_t wi = ((size_t)b * a.Tq + t0 + tt) * HI + h;
+          wv = a.w[wi];
+          if constexpr (QK == QK_FP8) wv *= reinterpret_cast<const float*>(a.qi_scale)[wi];
+        }
+        wr[rt][i] = wv;
+      }
     }
-  }
+#pragma unroll
+    for (int u = 0; u < FU; ++u) {
+      tok[u] = unit_token<HI>(u, g);
+      tne[u] = tok[u] < nt ? row_len(a, b, t0 + tok[u]) : 0;
+    }
+  };
+  load_operands();
   for (int i = tid; i < (FQ + 1) * HROW; i += FNT) (&sm.u.hist[0][0])[i] = 0u;
-  for (int i = tid; i < FQ * FBM; i += FNT) (&sm.bm[0][0])[i] = 0u;
   if (tid < FQ) sm.fb[tid] = 0;
   __syncthreads();
 
@@ -756,14 +794,20 @@ __global__ __launch_bounds__(FNT) void fused_prefill_kernel(IndexerArgs a) {
   const float* fsc = QK == QK_FP8 ? reinterpret_cast<const float*>(a.kic_scale) + (size_t)b * a.Nc_cap : nullptr;
 
   // Scores of entries e0 + 16 wave + r for e0 = first, first + stride, ...
-  // (< ne_max) for every row tile; f(rt, sp, entry, score) is called for
-  // each.  All MFMAs of an entry tile issue before the epilogue reads them.
-  // Two steps of loads are in flight ahead of the one being computed (the
-  // keys come from L2; one step of MFMA + epilogue is shorter than its
-  // latency).
+  // (< ne_max); f(u, e, score, valid, e0) is called for each ballot unit,
+  // valid = the entry is eligible for the lane's token (checked only in the
+  // steps that reach past the shortest row).  All MFMAs of an entry tile
+  // issue before the epilogue reads them.  Three key buffers rotate: each is
+  // reloaded right after its step has read it, so two steps of loads are in
+  // flight during each step's compute (the keys come from L2), and no
+  // in-flight load result is ever copied between registers (a copy would
+  // have to wait for it).
   auto pass = [&](int first, int stride, auto&& f) {
-    RawFrag<QK> kbA[KC], kbB[KC];
-    float ksA = 1.f, ksB = 1.f;
+    RawFrag<QK> kb0[KC], kb1[KC], kb2[KC];
+    float ks0 = 1.f, ks1 = 1.f, ks2 = 1.f;
+    // Loads are issued unconditionally (clamped to the last eligible entry):
+    // with a fixed number of loads per step the compiler's wait counts stay
+    // exact across the loop's back edge.
     auto load = [&](RawFrag<QK> (&kb)[KC], float& ks, int e0) {
       const int e = min(e0 + 16 * wave + r, ne_max - 1);
 #pragma unroll
@@ -772,7 +816,8 @@ __global__ __launch_bounds__(FNT) void fused_prefill_kernel(IndexerArgs a) {
                      8 * (g * KC + c));
       if constexpr (QK == QK_FP8) ks = fsc[e];
     };
-    auto step = [&](int e0, const RawFrag<QK> (&cur)[KC], float cks) {
+    auto step = [&](auto full, int e0, const RawFrag<QK> (&cur)[KC], float cks) {
+      constexpr bool FULL = decltype(full)::value;
       const int e = e0 + 16 * wave + r;
       f32x4 acc[NRT];
 #pragma unroll
@@ -793,33 +838,36 @@ __global__ __launch_bounds__(FNT) void fused_prefill_kernel(IndexerArgs a) {
             sc = fmaf(wr[rt][sp * HI + h], x, sc);
           }
           if constexpr (QK == QK_FP8) sc *= cks;
-          f(rt, sp, e, sc);
+          const int u = rt * SPL + sp;
+          f(u, e, sc, FULL || e < tne[u], e0);
         }
       }
     };
-    if (first < ne_max) load(kbA, ksA, first);
-    if (first + stride < ne_max) load(kbB, ksB, first + stride);
+    auto run = [&](int e0, const RawFrag<QK> (&cur)[KC], float cks) {
+      if (e0 + FSTEP <= ne_min) step(std::true_type{}, e0, cur, cks);    // uniform
+      else step(std::false_type{}, e0, cur, cks);
+    };
+    if (first >= ne_max) return;                               // uniform; also ne_max >= 1 below
+    load(kb0, ks0, first);
+    load(kb1, ks1, first + stride);
+    load(kb2, ks2, first + 2 * stride);
 #pragma unroll 1
-    for (int e0 = first; e0 < ne_max; e0 += 2 * stride) {
-      RawFrag<QK> cur[KC];
-#pragma unroll
-      for (int c = 0; c < KC; ++c) cur[c] = kbA[c];
-      float cks = ksA;
-      if (e0 + 2 * stride < ne_max) load(kbA, ksA, e0 + 2 * stride);
-      step(e0, cur, cks);
+    for (int e0 = first; e0 < ne_max; e0 += 3 * stride) {
+      run(e0, kb0, ks0);
+      load(kb0, ks0, e0 + 3 * stride);
       if (e0 + stride >= ne_max) break;                       // uniform
-#pragma unroll
-      for (int c = 0; c < KC; ++c) cur[c] = kbB[c];
-      cks = ksB;
-      if (e0 + 3 * stride < ne_max) load(kbB, ksB, e0 + 3 * stride);
-      step(e0 + stride, cur, cks);
+      run(e0 + stride, kb1, ks1);
+      load(kb1, ks1, e0 + 4 * stride);
+      if (e0 + 2 * stride >= ne_max) break;
+      run(e0 + 2 * stride, kb2, ks2);
+      load(kb2, ks2, e0 + 5 * stride);
     }
   };
 
   // ---- sample: per-token histograms of key bits 30..20 over a quarter of the row ----
-  pass(0, FSAMPLE * FSTEP, [&](int rt, int sp, int e, float sc) {
+  pass(0, FSAMPLE * FSTEP, [&](int u, int, float sc, bool valid, int) {
     const uint32_t bin = __float_as_uint(sc) >> 20;
-    atomicAdd(&sm.u.hist[e < tne[rt][sp] ? tok[rt][sp] : FQ][hpad(bin & 1023u)], 1u << ((bin >> 10) << 4));
+    atomicAdd(&sm.u.hist[valid ? tok[u] : FQ][hpad(bin & 1023u)], 1u << ((bin >> 10) << 4));
   });
   __syncthreads();
   // ---- each token's band from its sample ----
@@ -830,239 +878,276 @@ __global__ __launch_bounds__(FNT) void fused_prefill_kernel(IndexerArgs a) {
     uint32_t lo_key = 0x7F800000u, hi_key = 0x7F800000u;         // n_e <= k: nothing to select
     if (ne > k) {
       const uint32_t* hrow = sm.u.hist[tt];
+      // lane L's run: bins 2047 - 32 L down to 2016 - 32 L, the upper halves
+      // (lanes < 32) or lower halves (lanes >= 32) of 32 consecutive words
+      const int wb = 992 - 32 * (lane & 31), hs = lane < 32 ? 16 : 0;
+      uint32_t local = 0;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) local += (hrow[hpad(wb + i)] >> hs) & 0xFFFFu;
+      const uint32_t incl = wave_incl_scan(local);
       auto cnt = [&](int i) { return (hrow[hpad(i & 1023)] >> ((i >> 10) << 4)) & 0xFFFFu; };
       const int ns = sample_count(ne);
       const float p = (float)k / (float)ne;
       const float mean = (float)ns * p;
       const float dev = ceilf(3.f * sqrtf(mean * (1.f - p))) + 2.f;
       const int r_hi = (int)floorf(mean - dev), r_lo = (int)ceilf(mean + dev);
-      uint32_t bhi = 2047, blo = 0, ab;
-      if (r_hi >= 1) wave_find_bin(2048, (uint32_t)r_hi + 1u, cnt, bhi, ab);   // <= r_hi sampled above
-      if (r_lo <= ns) wave_find_bin(2048, (uint32_t)r_lo, cnt, blo, ab);      // >= r_lo sampled at or above
-      blo = min(blo, bhi);
-      lo_key = blo << 20;
-      hi_key = min((bhi + 1u) << 20, 0x7F800000u);
+      // Inside the digit that holds the wanted sampled rank, the band edge is
+      // placed by linear interpolation of the digit's key range over its
+      // sampled count (an estimate: the band is checked exactly later).
+      lo_key = 0u;
+      if (r_hi >= 1) {                                         // <= r_hi sampled at or above hi_key
+        uint32_t bin, ab;
+        wave_find_bin_runs(2048, 32, incl, local, (uint32_t)r_hi + 1u, cnt, bin, ab);
+        const uint32_t c = cnt((int)bin), top = (bin + 1u) << 20;
+        const uint32_t cut = (uint32_t)r_hi > ab
+            ? min((uint32_t)ceilf((float)((uint32_t)r_hi - ab) / (float)c * 1048576.f), 1u << 20) : 0u;
+        hi_key = min(top - cut, 0x7F800000u);
+      }
+      if (r_lo <= ns) {                                        // >= r_lo sampled at or above lo_key
+        uint32_t bin, ab;
+        wave_find_bin_runs(2048, 32, incl, local, (uint32_t)r_lo, cnt, bin, ab);
+        const uint32_t c = cnt((int)bin), top = (bin + 1u) << 20;
+        lo_key = top - min((uint32_t)ceilf((float)((uint32_t)r_lo - ab) / (float)c * 1048576.f), 1u << 20);
+      }
+      lo_key = min(lo_key, hi_key);
     }
     if (lane == 0) { sm.lo_key[tt] = lo_key; sm.hi_key[tt] = hi_key; }
   }
   __syncthreads();
-  float thr_lo[NRT][SPL], thr_hi[NRT][SPL];
+  float thr_lo[FU], thr_hi[FU];
 #pragma unroll
-  for (int rt = 0; rt < NRT; ++rt)
+  for (int u = 0; u < FU; ++u) {
+    const bool live = tok[u] < nt;
+    thr_lo[u] = __uint_as_float(live ? sm.lo_key[tok[u]] : 0x7F800000u);
+    thr_hi[u] = __uint_as_float(live ? sm.hi_key[tok[u]] : 0x7F800000u);
+  }
+  __syncthreads();                                           // the histograms become record streams
+  // ---- full pass: bitmap fields above the band, records inside it ----
+  uint32_t ncnt[FU];
 #pragma unroll
-    for (int sp = 0; sp < SPL; ++sp) {
-      const int tt = tok[rt][sp];
-      const bool live = tt < nt;
-      thr_lo[rt][sp] = __uint_as_float(live ? sm.lo_key[tt] : 0x7F800000u);
-      thr_hi[rt][sp] = __uint_as_float(live ? sm.hi_key[tt] : 0x7F800000u);
+  for (int u = 0; u < FU; ++u) ncnt[u] = 0;
+  const uint32_t gtag = (uint32_t)g << 16;
+  pass(0, FSTEP, [&](int u, int e, float sc, bool valid, int e0) {
+    const bool ge_lo = valid && sc >= thr_lo[u];
+    const bool ge_hi = valid && sc >= thr_hi[u];
+    const uint64_t mhi = __ballot(ge_hi);
+    const uint64_t mc = __ballot(ge_lo) & ~mhi;
+    if (lane == 0) sm.u.s.bm[(e0 >> 4) + wave][u] = mhi;
+    if (mc) {                                                 // uniform
+      const uint32_t slot = ncnt[u] + lanes_below(mc);
+      if (ge_lo && !ge_hi && slot < (uint32_t)FCAPS)
+        *reinterpret_cast<uint2*>(&sm.u.s.cand[u][wave][slot][0]) = make_uint2(__float_as_uint(sc), (uint32_t)e | gtag);
+      ncnt[u] += (uint32_t)__popcll(mc);
     }
-  __syncthreads();                                           // the histograms become candidate slots
-  // ---- full pass: bits above the band, candidates inside it ----
-  // Lane group g (lanes 16g..16g+15) holds one token's scores of the 16
-  // consecutive entries e - r .. e - r + 15, which share a bitmap half-word;
-  // the group's running candidate count of its token (the same in its 16
-  // lanes) places the candidates in this wave's slots of the token.
-  uint32_t cntr[NRT][SPL];
-#pragma unroll
-  for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-    for (int sp = 0; sp < SPL; ++sp) cntr[rt][sp] = 0;
-  pass(0, FSTEP, [&](int rt, int sp, int e, float sc) {
-    const bool ok = e < tne[rt][sp] && sc >= thr_lo[rt][sp];
-    const bool above = ok && sc >= thr_hi[rt][sp];
-    const bool inband = ok && !above;
-    const uint64_t ma = __ballot(above), mc = __ballot(inband);
-    if ((ma | mc) == 0) return;                              // uniform
-    const int tt = tok[rt][sp];
-    const uint32_t ga = (uint32_t)(ma >> (16 * g)) & 0xFFFFu;
-    const uint32_t gc = (uint32_t)(mc >> (16 * g)) & 0xFFFFu;
-    if (r == 0 && ga) atomicOr(&sm.bm[tt][e >> 5], ga << (e & 31));
-    const uint32_t slot = cntr[rt][sp] + (uint32_t)__popc(gc & ((1u << r) - 1u));
-    if (inband && slot < (uint32_t)FCAPW) {
-      sm.u.cand[tt][wave][slot][0] = __float_as_uint(sc);
-      sm.u.cand[tt][wave][slot][1] = (uint32_t)e;
-    }
-    cntr[rt][sp] += (uint32_t)__popc(gc);
   });
+  if (lane < FU) {
 #pragma unroll
-  for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-    for (int sp = 0; sp < SPL; ++sp)
-      if (r == 0 && tok[rt][sp] < nt) sm.ncw[tok[rt][sp]][wave] = cntr[rt][sp];
+    for (int u = 0; u < FU; ++u)
+      if (lane == u) sm.ncs[u][wave] = ncnt[u];
+  }
   __syncthreads();
-  // ---- resolve the band, write ascending lists ----
-  uint32_t* scr = sm.scr[wave];
-  constexpr int WPL = FBM / 64;                               // bitmap words per lane
-  for (int j = 0; j < TPW; ++j) {
-    const int tt = TPW * wave + j;
-    if (tt >= nt) break;
-    const int ne = row_len(a, b, t0 + tt);
-    int32_t* idx = a.idx_out + ((size_t)b * a.Tq + t0 + tt) * k;
-    if (ne <= k) {
-      for (int i = lane; i < k; i += 64) idx[i] = i < ne ? i : -1;
-      continue;
-    }
-    const uint32_t cw = lane < FNW ? sm.ncw[tt][lane] : 0u;
-    const uint32_t ncand = wave_sum_u32(min(cw, (uint32_t)FCAPW));
-    const bool ovf = wave_max_u32(cw) > (uint32_t)FCAPW;
-    uint32_t nabove = 0;
+  // ---- resolve the band, two tokens per wave one after the other; write ascending lists ----
+  {
+    const int u = wave >> 1, g0 = 2 * (wave & 1);
+    const uint32_t cs = lane < FNW ? sm.ncs[u][lane] : 0u;
+    const bool uovf = wave_max_u32(cs) > (uint32_t)FCAPS;
+    const uint32_t nrec = min(cs, (uint32_t)FCAPS);
+    uint32_t* scr = sm.scr[wave];
+    const uint16_t* bm16 = reinterpret_cast<const uint16_t*>(&sm.u.s.bm[0][0]);
+    uint32_t* bm32 = reinterpret_cast<uint32_t*>(&sm.u.s.bm[0][0]);
+    // f(ok, key, entry) over the records of the unit's streams with every
+    // lane active (so f may take ballots); ok: the lane holds a record of
+    // token slot gj.  A stream's slots (at most four per lane) are loaded
+    // together, then visited.
+    constexpr int RPL = (FCAPS + 63) / 64;
+    auto for_records = [&](int gj, auto&& f) {
+#pragma unroll 1
+      for (int st = 0; st < FNW; ++st) {
+        const int n = __builtin_amdgcn_readlane((int)nrec, st);
+        const uint32_t* src = &sm.u.s.cand[u][st][0][0];
+        uint2 rc[RPL];
 #pragma unroll
-    for (int q = 0; q < WPL; ++q) nabove += (uint32_t)__popc(sm.bm[tt][lane * WPL + q]);
-    nabove = wave_sum_u32(nabove);
-    if (nabove > (uint32_t)k || nabove + ncand < (uint32_t)k || ovf) {
-      if (lane == 0) {
-        sm.fb[tt] = 1u;
-        count_event(CNT_PREFILL_FALLBACK);
+        for (int it = 0; it < RPL; ++it) {
+          const int i = it * 64 + lane;
+          rc[it] = i < n ? *reinterpret_cast<const uint2*>(src + 2 * i) : make_uint2(0u, 0xFFFF0000u);
+        }
+#pragma unroll
+        for (int it = 0; it < RPL; ++it)
+          if (it * 64 < n) f((rc[it].y >> 16) == (uint32_t)gj, rc[it].x, rc[it].y & 0xFFFFu);   // uniform
       }
-      continue;
-    }
-    // compact the waves' slots of the token into one list, in place (each
-    // wave's run moves to a lower or equal offset, in wave order); a band of
-    // at most 256 digits is counted by digit on the way
-    uint32_t(*cand)[2] = reinterpret_cast<uint32_t(*)[2]>(&sm.u.cand[tt][0][0][0]);
-    const uint32_t blo = sm.lo_key[tt] >> 20;
-    const bool narrow = (sm.hi_key[tt] >> 20) - blo <= 256u;   // hi_key = (b_hi + 1) << 20, or +inf
-    for (int i = lane; i < SROW; i += 64) scr[i] = 0u;
-    wave_sync();
-    uint32_t at = 0;
-    for (int w = 0; w < FNW; ++w) {
-      const uint32_t n = (uint32_t)__builtin_amdgcn_readlane((int)cw, w);
-      const uint32_t* src = &sm.u.cand[tt][w][0][0];
-      for (uint32_t i = lane; i < n; i += 64) {
-        const uint32_t key = src[2 * i], ent = src[2 * i + 1];
-        if (at != (uint32_t)w * FCAPW) { cand[at + i][0] = key; cand[at + i][1] = ent; }
-        if (narrow) atomicAdd(&scr[spad(min((key >> 20) - blo, 255u))], 1u);
+    };
+    // bm[E][u] as 32-bit words: word 2 (E FU + u) + (g >> 1), bits 16 (g & 1) + (e & 15)
+    auto select = [&](int gj, uint32_t e) {
+      atomicOr(&bm32[(((e >> 4) * FU + u) << 1) + (gj >> 1)], 1u << (((gj & 1) << 4) + (e & 15u)));
+    };
+    for (int j = 0; j < 2; ++j) {
+      const int gj = g0 + j;
+      const int tt = unit_token<HI>(u, gj);
+      if (tt >= nt) continue;                                // uniform
+      const int ne = row_len(a, b, t0 + tt);
+      int32_t* idx = a.idx_out + ((size_t)b * a.Tq + t0 + tt) * k;
+      if (ne <= k) {
+        for (int i = lane; i < k; i += 64) idx[i] = i < ne ? i : -1;
+        continue;
       }
-      at += n;
-      wave_sync();
-    }
-    const uint32_t need = (uint32_t)k - nabove;
-    if (need > 0) {
-      // the 11-bit digit d1 of the need-th largest candidate key, and how many
-      // of digit d1 are still needed
-      uint32_t rem = need, d1 = 0;
-      if (narrow) {
-        uint32_t bin, ab;
-        wave_find_bin(256, need, [&](int i) { return scr[spad(i)]; }, bin, ab);
-        d1 = blo + bin;
-        rem = need - ab;
-      } else {
-        for (int p = 0; p < 2; ++p) {                        // 6 then 5 bits of the digit
-          const int sh = p == 0 ? 25 : 20, nb = p == 0 ? 64 : 32;
+      const int nE = (ne + 15) >> 4;
+      uint32_t nab = 0;
+      for (int E = lane; E < nE; E += 64) nab += (uint32_t)__popc(bm16[(E * FU + u) * 4 + gj]);
+      nab = wave_sum_u32(nab);
+      bool fb = uovf || nab > (uint32_t)k;
+      if (!fb && nab < (uint32_t)k) {
+        const uint32_t need = (uint32_t)k - nab;
+        // 256 bins over the band's key range [lo, hi)
+        const uint32_t lo = sm.lo_key[tt], hi = sm.hi_key[tt];
+        const uint32_t span = hi > lo ? hi - lo : 1u;
+        const uint32_t sh = span <= 256u ? 0u : (uint32_t)(32 - __clz((int)(span - 1u))) - 8u;
+        for (int i = lane; i < SROW; i += 64) scr[i] = 0u;
+        wave_sync();
+        uint32_t nc = 0;
+        for_records(gj, [&](bool ok, uint32_t key, uint32_t) {
+          if (ok) {
+            atomicAdd(&scr[spad((int)((key - lo) >> sh))], 1u);
+            ++nc;
+          }
+        });
+        nc = wave_sum_u32(nc);
+        wave_sync();
+        if (need > nc) {
+          fb = true;                                         // the band holds fewer than needed
+        } else {
+          uint32_t bb, ab;
+          wave_find_bin(256, need, [&](int i) { return scr[spad(i)]; }, bb, ab);
+          uint32_t rm = need - ab;                           // >= 1 still needed from bin bb
+          uint32_t cnt1 = scr[spad((int)bb)];
           wave_sync();
-          for (int i = lane; i < 64; i += 64) scr[i] = 0u;
-          wave_sync();
-          for (uint32_t i = lane; i < ncand; i += 64) {
-            const uint32_t key = cand[i][0];
-            if (p == 0 || (key >> 25) == (d1 >> 5)) atomicAdd(&scr[(key >> sh) & (nb - 1)], 1u);
+          // records above bin bb are selected; those in it are gathered (when at
+          // most 64) as (key, entry) pairs into the scratch row
+          {
+            uint32_t at = 0;
+            for_records(gj, [&](bool ok, uint32_t key, uint32_t e) {
+              const uint32_t bin = (key - lo) >> sh;
+              if (ok && bin > bb) select(gj, e);
+              const bool gat = ok && bin == bb && cnt1 <= 64u;
+              const uint64_t m = __ballot(gat);
+              if (gat) {
+                const uint32_t slot = at + lanes_below(m);
+                scr[2 * slot] = key;
+                scr[2 * slot + 1] = e;
+              }
+              at += (uint32_t)__popcll(m);
+            });
           }
           wave_sync();
-          uint32_t bin, ab;
-          wave_find_bin(64, rem, [&](int i) { return scr[i]; }, bin, ab);
-          d1 |= p == 0 ? bin << 5 : bin;
-          rem -= ab;
-        }
-      }
-      wave_sync();
-      // candidates above digit d1 are selected; those of digit d1 (up to 64)
-      // are gathered into scr for an exact rank
-      uint32_t n1 = 0;
-      for (uint32_t i0 = 0; i0 < ncand; i0 += 64) {
-        const uint32_t i = i0 + lane;
-        const uint32_t key = i < ncand ? cand[i][0] : 0u, ent = i < ncand ? cand[i][1] : 0u;
-        const uint32_t d = key >> 20;
-        if (i < ncand && d > d1) atomicOr(&sm.bm[tt][ent >> 5], 1u << (ent & 31));
-        const uint64_t m = __ballot(i < ncand && d == d1);
-        const uint32_t slot = n1 + (uint32_t)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-        if (i < ncand && d == d1 && slot < 64u) { scr[2 * slot] = key; scr[2 * slot + 1] = ent; }
-        n1 += (uint32_t)__popcll(m);
-      }
-      wave_sync();
-      if (n1 <= 64u) {
-        // rank of each gathered key among them: larger keys first, then lower index
-        const uint32_t kl = lane < (int)n1 ? scr[2 * lane] : 0u, el = lane < (int)n1 ? scr[2 * lane + 1] : 0u;
-        uint32_t rank = 0;
-        for (uint32_t j = 0; j < n1; ++j) {
-          const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)kl, (int)j);
-          const uint32_t ej = (uint32_t)__builtin_amdgcn_readlane((int)el, (int)j);
-          rank += (kj > kl || (kj == kl && ej < el)) ? 1u : 0u;
-        }
-        if (lane < (int)n1 && rank < rem) atomicOr(&sm.bm[tt][el >> 5], 1u << (el & 31));
-      } else {
-        // a crowded boundary digit: radix select over its low 20 bits
-        uint32_t prefix = 0, pmask = 0;
-        for (int p = 0; p < 3; ++p) {
-          const int sh = p == 0 ? 12 : (p == 1 ? 4 : 0);
-          const uint32_t dm = p == 2 ? 15u : 255u;
-          wave_sync();
-          for (int i = lane; i < SROW; i += 64) scr[i] = 0u;
-          wave_sync();
-          for (uint32_t i = lane; i < ncand; i += 64) {
-            const uint32_t key = cand[i][0], low = key & 0xFFFFFu;
-            if ((key >> 20) == d1 && (low & pmask) == prefix) atomicAdd(&scr[spad((low >> sh) & dm)], 1u);
+          uint32_t lo2 = lo + (bb << sh), sh2 = sh;          // the boundary bin's key range
+          bool ties = false;
+          // refine a crowded boundary bin over its own range until it holds at
+          // most 64 records or a single key
+#pragma unroll 1
+          while (cnt1 > 64u) {
+            if (sh2 == 0) { ties = true; break; }
+            const uint32_t bspan = 1u << sh2, sh3 = sh2 > 8u ? sh2 - 8u : 0u;
+            for (int i = lane; i < SROW; i += 64) scr[i] = 0u;
+            wave_sync();
+            for_records(gj, [&](bool ok, uint32_t key, uint32_t) {
+              if (ok && key - lo2 < bspan) atomicAdd(&scr[spad((int)((key - lo2) >> sh3))], 1u);
+            });
+            wave_sync();
+            uint32_t b3, ab3;
+            wave_find_bin(256, rm, [&](int i) { return scr[spad(i)]; }, b3, ab3);
+            rm -= ab3;
+            cnt1 = scr[spad((int)b3)];
+            wave_sync();
+            uint32_t at = 0;
+            for_records(gj, [&](bool ok, uint32_t key, uint32_t e) {
+              const bool in = ok && key - lo2 < bspan;
+              const uint32_t bin = (key - lo2) >> sh3;
+              if (in && bin > b3) select(gj, e);
+              const bool gat = in && bin == b3 && cnt1 <= 64u;
+              const uint64_t m = __ballot(gat);
+              if (gat) {
+                const uint32_t slot = at + lanes_below(m);
+                scr[2 * slot] = key;
+                scr[2 * slot + 1] = e;
+              }
+              at += (uint32_t)__popcll(m);
+            });
+            wave_sync();
+            lo2 += b3 << sh3;
+            sh2 = sh3;
           }
-          wave_sync();
-          uint32_t b2, ab2;
-          wave_find_bin(256, rem, [&](int i) { return scr[spad(i)]; }, b2, ab2);
-          prefix |= b2 << sh;
-          pmask |= dm << sh;
-          rem -= ab2;
-        }
-        // rem keys equal to the threshold key (d1, prefix) remain to be taken
-        const uint32_t tkey = (d1 << 20) | prefix;
-        uint32_t neq = 0;
-        for (uint32_t i = lane; i < ncand; i += 64) neq += cand[i][0] == tkey;
-        neq = wave_sum_u32(neq);
-        for (uint32_t i = lane; i < ncand; i += 64) {
-          const uint32_t key = cand[i][0];
-          bool take = (key >> 20) == d1 && key > tkey;
-          if (key == tkey) {
-            if (neq == rem) {
-              take = true;
-            } else {
-              uint32_t rank = 0;
-              for (uint32_t q = 0; q < ncand; ++q) rank += cand[q][0] == tkey && cand[q][1] < cand[i][1];
-              take = rank < rem;
+          if (!ties) {
+            // rank of each gathered record among them: larger key first, then lower index
+            const uint32_t kl = lane < (int)cnt1 ? scr[2 * lane] : 0u;
+            const uint32_t el = lane < (int)cnt1 ? scr[2 * lane + 1] : 0u;
+            uint32_t rank = 0;
+            for (uint32_t q = 0; q < cnt1; ++q) {
+              const uint32_t kq = (uint32_t)__builtin_amdgcn_readlane((int)kl, (int)q);
+              const uint32_t eq = (uint32_t)__builtin_amdgcn_readlane((int)el, (int)q);
+              rank += (kq > kl || (kq == kl && eq < el)) ? 1u : 0u;
+            }
+            if (lane < (int)cnt1 && rank < rm) select(gj, el);
+          } else {
+            // more than 64 records share the key lo2: the rm of lowest index, via
+            // a bitmap of their entries in the scratch row (ne / 32 <= 256 words)
+            for (int i = lane; i < SROW; i += 64) scr[i] = 0u;
+            wave_sync();
+            for_records(gj, [&](bool ok, uint32_t key, uint32_t e) {
+              if (ok && key == lo2) atomicOr(&scr[e >> 5], 1u << (e & 31u));
+            });
+            wave_sync();
+            uint32_t wv[4], c = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) { wv[q] = scr[4 * lane + q]; c += (uint32_t)__popc(wv[q]); }
+            uint32_t pos = wave_incl_scan(c) - c;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              uint32_t w = wv[q];
+              while (w && pos < rm) {
+                const int bit = __ffs(w) - 1;
+                w &= w - 1;
+                select(gj, (uint32_t)((4 * lane + q) * 32 + bit));
+                ++pos;
+              }
             }
           }
-          if (take) atomicOr(&sm.bm[tt][cand[i][1] >> 5], 1u << (cand[i][1] & 31));
+          wave_sync();
         }
       }
+      if (fb) {
+        if (lane == 0) { sm.fb[tt] = 1u; count_event(CNT_PREFILL_FALLBACK); }
+        continue;                                            // written by the exact select below
+      }
+      // the token's bitmap fields, group E = E0 + lane, in ascending order
+      uint32_t base = 0;
+      for (int E0 = 0; E0 < nE; E0 += 64) {
+        const int E = E0 + lane;
+        uint32_t w = E < nE ? (uint32_t)bm16[(E * FU + u) * 4 + gj] : 0u;
+        const uint32_t c = (uint32_t)__popc(w);
+        const uint32_t incl = wave_incl_scan(c);
+        uint32_t pos = base + incl - c;
+        while (w) {
+          const int bit = __ffs(w) - 1;
+          w &= w - 1;
+          if (pos < (uint32_t)k) idx[pos] = E * 16 + bit;
+          ++pos;
+        }
+        base += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+      }
+      for (uint32_t i = base + lane; i < (uint32_t)k; i += 64) idx[i] = -1;
       wave_sync();
     }
-    const int nw = (ne + 31) / 32;
-    uint32_t words[WPL];
-    uint32_t cnt = 0;
-#pragma unroll
-    for (int q = 0; q < WPL; ++q) {
-      const int w = lane * WPL + q;
-      words[q] = w < nw ? sm.bm[tt][w] : 0u;
-      cnt += (uint32_t)__popc(words[q]);
-    }
-    uint32_t pos = wave_incl_scan(cnt) - cnt;
-#pragma unroll
-    for (int q = 0; q < WPL; ++q) {
-      uint32_t word = words[q];
-      while (word) {
-        const int bit = __ffs(word) - 1;
-        word &= word - 1;
-        if (pos < (uint32_t)k) idx[pos] = (lane * WPL + q) * 32 + bit;
-        ++pos;
-      }
-    }
-    const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)pos, 63);
-    for (uint32_t i = tot + lane; i < (uint32_t)k; i += 64) idx[i] = -1;
-    wave_sync();
   }
   __syncthreads();
   // ---- exact fallback for tokens whose band missed or overflowed ----
+  bool any_fb = false;
+  for (int tt = 0; tt < nt; ++tt) any_fb |= sm.fb[tt] != 0u;
+  if (any_fb) load_operands();                               // uniform
   for (int tt = 0; tt < nt; ++tt) {
     if (!sm.fb[tt]) continue;                                // uniform: LDS after a barrier
     const int ne = row_len(a, b, t0 + tt);
     float* srow = reinterpret_cast<float*>(a.ws) + ((size_t)b * a.Tq + t0 + tt) * nc_pad(a.Nc_cap);
-    pass(0, FSTEP, [&](int rt, int sp, int e, float sc) {
-      if (e < tne[rt][sp] && tok[rt][sp] == tt) srow[e] = sc;
+    pass(0, FSTEP, [&](int u, int e, float sc, bool valid, int) {
+      if (valid && tok[u] == tt) srow[e] = sc;
     });
     __syncthreads();
     TopkSmem<FNT>& ts = *reinterpret_cast<TopkSmem<FNT>*>(&sm.scr[0][0]);
