@@ -611,14 +611,15 @@ __global__ __launch_bounds__(1024) void long_pick_kernel(IndexerArgs a) {
 //           over a wave holds four tokens' 16-entry bitmap fields and is
 //           stored whole by one lane (one writer per field: no atomics, no
 //           clearing); scores inside the band are appended as (key, entry)
-//           records to the wave's stream of the four tokens, placed by a
-//           wave-uniform counter and the lane's rank in the ballot;
-//   resolve: two waves per stream set (four tokens), each taking its two
-//           tokens one after the other.  The band holds the k-th largest
+//           records to the wave's stream of the lane's half of the ballot
+//           (two tokens), placed by wave-uniform counters and the lane's rank
+//           in the ballot;
+//   resolve: one wave per stream set (two tokens: the same half of one
+//           unit's ballots in every wave).  The band holds the k-th largest
 //           score exactly when the entries above it number at most k and
 //           those above plus inside it at least k (every dropped entry is
-//           below every kept one; checked).  A
-//           256-bin histogram of the token's records over its band range
+//           below every kept one; checked).  A 128-bin histogram of each
+//           token's records over its band range (both tokens in one pass)
 //           gives the bin of the k-th largest key; records above it are
 //           selected, and those of that bin (up to 64) ranked exactly —
 //           larger key first, then lower index; a bin holding more is
@@ -636,14 +637,14 @@ static constexpr int FK = 512;                 // largest top-k on this path
 static constexpr int FMAXN = 8192;             // largest eligible row on this path
 static constexpr int FG = FMAXN / 16;          // 16-entry groups per row
 static constexpr int FU = 4;                   // ballot units (row tile, score slot) of 4 tokens
-static constexpr int FCAPS = 216;              // band records per (unit, wave) stream
+static constexpr int FCAPH = 108;              // band records per (unit, wave, half) stream
 static constexpr int FSTEP = 16 * FNW;         // entries per step of the scoring loop
 static constexpr int FSAMPLE = 4;              // one step in FSAMPLE is sampled
 // Histogram rows are padded with one word after every 32 (sample) or 16
 // (resolve) so that the per-lane bin ranges of the top-down scan fall in
 // distinct LDS banks.
 static constexpr int HROW = 1024 + 1024 / 32;  // sample row: 2048 bins as 16-bit pairs
-static constexpr int SROW = 256 + 256 / 16;    // resolve row: 256 bins
+static constexpr int SROW = 2 * (128 + 128 / 16);   // resolve row: two tokens' 128 bins
 __device__ __forceinline__ int hpad(int w) { return w + (w >> 5); }
 __device__ __forceinline__ int spad(int w) { return w + (w >> 4); }
 
@@ -656,12 +657,12 @@ struct FusedSmem {
     uint32_t hist[FQ + 1][HROW];               // bin i: word hpad(i & 1023), half i >> 10;
                                                // row FQ absorbs ineligible entries
     struct {
-      uint32_t cand[FU][FNW][FCAPS][2];        // (key, entry | g << 16) per (unit, wave)
+      uint32_t cand[FU][FNW][2][FCAPH][2];     // (key, entry | g << 16) per (unit, wave, g >> 1)
       uint64_t bm[FG][FU];                     // 16-bit field g: entries 16E.. of token (u, g)
     } s;
   } u;
   uint32_t scr[FNW][SROW];                     // per-wave resolve scratch; fallback select
-  uint32_t ncs[FU][FNW];                       // records per (unit, wave)
+  uint32_t ncs[FU][FNW][2];                    // records per (unit, wave, half)
   uint32_t lo_key[FQ], hi_key[FQ], fb[FQ];
 };
 static_assert(sizeof(FusedSmem) <= 80 * 1024, "two workgroups per CU");
@@ -923,10 +924,13 @@ __global__ __launch_bounds__(FNT, 4) void fused_prefill_kernel(IndexerArgs a) {
   }
   __syncthreads();                                           // the histograms become record streams
   // ---- full pass: bitmap fields above the band, records inside it ----
-  uint32_t ncnt[FU];
+  // record counters per (unit, half of the ballot: lanes 0-31 hold token
+  // slots 0 and 1, lanes 32-63 slots 2 and 3)
+  uint32_t ncnt[FU][2];
 #pragma unroll
-  for (int u = 0; u < FU; ++u) ncnt[u] = 0;
+  for (int u = 0; u < FU; ++u) ncnt[u][0] = ncnt[u][1] = 0;
   const uint32_t gtag = (uint32_t)g << 16;
+  const int half = lane >> 5;
   pass(0, FSTEP, [&](int u, int e, float sc, bool valid, int e0) {
     const bool ge_lo = valid && sc >= thr_lo[u];
     const bool ge_hi = valid && sc >= thr_hi[u];
@@ -934,194 +938,228 @@ __global__ __launch_bounds__(FNT, 4) void fused_prefill_kernel(IndexerArgs a) {
     const uint64_t mc = __ballot(ge_lo) & ~mhi;
     if (lane == 0) sm.u.s.bm[(e0 >> 4) + wave][u] = mhi;
     if (mc) {                                                 // uniform
-      const uint32_t slot = ncnt[u] + lanes_below(mc);
-      if (ge_lo && !ge_hi && slot < (uint32_t)FCAPS)
-        *reinterpret_cast<uint2*>(&sm.u.s.cand[u][wave][slot][0]) = make_uint2(__float_as_uint(sc), (uint32_t)e | gtag);
-      ncnt[u] += (uint32_t)__popcll(mc);
+      const uint32_t plo = (uint32_t)__popc((uint32_t)mc), phi = (uint32_t)__popc((uint32_t)(mc >> 32));
+      const uint32_t slot = (half ? ncnt[u][1] - plo : ncnt[u][0]) + lanes_below(mc);
+      if (ge_lo && !ge_hi && slot < (uint32_t)FCAPH)
+        *reinterpret_cast<uint2*>(&sm.u.s.cand[u][wave][half][slot][0]) = make_uint2(__float_as_uint(sc), (uint32_t)e | gtag);
+      ncnt[u][0] += plo;
+      ncnt[u][1] += phi;
     }
   });
-  if (lane < FU) {
+  if (lane < 2 * FU) {
 #pragma unroll
     for (int u = 0; u < FU; ++u)
-      if (lane == u) sm.ncs[u][wave] = ncnt[u];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        if (lane == 2 * u + h) sm.ncs[u][wave][h] = ncnt[u][h];
   }
   __syncthreads();
-  // ---- resolve the band, two tokens per wave one after the other; write ascending lists ----
+  // ---- resolve the bands of the wave's two tokens, write ascending lists ----
   {
-    const int u = wave >> 1, g0 = 2 * (wave & 1);
-    const uint32_t cs = lane < FNW ? sm.ncs[u][lane] : 0u;
-    const bool uovf = wave_max_u32(cs) > (uint32_t)FCAPS;
-    const uint32_t nrec = min(cs, (uint32_t)FCAPS);
-    uint32_t* scr = sm.scr[wave];
+    const int u = wave >> 1, hf = wave & 1, g0 = 2 * hf;
+    const uint32_t cs = lane < FNW ? sm.ncs[u][lane][hf] : 0u;
+    const bool sovf = wave_max_u32(cs) > (uint32_t)FCAPH;
+    const uint32_t nrec = min(cs, (uint32_t)FCAPH);
     const uint16_t* bm16 = reinterpret_cast<const uint16_t*>(&sm.u.s.bm[0][0]);
     uint32_t* bm32 = reinterpret_cast<uint32_t*>(&sm.u.s.bm[0][0]);
-    // f(ok, key, entry) over the records of the unit's streams with every
-    // lane active (so f may take ballots); ok: the lane holds a record of
-    // token slot gj.  A stream's slots (at most four per lane) are loaded
-    // together, then visited.
-    constexpr int RPL = (FCAPS + 63) / 64;
-    auto for_records = [&](int gj, auto&& f) {
+    // f(ok, j, key, entry) over the records of the stream set with every lane
+    // active (so f may take ballots); ok: the lane holds a record, of token
+    // slot g0 + j.  A stream's slots (two per lane) are loaded together.
+    constexpr int RPL = (FCAPH + 63) / 64;
+    auto for_records = [&](auto&& f) {
 #pragma unroll 1
       for (int st = 0; st < FNW; ++st) {
         const int n = __builtin_amdgcn_readlane((int)nrec, st);
-        const uint32_t* src = &sm.u.s.cand[u][st][0][0];
+        const uint32_t* src = &sm.u.s.cand[u][st][hf][0][0];
         uint2 rc[RPL];
 #pragma unroll
         for (int it = 0; it < RPL; ++it) {
           const int i = it * 64 + lane;
-          rc[it] = i < n ? *reinterpret_cast<const uint2*>(src + 2 * i) : make_uint2(0u, 0xFFFF0000u);
+          rc[it] = i < n ? *reinterpret_cast<const uint2*>(src + 2 * i) : make_uint2(0u, 0u);
         }
 #pragma unroll
         for (int it = 0; it < RPL; ++it)
-          if (it * 64 < n) f((rc[it].y >> 16) == (uint32_t)gj, rc[it].x, rc[it].y & 0xFFFFu);   // uniform
+          if (it * 64 < n) f(it * 64 + lane < n, (rc[it].y >> 16) & 1u, rc[it].x, rc[it].y & 0xFFFFu);   // uniform
       }
     };
     // bm[E][u] as 32-bit words: word 2 (E FU + u) + (g >> 1), bits 16 (g & 1) + (e & 15)
-    auto select = [&](int gj, uint32_t e) {
-      atomicOr(&bm32[(((e >> 4) * FU + u) << 1) + (gj >> 1)], 1u << (((gj & 1) << 4) + (e & 15u)));
+    auto select = [&](int j, uint32_t e) {
+      atomicOr(&bm32[(((e >> 4) * FU + u) << 1) + hf], 1u << ((j << 4) + (e & 15u)));
     };
+    // token slot j's half of the scratch row: 128 bins (padded) or a 64-pair list
+    auto hrow = [&](int j) { return sm.scr[wave] + j * (SROW / 2); };
+    int tt[2], ne[2];
+    bool act[2], fbk[2];
+    uint32_t need[2], lo[2], sh[2];
+#pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int gj = g0 + j;
-      const int tt = unit_token<HI>(u, gj);
-      if (tt >= nt) continue;                                // uniform
-      const int ne = row_len(a, b, t0 + tt);
-      int32_t* idx = a.idx_out + ((size_t)b * a.Tq + t0 + tt) * k;
-      if (ne <= k) {
-        for (int i = lane; i < k; i += 64) idx[i] = i < ne ? i : -1;
-        continue;
-      }
-      const int nE = (ne + 15) >> 4;
+      tt[j] = unit_token<HI>(u, g0 + j);
+      ne[j] = tt[j] < nt ? row_len(a, b, t0 + tt[j]) : 0;
+      act[j] = ne[j] > k;
+      fbk[j] = false;
       uint32_t nab = 0;
-      for (int E = lane; E < nE; E += 64) nab += (uint32_t)__popc(bm16[(E * FU + u) * 4 + gj]);
-      nab = wave_sum_u32(nab);
-      bool fb = uovf || nab > (uint32_t)k;
-      if (!fb && nab < (uint32_t)k) {
-        const uint32_t need = (uint32_t)k - nab;
-        // 256 bins over the band's key range [lo, hi)
-        const uint32_t lo = sm.lo_key[tt], hi = sm.hi_key[tt];
-        const uint32_t span = hi > lo ? hi - lo : 1u;
-        const uint32_t sh = span <= 256u ? 0u : (uint32_t)(32 - __clz((int)(span - 1u))) - 8u;
-        for (int i = lane; i < SROW; i += 64) scr[i] = 0u;
-        wave_sync();
-        uint32_t nc = 0;
-        for_records(gj, [&](bool ok, uint32_t key, uint32_t) {
-          if (ok) {
-            atomicAdd(&scr[spad((int)((key - lo) >> sh))], 1u);
-            ++nc;
-          }
-        });
-        nc = wave_sum_u32(nc);
-        wave_sync();
-        if (need > nc) {
-          fb = true;                                         // the band holds fewer than needed
-        } else {
-          uint32_t bb, ab;
-          wave_find_bin(256, need, [&](int i) { return scr[spad(i)]; }, bb, ab);
-          uint32_t rm = need - ab;                           // >= 1 still needed from bin bb
-          uint32_t cnt1 = scr[spad((int)bb)];
-          wave_sync();
-          // records above bin bb are selected; those in it are gathered (when at
-          // most 64) as (key, entry) pairs into the scratch row
-          {
-            uint32_t at = 0;
-            for_records(gj, [&](bool ok, uint32_t key, uint32_t e) {
-              const uint32_t bin = (key - lo) >> sh;
-              if (ok && bin > bb) select(gj, e);
-              const bool gat = ok && bin == bb && cnt1 <= 64u;
-              const uint64_t m = __ballot(gat);
-              if (gat) {
-                const uint32_t slot = at + lanes_below(m);
-                scr[2 * slot] = key;
-                scr[2 * slot + 1] = e;
-              }
-              at += (uint32_t)__popcll(m);
-            });
-          }
-          wave_sync();
-          uint32_t lo2 = lo + (bb << sh), sh2 = sh;          // the boundary bin's key range
-          bool ties = false;
-          // refine a crowded boundary bin over its own range until it holds at
-          // most 64 records or a single key
+      if (act[j]) {
+        const int nE = (ne[j] + 15) >> 4;
+        for (int E = lane; E < nE; E += 64) nab += (uint32_t)__popc(bm16[(E * FU + u) * 4 + g0 + j]);
+        nab = wave_sum_u32(nab);
+        if (sovf || nab > (uint32_t)k) { fbk[j] = true; act[j] = false; }
+        else if (nab == (uint32_t)k) act[j] = false;         // the entries above the band are the k
+      }
+      need[j] = (uint32_t)k - nab;
+      const uint32_t lk = act[j] ? sm.lo_key[tt[j]] : 0u, hk = act[j] ? sm.hi_key[tt[j]] : 0u;
+      const uint32_t span = hk > lk ? hk - lk : 1u;
+      lo[j] = lk;
+      sh[j] = span <= 128u ? 0u : (uint32_t)(32 - __clz((int)(span - 1u))) - 7u;
+    }
+    if (act[0] || act[1]) {                                  // uniform
+      // histograms of both tokens' records over their band ranges
+      for (int i = lane; i < SROW; i += 64) sm.scr[wave][i] = 0u;
+      wave_sync();
+      uint32_t nc0 = 0, nc1 = 0;
+      for_records([&](bool ok, uint32_t j, uint32_t key, uint32_t) {
+        if (ok && (j ? act[1] : act[0])) {
+          atomicAdd(&hrow((int)j)[spad((int)((key - (j ? lo[1] : lo[0])) >> (j ? sh[1] : sh[0])))], 1u);
+          if (j) ++nc1; else ++nc0;
+        }
+      });
+      const uint32_t nc[2] = {wave_sum_u32(nc0), wave_sum_u32(nc1)};
+      wave_sync();
+      uint32_t bb[2] = {0u, 0u}, rem[2] = {0u, 0u}, n1[2] = {0u, 0u};
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        if (!act[j]) continue;
+        if (need[j] > nc[j]) { fbk[j] = true; act[j] = false; continue; }   // the band holds too few
+        uint32_t ab;
+        wave_find_bin(128, need[j], [&](int i) { return hrow(j)[spad(i)]; }, bb[j], ab);
+        rem[j] = need[j] - ab;                               // >= 1 still needed from bin bb
+        n1[j] = hrow(j)[spad((int)bb[j])];
+      }
+      wave_sync();
+      // records above the boundary bin are selected; those in it are gathered
+      // (when at most 64) as (key, entry) pairs into the token's half row
+      uint32_t at0 = 0, at1 = 0;
+      for_records([&](bool ok, uint32_t j, uint32_t key, uint32_t e) {
+        const bool on = ok && (j ? act[1] : act[0]);
+        const uint32_t bin = (key - (j ? lo[1] : lo[0])) >> (j ? sh[1] : sh[0]);
+        const uint32_t bj = j ? bb[1] : bb[0];
+        if (on && bin > bj) select((int)j, e);
+        const bool gat = on && bin == bj && (j ? n1[1] : n1[0]) <= 64u;
+        const uint64_t m0 = __ballot(gat && j == 0u), m1 = __ballot(gat && j == 1u);
+        if (gat) {
+          const uint32_t slot = j ? at1 + lanes_below(m1) : at0 + lanes_below(m0);
+          hrow((int)j)[2 * slot] = key;
+          hrow((int)j)[2 * slot + 1] = e;
+        }
+        at0 += (uint32_t)__popcll(m0);
+        at1 += (uint32_t)__popcll(m1);
+      });
+      wave_sync();
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        if (!act[j]) continue;
+        uint32_t* row = hrow(j);
+        uint32_t cnt1 = n1[j], rm = rem[j];
+        uint32_t lo2 = lo[j] + (bb[j] << sh[j]), sh2 = sh[j];   // the boundary bin's key range
+        bool ties = false;
+        // refine a crowded boundary bin over its own range until it holds at
+        // most 64 records or a single key
 #pragma unroll 1
-          while (cnt1 > 64u) {
-            if (sh2 == 0) { ties = true; break; }
-            const uint32_t bspan = 1u << sh2, sh3 = sh2 > 8u ? sh2 - 8u : 0u;
-            for (int i = lane; i < SROW; i += 64) scr[i] = 0u;
-            wave_sync();
-            for_records(gj, [&](bool ok, uint32_t key, uint32_t) {
-              if (ok && key - lo2 < bspan) atomicAdd(&scr[spad((int)((key - lo2) >> sh3))], 1u);
-            });
-            wave_sync();
-            uint32_t b3, ab3;
-            wave_find_bin(256, rm, [&](int i) { return scr[spad(i)]; }, b3, ab3);
-            rm -= ab3;
-            cnt1 = scr[spad((int)b3)];
-            wave_sync();
-            uint32_t at = 0;
-            for_records(gj, [&](bool ok, uint32_t key, uint32_t e) {
-              const bool in = ok && key - lo2 < bspan;
-              const uint32_t bin = (key - lo2) >> sh3;
-              if (in && bin > b3) select(gj, e);
-              const bool gat = in && bin == b3 && cnt1 <= 64u;
-              const uint64_t m = __ballot(gat);
-              if (gat) {
-                const uint32_t slot = at + lanes_below(m);
-                scr[2 * slot] = key;
-                scr[2 * slot + 1] = e;
-              }
-              at += (uint32_t)__popcll(m);
-            });
-            wave_sync();
-            lo2 += b3 << sh3;
-            sh2 = sh3;
-          }
-          if (!ties) {
-            // rank of each gathered record among them: larger key first, then lower index
-            const uint32_t kl = lane < (int)cnt1 ? scr[2 * lane] : 0u;
-            const uint32_t el = lane < (int)cnt1 ? scr[2 * lane + 1] : 0u;
-            uint32_t rank = 0;
-            for (uint32_t q = 0; q < cnt1; ++q) {
-              const uint32_t kq = (uint32_t)__builtin_amdgcn_readlane((int)kl, (int)q);
-              const uint32_t eq = (uint32_t)__builtin_amdgcn_readlane((int)el, (int)q);
-              rank += (kq > kl || (kq == kl && eq < el)) ? 1u : 0u;
+        while (cnt1 > 64u) {
+          if (sh2 == 0) { ties = true; break; }
+          const uint32_t bspan = 1u << sh2, sh3 = sh2 > 7u ? sh2 - 7u : 0u;
+          for (int i = lane; i < SROW / 2; i += 64) row[i] = 0u;
+          wave_sync();
+          for_records([&](bool ok, uint32_t jj, uint32_t key, uint32_t) {
+            if (ok && jj == (uint32_t)j && key - lo2 < bspan) atomicAdd(&row[spad((int)((key - lo2) >> sh3))], 1u);
+          });
+          wave_sync();
+          uint32_t b3, ab3;
+          wave_find_bin(128, rm, [&](int i) { return row[spad(i)]; }, b3, ab3);
+          rm -= ab3;
+          cnt1 = row[spad((int)b3)];
+          wave_sync();
+          uint32_t at = 0;
+          for_records([&](bool ok, uint32_t jj, uint32_t key, uint32_t e) {
+            const bool in = ok && jj == (uint32_t)j && key - lo2 < bspan;
+            const uint32_t bin = (key - lo2) >> sh3;
+            if (in && bin > b3) select(j, e);
+            const bool gat = in && bin == b3 && cnt1 <= 64u;
+            const uint64_t m = __ballot(gat);
+            if (gat) {
+              const uint32_t slot = at + lanes_below(m);
+              row[2 * slot] = key;
+              row[2 * slot + 1] = e;
             }
-            if (lane < (int)cnt1 && rank < rm) select(gj, el);
-          } else {
-            // more than 64 records share the key lo2: the rm of lowest index, via
-            // a bitmap of their entries in the scratch row (ne / 32 <= 256 words)
-            for (int i = lane; i < SROW; i += 64) scr[i] = 0u;
+            at += (uint32_t)__popcll(m);
+          });
+          wave_sync();
+          lo2 += b3 << sh3;
+          sh2 = sh3;
+        }
+        if (!ties) {
+          // rank of each gathered record among them: larger key first, then lower index
+          const uint32_t kl = lane < (int)cnt1 ? row[2 * lane] : 0u;
+          const uint32_t el = lane < (int)cnt1 ? row[2 * lane + 1] : 0u;
+          uint32_t rank = 0;
+          for (uint32_t q = 0; q < cnt1; ++q) {
+            const uint32_t kq = (uint32_t)__builtin_amdgcn_readlane((int)kl, (int)q);
+            const uint32_t eq = (uint32_t)__builtin_amdgcn_readlane((int)el, (int)q);
+            rank += (kq > kl || (kq == kl && eq < el)) ? 1u : 0u;
+          }
+          if (lane < (int)cnt1 && rank < rm) select(j, el);
+        } else {
+          // more than 64 records share the key lo2: the rm of lowest index, one
+          // 4096-entry range at a time through a bitmap in the half row
+#pragma unroll 1
+          for (int e0 = 0; e0 < ne[j] && rm > 0u; e0 += 4096) {
+            for (int i = lane; i < SROW / 2; i += 64) row[i] = 0u;
             wave_sync();
-            for_records(gj, [&](bool ok, uint32_t key, uint32_t e) {
-              if (ok && key == lo2) atomicOr(&scr[e >> 5], 1u << (e & 31u));
+            for_records([&](bool ok, uint32_t jj, uint32_t key, uint32_t e) {
+              if (ok && jj == (uint32_t)j && key == lo2 && e - (uint32_t)e0 < 4096u)
+                atomicOr(&row[(e - (uint32_t)e0) >> 5], 1u << (e & 31u));
             });
             wave_sync();
-            uint32_t wv[4], c = 0;
+            uint32_t wv[2], c = 0;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) { wv[q] = scr[4 * lane + q]; c += (uint32_t)__popc(wv[q]); }
-            uint32_t pos = wave_incl_scan(c) - c;
+            for (int q = 0; q < 2; ++q) { wv[q] = row[2 * lane + q]; c += (uint32_t)__popc(wv[q]); }
+            const uint32_t incl = wave_incl_scan(c);
+            uint32_t pos = incl - c;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
+            for (int q = 0; q < 2; ++q) {
               uint32_t w = wv[q];
               while (w && pos < rm) {
                 const int bit = __ffs(w) - 1;
                 w &= w - 1;
-                select(gj, (uint32_t)((4 * lane + q) * 32 + bit));
+                select(j, (uint32_t)(e0 + (2 * lane + q) * 32 + bit));
                 ++pos;
               }
             }
+            const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+            rm -= min(tot, rm);
+            wave_sync();
           }
-          wave_sync();
         }
+        wave_sync();
       }
-      if (fb) {
-        if (lane == 0) { sm.fb[tt] = 1u; count_event(CNT_PREFILL_FALLBACK); }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (tt[j] >= nt) continue;                             // uniform
+      int32_t* idx = a.idx_out + ((size_t)b * a.Tq + t0 + tt[j]) * k;
+      if (ne[j] <= k) {
+        for (int i = lane; i < k; i += 64) idx[i] = i < ne[j] ? i : -1;
+        continue;
+      }
+      if (fbk[j]) {
+        if (lane == 0) { sm.fb[tt[j]] = 1u; count_event(CNT_PREFILL_FALLBACK); }
         continue;                                            // written by the exact select below
       }
       // the token's bitmap fields, group E = E0 + lane, in ascending order
+      const int nE = (ne[j] + 15) >> 4;
       uint32_t base = 0;
       for (int E0 = 0; E0 < nE; E0 += 64) {
         const int E = E0 + lane;
-        uint32_t w = E < nE ? (uint32_t)bm16[(E * FU + u) * 4 + gj] : 0u;
+        uint32_t w = E < nE ? (uint32_t)bm16[(E * FU + u) * 4 + g0 + j] : 0u;
         const uint32_t c = (uint32_t)__popc(w);
         const uint32_t incl = wave_incl_scan(c);
         uint32_t pos = base + incl - c;
@@ -1134,7 +1172,6 @@ __global__ __launch_bounds__(FNT, 4) void fused_prefill_kernel(IndexerArgs a) {
         base += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
       }
       for (uint32_t i = base + lane; i < (uint32_t)k; i += 64) idx[i] = -1;
-      wave_sync();
     }
   }
   __syncthreads();
