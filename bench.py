@@ -81,7 +81,8 @@ def parse():
 # measured HBM traffic of the dominant kernel (from rocprofv3 counters)
 # ----------------------------------------------------------------------------
 TRAFFIC_KERNEL = "score_row_kernel"           # the decode indexer score kernel
-TRAFFIC_SOURCES = ("sparse_attention_17_amd/csrc/indexer.hip", "sparse_attention_17_amd/csrc/common.hpp")
+TRAFFIC_SOURCES = ("sparse_attention_17_amd/csrc/indexer.hip", "sparse_attention_17_amd/csrc/common.hpp",
+                   "sparse_attention_17_amd/csrc/pick_impl.hpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_score_hybrid_1m_fp8_traffic.json")
 COPY_BYTES = 256 << 20
 

@@ -657,7 +657,7 @@ struct FusedSmem {
     uint32_t hist[FQ + 1][HROW];               // bin i: word hpad(i & 1023), half i >> 10;
                                                // row FQ absorbs ineligible entries
     struct {
-      uint32_t cand[FU][FNW][2][FCAPH][2];     // (key, entry | g << 16) per (unit, wave, g >> 1)
+      uint32_t cand[FU][2][FNW][FCAPH][2];     // (key, entry | g << 16) per (unit, g >> 1, wave)
       uint64_t bm[FG][FU];                     // 16-bit field g: entries 16E.. of token (u, g)
     } s;
   } u;
@@ -786,7 +786,8 @@ __global__ __launch_bounds__(FNT, 4) void fused_prefill_kernel(IndexerArgs a) {
     }
   };
   load_operands();
-  for (int i = tid; i < (FQ + 1) * HROW; i += FNT) (&sm.u.hist[0][0])[i] = 0u;
+  static_assert((FQ + 1) * HROW % 4 == 0, "histograms cleared 16 bytes at a time");
+  for (int i = tid; i < (FQ + 1) * HROW / 4; i += FNT) reinterpret_cast<uint4*>(&sm.u.hist[0][0])[i] = make_uint4(0u, 0u, 0u, 0u);
   if (tid < FQ) sm.fb[tid] = 0;
   __syncthreads();
 
@@ -941,7 +942,7 @@ __global__ __launch_bounds__(FNT, 4) void fused_prefill_kernel(IndexerArgs a) {
       const uint32_t plo = (uint32_t)__popc((uint32_t)mc), phi = (uint32_t)__popc((uint32_t)(mc >> 32));
       const uint32_t slot = (half ? ncnt[u][1] - plo : ncnt[u][0]) + lanes_below(mc);
       if (ge_lo && !ge_hi && slot < (uint32_t)FCAPH)
-        *reinterpret_cast<uint2*>(&sm.u.s.cand[u][wave][half][slot][0]) = make_uint2(__float_as_uint(sc), (uint32_t)e | gtag);
+        *reinterpret_cast<uint2*>(&sm.u.s.cand[u][half][wave][slot][0]) = make_uint2(__float_as_uint(sc), (uint32_t)e | gtag);
       ncnt[u][0] += plo;
       ncnt[u][1] += phi;
     }
@@ -970,7 +971,7 @@ __global__ __launch_bounds__(FNT, 4) void fused_prefill_kernel(IndexerArgs a) {
 #pragma unroll 1
       for (int st = 0; st < FNW; ++st) {
         const int n = __builtin_amdgcn_readlane((int)nrec, st);
-        const uint32_t* src = &sm.u.s.cand[u][st][hf][0][0];
+        const uint32_t* src = &sm.u.s.cand[u][hf][st][0][0];
         uint2 rc[RPL];
 #pragma unroll
         for (int it = 0; it < RPL; ++it) {
