@@ -539,21 +539,20 @@ __global__ __launch_bounds__(256) void score_row_fp4_kernel(IndexerArgs a) {
       atomicAdd(&hist[__float_as_uint(sc) >> (32 - H1_BITS)], 1u);
     }
   };
+  // The chunk's groups of this wave (64 entries each, 256 apart) are all
+  // requested up front — unconditionally, addresses clamped to the last
+  // entry — and then scored in order: every load is in flight before the
+  // first wait, and a fixed load count keeps the wait counts exact.
   constexpr int STRIDE = 4 * EPC;
-  u32x4 kvA[NM], kvB[NM];
-  int ksA[NM], ksB[NM];
-  int e0 = c0 + wave * EPC;
-  if (e0 < c1) load_group(e0, kvA, ksA);
-  if (e0 + STRIDE < c1) load_group(e0 + STRIDE, kvB, ksB);
-#pragma unroll 1
-  for (; e0 < c1; e0 += 2 * STRIDE) {
-    process(e0, kvA, ksA);
-    if (e0 + 2 * STRIDE < c1) load_group(e0 + 2 * STRIDE, kvA, ksA);
-    if (e0 + STRIDE < c1) {
-      process(e0 + STRIDE, kvB, ksB);
-      if (e0 + 3 * STRIDE < c1) load_group(e0 + 3 * STRIDE, kvB, ksB);
-    }
-  }
+  constexpr int NGW = SCORE_CHUNK / STRIDE;
+  u32x4 kv[NGW][NM];
+  int ks[NGW][NM];
+  const int e0 = c0 + wave * EPC;
+#pragma unroll
+  for (int gi = 0; gi < NGW; ++gi) load_group(e0 + gi * STRIDE, kv[gi], ks[gi]);
+#pragma unroll
+  for (int gi = 0; gi < NGW; ++gi)
+    if (e0 + gi * STRIDE < c1) process(e0 + gi * STRIDE, kv[gi], ks[gi]);   // uniform
   __syncthreads();
   if (n > a.topk) chunk_cut(a, L, row, chunk, n, c0, c1 - c0, sk, hist, cut_ws);
 }
