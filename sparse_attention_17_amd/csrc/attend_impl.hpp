@@ -82,6 +82,7 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
   constexpr int VS = KT + VPAD;                // Vt row stride (elements)
   constexpr int DSTEP = D / 16;                // k-steps of S^T
   constexpr int DVT = D / 32;                  // 32-wide dv tiles of O^T
+  static_assert(D <= 128, "the V-tile swizzle term (dim >> 3) must stay below 16");
 
   T* Ks = reinterpret_cast<T*>(smem_raw);
   T* Vt = Ks + KT * KS;
@@ -356,13 +357,26 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
         if constexpr (KV8)
           if ((!vshared || ch < DN / VEC) && ent(s0 + kg * 4 + u) >= 0) vr[u] = widen8(vr[u]);
       }
-      const T* rows = reinterpret_cast<const T*>(vr);           // [4][VEC]
+      if constexpr (sizeof(T) == 2) {
+        // dim ch*8+e of the four keys: 16-bit half e&1 of word e>>1 of each
+        // row, paired by byte permutes; the 8 dims share one swizzled block
+        // (vt_block depends on the dim's 8-group only), 8 rows apart
+        T* dst = Vt + ch * VEC * VS + vt_block(ch * VEC, kg) * 4;
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        T four[4] = {rows[e], rows[VEC + e], rows[2 * VEC + e], rows[3 * VEC + e]};
-        T* dst = Vt + (ch * VEC + e) * VS + vt_block(ch * VEC + e, kg) * 4;
-        if constexpr (sizeof(T) == 2) *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<uint2*>(four);
-        else *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<u32x4*>(four);
+        for (int e = 0; e < VEC; ++e) {
+          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+          const uint32_t w01 = __builtin_amdgcn_perm(vr[1][e >> 1], vr[0][e >> 1], sel);
+          const uint32_t w23 = __builtin_amdgcn_perm(vr[3][e >> 1], vr[2][e >> 1], sel);
+          *reinterpret_cast<uint2*>(dst + e * VS) = uint2{w01, w23};
+        }
+      } else {
+        const T* rows = reinterpret_cast<const T*>(vr);         // [4][VEC]
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          T four[4] = {rows[e], rows[VEC + e], rows[2 * VEC + e], rows[3 * VEC + e]};
+          T* dst = Vt + (ch * VEC + e) * VS + vt_block(ch * VEC + e, kg) * 4;
+          *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<u32x4*>(four);
+        }
       }
     }
   };
@@ -371,6 +385,13 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
   if constexpr (PF == 2) {
     if (kbeg + KT < kend) stage_load(kregB, vregB, sclB, kbeg + KT);
   }
+  // One tile ahead: the first staging store needs the first tile, so waiting
+  // here for every load (the query fragments included) costs nothing, and it
+  // tells the compiler's wait insertion that the query registers are ready,
+  // so the loop does not wait on the vector-memory counter at the query's
+  // uses (which, in steady state, would hold the MFMAs until the next tile's
+  // prefetch had landed).
+  if constexpr (PF == 1) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   // the row scales of a lane's 16 keys in sub-tile `sub` (S^T rows
   // 8 (r >> 2) + 4 half + (r & 3)), from the staged scale array
   auto lane_scales = [&](const float* scl_arr, int sub, float (&out)[16]) {
@@ -499,23 +520,31 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
     l_run += psum;
 
     // ---- O^T += V^T P^T ----
+    // Lane (col, half) reads dim row 32i + col, 4-key blocks kb/4 and kb/4 + 2
+    // with kb/4 = 8 sub + 4 ks + half.  The row's swizzle term (row >> 3) is
+    // 4i + (col >> 3), so the block position splits into a per-lane part
+    // (bits 0-1: (2 hi + half) ^ (col >> 3)) and a part fixed by (i, sub, ks)
+    // (bits 2-3: (2 sub + ks) ^ i): two base addresses per lane and
+    // immediate offsets address every read.
+    const int c3 = col >> 3;
+    const T* vb0 = Vt + col * VS + 4 * ((half) ^ c3);
+    const T* vb1 = Vt + col * VS + 4 * ((2 + half) ^ c3);
 #pragma unroll
     for (int i = 0; i < DVT; ++i) {
-      const T* vrow = Vt + (i * 32 + col) * VS;
 #pragma unroll
       for (int si = 0; si < NSUB; ++si) {
         const int sub = KG == 2 ? kg : si;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const int kb = sub * 32 + 16 * ks + 4 * half;    // first of keys kb..kb+3, kb+8..kb+11
+          const int off = 32 * i * VS + 16 * ((2 * sub + ks) ^ i);
           Frag<T> vf;
           if constexpr (sizeof(T) == 2) {
-            const uint2 lo = *reinterpret_cast<const uint2*>(vrow + vt_block(i * 32 + col, kb / 4) * 4);
-            const uint2 hi = *reinterpret_cast<const uint2*>(vrow + vt_block(i * 32 + col, kb / 4 + 2) * 4);
+            const uint2 lo = *reinterpret_cast<const uint2*>(vb0 + off);
+            const uint2 hi = *reinterpret_cast<const uint2*>(vb1 + off);
             vf.v = u32x4{lo.x, lo.y, hi.x, hi.y};
           } else {
-            const f32x4 lo = *reinterpret_cast<const f32x4*>(vrow + vt_block(i * 32 + col, kb / 4) * 4);
-            const f32x4 hi = *reinterpret_cast<const f32x4*>(vrow + vt_block(i * 32 + col, kb / 4 + 2) * 4);
+            const f32x4 lo = *reinterpret_cast<const f32x4*>(vb0 + off);
+            const f32x4 hi = *reinterpret_cast<const f32x4*>(vb1 + off);
             float* fv = reinterpret_cast<float*>(&vf);
             fv[0] = lo[0]; fv[1] = lo[1]; fv[2] = lo[2]; fv[3] = lo[3];
             fv[4] = hi[0]; fv[5] = hi[1]; fv[6] = hi[2]; fv[7] = hi[3];

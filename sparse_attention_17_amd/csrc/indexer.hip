@@ -420,7 +420,9 @@ __global__ __launch_bounds__(256) void score_row_kernel(IndexerArgs a) {
       if (e < c1) {
         if constexpr (QK == QK_FP8) sc *= cscl[s];
         sc += 0.f;
-        srow[e] = sc;
+        // written once, read back only by a second pick round: streamed
+        // past the caches
+        __builtin_nontemporal_store(sc, srow + e);
         sk[e - c0] = __float_as_uint(sc);
         atomicAdd(&hist[__float_as_uint(sc) >> (32 - H1_BITS)], 1u);
       }
@@ -534,7 +536,7 @@ __global__ __launch_bounds__(256) void score_row_fp4_kernel(IndexerArgs a) {
     }
     if (e < c1) {
       sc += 0.f;
-      srow[e] = sc;
+      __builtin_nontemporal_store(sc, srow + e);
       sk[e - c0] = __float_as_uint(sc);
       atomicAdd(&hist[__float_as_uint(sc) >> (32 - H1_BITS)], 1u);
     }
