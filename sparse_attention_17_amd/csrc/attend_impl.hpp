@@ -828,9 +828,13 @@ static inline int keys_per_split(bool sparse, int Tq) {
   return sparse ? 128 : 256;
 }
 
-static inline int tokens_per_tile(bool sparse, int H, int Tq) {
+// Dense (HCA) prefill tiles of bf16 problems hold up to 256 (token, head)
+// rows, so that eight row-waves share every staged key tile (half the
+// staging work and LDS writes per MFMA of a 128-row tile); other tiles hold
+// up to 128 rows.
+static inline int tokens_per_tile(bool sparse, int H, int Tq, bool wide) {
   if (sparse) return 1;
-  return std::max(1, std::min(128 / H, Tq));
+  return std::max(1, std::min((wide ? 256 : 128) / H, Tq));
 }
 
 static inline int nkeys_upper(bool sparse, int topk, int window, int Nc_cap, int m_prime, int max_pos) {
@@ -841,7 +845,7 @@ static inline int nkeys_upper(bool sparse, int topk, int window, int Nc_cap, int
 
 static inline AttnGeom make_geom(const AttendArgs& a) {
   AttnGeom gm;
-  gm.TT = tokens_per_tile(a.sparse, a.H, a.Tq);
+  gm.TT = tokens_per_tile(a.sparse, a.H, a.Tq, !a.f32 && !a.kv8 && a.Tq > 1);
   const int kps = keys_per_split(a.sparse, a.Tq);
   const long nk = nkeys_upper(a.sparse, a.topk, a.window, a.Nc_cap, a.m_prime, a.max_pos);
   gm.nsplit = (int)std::max(1L, (nk + kps - 1) / kps);
@@ -856,7 +860,8 @@ static inline void wave_shape(int rows, int* RW, int* KG) {
   if (rows <= 32) { *RW = 1; *KG = 2; }
   else if (rows <= 64) { *RW = 2; *KG = 2; }
   else if (rows <= 96) { *RW = 3; *KG = 1; }
-  else { *RW = 4; *KG = 1; }
+  else if (rows <= 128) { *RW = 4; *KG = 1; }
+  else { *RW = 8; *KG = 1; }
 }
 
 static inline size_t partial_rows(const AttendArgs& a) { return (size_t)a.B * a.Tq * a.H; }
@@ -918,7 +923,10 @@ static hipError_t launch3(const AttendArgs& a, const AttnGeom& gm, const AttendL
   if (RW == 1) return launch4<T, D, 1, 2, SPARSE, KV8>(a, gm, how, st);
   if (RW == 2) return launch4<T, D, 2, 2, SPARSE, KV8>(a, gm, how, st);
   if (RW == 3) return launch4<T, D, 3, 1, SPARSE, KV8>(a, gm, how, st);
-  return launch4<T, D, 4, 1, SPARSE, KV8>(a, gm, how, st);
+  if (RW == 4) return launch4<T, D, 4, 1, SPARSE, KV8>(a, gm, how, st);
+  // 256-row tiles are formed only for dense bf16 prefill problems
+  if constexpr (!SPARSE && !KV8 && sizeof(T) == 2) return launch4<T, D, 8, 1, SPARSE, KV8>(a, gm, how, st);
+  return hipErrorInvalidValue;
 }
 
 // One attention problem (its kernel, and its split merge if asked).
