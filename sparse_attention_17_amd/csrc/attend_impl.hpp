@@ -491,8 +491,28 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
     float psum = 0.f;
     // P for the value dims; FP8 caches: P times the value row scale for the
     // code dims (pf), and, when values are the key rows, plain P for their
-    // bf16 RoPE dims (pr)
-    Frag<T> pf[NSUB][2], pr[VSH ? NSUB : 1][2];
+    // bf16 RoPE dims (pr).  A lane's 16 values of a 32-key sub-tile are keys
+    // 8 (r >> 2) + 4 half + (r & 3); fragment g of the sub-tile takes the
+    // 4-key runs r = 4g..4g+3 and 8+4g..8+4g+3 (keys 4 half + 8g and
+    // 16 + 4 half + 8g), which are the two V blocks one paired LDS read brings.
+    // For odd dv tiles the swizzle puts the ks = 1 block of a pair below the
+    // ks = 0 block, so those tiles take the pair in address order and the
+    // fragments in the matching order (pfs; plain caches only).
+    constexpr bool SWAPF = !KV8;
+    Frag<T> pf[NSUB][2], pr[VSH ? NSUB : 1][2], pfs[SWAPF ? NSUB : 1][2];
+    auto split_frags = [](Frag<T> (&f)[2], const float* x, bool swap) {
+      float a[8], c[8];
+      const int lo = swap ? 8 : 0, hi = swap ? 0 : 8;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        a[u] = x[lo + u];
+        a[4 + u] = x[hi + u];
+        c[u] = x[lo + 4 + u];
+        c[4 + u] = x[hi + 4 + u];
+      }
+      frag_from_f32(f[0], a);
+      frag_from_f32(f[1], c);
+    };
 #pragma unroll
     for (int si = 0; si < NSUB; ++si) {
       float pv[16];
@@ -506,15 +526,11 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
         lane_scales(VSH ? kscl : vscl, KG == 2 ? kg : si, vs);
 #pragma unroll
         for (int r = 0; r < 16; ++r) pw[r] = pv[r] * vs[r];
-        frag_from_f32(pf[si][0], pw);
-        frag_from_f32(pf[si][1], pw + 8);
-        if constexpr (VSH) {
-          frag_from_f32(pr[si][0], pv);
-          frag_from_f32(pr[si][1], pv + 8);
-        }
+        split_frags(pf[si], pw, false);
+        if constexpr (VSH) split_frags(pr[si], pv, false);
       } else {
-        frag_from_f32(pf[si][0], pv);
-        frag_from_f32(pf[si][1], pv + 8);
+        split_frags(pf[si], pv, false);
+        split_frags(pfs[si], pv, true);
       }
     }
     l_run += psum;
@@ -525,32 +541,36 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
     // 4i + (col >> 3), so the block position splits into a per-lane part
     // (bits 0-1: (2 hi + half) ^ (col >> 3)) and a part fixed by (i, sub, ks)
     // (bits 2-3: (2 sub + ks) ^ i): two base addresses per lane and
-    // immediate offsets address every read.
+    // immediate offsets address every read.  Fragment g pairs the blocks of
+    // ks = 0 and 1 read from base g, so each read pair fills its operand.
     const int c3 = col >> 3;
-    const T* vb0 = Vt + col * VS + 4 * ((half) ^ c3);
-    const T* vb1 = Vt + col * VS + 4 * ((2 + half) ^ c3);
+    const T* vb[2] = {Vt + col * VS + 4 * ((half) ^ c3), Vt + col * VS + 4 * ((2 + half) ^ c3)};
 #pragma unroll
     for (int i = 0; i < DVT; ++i) {
 #pragma unroll
       for (int si = 0; si < NSUB; ++si) {
         const int sub = KG == 2 ? kg : si;
+        const int off0 = 32 * i * VS + 16 * ((2 * sub) ^ i);
+        const int off1 = 32 * i * VS + 16 * ((2 * sub + 1) ^ i);
+        const bool sw = SWAPF && (i & 1);                  // compile-time after unrolling
+        const int oa = sw ? off1 : off0, oc = sw ? off0 : off1;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int off = 32 * i * VS + 16 * ((2 * sub + ks) ^ i);
+        for (int g = 0; g < 2; ++g) {
           Frag<T> vf;
           if constexpr (sizeof(T) == 2) {
-            const uint2 lo = *reinterpret_cast<const uint2*>(vb0 + off);
-            const uint2 hi = *reinterpret_cast<const uint2*>(vb1 + off);
-            vf.v = u32x4{lo.x, lo.y, hi.x, hi.y};
+            const uint2 a = *reinterpret_cast<const uint2*>(vb[g] + oa);
+            const uint2 c = *reinterpret_cast<const uint2*>(vb[g] + oc);
+            vf.v = u32x4{a.x, a.y, c.x, c.y};
           } else {
-            const f32x4 lo = *reinterpret_cast<const f32x4*>(vb0 + off);
-            const f32x4 hi = *reinterpret_cast<const f32x4*>(vb1 + off);
+            const f32x4 a = *reinterpret_cast<const f32x4*>(vb[g] + oa);
+            const f32x4 c = *reinterpret_cast<const f32x4*>(vb[g] + oc);
             float* fv = reinterpret_cast<float*>(&vf);
-            fv[0] = lo[0]; fv[1] = lo[1]; fv[2] = lo[2]; fv[3] = lo[3];
-            fv[4] = hi[0]; fv[5] = hi[1]; fv[6] = hi[2]; fv[7] = hi[3];
+            fv[0] = a[0]; fv[1] = a[1]; fv[2] = a[2]; fv[3] = a[3];
+            fv[4] = c[0]; fv[5] = c[1]; fv[6] = c[2]; fv[7] = c[3];
           }
-          if constexpr (VSH) mma32(o[i], vf, 32 * i >= DN ? pr[si][ks] : pf[si][ks]);
-          else mma32(o[i], vf, pf[si][ks]);
+          if constexpr (VSH) mma32(o[i], vf, 32 * i >= DN ? pr[si][g] : pf[si][g]);
+          else if constexpr (SWAPF) mma32(o[i], vf, sw ? pfs[si][g] : pf[si][g]);
+          else mma32(o[i], vf, pf[si][g]);
         }
       }
     }
