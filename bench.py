@@ -146,9 +146,9 @@ def pmc_summary(fetch_dir, write_dir):
            "copy_kib_read": [round(v, 1) for v in copy_f], "copy_kib_written": [round(v, 1) for v in copy_w],
            "sources_sha256": _sources_hash(),
            "commands": ["rocprofv3 --pmc FETCH_SIZE -d <FETCH_DIR> -o run --output-format csv -- "
-                        "python3 bench.py --copy-calibration --graph 0 --steps 5 --warmup 2 --no-cpu",
+                        "python3 bench.py --copy-calibration --graph 0 --steps 5 --warmup 2 --no-cpu --extra 0",
                         "rocprofv3 --pmc WRITE_SIZE -d <WRITE_DIR> -o run --output-format csv -- "
-                        "python3 bench.py --copy-calibration --graph 0 --steps 5 --warmup 2 --no-cpu",
+                        "python3 bench.py --copy-calibration --graph 0 --steps 5 --warmup 2 --no-cpu --extra 0",
                         "python3 bench.py --pmc-summary <FETCH_DIR> <WRITE_DIR>"]}
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as fh:
