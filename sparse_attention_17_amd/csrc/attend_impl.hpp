@@ -26,6 +26,7 @@
 
 #include <algorithm>
 #include <climits>
+#include <type_traits>
 
 namespace csa {
 
@@ -65,6 +66,9 @@ __device__ __forceinline__ int vt_block(int dim, int kb) { return kb ^ ((dim >> 
 // with device-scope (sc1) accesses, coherent across the XCDs' L2 caches, for
 // an index producer or a merge running in the same launch.
 static constexpr int COH_IDX = 1, COH_PART = 2;
+__host__ __device__ constexpr bool attend_double_buffered(bool sparse, bool kv8, int rw, int pf) {
+  return !sparse && !kv8 && rw == 8 && pf == 1;
+}
 template <typename T, int D, int RW, int KG, bool SPARSE, int PF, bool KV8 = false, bool VSH = false,
           int COH = 0>
 __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom& gm, int bx, int by,
@@ -86,6 +90,10 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
 
   T* Ks = reinterpret_cast<T*>(smem_raw);
   T* Vt = Ks + KT * KS;
+  // double-buffered key tiles (dense 256-row prefill tiles): the second
+  // buffer starts DBUF elements after the first
+  constexpr bool DB = attend_double_buffered(SPARSE, KV8, RW, PF);
+  constexpr int DBUF = KT * KS + D * VS;
   // FP8 caches: the row scales of the tile's keys (1 for window rows), applied
   // to the logits of the code half and to the probabilities, in fp32
   float* kscl = reinterpret_cast<float*>(Vt + D * VS);
@@ -589,6 +597,45 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
       tile(s0 + KT);
       __syncthreads();
     }
+  } else if constexpr (DB) {
+    // Two key-tile buffers: tile j is computed from buffer j & 1 while tile
+    // j + 1 is staged into the other, so one barrier per tile suffices (it
+    // publishes tile j + 1 and frees buffer j & 1 for tile j + 2).  The
+    // second half of the waves stages the next tile before computing, the
+    // first half after: each SIMD holds one wave of each half, so one wave's
+    // staging work runs beside the other's MFMAs.
+    T* const k0 = Ks;
+    T* const v0 = Vt;
+    const bool early = wave >= NW / 2;
+    if (kbeg < kend) {
+      stage_store(kregA, vregA, sclA, kbeg);
+      if (kbeg + KT < kend) stage_load(kregA, vregA, sclA, kbeg + KT);
+    }
+    __syncthreads();
+    // the loop is unrolled over the two buffers so that each half addresses
+    // its buffer with compile-time offsets
+    auto step = [&](int s0, auto buf) {
+      constexpr int cur = decltype(buf)::value;
+      auto stage_next = [&]() {
+        if (s0 + KT < kend) {
+          Ks = k0 + (cur ^ 1) * DBUF;
+          Vt = v0 + (cur ^ 1) * DBUF;
+          stage_store(kregA, vregA, sclA, s0 + KT);
+          if (s0 + 2 * KT < kend) stage_load(kregA, vregA, sclA, s0 + 2 * KT);
+        }
+      };
+      if (early) stage_next();
+      Ks = k0 + cur * DBUF;
+      Vt = v0 + cur * DBUF;
+      tile(s0);
+      if (!early) stage_next();
+      __syncthreads();
+    };
+    for (int s0 = kbeg; s0 < kend; s0 += 2 * KT) {
+      step(s0, std::integral_constant<int, 0>{});
+      if (s0 + KT >= kend) break;
+      step(s0 + KT, std::integral_constant<int, 1>{});
+    }
   } else {
     for (int s0 = kbeg; s0 < kend; s0 += KT) {
       stage_store(kregA, vregA, sclA, s0);
@@ -895,7 +942,9 @@ template <typename T, int D, bool SPARSE>
 static size_t attend_lds(const AttendArgs& a, int RW, int KG) {
   constexpr int KS = D + 16 / sizeof(T);
   constexpr int VS = KT + 4;
-  size_t lds = (size_t)(KT * KS + D * VS) * sizeof(T) + (SPARSE ? (size_t)a.topk * 4 : 0) +
+  // 256-row dense tiles are only formed for prefill (one split, one tile ahead)
+  const size_t bufs = attend_double_buffered(SPARSE, a.kv8, RW, 1) ? 2 : 1;
+  size_t lds = bufs * (KT * KS + D * VS) * sizeof(T) + (SPARSE ? (size_t)a.topk * 4 : 0) +
                (a.kv8 ? 2 * KT * sizeof(float) : 0);
   if (KG == 2) lds = std::max(lds, (size_t)RW * 64 * ((D / 32) * 16 + 2) * sizeof(float));
   return lds;
