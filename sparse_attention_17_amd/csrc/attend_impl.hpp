@@ -329,6 +329,34 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a, const AttnGeom&
         load_all([&](bool k, int s, int ch) { return ld(k ? rkw : rvw, win_off(s), ch); });
       else
         load_all([&](bool k, int s, int ch) { return comp8(k, s, ch) | ld(k ? rkw : rvw, win_off(s), ch); });
+    } else if (s0 + KT <= ncomp && s0 + KT <= kend) {
+      // every slot of the tile holds a compressed entry of this split: row
+      // offsets straight from the entry (sparse: from the index list, an
+      // invalid entry giving an out-of-range offset, read as zeros and masked
+      // in the softmax), without the per-slot range checks
+      auto eoff = [&](int e) -> uint32_t { return (e >= 0 && e < a.Nc_cap) ? (uint32_t)e * ROWB : OOB; };
+#pragma unroll
+      for (int i = 0; i < KLD; ++i) {
+        const int c = tid + i * NT;
+        const int s = s0 + krow(c);
+        int e = s;
+        if constexpr (SPARSE) e = c < KT * KCH ? sel[s - sel_base] : -1;
+        kreg[i] = ld(rkc, c < KT * KCH ? eoff(e) : OOB, kch(c));
+      }
+#pragma unroll
+      for (int i = 0; i < VTK; ++i) {
+        const int c = tid + i * NT;
+        const int s = s0 + (c / KCH) * 4;                    // four consecutive slots
+        int e4[4] = {s, s + 1, s + 2, s + 3};
+        if constexpr (SPARSE) {
+          if (c < VTOT) {
+            const int4 v = *reinterpret_cast<const int4*>(sel + (s - sel_base));
+            e4[0] = v.x; e4[1] = v.y; e4[2] = v.z; e4[3] = v.w;
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) vreg[i][u] = ld(rvc, c < VTOT ? eoff(e4[u]) : OOB, c % KCH);
+      }
     } else if (s0 + KT <= ncomp || nwin == 0) {
       load_all([&](bool k, int s, int ch) { return ld(k ? rkc : rvc, comp_off(s), ch); });
     } else if (s0 >= ncomp) {
