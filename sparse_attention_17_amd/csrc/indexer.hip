@@ -800,14 +800,16 @@ __global__ __launch_bounds__(FNT, 4) void fused_prefill_kernel(IndexerArgs a) {
   // (< ne_max); f(u, e, score, valid, e0) is called for each ballot unit,
   // valid = the entry is eligible for the lane's token (checked only in the
   // steps that reach past the shortest row).  All MFMAs of an entry tile
-  // issue before the epilogue reads them.  Three key buffers rotate: each is
-  // reloaded right after its step has read it, so two steps of loads are in
-  // flight during each step's compute (the keys come from L2), and no
+  // issue before the epilogue reads them.  Two key buffers rotate: each is
+  // reloaded right after its step has read it, so the next step's loads are
+  // in flight during each step's compute (the keys come from L2), and no
   // in-flight load result is ever copied between registers (a copy would
-  // have to wait for it).
+  // have to wait for it).  A third buffer pushed the kernel past its 128
+  // registers: its spill reloads, which share the vector-memory counter with
+  // the key loads, then waited for every prefetch in flight.
   auto pass = [&](int first, int stride, auto&& f) {
-    RawFrag<QK> kb0[KC], kb1[KC], kb2[KC];
-    float ks0 = 1.f, ks1 = 1.f, ks2 = 1.f;
+    RawFrag<QK> kb0[KC], kb1[KC];
+    float ks0 = 1.f, ks1 = 1.f;
     // Loads are issued unconditionally (clamped to the last eligible entry):
     // with a fixed number of loads per step the compiler's wait counts stay
     // exact across the loop's back edge.
@@ -853,17 +855,13 @@ __global__ __launch_bounds__(FNT, 4) void fused_prefill_kernel(IndexerArgs a) {
     if (first >= ne_max) return;                               // uniform; also ne_max >= 1 below
     load(kb0, ks0, first);
     load(kb1, ks1, first + stride);
-    load(kb2, ks2, first + 2 * stride);
 #pragma unroll 1
-    for (int e0 = first; e0 < ne_max; e0 += 3 * stride) {
+    for (int e0 = first; e0 < ne_max; e0 += 2 * stride) {
       run(e0, kb0, ks0);
-      load(kb0, ks0, e0 + 3 * stride);
+      load(kb0, ks0, e0 + 2 * stride);
       if (e0 + stride >= ne_max) break;                       // uniform
       run(e0 + stride, kb1, ks1);
-      load(kb1, ks1, e0 + 4 * stride);
-      if (e0 + 2 * stride >= ne_max) break;
-      run(e0 + 2 * stride, kb2, ks2);
-      load(kb2, ks2, e0 + 5 * stride);
+      load(kb1, ks1, e0 + 3 * stride);
     }
   };
 
