@@ -1005,9 +1005,12 @@ static hipError_t launch5(const AttendArgs& a, const AttnGeom& gm, const AttendL
 template <typename T, int D, int RW, int KG, bool SPARSE, bool KV8>
 static hipError_t launch4(const AttendArgs& a, const AttnGeom& gm, const AttendLaunch& how, hipStream_t st) {
   if constexpr (KV8) {
+    // FP8 caches keep one tile in flight ahead also in split decode: with two
+    // the staging registers pushed the kernel past 256 registers, and its
+    // spill reloads waited for every load in flight
     if (a.v8 == nullptr)                     // values are the key rows
-      return gm.nsplit > 1 ? launch5<T, D, RW, KG, SPARSE, 2, true, true>(a, gm, how, st)
-                           : launch5<T, D, RW, KG, SPARSE, 1, true, true>(a, gm, how, st);
+      return launch5<T, D, RW, KG, SPARSE, 1, true, true>(a, gm, how, st);
+    return launch5<T, D, RW, KG, SPARSE, 1, true, false>(a, gm, how, st);
   }
   return gm.nsplit > 1 ? launch5<T, D, RW, KG, SPARSE, 2, KV8, false>(a, gm, how, st)
                        : launch5<T, D, RW, KG, SPARSE, 1, KV8, false>(a, gm, how, st);
