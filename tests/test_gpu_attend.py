@@ -111,3 +111,14 @@ def test_full_topk_equals_dense_attention():
                        kw=g["k"], vw=g["v"], raw_pos0=pos0)
     torch.cuda.synchronize()
     assert_close(a, f64(h), "f32", "csa(k>=n_e) vs dense")
+    # and both against the oracle's dense attention over every eligible
+    # entry + window + sink, on the GPU's compressed caches
+    kc_, vc_ = f64(kc[0]), f64(vc[0])
+    T = w.ctx
+    full = np.full((T, kc_.shape[0]), -1, dtype=np.int32)
+    for t in range(T):
+        ne = oracle.csa.n_eligible(t, w.m)
+        full[t, :ne] = np.arange(ne)
+    ref, _ = oracle.csa.sparse_attend(f64(x["q"][0]), kc_, vc_, full, f64(x["k"][0]), f64(x["v"][0]), 0,
+                                      np.arange(T), w.window, f64(x["sink"]), w.scale)
+    assert_close(a[0], ref, "f32", "csa(k>=n_e) vs oracle dense")
