@@ -58,8 +58,11 @@ __device__ __forceinline__ int vt_block(int dim, int kb) { return kb ^ ((dim >> 
 // takes one 32-key half of every 64-key tile; the two partial softmax states
 // are merged in LDS at the end).  PF key tiles are in flight ahead of the one
 // being computed (PF=2 for split decode: a 128-key CSA split is then requested
-// at once).  Every instance fits 256 VGPRs, two waves per SIMD, so two
-// workgroups share a compute unit and one's loads overlap the other's math.
+// at once; FP8 caches keep one tile ahead).  Every instance fits 256 VGPRs,
+// two waves per SIMD: two four-wave workgroups share a compute unit and one's
+// loads overlap the other's math, or one eight-wave workgroup (256-row dense
+// prefill tiles) holds it, its two halves staggered by the double-buffered
+// key tiles.
 // The body takes its workgroup's coordinates (token tile bx, split by,
 // sequence bz) and the dynamic LDS block from the kernel that runs it.  COH
 // (bit mask): COH_IDX reads the index row, COH_PART writes the split partials
@@ -950,7 +953,8 @@ static inline AttnGeom make_geom(const AttendArgs& a) {
 }
 
 // Row-waves cover the tile's (token, head) rows; tiles of at most 64 rows get
-// a second key group so that four waves share every staged tile.
+// a second key group so that four waves share every staged tile; 256-row
+// tiles (dense bf16 prefill) take eight row-waves.
 static inline void wave_shape(int rows, int* RW, int* KG) {
   if (rows <= 32) { *RW = 1; *KG = 2; }
   else if (rows <= 64) { *RW = 2; *KG = 2; }
