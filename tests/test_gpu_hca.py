@@ -93,3 +93,30 @@ def test_window_and_empty_key_sets():
                                        np.arange(w.ctx), f64(x["sink_hca"]) if sink else None,
                                        w.scale, f64(x["k"][0]), f64(x["v"][0]), 0, win)
         assert_close(out[0], ro, "f32", f"win={win} sink={sink}", lse[0], rl)
+
+
+@pytest.mark.parametrize("H,Tq,d,window", [(64, 1001, 128, 0), (48, 130, 128, 16), (64, 77, 64, 16)])
+def test_dense_prefill_wide_tiles_edges(H, Tq, d, window):
+    # bf16 prefill tiles of up to 256 (token, head) rows with double-buffered
+    # key tiles: a ragged last token tile, key counts growing with the token
+    # (odd and even numbers of 64-key tiles, a partial last tile, early tokens
+    # with no completed block), rows left over when H does not divide 256,
+    # and a window branch; every query against the oracle
+    mp, ctx = 8, Tq
+    n = ctx // mp
+    wid = 60 + H + d
+    q = inputs.to_dtype(inputs.normal(wid, "q", (1, Tq, H, d)) * 4, "bf16")
+    kc = inputs.to_dtype(inputs.normal(wid, "kc", (1, n, d)), "bf16")
+    vc = inputs.to_dtype(inputs.normal(wid, "vc", (1, n, d)), "bf16")
+    kw = inputs.to_dtype(inputs.normal(wid, "kw", (1, ctx, d)), "bf16")
+    vw = inputs.to_dtype(inputs.normal(wid, "vw", (1, ctx, d)), "bf16")
+    sink = inputs.normal(wid, "sink", (H,), scaled_by_last=False)
+    pos0 = torch.zeros(1, dtype=torch.int32, device=dev())
+    out, lse = ops.hca_attend(q.to(dev()), kc.to(dev()), vc.to(dev()), mp, pos0, ctx - 1,
+                              sink=sink.to(dev()), window=window,
+                              kw=kw.to(dev()) if window else None, vw=vw.to(dev()) if window else None,
+                              raw_pos0=pos0 if window else None, return_lse=True)
+    torch.cuda.synchronize()
+    ro, rl = oracle.hca.hca_attend(f64(q[0]), f64(kc[0]), f64(vc[0]), mp, np.arange(Tq), f64(sink),
+                                   d ** -0.5, f64(kw[0]), f64(vw[0]), 0, window)
+    assert_close(out[0], ro, "bf16", f"wide-tile prefill H={H} Tq={Tq} d={d} W={window}", lse[0], rl)
