@@ -23,8 +23,8 @@ extern template hipError_t combine_pair_variant<bf16, 128>(const AttendArgs&, co
 
 size_t attend_workspace(bool sparse, int B, int Tq, int H, int d, int topk, int window,
                         int Nc_cap, int m_prime, int max_pos) {
-  const int kps = keys_per_split(sparse, Tq);
   const long nk = nkeys_upper(sparse, topk, window, Nc_cap, m_prime, max_pos);
+  const int kps = keys_per_split(sparse, Tq, nk);
   const long ns = std::max(1L, (nk + kps - 1) / kps);
   if (ns <= 1) return 0;
   return (size_t)ns * B * Tq * H * (d + 2) * sizeof(float);

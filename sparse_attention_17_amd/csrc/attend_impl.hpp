@@ -921,9 +921,15 @@ __global__ __launch_bounds__(256) void combine_pair_kernel(AttendArgs a0, int ns
 // ------------------------- host launch templates ---------------------------
 // Instantiated per (element type, head dim, cache format) in the attend_v_*.hip
 // translation units; attend.hip dispatches to them.
-static inline int keys_per_split(bool sparse, int Tq) {
+// Keys per split of a one-token (decode) problem, from the key count only (so
+// results never depend on the batch): dense 256; sparse 192 for lists of up
+// to 1536 keys (a top-1024 list + window in 6 splits: fewer workgroups and
+// partials), 128 beyond (a top-2048 list + window in 17 two-tile splits,
+// which stay shorter than the dense problem's in a layer pair's launch).
+static inline int keys_per_split(bool sparse, int Tq, long nk) {
   if (Tq != 1) return INT_MAX / 2;
-  return sparse ? 128 : 256;
+  if (!sparse) return 256;
+  return nk <= 1536 ? 192 : 128;
 }
 
 // Dense (HCA) prefill tiles of bf16 problems hold up to 256 (token, head)
@@ -944,8 +950,8 @@ static inline int nkeys_upper(bool sparse, int topk, int window, int Nc_cap, int
 static inline AttnGeom make_geom(const AttendArgs& a) {
   AttnGeom gm;
   gm.TT = tokens_per_tile(a.sparse, a.H, a.Tq, !a.f32 && !a.kv8 && a.Tq > 1);
-  const int kps = keys_per_split(a.sparse, a.Tq);
   const long nk = nkeys_upper(a.sparse, a.topk, a.window, a.Nc_cap, a.m_prime, a.max_pos);
+  const int kps = keys_per_split(a.sparse, a.Tq, nk);
   gm.nsplit = (int)std::max(1L, (nk + kps - 1) / kps);
   gm.kps = gm.nsplit > 1 ? kps : INT_MAX / 2;
   gm.scale_log2 = a.scale * LOG2E;
