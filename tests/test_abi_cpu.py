@@ -98,7 +98,7 @@ def test_indexer_validation(lib):
 
 
 def _sparse(lib, **kw):
-    a = dict(q=FAKE, kc=FAKE, vc=FAKE, idx=FAKE, topk=64, kw=FAKE, vw=FAKE, raw_pos0=FAKE, R=128,
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, idx=FAKE, topk=256, kw=FAKE, vw=FAKE, raw_pos0=FAKE, R=128,
              pos0=FAKE, max_pos=4095, window=128, sink=None, scale=C.c_float(0.1), B=2, Tq=1,
              H=64, d=128, Nc_cap=1024, dt=L.BF16, out=FAKE, lse=None, ws=None, ws_bytes=0,
              stream=None)
@@ -117,7 +117,7 @@ def test_sparse_attend_validation(lib):
     assert _sparse(lib, max_pos=-5) == L.INVALID_ARGUMENT
     assert _sparse(lib, scale=C.c_float(0.0)) == L.INVALID_ARGUMENT      # the scale must be > 0
     assert _sparse(lib, scale=C.c_float(-0.1)) == L.INVALID_ARGUMENT
-    need = lib.csa_sparse_attend_workspace(2, 1, 64, 128, 64, 128)
+    need = lib.csa_sparse_attend_workspace(2, 1, 64, 128, 256, 128)
     assert need > 0                                          # one decode token: split-KV partials
     assert _sparse(lib, ws=FAKE, ws_bytes=need - 1) == L.WORKSPACE_TOO_SMALL
     assert lib.csa_sparse_attend_workspace(1, 4096, 64, 128, 512, 128) == 0   # prefill: no split
@@ -147,7 +147,7 @@ WS_C, WS_H = 0x10000000, 0x20000000    # separate fake workspaces
 
 
 def _hybrid(lib, csa=None, hca=None):
-    c = dict(q=FAKE, kc=FAKE, vc=FAKE, idx=FAKE, topk=64, kw=FAKE, vw=FAKE, raw_pos0=FAKE, R=128,
+    c = dict(q=FAKE, kc=FAKE, vc=FAKE, idx=FAKE, topk=256, kw=FAKE, vw=FAKE, raw_pos0=FAKE, R=128,
              pos0=FAKE, max_pos=4095, window=128, sink=None, scale=C.c_float(0.1), B=2, Tq=1,
              H=64, d=128, Nc_cap=1024, dt=L.BF16, out=FAKE, lse=None, ws=WS_C, ws_bytes=1 << 26)
     h = dict(q=FAKE, kc=FAKE, vc=FAKE, m_prime=128, Nc_cap=8192, kw=None, vw=None, raw_pos0=None,
@@ -167,7 +167,7 @@ def test_hybrid_attend_validation(lib):
     assert lib.csa_last_error().startswith(b"HCA part: m_prime")
     assert _hybrid(lib, hca=dict(d=96)) == L.UNSUPPORTED
     assert _hybrid(lib, csa=dict(scale=C.c_float(0.0))) == L.INVALID_ARGUMENT
-    cn = lib.csa_sparse_attend_workspace(2, 1, 64, 128, 64, 128)
+    cn = lib.csa_sparse_attend_workspace(2, 1, 64, 128, 256, 128)
     hn = lib.hca_attend_workspace(16, 1, 64, 128, 8192, 128, 0)
     assert _hybrid(lib, csa=dict(ws_bytes=cn - 1)) == L.WORKSPACE_TOO_SMALL
     assert lib.csa_last_error().startswith(b"CSA part")
